@@ -1,0 +1,298 @@
+"""CPU oracle of the DeepSeekMoE layer forward -- TEST INFRASTRUCTURE.
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (``libmoe.so`` and
+``sparse_mixture_experts_51_amd``) never imports, links or calls it.
+
+The arithmetic lives in ``moe_oracle.c`` (plain loops, fp64 except where the
+definition fixes fp32); this module only builds it with gcc and marshals
+numpy arrays through ctypes.  Functions mirror the library's five calls with
+the prefix ``oracle_`` plus the dense, masked evaluation used as a
+brute-force cross-check.
+
+Parity pins (tests/test_oracle_pins.py) tie every function here to something
+other than itself: hand-worked values, closed forms, brute force on tiny
+inputs and library routines on special cases.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB = os.path.join(_HERE, "libmoe_oracle.so")
+
+# -mfma only inlines fmaf(); results are identical with or without it.
+_CFLAGS = ["-O2", "-std=c11", "-mfma", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
+           "-shared", "-Wall", "-Wextra", "-Wno-unused-parameter"]
+
+
+def build(force: bool = True) -> str:
+    """Compile moe_oracle.c into libmoe_oracle.so with gcc."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.run(["gcc", *_CFLAGS, "-o", tmp, _SRC, "-lm", "-lpthread"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        build(force=False)
+        _lib = ctypes.CDLL(_LIB)
+        _declare(_lib)
+    return _lib
+
+
+P = ctypes.c_void_p
+I64 = ctypes.c_int64
+I32 = ctypes.c_int
+
+
+def _declare(L):
+    L.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
+    L.oracle_f32_to_bf16.restype = ctypes.c_uint16
+    L.oracle_f64_to_bf16.argtypes = [ctypes.c_double]
+    L.oracle_f64_to_bf16.restype = ctypes.c_uint16
+    L.oracle_sigmoid.argtypes = [ctypes.c_float]
+    L.oracle_sigmoid.restype = ctypes.c_float
+    L.oracle_route.argtypes = [I64, I32, I32, I32, P, P, P, P, P, P, P, I32]
+    L.oracle_route.restype = None
+    L.oracle_logits.argtypes = [I64, I32, I32, P, P, P]
+    L.oracle_logits.restype = None
+    L.oracle_select.argtypes = [I64, I32, I32, P, P]
+    L.oracle_select.restype = None
+    L.oracle_seq_balance.argtypes = [I64, I32, I32, I32, P, P, ctypes.c_double, P]
+    L.oracle_seq_balance.restype = None
+    L.oracle_permute.argtypes = [I64, I32, I32, P, P, P, P, P]
+    L.oracle_permute.restype = None
+    L.oracle_expert_ffn.argtypes = [I32, I32, P, P, P, P, P]
+    L.oracle_expert_ffn.restype = None
+    L.oracle_grouped_ffn.argtypes = [I64, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P, P,
+                                     P, P, I32]
+    L.oracle_grouped_ffn.restype = None
+    L.oracle_combine.argtypes = [I64, I32, I32, I32, P, P, P, P, P, P, P]
+    L.oracle_combine.restype = None
+    L.oracle_dense_masked.argtypes = [I64, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P, P,
+                                      P, P, I32]
+    L.oracle_dense_masked.restype = None
+    L.oracle_update_bias.argtypes = [I64, I32, I32, P, P, ctypes.c_float]
+    L.oracle_update_bias.restype = None
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _c(a: np.ndarray, dtype) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.dtype(dtype):
+        if np.dtype(dtype) == np.uint16 and a.dtype == np.int16:
+            a = a.view(np.uint16)
+        else:
+            a = a.astype(dtype)
+    return a
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def as_bf16_bits(t) -> np.ndarray:
+    """torch bf16 tensor (any device) or uint16 array -> uint16 numpy bits."""
+    if isinstance(t, np.ndarray):
+        return _c(t, np.uint16)
+    import torch
+    assert t.dtype == torch.bfloat16
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def f32_to_bf16(v: float) -> int:
+    return int(lib().oracle_f32_to_bf16(float(v)))
+
+
+def f64_to_bf16(v: float) -> int:
+    return int(lib().oracle_f64_to_bf16(float(v)))
+
+
+def sigmoid(logit: float) -> float:
+    return float(lib().oracle_sigmoid(float(logit)))
+
+
+def logits(x_bits, w_router) -> np.ndarray:
+    x = _c(x_bits, np.uint16)
+    w = _c(w_router, np.float32)
+    T, d = x.shape
+    E = w.shape[1]
+    out = np.empty((T, E), np.float32)
+    lib().oracle_logits(T, d, E, _p(x), _p(w), _p(out))
+    return out
+
+
+def select(keys, k: int) -> np.ndarray:
+    keys = _c(keys, np.float32)
+    T, E = keys.shape
+    idx = np.empty((T, k), np.int32)
+    lib().oracle_select(T, E, k, _p(keys), _p(idx))
+    return idx
+
+
+def route(x_bits, w_router, bias, k: int, nthreads: int | None = None) -> dict:
+    """Steps a1-a4.  Returns idx [T,k], gate [T,k], margin [T], scores [T,E]."""
+    x = _c(x_bits, np.uint16)
+    w = _c(w_router, np.float32)
+    b = _c(bias, np.float32)
+    T, d = x.shape
+    E = w.shape[1]
+    idx = np.empty((T, k), np.int32)
+    gate = np.empty((T, k), np.float32)
+    margin = np.empty((T,), np.float32)
+    scores = np.empty((T, E), np.float32)
+    lib().oracle_route(T, d, E, k, _p(x), _p(w), _p(b), _p(idx), _p(gate), _p(margin),
+                       _p(scores), nthreads or default_threads())
+    return {"idx": idx, "gate": gate, "margin": margin, "scores": scores}
+
+
+def seq_balance(scores, idx, seq_len: int, alpha: float = 1e-4) -> np.ndarray:
+    """Step a5: per-sequence balance statistic L_b, fp64."""
+    s = _c(scores, np.float32)
+    ix = _c(idx, np.int32)
+    T, E = s.shape
+    k = ix.shape[1]
+    out = np.empty((T // seq_len,), np.float64)
+    lib().oracle_seq_balance(T, E, k, seq_len, _p(s), _p(ix), float(alpha), _p(out))
+    return out
+
+
+def permute(idx, E: int) -> dict:
+    """Steps a6-a7: counts, offsets, perm_src, pos."""
+    ix = _c(idx, np.int32)
+    T, k = ix.shape
+    counts = np.empty((E,), np.int32)
+    offsets = np.empty((E + 1,), np.int32)
+    perm_src = np.empty((T * k,), np.int32)
+    pos = np.empty((T, k), np.int32)
+    lib().oracle_permute(T, E, k, _p(ix), _p(counts), _p(offsets), _p(perm_src), _p(pos))
+    return {"counts": counts, "offsets": offsets, "perm_src": perm_src, "pos": pos}
+
+
+def expert_ffn(x_row_bits, w1, w3, w2) -> np.ndarray:
+    """One expert on one token row -> y bf16 bits [d]."""
+    x = _c(x_row_bits, np.uint16)
+    w1 = _c(w1, np.uint16)
+    w3 = _c(w3, np.uint16)
+    w2 = _c(w2, np.uint16)
+    H, d = w1.shape
+    y = np.empty((d,), np.uint16)
+    lib().oracle_expert_ffn(d, H, _p(x), _p(w1), _p(w3), _p(w2), _p(y))
+    return y
+
+
+def grouped_ffn(x_bits, perm_src, offsets, w1, w3, w2, ws1=None, ws3=None, ws2=None,
+                nthreads: int | None = None) -> dict:
+    """Steps a8-a9 over the expert groups plus the shared expert."""
+    x = _c(x_bits, np.uint16)
+    ps = _c(perm_src, np.int32)
+    off = _c(offsets, np.int32)
+    w1 = _c(w1, np.uint16)
+    w3 = _c(w3, np.uint16)
+    w2 = _c(w2, np.uint16)
+    T, d = x.shape
+    E, H, _ = w1.shape
+    k = ps.shape[0] // T if T else 0
+    has_shared = ws1 is not None
+    if has_shared:
+        ws1 = _c(ws1, np.uint16)
+        ws3 = _c(ws3, np.uint16)
+        ws2 = _c(ws2, np.uint16)
+    Hs = ws1.shape[0] if has_shared else 0
+    y_perm = np.empty((T * k, d), np.uint16)
+    y_shared = np.empty((T, d), np.uint16) if has_shared else None
+    lib().oracle_grouped_ffn(T, d, E, k, H, Hs, _p(x), _p(ps), _p(off), _p(w1), _p(w3), _p(w2),
+                             _p(ws1), _p(ws3), _p(ws2), _p(y_perm), _p(y_shared),
+                             nthreads or default_threads())
+    return {"y_perm": y_perm, "y_shared": y_shared}
+
+
+def combine(y_perm, y_shared, gate, idx, pos, residual=None) -> np.ndarray:
+    """Step a10."""
+    yp = _c(y_perm, np.uint16)
+    ys = None if y_shared is None else _c(y_shared, np.uint16)
+    g = _c(gate, np.float32)
+    ix = _c(idx, np.int32)
+    ps = _c(pos, np.int32)
+    res = None if residual is None else _c(residual, np.uint16)
+    T, k = ix.shape
+    d = yp.shape[1]
+    E = int(ix.max()) + 1 if ix.size else 1
+    out = np.empty((T, d), np.uint16)
+    lib().oracle_combine(T, d, E, k, _p(yp), _p(ys), _p(g), _p(ix), _p(ps), _p(res), _p(out))
+    return out
+
+
+def dense_masked(x_bits, gate, idx, w1, w3, w2, ws1=None, ws3=None, ws2=None, residual=None,
+                 nthreads: int | None = None) -> np.ndarray:
+    """Every expert on every token, unchosen experts weighted by zero."""
+    x = _c(x_bits, np.uint16)
+    g = _c(gate, np.float32)
+    ix = _c(idx, np.int32)
+    w1 = _c(w1, np.uint16)
+    w3 = _c(w3, np.uint16)
+    w2 = _c(w2, np.uint16)
+    T, d = x.shape
+    E, H, _ = w1.shape
+    k = ix.shape[1]
+    has_shared = ws1 is not None
+    if has_shared:
+        ws1 = _c(ws1, np.uint16)
+        ws3 = _c(ws3, np.uint16)
+        ws2 = _c(ws2, np.uint16)
+    Hs = ws1.shape[0] if has_shared else 0
+    res = None if residual is None else _c(residual, np.uint16)
+    out = np.empty((T, d), np.uint16)
+    lib().oracle_dense_masked(T, d, E, k, H, Hs, _p(x), _p(g), _p(ix), _p(w1), _p(w3), _p(w2),
+                              _p(ws1), _p(ws3), _p(ws2), _p(res), _p(out),
+                              nthreads or default_threads())
+    return out
+
+
+def update_bias(counts, bias, T: int, k: int, gamma: float = 1e-3) -> np.ndarray:
+    """Step a11; returns the updated bias (input left untouched)."""
+    c = _c(counts, np.int32)
+    b = np.array(bias, dtype=np.float32, copy=True)
+    lib().oracle_update_bias(T, b.shape[0], k, _p(c), _p(b), ctypes.c_float(gamma))
+    return b
+
+
+def layer(x_bits, params: dict, k: int, seq_len: int = 0, alpha: float = 1e-4,
+          residual=None, nthreads: int | None = None) -> dict:
+    """The five steps in order for one layer (composition of the calls above)."""
+    r = route(x_bits, params["w_router"], params["bias"], k, nthreads)
+    E = params["w_router"].shape[1]
+    pm = permute(r["idx"], E)
+    f = grouped_ffn(x_bits, pm["perm_src"], pm["offsets"], params["w1"], params["w3"],
+                    params["w2"], params.get("ws1"), params.get("ws3"), params.get("ws2"),
+                    nthreads)
+    out = combine(f["y_perm"], f["y_shared"], r["gate"], r["idx"], pm["pos"], residual)
+    res = dict(r)
+    res.update(pm)
+    res.update(f)
+    res["out"] = out
+    if seq_len:
+        res["seq_balance"] = seq_balance(r["scores"], r["idx"], seq_len, alpha)
+    return res

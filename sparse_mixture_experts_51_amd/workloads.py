@@ -1,0 +1,206 @@
+"""Seeded synthetic inputs for the DeepSeekMoE layer forward.
+
+This module only *draws* tensors: token activations, router weights, the
+per-expert balancing bias and the expert weights, for five named workloads
+and for ad-hoc test shapes.  It holds none of the layer's arithmetic.  Both
+the HIP path and the CPU oracle receive their inputs from here, so that the
+two sides never share anything but the data they are compared on.
+
+Workload shapes follow the pages:
+  * the mini model: 16 routed experts, top-4, one always-on shared expert
+    (190行JAX复刻DeepSeek V3, section 190行代码到底装进了什么; DeepSeek V3 viết
+    lại bằng 190 dòng JAX thuần, section Những gì có trong 190 dòng code);
+    training batches of 256-token sequences (same page, comparison table in
+    先说结论);
+  * the official DeepSeek-V3 shape: 256 routed experts, 8 per token, one
+    shared expert (190行JAX复刻DeepSeek V3, comparison table in 先说结论).
+Sizes that the pages leave open (d_model, hidden sizes, value
+distributions) are fixed here and listed with their reasons in the design
+notes.
+
+Seeds: seed = 51000 + 100*cfg + 10*layer + role + 1000*(expert+1)
+             + 10_000_000*step
+where role is one of the ROLE_* constants and expert is -1 for tensors that
+are not per-expert.  Every expert is drawn from its own generator, so any
+single expert can be regenerated alone.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import torch
+
+ROLE_X = 0
+ROLE_ROUTER = 1
+ROLE_BIAS = 2
+ROLE_W1 = 3
+ROLE_W3 = 4
+ROLE_W2 = 5
+ROLE_WS1 = 6
+ROLE_WS3 = 7
+ROLE_WS2 = 8
+ROLE_IMBALANCE = 9
+
+
+def seed_of(cfg: int, layer: int, role: int, expert: int = -1, step: int = 0) -> int:
+    return 51000 + 100 * cfg + 10 * layer + role + 1000 * (expert + 1) + 10_000_000 * step
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    cfg_id: int          # seed namespace of the activations
+    weight_cfg_id: int   # seed namespace of the weights (decode reuses prefill's)
+    tokens: int
+    seq_len: int         # 0: no sequence structure (balance statistic off)
+    d_model: int
+    n_experts: int
+    top_k: int
+    hidden: int
+    shared_hidden: int   # 0: no shared expert
+    layers: int
+    steps: int
+    x_std: float
+    w_std: float
+    router_std: float
+    bias_kind: str       # "zero" or "uniform"
+    bias_range: float
+    imbalance: float     # 0: none; else half-width c of the per-expert logit offsets
+    description: str = ""
+
+    @property
+    def rows(self) -> int:
+        """Routed rows T*k plus shared rows T."""
+        return self.tokens * self.top_k + (self.tokens if self.shared_hidden else 0)
+
+
+WORKLOADS = {
+    "mini_2048": Workload(
+        "mini_2048", 1, 1, 2048, 256, 384, 16, 4, 256, 256, 1, 1,
+        1.0, 0.02, 0.02, "zero", 0.0, 0.0,
+        "mini DeepSeekMoE layer, 8 seqs x 256 tokens, bias 0"),
+    "mini_train_8192x6": Workload(
+        "mini_train_8192x6", 2, 2, 8192, 256, 384, 16, 4, 256, 256, 6, 10,
+        1.0, 0.02, 0.02, "uniform", 0.05, 0.0,
+        "mini-model training batch, 32 seqs x 256 tokens, 6 stacked layers"),
+    "mini_imbalanced_8192": Workload(
+        "mini_imbalanced_8192", 3, 3, 8192, 256, 384, 16, 4, 256, 256, 1, 200,
+        1.0, 0.02, 0.02, "zero", 0.0, 0.7,
+        "imbalanced routing stress: per-expert logit offsets, 200 bias steps"),
+    "v3_prefill_4096": Workload(
+        "v3_prefill_4096", 4, 4, 4096, 4096, 7168, 256, 8, 2048, 2048, 1, 1,
+        1.0, 0.006, 0.006, "uniform", 0.01, 0.0,
+        "DeepSeek-V3-shaped prefill layer, one 4096-token sequence"),
+    "v3_decode_64": Workload(
+        "v3_decode_64", 5, 4, 64, 0, 7168, 256, 8, 2048, 2048, 1, 1,
+        1.0, 0.006, 0.006, "uniform", 0.01, 0.0,
+        "DeepSeek-V3-shaped decode step, 64 independent tokens"),
+}
+
+DEFAULT_BENCH_WORKLOAD = "mini_train_8192x6"
+
+
+def _gen(device, seed: int) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def normal(shape, std: float, seed: int, device="cpu", dtype=torch.float32) -> torch.Tensor:
+    """N(0, std^2) draws in fp32, then cast (bf16 casts round to nearest even)."""
+    g = _gen(device, seed)
+    t = torch.randn(*shape, generator=g, device=device, dtype=torch.float32)
+    if std != 1.0:
+        t.mul_(std)
+    return t.to(dtype)
+
+
+def uniform(shape, lo: float, hi: float, seed: int, device="cpu") -> torch.Tensor:
+    g = _gen(device, seed)
+    t = torch.rand(*shape, generator=g, device=device, dtype=torch.float32)
+    return t.mul_(hi - lo).add_(lo)
+
+
+def tokens(wl: Workload, step: int = 0, device="cpu", layer: int = 0) -> torch.Tensor:
+    """x[T, d] bf16.  The imbalance workload pins channel d-1 to 1.0 so that the
+    router's last row acts as a per-expert logit offset."""
+    x = normal((wl.tokens, wl.d_model), wl.x_std,
+               seed_of(wl.cfg_id, layer, ROLE_X, step=step), device, torch.bfloat16)
+    if wl.imbalance:
+        x[:, wl.d_model - 1] = 1.0
+    return x
+
+
+def router(wl: Workload, layer: int = 0, device="cpu") -> torch.Tensor:
+    """W_r[d, E] fp32; with imbalance, row d-1 holds a seeded permutation of
+    linspace(-c, c, E)."""
+    w = normal((wl.d_model, wl.n_experts), wl.router_std,
+               seed_of(wl.weight_cfg_id, layer, ROLE_ROUTER), device)
+    if wl.imbalance:
+        c = wl.imbalance
+        lin = torch.linspace(-c, c, wl.n_experts, dtype=torch.float32)
+        perm = torch.randperm(wl.n_experts, generator=_gen("cpu", seed_of(
+            wl.weight_cfg_id, layer, ROLE_IMBALANCE)))
+        w[wl.d_model - 1] = lin[perm].to(device)
+    return w
+
+
+def bias(wl: Workload, layer: int = 0, device="cpu") -> torch.Tensor:
+    if wl.bias_kind == "zero":
+        return torch.zeros(wl.n_experts, dtype=torch.float32, device=device)
+    r = wl.bias_range
+    return uniform((wl.n_experts,), -r, r, seed_of(wl.weight_cfg_id, layer, ROLE_BIAS), device)
+
+
+def expert_weights(wl: Workload, layer: int = 0, device="cpu",
+                   experts: Optional[list] = None) -> dict:
+    """Routed expert weights: w1, w3 [E, H, d] and w2 [E, d, H], bf16.
+    Each expert comes from its own generator.  `experts` restricts the draw to
+    a subset (the others stay zero), for host copies of a few experts."""
+    E, H, d = wl.n_experts, wl.hidden, wl.d_model
+    out = {}
+    for name, role, shape in (("w1", ROLE_W1, (H, d)), ("w3", ROLE_W3, (H, d)),
+                              ("w2", ROLE_W2, (d, H))):
+        t = torch.zeros((E,) + shape, dtype=torch.bfloat16, device=device)
+        for e in (range(E) if experts is None else experts):
+            t[e] = normal(shape, wl.w_std, seed_of(wl.weight_cfg_id, layer, role, e),
+                          device, torch.bfloat16)
+        out[name] = t
+    return out
+
+
+def shared_weights(wl: Workload, layer: int = 0, device="cpu") -> dict:
+    """Shared expert weights ws1, ws3 [Hs, d] and ws2 [d, Hs], bf16 (empty dict
+    when the workload has no shared expert)."""
+    if not wl.shared_hidden:
+        return {}
+    Hs, d = wl.shared_hidden, wl.d_model
+    return {
+        "ws1": normal((Hs, d), wl.w_std, seed_of(wl.weight_cfg_id, layer, ROLE_WS1), device, torch.bfloat16),
+        "ws3": normal((Hs, d), wl.w_std, seed_of(wl.weight_cfg_id, layer, ROLE_WS3), device, torch.bfloat16),
+        "ws2": normal((d, Hs), wl.w_std, seed_of(wl.weight_cfg_id, layer, ROLE_WS2), device, torch.bfloat16),
+    }
+
+
+def layer_params(wl: Workload, layer: int = 0, device="cpu") -> dict:
+    p = {"w_router": router(wl, layer, device), "bias": bias(wl, layer, device)}
+    p.update(expert_weights(wl, layer, device))
+    p.update(shared_weights(wl, layer, device))
+    return p
+
+
+def custom(name: str = "custom", tokens: int = 1000, seq_len: int = 0, d_model: int = 384,
+           n_experts: int = 16, top_k: int = 4, hidden: int = 256, shared_hidden: int = 256,
+           cfg_id: int = 90, x_std: float = 1.0, w_std: float = 0.02, router_std: float = 0.02,
+           bias_kind: str = "uniform", bias_range: float = 0.05, imbalance: float = 0.0) -> Workload:
+    """An ad-hoc shape for tests (ragged tails, edge cases)."""
+    return Workload(name, cfg_id, cfg_id, tokens, seq_len, d_model, n_experts, top_k, hidden,
+                    shared_hidden, 1, 1, x_std, w_std, router_std, bias_kind, bias_range,
+                    imbalance, "test shape")
+
+
+def bf16_bits(t: torch.Tensor) -> torch.Tensor:
+    """Reinterpret a bf16 tensor as its uint16 bit patterns (int16 storage)."""
+    assert t.dtype == torch.bfloat16
+    return t.view(torch.int16)
