@@ -1,0 +1,192 @@
+"""Benchmark of the DeepSeekMoE layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole hot path over one batch: for every layer of
+the workload, moe_route -> moe_permute -> moe_grouped_ffn -> moe_combine
+(the combine also adds the residual stream of stacked layers), then
+moe_update_bias for every layer.  Inputs are seeded synthetic tensors already
+resident in HBM before the timed region.  Prints ONE JSON line.
+
+value = tokens x layers / second (each token counted once per MoE layer
+forward).  The roofline object covers the dominant kernel pair -- the grouped
+expert GEMMs of moe_grouped_ffn -- timed live with HIP events on the stream
+they are launched on.  cpu_baseline times the CPU oracle on a bounded token
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer fwd tokens/sec (1 MI355X); % bf16 MFMA peak / % HBM peak"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target wall time of the CPU oracle sample")
+    return ap.parse_args()
+
+
+def ffn_algorithmic(wl, counts_per_layer):
+    """Algorithmic FLOPs and HBM bytes of one moe_grouped_ffn call per layer:
+    FLOPs = 6*d*H per routed row + 6*d*Hs per shared row; bytes = weights of
+    the experts that received rows + shared weights + x read once + y_perm and
+    y_shared written once (bf16)."""
+    d, H, Hs, T, k = wl.d_model, wl.hidden, wl.shared_hidden, wl.tokens, wl.top_k
+    flops = 6.0 * d * H * T * k + 6.0 * d * Hs * T
+    out = []
+    for counts in counts_per_layer:
+        touched = int((counts > 0).sum())
+        byts = 2.0 * (3 * H * d * touched + 3 * Hs * d + T * d + T * k * d + (T * d if Hs else 0))
+        out.append((flops, byts))
+    return out
+
+
+def cpu_baseline(wl, target_s: float):
+    import numpy as np
+    import torch
+
+    import oracle
+    from sparse_mixture_experts_51_amd import workloads
+
+    x = workloads.tokens(wl, 0, "cpu")
+    p = workloads.layer_params(wl, 0, "cpu")
+    hp = {k: (oracle.as_bf16_bits(v) if v.dtype == torch.bfloat16 else v.numpy())
+          for k, v in p.items()}
+    xb = oracle.as_bf16_bits(x)
+    threads = oracle.default_threads()
+    n = min(wl.tokens, 64)
+    while True:
+        t0 = time.perf_counter()
+        oracle.layer(xb[:n], hp, wl.top_k, nthreads=threads)
+        dt = time.perf_counter() - t0
+        if dt >= target_s / 4 or n >= wl.tokens:
+            break
+        n = min(wl.tokens, int(n * max(2.0, min(8.0, target_s / 4 / max(dt, 1e-3)))))
+    return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of {wl.tokens} tokens through one layer (route, permute, grouped "
+                      f"FFN, combine) of {wl.name}, fp64 oracle, {dt:.1f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from sparse_mixture_experts_51_amd import moe, workloads
+
+    name = args.workload or workloads.DEFAULT_BENCH_WORKLOAD
+    wl = workloads.WORKLOADS[name]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    moe.load()
+    shape = moe.Shape.of(wl)
+    L = wl.layers
+    params = [workloads.layer_params(wl, l, dev) for l in range(L)]
+    n_x = 2 if wl.steps > 1 else 1
+    xs = [workloads.tokens(wl, s, dev) for s in range(n_x)]
+    bufs = [moe.alloc_buffers(shape, dev) for _ in range(L)]
+    stream = torch.cuda.current_stream()
+    stacked = L > 1
+    ev = []  # (start, end) events around every moe_grouped_ffn in the timed region
+
+    def step(i, timed):
+        x = xs[i % n_x]
+        for l in range(L):
+            b, p = bufs[l], params[l]
+            ws = b["workspace"]
+            moe.moe_route(shape, x, p["w_router"], p["bias"], b["topk_idx"], b["topk_gate"],
+                          b["margin"], b["seq_balance"], 1e-4, ws, stream)
+            moe.moe_permute(shape, b["topk_idx"], b["counts"], b["offsets"], b["perm_src"],
+                            b["pos"], None, None, ws, stream)
+            if timed:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            moe.moe_grouped_ffn(shape, x, None, b["perm_src"], b["offsets"], p["w1"], p["w3"],
+                                p["w2"], p.get("ws1"), p.get("ws3"), p.get("ws2"), b["y_perm"],
+                                b["y_shared"], ws, stream)
+            if timed:
+                e1.record(stream)
+                ev.append((e0, e1))
+            moe.moe_combine(shape, b["y_perm"], b["y_shared"], b["topk_gate"], b["pos"],
+                            x if stacked else None, b["out"], stream)
+            x = b["out"]
+        for l in range(L):
+            moe.moe_update_bias(shape, bufs[l]["counts"], params[l]["bias"], 1e-3, stream)
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i, True)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms = t_start.elapsed_time(t_end) / args.steps
+    tokens_per_s = wl.tokens * L / (ms * 1e-3)
+
+    ffn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    counts = [bufs[l]["counts"].cpu().numpy() for l in range(L)]
+    algo = ffn_algorithmic(wl, counts)
+    flops = float(np.mean([f for f, _ in algo]))
+    byts = float(np.mean([b for _, b in algo]))
+    t_s = ffn_ms * 1e-3
+    ai = flops / byts
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if ai >= ridge:
+        roof = {"bound": "mfma", "achieved": flops / t_s / 1e12, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": byts / t_s / 1e9, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = "moe_grouped_ffn = grouped_gemm_kernel<true> + grouped_gemm_kernel<false>"
+    roof["ms_per_launch"] = ffn_ms
+    roof["algorithmic_flop"] = flops
+    roof["algorithmic_bytes"] = byts
+    roof["mfma_frac"] = flops / t_s / 1e12 / PEAK_BF16_TFLOPS
+    roof["hbm_frac"] = byts / t_s / 1e9 / PEAK_HBM_GBS
+
+    line = {
+        "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "tokens": wl.tokens, "layers": L,
+                   "seq_len": wl.seq_len, "d_model": wl.d_model, "n_experts": wl.n_experts,
+                   "top_k": wl.top_k, "hidden": wl.hidden, "shared_hidden": wl.shared_hidden,
+                   "value_counts": "tokens x layers per second",
+                   "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,178 @@
+/*
+ * moe.h -- C ABI of libmoe.so: the DeepSeekMoE layer forward on gfx950.
+ *
+ * Five calls make one layer forward, in this order, on one HIP stream:
+ *   moe_route -> moe_permute -> moe_grouped_ffn -> moe_combine
+ * and, once per training step and layer, moe_update_bias.
+ *
+ * Pages cited (title, then section):
+ *   [ZH] "190行JAX复刻DeepSeek V3" (openai-hub.com news)
+ *   [VI] "DeepSeek V3 viết lại bằng 190 dòng JAX thuần" (lehuy.net)
+ *
+ * Conventions shared by every call
+ *   - Every array pointer is a DEVICE pointer owned by the caller.  The
+ *     library allocates nothing, keeps no state between calls and never
+ *     synchronises: each call only enqueues kernels on `stream` (a
+ *     hipStream_t passed as void*; NULL means the default stream) and returns.
+ *   - bf16 arrays are passed as uint16_t bit patterns.  Layouts are
+ *     row-major and contiguous.
+ *   - Arguments are checked on the host before anything is enqueued.  A bad
+ *     argument returns MOE_ERR_INVALID_ARGUMENT (or MOE_ERR_UNSUPPORTED for a
+ *     legal shape this build does not handle, MOE_ERR_WORKSPACE for a too
+ *     small workspace) and nothing is launched.  A failed launch returns
+ *     MOE_ERR_HIP.  Faults inside a kernel surface at the caller's next
+ *     synchronisation, as with any stream API.
+ *   - tokens == 0 is valid: nothing is computed, except that moe_permute
+ *     still writes zero counts and offsets.
+ *   - Outputs must not overlap inputs (except `bias` in moe_update_bias).
+ *   - Calls are stateless and thread-safe; calls that share a workspace must
+ *     be ordered (same stream, or synchronised).
+ *
+ * Supported shapes: 1 <= E <= 1024, 1 <= k <= min(E, 32), d, H and Hs
+ * multiples of 64, T*(k+1) < 2^31.  When seq_len > 0 it must divide T.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1,
+  MOE_ERR_UNSUPPORTED = 2,
+  MOE_ERR_WORKSPACE = 3,
+  MOE_ERR_HIP = 4
+} moe_status;
+
+/* Layer shape.
+ *   tokens        T, rows of x
+ *   d_model       d
+ *   n_experts     E routed experts (16 in the mini model, 256 in the official
+ *                 shape: [ZH] 190行代码到底装进了什么 and the table in 先说结论)
+ *   top_k         k experts chosen per token (4 mini, 8 official)
+ *   hidden        H, hidden size of a routed expert
+ *   shared_hidden Hs, hidden size of the always-on shared expert; 0 = none
+ *   seq_len       S, tokens per sequence for the balance statistic; 0 = off */
+typedef struct moe_shape {
+  int64_t tokens;
+  int32_t d_model;
+  int32_t n_experts;
+  int32_t top_k;
+  int32_t hidden;
+  int32_t shared_hidden;
+  int32_t seq_len;
+} moe_shape;
+
+/* Static description of a status code; never NULL. */
+const char* moe_status_str(int status);
+
+/* Bytes of device workspace the calls need for `shape` (one buffer serves all
+ * five calls of a layer).  The caller allocates it (256-byte alignment or
+ * better) and passes it with its size.  Writes *bytes; MOE_ERR_INVALID_ARGUMENT
+ * / MOE_ERR_UNSUPPORTED for a bad shape.  Host only: launches nothing. */
+moe_status moe_workspace_bytes(const moe_shape* shape, size_t* bytes);
+
+/* Routing (steps: router GEMM, affinity, biased top-k, gates, balance
+ * statistic).  For every token t:
+ *   logit[e] = fp32 fused multiply-add chain over d in ascending order of
+ *              f32(x[t,i]) * w_router[i,e]
+ *   s[e]     = sigmoid(logit[e]) evaluated in fp64, rounded once to fp32
+ *   key[e]   = s[e] + bias[e]                       (fp32)
+ *   topk_idx[t,j]  = expert with the j-th largest key; equal keys go to the
+ *                    lower index; NaN keys rank below all others
+ *   topk_gate[t,j] = s[idx_j] / sum_j' s[idx_j'] (fp32 sum in slot order;
+ *                    1/k if that sum is 0)
+ *   margin[t]      = key_(k) - key_(k+1) (fp32), +inf when k == E
+ * The bias moves the choice of experts and never the gate values
+ * ([ZH] 最有价值的实验:无辅助损失均衡真的有效; [VI] Những gì có trong 190 dòng
+ * code).  When shape->seq_len > 0 and seq_balance != NULL, for each sequence b
+ * of S tokens: seq_balance[b] = alpha * sum_i f_i P_i with
+ * f_i = E/(kS) * #{t in b choosing i}, P_i = mean over t in b of
+ * s[t,i]/sum_j s[t,j] -- the small sequence-wise balance loss, alpha = 1e-4 in
+ * [ZH] 最有价值的实验 (formula: stated reading).
+ *   x          [T, d]  bf16            (in)
+ *   w_router   [d, E]  fp32            (in)
+ *   bias       [E]     fp32            (in)
+ *   topk_idx   [T, k]  int32           (out)
+ *   topk_gate  [T, k]  fp32            (out)
+ *   margin     [T]     fp32 or NULL    (out)
+ *   seq_balance[T/S]   fp32 or NULL    (out)
+ *   workspace  >= moe_workspace_bytes(shape) bytes                        */
+moe_status moe_route(const moe_shape* shape, const uint16_t* x, const float* w_router,
+                     const float* bias, int32_t* topk_idx, float* topk_gate, float* margin,
+                     float* seq_balance, float alpha, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/* Grouping by expert (steps: histogram, scan, permutation).
+ *   counts[e]    = number of (t, j) with topk_idx[t,j] == e (the per-expert
+ *                  load behind the bias rule, [ZH] 最有价值的实验)
+ *   offsets[e]   = sum_{e' < e} counts[e'], offsets[E] = T*k
+ *   perm_src[r]  = token of row r; rows offsets[e] .. offsets[e+1]-1 hold the
+ *                  tokens that chose e in ascending token order
+ *   pos[t,j]     = row of (t, topk_idx[t,j])
+ *   x_perm[r,:]  = x[perm_src[r], :] when x and x_perm are both non-NULL
+ *                  (optional materialised gather; moe_grouped_ffn can gather
+ *                  on the fly instead)
+ * Only the chosen experts will run -- the sparse dispatch the pages' dense
+ * reference does without ([VI] Những gì đã được đơn giản hóa).
+ *   topk_idx [T, k] int32 (in; every entry must lie in [0, E) and a token's k
+ *            entries must be distinct -- moe_route guarantees both; other
+ *            input gives unspecified rows but no out-of-bounds access)
+ *   counts [E], offsets [E+1], perm_src [T*k], pos [T, k] int32 (out)
+ *   x [T, d] bf16 or NULL (in); x_perm [T*k, d] bf16 or NULL (out)      */
+moe_status moe_permute(const moe_shape* shape, const int32_t* topk_idx, int32_t* counts,
+                       int32_t* offsets, int32_t* perm_src, int32_t* pos, const uint16_t* x,
+                       uint16_t* x_perm, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Expert feed-forward networks over the expert groups, plus the shared
+ * expert on every token (steps: grouped GEMM 1 with SwiGLU, grouped GEMM 2).
+ * For row r in group e (offsets[e] <= r < offsets[e+1]) with token
+ * t = perm_src[r]:
+ *   h        = bf16( silu(W1[e] x_t) * (W3[e] x_t) )    fp32 accumulation
+ *   y_perm[r]= bf16( W2[e] h )                          fp32 accumulation
+ * and y_shared[t] likewise with ws1, ws3, ws2.  The experts are feed-forward
+ * networks and one shared expert always runs ([ZH] 190行代码到底装进了什么);
+ * the gated-SiLU form is a stated reading.  Experts with no rows cost nothing.
+ *   x        [T, d] bf16 (in), used when x_perm is NULL (rows gathered through
+ *            perm_src); x_perm [T*k, d] bf16 or NULL (in)
+ *   perm_src [T*k], offsets [E+1] int32 (in, from moe_permute)
+ *   w1, w3   [E, H, d] bf16; w2 [E, d, H] bf16 (in)
+ *   ws1, ws3 [Hs, d] bf16; ws2 [d, Hs] bf16 (in; NULL iff Hs == 0)
+ *   y_perm   [T*k, d] bf16 (out); y_shared [T, d] bf16 (out; NULL iff Hs == 0)
+ *   workspace >= moe_workspace_bytes(shape) bytes (holds h)             */
+moe_status moe_grouped_ffn(const moe_shape* shape, const uint16_t* x, const uint16_t* x_perm,
+                           const int32_t* perm_src, const int32_t* offsets, const uint16_t* w1,
+                           const uint16_t* w3, const uint16_t* w2, const uint16_t* ws1,
+                           const uint16_t* ws3, const uint16_t* ws2, uint16_t* y_perm,
+                           uint16_t* y_shared, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* Gate-weighted combine with the shared expert (step: combine):
+ *   out[t] = bf16( residual[t] + y_shared[t] + sum_j topk_gate[t,j] * y_perm[pos[t,j]] )
+ * accumulated in fp32.  The shared expert's output is added to the routed
+ * mixture ([ZH] 190行代码到底装进了什么).  residual (the Transformer block's
+ * residual stream) and y_shared may be NULL.
+ *   y_perm [T*k, d], y_shared [T, d] or NULL, residual [T, d] or NULL: bf16 (in)
+ *   topk_gate [T, k] fp32, pos [T, k] int32 (in); out [T, d] bf16 (out)   */
+moe_status moe_combine(const moe_shape* shape, const uint16_t* y_perm, const uint16_t* y_shared,
+                       const float* topk_gate, const int32_t* pos, const uint16_t* residual,
+                       uint16_t* out, void* stream);
+
+/* Auxiliary-loss-free balancing (step: bias update), once per step and layer:
+ *   bias[i] = bias[i] + gamma * sgn(T*k - E*counts[i])      (fp32; sgn(0) = 0)
+ * i.e. an overloaded expert's bias goes down and an idle one's goes up, at
+ * speed gamma (1e-3 in [ZH] 最有价值的实验).  The sign is taken on integers.
+ *   counts [E] int32 (in, from moe_permute); bias [E] fp32 (in/out)      */
+moe_status moe_update_bias(const moe_shape* shape, const int32_t* counts, float* bias,
+                           float gamma, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -89,10 +89,13 @@ def _declare(L):
 
 
 def default_threads() -> int:
+    """Host threads for the oracle: the CPUs this process may run on, capped by
+    ORACLE_THREADS (default 16, a one-GPU share of a GPU host)."""
     try:
-        return max(1, len(os.sched_getaffinity(0)))
+        n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
-        return os.cpu_count() or 1
+        n = os.cpu_count() or 1
+    return max(1, min(n, int(os.environ.get("ORACLE_THREADS", "16"))))
 
 
 def _c(a: np.ndarray, dtype) -> np.ndarray:

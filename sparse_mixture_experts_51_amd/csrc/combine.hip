@@ -1,0 +1,83 @@
+// combine.hip -- gate-weighted combine with the shared expert, and the bias update.
+//
+// "190行JAX复刻DeepSeek V3" (openai-hub.com): section 190行代码到底装进了什么
+// (the always-on shared expert is added to the routed experts' mixture) and
+// section 最有价值的实验:无辅助损失均衡真的有效 (after every step the bias of an
+// overloaded expert is lowered and that of an idle expert raised, speed 1e-3).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+// One wave per token; each lane owns 16-byte (8 x bf16) column chunks.
+// out[t] = bf16(residual[t] + y_shared[t] + sum_j g[t,j] * y_perm[pos[t,j]]),
+// fp32 accumulation, slots in order.  Rows outside [0, T*k) are skipped.
+__global__ __launch_bounds__(256) void combine_kernel(
+    const uint16_t* __restrict__ y_perm, const uint16_t* __restrict__ y_shared,
+    const float* __restrict__ gate, const int32_t* __restrict__ pos,
+    const uint16_t* __restrict__ residual, uint16_t* __restrict__ out, int64_t T, int d, int k) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int chunks = d / 8;
+  const int64_t nrows = T * k;
+  for (int c = lane; c < chunks; c += kWave) {
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+    float v[8];
+    if (residual) {
+      bf16x8_to_f32(reinterpret_cast<const uint4*>(residual + t * d)[c], v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    }
+    if (y_shared) {
+      bf16x8_to_f32(reinterpret_cast<const uint4*>(y_shared + t * d)[c], v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    }
+    for (int j = 0; j < k; ++j) {
+      const int row = pos[t * k + j];
+      if (row < 0 || row >= nrows) continue;
+      const float g = gate[t * k + j];
+      bf16x8_to_f32(reinterpret_cast<const uint4*>(y_perm + static_cast<int64_t>(row) * d)[c], v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(g, v[i], acc[i]);
+    }
+    uint4 o;
+    o.x = pack_bf16x2(acc[0], acc[1]);
+    o.y = pack_bf16x2(acc[2], acc[3]);
+    o.z = pack_bf16x2(acc[4], acc[5]);
+    o.w = pack_bf16x2(acc[6], acc[7]);
+    reinterpret_cast<uint4*>(out + t * d)[c] = o;
+  }
+}
+
+hipError_t launch_combine(const uint16_t* y_perm, const uint16_t* y_shared, const float* gate,
+                          const int32_t* pos, const uint16_t* residual, uint16_t* out,
+                          int64_t T, int d, int k, hipStream_t s) {
+  const int64_t nblk = (T + 3) / 4;
+  hipLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, s, y_perm,
+                     y_shared, gate, pos, residual, out, T, d, k);
+  return hipGetLastError();
+}
+
+// b_i <- b_i + gamma * sgn(T*k - E*counts_i), the sign taken on integers.
+__global__ __launch_bounds__(256) void update_bias_kernel(const int32_t* __restrict__ counts,
+                                                          float* __restrict__ bias, float gamma,
+                                                          int64_t T, int E, int k) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= E) return;
+  const long long diff = static_cast<long long>(T) * k - static_cast<long long>(E) * counts[i];
+  const float sg = diff > 0 ? 1.0f : (diff < 0 ? -1.0f : 0.0f);
+  bias[i] = bias[i] + gamma * sg;
+}
+
+hipError_t launch_update_bias(const int32_t* counts, float* bias, float gamma, int64_t T, int E,
+                              int k, hipStream_t s) {
+  hipLaunchKernelGGL(update_bias_kernel, dim3((E + 255) / 256), dim3(256), 0, s, counts, bias,
+                     gamma, T, E, k);
+  return hipGetLastError();
+}
+
+}  // namespace moe

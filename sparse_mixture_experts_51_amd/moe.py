@@ -1,0 +1,198 @@
+"""Python binding of libmoe.so (include/moe.h): argument marshalling only.
+
+Each function has the name of the C entry point it calls and takes torch
+tensors that already live on the GPU; it passes their device pointers and the
+current HIP stream (or the one given) and raises MoeError on a non-OK status.
+Every step of the layer runs in the library's HIP kernels; PyTorch only
+supplies device memory and streams.  There is no fallback: if libmoe.so has
+not been built, importing the library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe.so")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARGUMENT = 1
+MOE_ERR_UNSUPPORTED = 2
+MOE_ERR_WORKSPACE = 3
+MOE_ERR_HIP = 4
+
+EXPORTED = ("moe_status_str", "moe_workspace_bytes", "moe_route", "moe_permute",
+            "moe_grouped_ffn", "moe_combine", "moe_update_bias")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        super().__init__(f"{call}: {status_str(status)}")
+
+
+class MoeShape(ctypes.Structure):
+    _fields_ = [("tokens", ctypes.c_int64), ("d_model", ctypes.c_int32),
+                ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("hidden", ctypes.c_int32), ("shared_hidden", ctypes.c_int32),
+                ("seq_len", ctypes.c_int32)]
+
+
+@dataclass(frozen=True)
+class Shape:
+    tokens: int
+    d_model: int
+    n_experts: int
+    top_k: int
+    hidden: int
+    shared_hidden: int = 0
+    seq_len: int = 0
+
+    def c(self) -> MoeShape:
+        return MoeShape(self.tokens, self.d_model, self.n_experts, self.top_k, self.hidden,
+                        self.shared_hidden, self.seq_len)
+
+    @staticmethod
+    def of(wl) -> "Shape":
+        return Shape(wl.tokens, wl.d_model, wl.n_experts, wl.top_k, wl.hidden,
+                     wl.shared_hidden, wl.seq_len)
+
+
+_lib = None
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load() -> ctypes.CDLL:
+    """Load libmoe.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it with "
+                          "`python -m sparse_mixture_experts_51_amd.build`")
+    L = ctypes.CDLL(_LIB_PATH)
+    P, S = ctypes.c_void_p, ctypes.POINTER(MoeShape)
+    L.moe_status_str.argtypes = [ctypes.c_int]
+    L.moe_status_str.restype = ctypes.c_char_p
+    L.moe_workspace_bytes.argtypes = [S, ctypes.POINTER(ctypes.c_size_t)]
+    L.moe_route.argtypes = [S, P, P, P, P, P, P, P, ctypes.c_float, P, ctypes.c_size_t, P]
+    L.moe_permute.argtypes = [S, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    L.moe_grouped_ffn.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    L.moe_combine.argtypes = [S, P, P, P, P, P, P, P]
+    L.moe_update_bias.argtypes = [S, P, P, ctypes.c_float, P]
+    for name in EXPORTED[1:]:
+        getattr(L, name).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def status_str(status: int) -> str:
+    return load().moe_status_str(int(status)).decode()
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _s(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _ok(status: int, call: str):
+    if status != MOE_OK:
+        raise MoeError(status, call)
+
+
+def _ws(ws: Optional[torch.Tensor]):
+    return (None, 0) if ws is None else (_p(ws), ws.numel() * ws.element_size())
+
+
+def moe_workspace_bytes(shape: Shape) -> int:
+    n = ctypes.c_size_t(0)
+    _ok(load().moe_workspace_bytes(ctypes.byref(shape.c()), ctypes.byref(n)), "moe_workspace_bytes")
+    return int(n.value)
+
+
+def moe_route(shape: Shape, x, w_router, bias, topk_idx, topk_gate, margin=None,
+              seq_balance=None, alpha: float = 1e-4, workspace=None, stream=None):
+    wp, wn = _ws(workspace)
+    _ok(load().moe_route(ctypes.byref(shape.c()), _p(x), _p(w_router), _p(bias), _p(topk_idx),
+                         _p(topk_gate), _p(margin), _p(seq_balance), ctypes.c_float(alpha), wp,
+                         wn, _s(stream)), "moe_route")
+
+
+def moe_permute(shape: Shape, topk_idx, counts, offsets, perm_src, pos, x=None, x_perm=None,
+                workspace=None, stream=None):
+    wp, wn = _ws(workspace)
+    _ok(load().moe_permute(ctypes.byref(shape.c()), _p(topk_idx), _p(counts), _p(offsets),
+                           _p(perm_src), _p(pos), _p(x), _p(x_perm), wp, wn, _s(stream)),
+        "moe_permute")
+
+
+def moe_grouped_ffn(shape: Shape, x, x_perm, perm_src, offsets, w1, w3, w2, ws1, ws3, ws2,
+                    y_perm, y_shared, workspace=None, stream=None):
+    wp, wn = _ws(workspace)
+    _ok(load().moe_grouped_ffn(ctypes.byref(shape.c()), _p(x), _p(x_perm), _p(perm_src),
+                               _p(offsets), _p(w1), _p(w3), _p(w2), _p(ws1), _p(ws3), _p(ws2),
+                               _p(y_perm), _p(y_shared), wp, wn, _s(stream)), "moe_grouped_ffn")
+
+
+def moe_combine(shape: Shape, y_perm, y_shared, topk_gate, pos, residual, out, stream=None):
+    _ok(load().moe_combine(ctypes.byref(shape.c()), _p(y_perm), _p(y_shared), _p(topk_gate),
+                           _p(pos), _p(residual), _p(out), _s(stream)), "moe_combine")
+
+
+def moe_update_bias(shape: Shape, counts, bias, gamma: float = 1e-3, stream=None):
+    _ok(load().moe_update_bias(ctypes.byref(shape.c()), _p(counts), _p(bias),
+                               ctypes.c_float(gamma), _s(stream)), "moe_update_bias")
+
+
+# --------------------------------------------------------------------------
+# Plumbing: device buffers for one layer, and the five calls in order.
+
+def alloc_buffers(shape: Shape, device="cuda", x_perm: bool = False) -> dict:
+    """Outputs and workspace of one layer, allocated with torch."""
+    T, d, E, k = shape.tokens, shape.d_model, shape.n_experts, shape.top_k
+    i32, f32, b16 = torch.int32, torch.float32, torch.bfloat16
+    ws_bytes = moe_workspace_bytes(shape)
+    nseq = T // shape.seq_len if shape.seq_len else 0
+    return {
+        "topk_idx": torch.empty((T, k), dtype=i32, device=device),
+        "topk_gate": torch.empty((T, k), dtype=f32, device=device),
+        "margin": torch.empty((T,), dtype=f32, device=device),
+        "seq_balance": torch.empty((max(nseq, 1),), dtype=f32, device=device) if nseq else None,
+        "counts": torch.empty((E,), dtype=i32, device=device),
+        "offsets": torch.empty((E + 1,), dtype=i32, device=device),
+        "perm_src": torch.empty((T * k,), dtype=i32, device=device),
+        "pos": torch.empty((T, k), dtype=i32, device=device),
+        "x_perm": torch.empty((T * k, d), dtype=b16, device=device) if x_perm else None,
+        "y_perm": torch.empty((T * k, d), dtype=b16, device=device),
+        "y_shared": torch.empty((T, d), dtype=b16, device=device) if shape.shared_hidden else None,
+        "out": torch.empty((T, d), dtype=b16, device=device),
+        "workspace": torch.empty((max(ws_bytes, 256),), dtype=torch.uint8, device=device),
+    }
+
+
+def layer_forward(shape: Shape, x, params: dict, bufs: dict, residual=None, alpha: float = 1e-4,
+                  use_x_perm: bool = False, stream=None):
+    """route -> permute -> grouped_ffn -> combine, all enqueued on one stream."""
+    ws = bufs["workspace"]
+    moe_route(shape, x, params["w_router"], params["bias"], bufs["topk_idx"], bufs["topk_gate"],
+              bufs["margin"], bufs["seq_balance"], alpha, ws, stream)
+    xp = bufs["x_perm"] if use_x_perm else None
+    moe_permute(shape, bufs["topk_idx"], bufs["counts"], bufs["offsets"], bufs["perm_src"],
+                bufs["pos"], x if use_x_perm else None, xp, ws, stream)
+    moe_grouped_ffn(shape, x, xp, bufs["perm_src"], bufs["offsets"], params["w1"], params["w3"],
+                    params["w2"], params.get("ws1"), params.get("ws3"), params.get("ws2"),
+                    bufs["y_perm"], bufs["y_shared"], ws, stream)
+    moe_combine(shape, bufs["y_perm"], bufs["y_shared"], bufs["topk_gate"], bufs["pos"], residual,
+                bufs["out"], stream)
+    return bufs["out"]
