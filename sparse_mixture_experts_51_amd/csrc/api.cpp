@@ -5,6 +5,7 @@
 // synchronisation, no state beyond a per-device cache of the CU count.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdint>
 
@@ -71,6 +72,12 @@ moe_status check_shape(const moe_shape* s) {
   if (s->n_experts > 1024 || s->top_k > 32) return MOE_ERR_UNSUPPORTED;
   if (s->d_model % 64 || s->hidden % 64 || s->shared_hidden % 64) return MOE_ERR_UNSUPPORTED;
   if (s->tokens * (static_cast<int64_t>(s->top_k) + 1) >= (int64_t{1} << 31))
+    return MOE_ERR_UNSUPPORTED;
+  // grouped-GEMM operands are addressed with 32-bit byte offsets
+  const int64_t widest = std::max<int64_t>({s->d_model, s->hidden, s->shared_hidden});
+  if (2 * s->tokens * s->top_k * widest >= (int64_t{1} << 31) ||
+      2 * static_cast<int64_t>(s->hidden) * s->d_model >= (int64_t{1} << 31) ||
+      2 * static_cast<int64_t>(s->shared_hidden) * s->d_model >= (int64_t{1} << 31))
     return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
@@ -185,6 +192,8 @@ moe_status moe_grouped_ffn(const moe_shape* shape, const uint16_t* x, const uint
   g1.a_routed = x_perm ? x_perm : x;
   g1.a_row_map = x_perm ? nullptr : perm_src;
   g1.a_shared = shared ? x : nullptr;
+  g1.a_routed_bytes = 2 * d * (x_perm ? T * shape->top_k : T);
+  g1.a_shared_bytes = 2 * d * T;
   g1.w_routed = w1;
   g1.w3_routed = w3;
   g1.w_shared = shared ? ws1 : nullptr;
@@ -194,6 +203,7 @@ moe_status moe_grouped_ffn(const moe_shape* shape, const uint16_t* x, const uint
   g1.offsets = offsets;
   g1.T = T;
   g1.E = E;
+  g1.top_k = shape->top_k;
   g1.K_r = d;
   g1.K_s = d;
   g1.N_r = H;
@@ -205,6 +215,8 @@ moe_status moe_grouped_ffn(const moe_shape* shape, const uint16_t* x, const uint
   g2.a_routed = w.h_routed;
   g2.a_row_map = nullptr;
   g2.a_shared = shared ? w.h_shared : nullptr;
+  g2.a_routed_bytes = 2 * static_cast<int64_t>(H) * T * shape->top_k;
+  g2.a_shared_bytes = 2 * static_cast<int64_t>(Hs) * T;
   g2.w_routed = w2;
   g2.w_shared = shared ? ws2 : nullptr;
   g2.c_routed = y_perm;
@@ -212,6 +224,7 @@ moe_status moe_grouped_ffn(const moe_shape* shape, const uint16_t* x, const uint
   g2.offsets = offsets;
   g2.T = T;
   g2.E = E;
+  g2.top_k = shape->top_k;
   g2.K_r = H;
   g2.K_s = Hs;
   g2.N_r = d;

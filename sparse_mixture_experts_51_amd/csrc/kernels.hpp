@@ -50,6 +50,7 @@ struct GroupedGemmArgs {
   const uint16_t* a_routed;
   const int32_t* a_row_map;  // NULL: A row = group row; else A row = a_row_map[group row]
   const uint16_t* a_shared;  // shared group's A rows (row t), NULL if no shared group
+  int64_t a_routed_bytes, a_shared_bytes;  // extents of the A buffers (bounds of the loads)
   // B operand: weights [N_rows, K] per group, K contiguous
   const uint16_t* w_routed;   // [E, N, K]   (gate projection W1 for the SwiGLU stage)
   const uint16_t* w3_routed;  // [E, N, K]   up projection W3 (SwiGLU stage only)
@@ -60,6 +61,7 @@ struct GroupedGemmArgs {
   const int32_t* offsets;
   int64_t T;
   int E;
+  int top_k;     // choices per token (tile configuration heuristic)
   int K_r, K_s;  // reduction lengths
   int N_r, N_s;  // output columns
 };
