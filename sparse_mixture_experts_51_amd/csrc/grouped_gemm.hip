@@ -460,12 +460,15 @@ static int persistent_grid() {
   return g > 0 ? g : kXcds;
 }
 
-// Weight-streaming shapes: few rows per routed expert and expert weights far
-// beyond the on-chip caches.
+// The 256-row tile pays off when experts hold between one and two 128-row
+// m-tiles of rows and their weights are far beyond the on-chip caches (each
+// weight byte is then read once instead of once per m-tile).  With fewer
+// rows (decode) a 128-row m-tile already covers an expert and two blocks per
+// CU keep more weight bytes in flight.
 static bool streaming_shape(const GroupedGemmArgs& a) {
   const int64_t rows_per_expert = a.T * a.top_k / (a.E > 0 ? a.E : 1);
   const int64_t weight_bytes = static_cast<int64_t>(a.E) * a.N_r * a.K_r * 2 * 3;
-  return rows_per_expert <= 256 && weight_bytes > (int64_t{1} << 30);
+  return rows_per_expert > 64 && rows_per_expert <= 256 && weight_bytes > (int64_t{1} << 30);
 }
 
 template <bool kSwiGLU>

@@ -85,14 +85,70 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(
   if (e == 0) offsets[E] = total;
 }
 
+// Exclusive scan of one int per thread over a kPermTokens-thread block.
+__device__ int block_exclusive_scan_256(int v, int* total) {
+  __shared__ int wsum[kPermTokens / 64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int inc = v;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(inc, off, 64);
+    if (lane >= off) inc += o;
+  }
+  if (lane == 63) wsum[w] = inc;
+  __syncthreads();
+  int base = 0, tot = 0;
+  for (int i = 0; i < kPermTokens / 64; ++i) {
+    base += i < w ? wsum[i] : 0;
+    tot += wsum[i];
+  }
+  *total = tot;
+  __syncthreads();
+  return base + inc - v;
+}
+
+// fused_scan: the block derives its own first rows (and block 0 the counts and
+// offsets) from the per-block count table, which is small enough for LDS;
+// otherwise blk_base comes from perm_scan_kernel.
 __global__ __launch_bounds__(kPermTokens) void perm_scatter_kernel(
-    const int32_t* __restrict__ idx, const int32_t* __restrict__ blk_base,
-    int32_t* __restrict__ perm_src, int32_t* __restrict__ pos, const uint16_t* __restrict__ x,
-    uint16_t* __restrict__ x_perm, int64_t T, int d, int E, int k) {
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ blk_cnt,
+    const int32_t* __restrict__ blk_base, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src, int32_t* __restrict__ pos,
+    const uint16_t* __restrict__ x, uint16_t* __restrict__ x_perm, int64_t T, int d, int E, int k,
+    int nblk, int fused_scan) {
   constexpr int W = kPermTokens / 32;  // 32-bit words per expert row of the bitmap
-  extern __shared__ uint32_t bits[];   // [E][W], then rows [kPermTokens * k]
+  extern __shared__ uint32_t bits[];   // [E][W], rows [kPermTokens * k], base [E] (fused)
   int32_t* rows = reinterpret_cast<int32_t*>(bits + E * W);
+  int32_t* base = rows + kPermTokens * k;
   for (int i = threadIdx.x; i < E * W; i += kPermTokens) bits[i] = 0;
+  if (fused_scan) {
+    // expert chunk per thread: e in [c0, c0 + per)
+    const int per = (E + kPermTokens - 1) / kPermTokens;
+    const int c0 = threadIdx.x * per;
+    int tot_local = 0;
+    for (int e = c0; e < c0 + per && e < E; ++e) {
+      int before = 0, total = 0;
+      for (int b2 = 0; b2 < nblk; ++b2) {
+        const int c = blk_cnt[static_cast<int64_t>(b2) * E + e];
+        before += b2 < static_cast<int>(blockIdx.x) ? c : 0;
+        total += c;
+      }
+      base[e] = before;       // rows before this block, inside expert e
+      rows[e] = total;        // expert e's load (rows[] is reused below)
+      tot_local += total;
+    }
+    int all;
+    int run = block_exclusive_scan_256(tot_local, &all);
+    for (int e = c0; e < c0 + per && e < E; ++e) {
+      const int total = rows[e];
+      base[e] += run;
+      if (blockIdx.x == 0) {
+        counts[e] = total;
+        offsets[e] = run;
+      }
+      run += total;
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) offsets[E] = all;
+  }
   __syncthreads();
   const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kPermTokens;
   const int64_t t = t0 + threadIdx.x;
@@ -111,7 +167,7 @@ __global__ __launch_bounds__(kPermTokens) void perm_scatter_kernel(
       if (e >= 0 && e < E) {
         int rank = __popc(bits[e * W + word] & ((1u << bit) - 1u));
         for (int w = 0; w < word; ++w) rank += __popc(bits[e * W + w]);
-        row = blk_base[static_cast<int64_t>(blockIdx.x) * E + e] + rank;
+        row = (fused_scan ? base[e] : blk_base[static_cast<int64_t>(blockIdx.x) * E + e]) + rank;
         perm_src[row] = static_cast<int32_t>(t);
       }
       pos[t * k + j] = row;
@@ -146,13 +202,27 @@ hipError_t launch_permute(const int32_t* idx, int32_t* counts, int32_t* offsets,
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, s, blk_cnt, blk_base, counts,
-                     offsets, nblk, E);
-  err = hipGetLastError();
-  if (err != hipSuccess || nblk == 0) return err;
-  const size_t lds = sizeof(uint32_t) * E * (kPermTokens / 32) + sizeof(int32_t) * kPermTokens * k;
-  hipLaunchKernelGGL(perm_scatter_kernel, dim3(nblk), dim3(kPermTokens), lds, s, idx, blk_base,
-                     perm_src, pos, x, x_perm, T, d, E, k);
+  if (nblk == 0) {
+    hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, s, blk_cnt, blk_base, counts,
+                       offsets, nblk, E);
+    return hipGetLastError();
+  }
+  // Small count tables are summed by every scatter block itself (one launch
+  // fewer); large ones go through the single-block scan.
+  const size_t lds_base = sizeof(uint32_t) * E * (kPermTokens / 32) +
+                          sizeof(int32_t) * kPermTokens * (k > 1 ? k : 1);
+  const size_t lds_fused = lds_base + sizeof(int32_t) * E;
+  const int fused = nblk > 0 && static_cast<int64_t>(nblk) * E <= 16384 &&
+                    lds_fused <= 64 * 1024 && kPermTokens * (k > 1 ? k : 1) >= E;
+  if (!fused) {
+    hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, s, blk_cnt, blk_base, counts,
+                       offsets, nblk, E);
+    err = hipGetLastError();
+    if (err != hipSuccess || nblk == 0) return err;
+  }
+  hipLaunchKernelGGL(perm_scatter_kernel, dim3(nblk), dim3(kPermTokens), fused ? lds_fused : lds_base,
+                     s, idx, blk_cnt, blk_base, counts, offsets, perm_src, pos, x, x_perm, T, d, E,
+                     k, nblk, fused);
   return hipGetLastError();
 }
 

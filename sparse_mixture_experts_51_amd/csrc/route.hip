@@ -24,75 +24,120 @@
 namespace moe {
 
 constexpr int kRouteThreads = 256;
-constexpr int kKC = 32;  // d-chunk staged per LDS pass
+constexpr int kRouteLds = 64 * 1024;  // LDS budget of one router block
 
+// LDS-only barrier: waits for this wave's LDS traffic, not for global loads,
+// so the next chunk's loads stay in flight across it.
+__device__ __forceinline__ void route_lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+}
+
+// Block tile: BT tokens x BE experts; thread tile: TPT tokens x EPT experts
+// (TPR = BE/EPT threads per token row).  d is walked in chunks of KC.  A
+// chunk's x rows (bf16, [BT][KC]) and W_r columns (fp32, [TPR][KC][EPT]:
+// a thread's EPT experts adjacent) sit in LDS with rows padded by 16 bytes,
+// so the lanes of a wave read distinct banks and one 16-byte LDS read gives a
+// thread 8 values of x or 4 of W.  With more than one chunk, the next chunk is
+// prefetched into registers while this one is multiplied.  Every (token,
+// expert) logit is one fp32 fmaf chain over d in ascending order.
 template <int EPT, int TPT>
 __global__ __launch_bounds__(kRouteThreads) void router_scores_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ w_router,
-    float* __restrict__ scores, int64_t T, int d, int E, int BE) {
-  const int TPR = BE / EPT;                 // threads per token row
-  const int rows = kRouteThreads / TPR;     // token rows per block
-  const int BT = rows * TPT;                // tokens per block
+    float* __restrict__ scores, int64_t T, int d, int E, int BE, int KC) {
+  const int TPR = BE / EPT;
+  const int rows = kRouteThreads / TPR;
+  const int BT = rows * TPT;
   const int tid = threadIdx.x;
   const int tx = tid % TPR, ty = tid / TPR;
   const int n_eblk = (E + BE - 1) / BE;
-  const int eb = blockIdx.x % n_eblk;
+  const int e0 = (blockIdx.x % n_eblk) * BE;
   const int64_t t0 = static_cast<int64_t>(blockIdx.x / n_eblk) * BT;
-  const int e0 = eb * BE;
+  const int nchunks = d / KC;
 
-  extern __shared__ float lds[];
-  float* xs = lds;               // [kKC][BT]
-  float* ws = lds + kKC * BT;    // [kKC][BE]
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+  const int xrow = KC * 2 + 16, wrow = KC * EPT * 4 + 16;  // padded row strides (bytes)
+  const int bufbytes = BT * xrow + TPR * wrow;
+  auto xs = [&](int b) { return lds_raw + b * bufbytes; };
+  auto ws = [&](int b) { return lds_raw + b * bufbytes + BT * xrow; };
 
-  // Register staging of one d-chunk: x as 16-byte pieces (8 bf16), W as floats.
-  const int x_pieces = BT * (kKC / 8);
-  const int x_per_thr = (x_pieces + kRouteThreads - 1) / kRouteThreads;   // <= 4
-  const int w_elems = kKC * BE;
-  const int w_per_thr = (w_elems + kRouteThreads - 1) / kRouteThreads;    // <= 8
-  uint4 xr[4];
-  float wr[8];
-
+  // A chunk is BT*KC/8 16-byte pieces of x (a row has CX = KC/8) and KC*BE/4
+  // pieces of W (a d-row has CW = BE/4).  Thread tid takes pieces tid,
+  // tid + 256, ...; their (row, column) advance incrementally (no divisions).
+  const int CX = KC / 8, CW = BE / 4;
+  const int nx = (BT * CX - tid + kRouteThreads - 1) / kRouteThreads;  // x pieces of this thread
+  const int nw = (KC * CW - tid + kRouteThreads - 1) / kRouteThreads;  // W pieces of this thread
+  const int x_r0 = tid / CX, x_c0 = tid % CX;
+  const int w_r0 = tid / CW, w_c0 = tid % CW;
+  const int x_dr = kRouteThreads / CX, x_dc = kRouteThreads % CX;
+  const int w_dr = kRouteThreads / CW, w_dc = kRouteThreads % CW;
+  constexpr int kMaxX = 8, kMaxW = 8;  // LDS budget bounds both
+  uint4 rx[kMaxX], rw[kMaxW];
   auto fetch = [&](int k0) {
+    int r = x_r0, c = x_c0;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      if (p >= x_per_thr) break;
-      const int piece = tid + p * kRouteThreads;
-      xr[p] = make_uint4(0, 0, 0, 0);
-      if (piece < x_pieces) {
-        const int tok = piece / (kKC / 8), c = piece % (kKC / 8);
-        const int64_t t = t0 + tok;
-        if (t < T) xr[p] = *reinterpret_cast<const uint4*>(x + t * d + k0 + c * 8);
-      }
+    for (int p = 0; p < kMaxX; ++p) {
+      if (p >= nx) break;
+      const int64_t t = t0 + r;
+      rx[p] = t < T ? *reinterpret_cast<const uint4*>(x + t * d + k0 + c * 8) : make_uint4(0, 0, 0, 0);
+      r += x_dr;
+      c += x_dc;
+      if (c >= CX) { c -= CX; ++r; }
     }
+    r = w_r0;
+    c = w_c0;
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      if (p >= w_per_thr) break;
-      const int el = tid + p * kRouteThreads;
-      wr[p] = 0.0f;
-      if (el < w_elems) {
-        const int kk = el / BE, c = el % BE;
-        if (e0 + c < E) wr[p] = w_router[static_cast<int64_t>(k0 + kk) * E + e0 + c];
+    for (int p = 0; p < kMaxW; ++p) {
+      if (p >= nw) break;
+      const int e = e0 + c * 4;
+      const float* src = w_router + static_cast<int64_t>(k0 + r) * E + e;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (e + 3 < E && ((E & 3) == 0)) {
+        v = *reinterpret_cast<const float4*>(src);
+      } else {
+        if (e + 0 < E) v.x = src[0];
+        if (e + 1 < E) v.y = src[1];
+        if (e + 2 < E) v.z = src[2];
+        if (e + 3 < E) v.w = src[3];
       }
+      rw[p] = make_uint4(__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z),
+                         __float_as_uint(v.w));
+      r += w_dr;
+      c += w_dc;
+      if (c >= CW) { c -= CW; ++r; }
     }
   };
-  auto stash = [&]() {
+  auto stash = [&](int b) {
+    unsigned char* xb = xs(b);
+    unsigned char* wb = ws(b);
+    int r = x_r0, c = x_c0;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      if (p >= x_per_thr) break;
-      const int piece = tid + p * kRouteThreads;
-      if (piece < x_pieces) {
-        const int tok = piece / (kKC / 8), c = piece % (kKC / 8);
-        float v[8];
-        bf16x8_to_f32(xr[p], v);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) xs[(c * 8 + i) * BT + tok] = v[i];
-      }
+    for (int p = 0; p < kMaxX; ++p) {
+      if (p >= nx) break;
+      *reinterpret_cast<uint4*>(xb + r * xrow + c * 16) = rx[p];
+      r += x_dr;
+      c += x_dc;
+      if (c >= CX) { c -= CX; ++r; }
     }
+    r = w_r0;
+    c = w_c0;
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      if (p >= w_per_thr) break;
-      const int el = tid + p * kRouteThreads;
-      if (el < w_elems) ws[el] = wr[p];  // [kk][c] layout == el
+    for (int p = 0; p < kMaxW; ++p) {
+      if (p >= nw) break;
+      // experts c*4 .. c*4+3 at d-row r -> [expert / EPT][r][expert % EPT]
+      const uint32_t v[4] = {rw[p].x, rw[p].y, rw[p].z, rw[p].w};
+      if constexpr (EPT == 4) {
+        *reinterpret_cast<uint4*>(wb + c * wrow + r * 16) = rw[p];
+      } else if constexpr (EPT == 2) {
+        *reinterpret_cast<uint2*>(wb + (2 * c) * wrow + r * 8) = make_uint2(v[0], v[1]);
+        *reinterpret_cast<uint2*>(wb + (2 * c + 1) * wrow + r * 8) = make_uint2(v[2], v[3]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<uint32_t*>(wb + (c * 4 + i) * wrow + r * 4) = v[i];
+      }
+      r += w_dr;
+      c += w_dc;
+      if (c >= CW) { c -= CW; ++r; }
     }
   };
 
@@ -102,23 +147,39 @@ __global__ __launch_bounds__(kRouteThreads) void router_scores_kernel(
 #pragma unroll
     for (int j = 0; j < EPT; ++j) acc[i][j] = 0.0f;
 
+  auto compute = [&](int b) {
+    const unsigned char* xb = xs(b) + ty * TPT * xrow;
+    const unsigned char* wb = ws(b) + tx * wrow;
+    for (int kk = 0; kk < KC; kk += 8) {
+      float xv[TPT][8], wv[8 * EPT];
+#pragma unroll
+      for (int i = 0; i < TPT; ++i) {
+        const uint4 q = *reinterpret_cast<const uint4*>(xb + i * xrow + kk * 2);
+        bf16x8_to_f32(q, xv[i]);
+      }
+#pragma unroll
+      for (int h = 0; h < 2 * EPT; ++h) {
+        const float4 q = *reinterpret_cast<const float4*>(wb + kk * EPT * 4 + h * 16);
+        wv[4 * h] = q.x; wv[4 * h + 1] = q.y; wv[4 * h + 2] = q.z; wv[4 * h + 3] = q.w;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int i = 0; i < TPT; ++i)
+#pragma unroll
+          for (int j = 0; j < EPT; ++j) acc[i][j] = fmaf(xv[i][u], wv[u * EPT + j], acc[i][j]);
+    }
+  };
+
   fetch(0);
-  for (int k0 = 0; k0 < d; k0 += kKC) {
-    __syncthreads();          // previous chunk fully consumed
-    stash();
-    __syncthreads();
-    if (k0 + kKC < d) fetch(k0 + kKC);  // in flight during the FMAs below
-#pragma unroll 8
-    for (int kk = 0; kk < kKC; ++kk) {
-      float xv[TPT], wv[EPT];
-#pragma unroll
-      for (int i = 0; i < TPT; ++i) xv[i] = xs[kk * BT + ty * TPT + i];
-#pragma unroll
-      for (int j = 0; j < EPT; ++j) wv[j] = ws[kk * BE + tx * EPT + j];
-#pragma unroll
-      for (int i = 0; i < TPT; ++i)
-#pragma unroll
-        for (int j = 0; j < EPT; ++j) acc[i][j] = fmaf(xv[i], wv[j], acc[i][j]);
+  stash(0);
+  route_lds_barrier();
+  for (int c = 0; c < nchunks; ++c) {
+    if (c + 1 < nchunks) fetch((c + 1) * KC);  // in flight during the FMAs below
+    compute(c & 1);
+    if (c + 1 < nchunks) {
+      stash((c + 1) & 1);
+      route_lds_barrier();
     }
   }
 
@@ -129,7 +190,9 @@ __global__ __launch_bounds__(kRouteThreads) void router_scores_kernel(
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
       const int e = e0 + tx * EPT + j;
-      if (e < E) scores[t * E + e] = static_cast<float>(1.0 / (1.0 + exp(-static_cast<double>(acc[i][j]))));
+      if (e < E)
+        scores[t * E + e] =
+            static_cast<float>(1.0 / (1.0 + exp(-static_cast<double>(acc[i][j]))));
     }
   }
 }
@@ -140,51 +203,70 @@ static int next_pow2(int v) {
   return p;
 }
 
-template <int EPT, int TPT>
-static hipError_t launch_scores_cfg(const uint16_t* x, const float* w, float* sc, int64_t T, int d,
-                                    int E, int BE, hipStream_t s) {
-  const int TPR = BE / EPT;
-  const int BT = (kRouteThreads / TPR) * TPT;
-  const int64_t nblk = ((T + BT - 1) / BT) * ((E + BE - 1) / BE);
-  const size_t lds = sizeof(float) * kKC * (BT + BE);
-  hipLaunchKernelGGL((router_scores_kernel<EPT, TPT>), dim3(static_cast<unsigned>(nblk)),
-                     dim3(kRouteThreads), lds, s, x, w, sc, T, d, E, BE);
-  return hipGetLastError();
-}
+struct RouterCfg {
+  int BE, EPT, TPT, KC;
+  int64_t blocks;
+  size_t lds;
+};
 
-hipError_t launch_router_scores(const uint16_t* x, const float* w_router, float* scores,
-                                int64_t T, int d, int E, hipStream_t s) {
-  // Pick the largest per-thread tile that still gives one block per CU; with
-  // few tokens, trade tile size for blocks (each (token, expert) chain is
-  // sequential over d, so parallelism is bounded by T*E lanes).
+static RouterCfg router_cfg(int64_t T, int d, int E, int want_blocks) {
+  // Largest per-thread tile that still gives one block per CU (with few
+  // tokens, trade tile size for blocks: each (token, expert) chain is serial
+  // over d, so parallelism is bounded by T*E lanes).  A chunk of d is the
+  // whole of d when x and W_r tiles fit the LDS budget; else 64- or 32-wide
+  // double-buffered chunks.
   const int Emax = next_pow2(E) < 64 ? next_pow2(E) : 64;
-  struct Cfg { int BE, EPT, TPT; };
   auto ept_of = [](int BE) { return BE >= 64 ? 4 : (BE >= 32 ? 2 : 1); };
-  const int want = device_cus();
-  Cfg pick{0, 0, 0};
-  int64_t best_blocks = -1;
-  Cfg last{0, 0, 0};
+  RouterCfg best{0, 0, 0, 0, -1, 0};
   const int be_list[4] = {64, 32, 16, 8};
   const int tpt_list[3] = {4, 2, 1};
-  for (int ti = 0; ti < 3 && !pick.BE; ++ti) {
+  for (int ti = 0; ti < 3; ++ti) {
     for (int bi = 0; bi < 4; ++bi) {
-      int BE = be_list[bi] < Emax ? be_list[bi] : Emax;
-      if (bi > 0 && BE == (be_list[bi - 1] < Emax ? be_list[bi - 1] : Emax)) continue;
+      const int BE = be_list[bi] < Emax ? be_list[bi] : Emax;
       const int EPT = ept_of(BE) > BE ? BE : ept_of(BE);
       const int TPR = BE / EPT;
       const int TPT = tpt_list[ti];
       const int BT = (kRouteThreads / TPR) * TPT;
       if (BT > 256) continue;
       const int64_t blocks = ((T + BT - 1) / BT) * ((E + BE - 1) / BE);
-      if (blocks >= want) { pick = {BE, EPT, TPT}; break; }
-      if (blocks > best_blocks) { best_blocks = blocks; last = {BE, EPT, TPT}; }
+      auto bytes = [&](int KC) {
+        return static_cast<size_t>(BT * (KC * 2 + 16) + TPR * (KC * EPT * 4 + 16));
+      };
+      auto fits = [&](int KC) {  // at most 8 pieces of x and 8 of W per thread
+        return static_cast<int64_t>(BT) * (KC / 8) <= 8 * kRouteThreads &&
+               static_cast<int64_t>(KC) * (BE / 4) <= 8 * kRouteThreads;
+      };
+      int KC;
+      size_t lds;
+      if (bytes(d) <= static_cast<size_t>(kRouteLds) && fits(d)) {
+        KC = d;
+        lds = bytes(d);
+      } else {
+        KC = (d % 64 == 0 && 2 * bytes(64) <= static_cast<size_t>(kRouteLds) && fits(64)) ? 64 : 32;
+        lds = 2 * bytes(KC);
+      }
+      const RouterCfg c{BE, EPT, TPT, KC, blocks, lds};
+      if (blocks >= want_blocks) return c;
+      if (blocks > best.blocks) best = c;
     }
   }
-  if (!pick.BE) pick = last;
-  if (!pick.BE) pick = {Emax, 1, 1};
-#define MOE_SCORES_CASE(e, t)                                                      \
-  if (pick.EPT == e && pick.TPT == t)                                              \
-    return launch_scores_cfg<e, t>(x, w_router, scores, T, d, E, pick.BE, s);
+  return best;
+}
+
+template <int EPT, int TPT>
+static hipError_t launch_scores_cfg(const uint16_t* x, const float* w, float* sc, int64_t T, int d,
+                                    int E, const RouterCfg& c, hipStream_t s) {
+  hipLaunchKernelGGL((router_scores_kernel<EPT, TPT>), dim3(static_cast<unsigned>(c.blocks)),
+                     dim3(kRouteThreads), c.lds, s, x, w, sc, T, d, E, c.BE, c.KC);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_scores(const uint16_t* x, const float* w_router, float* scores,
+                                int64_t T, int d, int E, hipStream_t s) {
+  const RouterCfg pick = router_cfg(T, d, E, device_cus());
+#define MOE_SCORES_CASE(e, t)                                               \
+  if (pick.EPT == e && pick.TPT == t)                                       \
+    return launch_scores_cfg<e, t>(x, w_router, scores, T, d, E, pick, s);
   MOE_SCORES_CASE(4, 4) MOE_SCORES_CASE(4, 2) MOE_SCORES_CASE(4, 1)
   MOE_SCORES_CASE(2, 4) MOE_SCORES_CASE(2, 2) MOE_SCORES_CASE(2, 1)
   MOE_SCORES_CASE(1, 4) MOE_SCORES_CASE(1, 2) MOE_SCORES_CASE(1, 1)
@@ -296,29 +378,46 @@ int seq_splits(int64_t T, int S) {
   return static_cast<int>(sp);
 }
 
-// grid (nseq * nsplit): each block walks a slice of one sequence; thread e
-// accumulates sum_t s[t,e]/tok_sum[t] in fp64 in token order, and the block
-// counts choices with LDS atomics.
+// grid (nseq * nsplit): each block walks a slice of one sequence.  Thread
+// (token lane tl, expert e) sums s[t,e]/tok_sum[t] in fp64 over the slice's
+// tokens t = a + tl, a + tl + L, ...; the L lanes of an expert are then added
+// in lane order (deterministic).  Choices are counted with LDS atomics.
 __global__ __launch_bounds__(256) void seq_partial_kernel(
     const float* __restrict__ scores, const double* __restrict__ tok_sum,
     const int32_t* __restrict__ idx, double* __restrict__ seq_p, int32_t* __restrict__ seq_cnt,
     int E, int k, int S, int nsplit) {
-  extern __shared__ int32_t cnt[];  // [E]
+  extern __shared__ int32_t cnt[];               // [E]
+  __shared__ double part[256];
   const int q = blockIdx.x / nsplit, sp = blockIdx.x % nsplit;
   const int64_t a = static_cast<int64_t>(q) * S + static_cast<int64_t>(S) * sp / nsplit;
   const int64_t b = static_cast<int64_t>(q) * S + static_cast<int64_t>(S) * (sp + 1) / nsplit;
   for (int e = threadIdx.x; e < E; e += 256) cnt[e] = 0;
   __syncthreads();
-  for (int64_t i = a * k + threadIdx.x; i < b * k; i += 256) atomicAdd(&cnt[idx[i]], 1);
-  for (int e = threadIdx.x; e < E; e += 256) {
-    double p = 0.0;
-    for (int64_t t = a; t < b; ++t) {
-      const double tot = tok_sum[t];
-      p += (tot == 0.0) ? 1.0 / E : static_cast<double>(scores[t * E + e]) / tot;
-    }
-    seq_p[static_cast<int64_t>(blockIdx.x) * E + e] = p;
+  for (int64_t i = a * k + threadIdx.x; i < b * k; i += 256) {
+    const int e = idx[i];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
   }
-  __syncthreads();
+  const double inv_e = 1.0 / E;
+  for (int e0 = 0; e0 < E; e0 += 256) {
+    const int ne = (E - e0) < 256 ? (E - e0) : 256;
+    const int L = 256 / ne;  // token lanes per expert
+    const int e = e0 + threadIdx.x % ne, tl = threadIdx.x / ne;
+    double p = 0.0;
+    if (tl < L) {
+      for (int64_t t = a + tl; t < b; t += L) {
+        const double tot = tok_sum[t];
+        p += (tot == 0.0) ? inv_e : static_cast<double>(scores[t * E + e]) / tot;
+      }
+    }
+    part[threadIdx.x] = p;
+    __syncthreads();
+    if (threadIdx.x < ne) {
+      double s2 = 0.0;
+      for (int l = 0; l < L; ++l) s2 += part[l * ne + threadIdx.x];
+      seq_p[static_cast<int64_t>(blockIdx.x) * E + e0 + threadIdx.x] = s2;
+    }
+    __syncthreads();
+  }
   for (int e = threadIdx.x; e < E; e += 256) seq_cnt[static_cast<int64_t>(blockIdx.x) * E + e] = cnt[e];
 }
 
