@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target wall time of the CPU oracle sample")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a plain device copy of 1 GiB (counter calibration)")
     return ap.parse_args()
 
 
@@ -58,29 +60,70 @@ def ffn_algorithmic(wl, counts_per_layer):
 
 
 def cpu_baseline(wl, target_s: float):
+    """The CPU oracle, as it stands, on a bounded sample of the workload.
+
+    Mini shapes: whole layer passes over all tokens (layer i % L of step
+    i // L) until the timed oracle work reaches target_s.  V3 shapes (22.5 GB
+    of experts): the first n tokens are routed on the host, only the experts
+    they chose are drawn, and the oracle's expert FFN and combine run for
+    them.  Weight generation is outside the timed part."""
     import numpy as np
     import torch
 
     import oracle
     from sparse_mixture_experts_51_amd import workloads
 
-    x = workloads.tokens(wl, 0, "cpu")
-    p = workloads.layer_params(wl, 0, "cpu")
-    hp = {k: (oracle.as_bf16_bits(v) if v.dtype == torch.bfloat16 else v.numpy())
-          for k, v in p.items()}
-    xb = oracle.as_bf16_bits(x)
     threads = oracle.default_threads()
-    n = min(wl.tokens, 64)
+    if wl.n_experts * wl.hidden * wl.d_model * 6 <= (1 << 31):
+        hp = {}
+        done, dt = 0, 0.0
+        while dt < target_s and done < wl.layers * wl.steps:
+            l, st = done % wl.layers, done // wl.layers
+            if l not in hp:
+                p = workloads.layer_params(wl, l, "cpu")
+                hp[l] = {k: (oracle.as_bf16_bits(v) if v.dtype == torch.bfloat16 else v.numpy())
+                         for k, v in p.items()}
+            xb = oracle.as_bf16_bits(workloads.tokens(wl, st, "cpu"))
+            t0 = time.perf_counter()
+            oracle.layer(xb, hp[l], wl.top_k, seq_len=wl.seq_len, nthreads=threads)
+            dt += time.perf_counter() - t0
+            done += 1
+        return {"value": done * wl.tokens / dt, "unit": "tokens/s", "cores": threads,
+                "kind": "oracle",
+                "sample": f"{done} layer passes over all {wl.tokens} tokens of {wl.name} (route, "
+                          f"balance statistic, permute, grouped FFN, combine), fp64 oracle, "
+                          f"{dt:.1f} s on {threads} threads; counts tokens x layers per second"}
+
+    import concurrent.futures as cf
+    xb = oracle.as_bf16_bits(workloads.tokens(wl, 0, "cpu"))
+    w_r = workloads.router(wl, 0, "cpu").numpy()
+    b = workloads.bias(wl, 0, "cpu").numpy()
+    sh = {k: oracle.as_bf16_bits(v) for k, v in workloads.shared_weights(wl, 0, "cpu").items()}
+    cache = {}
+    n = 4
     while True:
+        r = oracle.route(xb[:n], w_r, b, wl.top_k, threads)
+        for e in np.unique(r["idx"]):
+            if e not in cache:
+                ew = workloads.one_expert(wl, int(e), 0, "cpu")
+                cache[e] = tuple(oracle.as_bf16_bits(ew[k]) for k in ("w1", "w3", "w2"))
         t0 = time.perf_counter()
-        oracle.layer(xb[:n], hp, wl.top_k, nthreads=threads)
+        r = oracle.route(xb[:n], w_r, b, wl.top_k, threads)
+        jobs = [(t, j) for t in range(n) for j in range(wl.top_k)]
+        with cf.ThreadPoolExecutor(threads) as ex:
+            ys = list(ex.map(lambda tj: oracle.expert_ffn(xb[tj[0]], *cache[r["idx"][tj]]), jobs))
+            ysh = list(ex.map(lambda t: oracle.expert_ffn(xb[t], sh["ws1"], sh["ws3"], sh["ws2"]),
+                              range(n)))
+        pos = np.arange(n * wl.top_k, dtype=np.int32).reshape(n, wl.top_k)
+        oracle.combine(np.stack(ys), np.stack(ysh), r["gate"], r["idx"], pos)
         dt = time.perf_counter() - t0
-        if dt >= target_s / 4 or n >= wl.tokens:
+        if dt >= target_s / 2 or n >= min(64, wl.tokens):
             break
-        n = min(wl.tokens, int(n * max(2.0, min(8.0, target_s / 4 / max(dt, 1e-3)))))
+        n = min(64, wl.tokens, n * 2)
     return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} of {wl.tokens} tokens through one layer (route, permute, grouped "
-                      f"FFN, combine) of {wl.name}, fp64 oracle, {dt:.1f} s wall"}
+            "sample": f"first {n} of {wl.tokens} tokens of {wl.name}: routed on the host, then "
+                      f"expert FFN of their {wl.top_k} chosen experts plus the shared expert and "
+                      f"the combine, fp64 oracle, {dt:.1f} s on {threads} threads"}
 
 
 def main():
@@ -93,7 +136,16 @@ def main():
     import numpy as np
     import torch
 
-    from sparse_mixture_experts_51_amd import moe, workloads
+    from sparse_mixture_experts_51_amd import moe, profiling, workloads
+
+    if args.calibrate_copy:
+        # a plain device-to-device copy of profiling.COPY_BYTES bytes, three times
+        src = torch.empty(profiling.COPY_BYTES, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     name = args.workload or workloads.DEFAULT_BENCH_WORKLOAD
     wl = workloads.WORKLOADS[name]
@@ -163,7 +215,10 @@ def main():
         roof = {"bound": "hbm", "achieved": byts / t_s / 1e9, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    recorded = profiling.load_traffic(os.path.join(ROOT, "profiles"), wl.name)
+    roof["traffic"] = recorded["hbm_bytes_per_launch"] if recorded else None
+    if recorded:
+        roof["traffic_over_algorithmic"] = roof["traffic"] / byts
     roof["kernel"] = "moe_grouped_ffn = grouped_gemm_kernel<true> + grouped_gemm_kernel<false>"
     roof["ms_per_launch"] = ffn_ms
     roof["algorithmic_flop"] = flops

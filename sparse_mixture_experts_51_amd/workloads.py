@@ -160,14 +160,25 @@ def expert_weights(wl: Workload, layer: int = 0, device="cpu",
     a subset (the others stay zero), for host copies of a few experts."""
     E, H, d = wl.n_experts, wl.hidden, wl.d_model
     out = {}
-    for name, role, shape in (("w1", ROLE_W1, (H, d)), ("w3", ROLE_W3, (H, d)),
-                              ("w2", ROLE_W2, (d, H))):
-        t = torch.zeros((E,) + shape, dtype=torch.bfloat16, device=device)
+    for name, role, shape in _EXPERT_ROLES:
+        t = torch.zeros((E,) + shape(H, d), dtype=torch.bfloat16, device=device)
         for e in (range(E) if experts is None else experts):
-            t[e] = normal(shape, wl.w_std, seed_of(wl.weight_cfg_id, layer, role, e),
+            t[e] = normal(shape(H, d), wl.w_std, seed_of(wl.weight_cfg_id, layer, role, e),
                           device, torch.bfloat16)
         out[name] = t
     return out
+
+
+_EXPERT_ROLES = (("w1", ROLE_W1, lambda H, d: (H, d)), ("w3", ROLE_W3, lambda H, d: (H, d)),
+                 ("w2", ROLE_W2, lambda H, d: (d, H)))
+
+
+def one_expert(wl: Workload, e: int, layer: int = 0, device="cpu") -> dict:
+    """Expert e's w1, w3 [H, d] and w2 [d, H] alone: the same values as
+    expert_weights(...)[name][e], without the [E, ...] tensors."""
+    H, d = wl.hidden, wl.d_model
+    return {name: normal(shape(H, d), wl.w_std, seed_of(wl.weight_cfg_id, layer, role, e),
+                         device, torch.bfloat16) for name, role, shape in _EXPERT_ROLES}
 
 
 def shared_weights(wl: Workload, layer: int = 0, device="cpu") -> dict:

@@ -1,0 +1,61 @@
+"""Host-side checks of the rocprofv3 summary helpers (synthetic CSV input)."""
+import csv
+import json
+import os
+
+import pytest
+
+from sparse_mixture_experts_51_amd import profiling
+
+SWIG = "void moe::grouped_gemm_kernel<moe::TileCfg<128, 128, 2, 2, 2, true>, true>(moe::GroupedGemmArgs)"
+DOWN = "void moe::grouped_gemm_kernel<moe::TileCfg<128, 128, 2, 2, 2, true>, false>(moe::GroupedGemmArgs)"
+
+
+def _write(dirpath, counter, rows):
+    os.makedirs(dirpath, exist_ok=True)
+    with open(os.path.join(dirpath, "x_counter_collection.csv"), "w", newline="") as f:
+        w = csv.DictWriter(f, ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for i, (name, v) in enumerate(rows):
+            w.writerow({"Dispatch_Id": i, "Kernel_Name": name, "Counter_Name": counter,
+                        "Counter_Value": v})
+
+
+def test_traffic_scales_by_the_calibration_copy(tmp_path):
+    kib = profiling.COPY_BYTES / 1024
+    # the counter reads 2x the true bytes on the copy, so the factor is 0.5;
+    # a small upload copy must not enter the calibration
+    _write(tmp_path / "f", "FETCH_SIZE", [("__amd_rocclr_copyBuffer", 4.0),
+                                          ("__amd_rocclr_copyBuffer", 2 * kib),
+                                          ("__amd_rocclr_copyBuffer", 2 * kib),
+                                          (SWIG, 1000.0), (SWIG, 3000.0), (DOWN, 500.0)])
+    _write(tmp_path / "w", "WRITE_SIZE", [("__amd_rocclr_copyBuffer", kib),
+                                          (SWIG, 100.0), (DOWN, 300.0)])
+    t = profiling.traffic(str(tmp_path / "f"), str(tmp_path / "w"))
+    assert t["FETCH_SIZE"]["factor"] == pytest.approx(0.5)
+    assert t["FETCH_SIZE"]["bytes_per_launch"] == pytest.approx((2000.0 + 500.0) * 1024 * 0.5)
+    assert t["WRITE_SIZE"]["bytes_per_launch"] == pytest.approx(400.0 * 1024)
+
+
+def test_traffic_record_is_tied_to_the_gemm_source(tmp_path):
+    kib = profiling.COPY_BYTES / 1024
+    _write(tmp_path / "f", "FETCH_SIZE", [("__amd_rocclr_copyBuffer", kib), (SWIG, 10.0), (DOWN, 10.0)])
+    _write(tmp_path / "w", "WRITE_SIZE", [("__amd_rocclr_copyBuffer", kib), (SWIG, 1.0), (DOWN, 1.0)])
+    md = profiling.traffic_markdown(str(tmp_path / "f"), str(tmp_path / "w"), "wl", "cmd-f", "cmd-w")
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    (prof / "grouped_ffn_traffic_wl.md").write_text(md)
+    rec = profiling.load_traffic(str(prof), "wl")
+    assert rec["hbm_bytes_per_launch"] == pytest.approx(22.0 * 1024)
+    stale = md.replace(profiling.gemm_source_sha(), "0" * 64)
+    (prof / "grouped_ffn_traffic_wl.md").write_text(stale)
+    assert profiling.load_traffic(str(prof), "wl") is None
+    assert profiling.load_traffic(str(prof), "other") is None
+
+
+def test_stats_markdown(tmp_path):
+    p = tmp_path / "k_kernel_stats.csv"
+    p.write_text('"Name","Calls","TotalDurationNs","AverageNs","Percentage","MinNs","MaxNs","StdDev"\n'
+                 f'"{SWIG}",2,2000,1000.0,50.0,900,1100,1.0\n')
+    md = profiling.stats_markdown(str(p), "rocprofv3 ...", "t")
+    assert "| 2 | 1.0 | 0.9 | 1.1 | 50.00% |" in md
