@@ -45,15 +45,17 @@ namespace moe {
 constexpr int kBK = 64;                      // K per step
 constexpr int kChunksPerRow = kBK / 8;       // 16-byte chunks per tile row
 constexpr int kMaxGroups = 1025;
+typedef __attribute__((address_space(3))) void* lds_ptr_t;  // LDS address (DMA destination)
 
-template <int BM_, int BW_, int WM_, int WN_, int BPC_, bool XU_>
+template <int BM_, int BW_, int WM_, int WN_, int BPC_, bool DMAB_>
 struct TileCfg {
   static constexpr int BM = BM_;     // rows per unit
   static constexpr int BW = BW_;     // weight rows per unit
   static constexpr int WM = WM_;     // waves along M
   static constexpr int WN = WN_;     // waves along the weight tile
   static constexpr int BPC = BPC_;   // blocks per CU
-  static constexpr bool XU = XU_;    // prefetch across unit boundaries
+  static constexpr bool DMAB = DMAB_;  // weight tiles go from memory straight to LDS
+  static constexpr int NSB = DMAB ? 3 : 2;  // LDS buffers of the weight tile
   static constexpr int kThreads = 64 * WM * WN;
   static constexpr int kRowsPerPass = kThreads / kChunksPerRow;
   static constexpr int kLoadsA = BM / kRowsPerPass;
@@ -63,13 +65,18 @@ struct TileCfg {
   static_assert(BM % kRowsPerPass == 0 && BW % (2 * kRowsPerPass) == 0, "load passes");
   static_assert(TN % 2 == 0, "SwiGLU pairs gate and up tiles inside a wave");
 };
-using kStream = TileCfg<256, 128, 4, 2, 1, true>;
-using kCompute = TileCfg<128, 128, 2, 2, 2, true>;
+using kStream = TileCfg<192, 256, 2, 4, 1, true>;
+using kCompute = TileCfg<128, 128, 2, 2, 2, false>;
 
-// XOR swizzle of the 16-byte chunks of a row, so that the 32 rows an MFMA
-// fragment read touches at one chunk hit distinct LDS banks.
+// XOR swizzle of the 16-byte chunks of a 128-byte row.  gfx950's LDS has 64
+// four-byte banks (256 bytes per clock), so a 16-byte-per-lane access is
+// served 16 lanes at a time.  An MFMA fragment read has those 16 lanes on 16
+// consecutive rows at one logical chunk: rows 2j and 2j+1 fall in different
+// 128-byte halves of a bank line, and XOR with (row / 2) mod 8 spreads the 8
+// row pairs over the 8 chunks.  The stores (8 lanes per row, 2 rows per 16
+// lanes) stay conflict-free too.
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return row * kChunksPerRow + (chunk ^ (row & (kChunksPerRow - 1)));
+  return row * kChunksPerRow + (chunk ^ ((row >> 1) & (kChunksPerRow - 1)));
 }
 
 // Compile-time loop: calls f(integral_constant<int, I>) for I = 0..N-1, so
@@ -84,6 +91,22 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 #define MOE_FOR(I, N, ...) \
   static_for<0, N>([&](auto I##_c) { constexpr int I = decltype(I##_c)::value; __VA_ARGS__ });
+
+// Two 16-byte LDS reads, complete on return: the wait sits in the same asm
+// block, so the destination registers are never live while a read is in
+// flight.
+__device__ __forceinline__ void lds_read2_b128(const u32x4* p0, const u32x4* p1, u32x4& v0,
+                                               u32x4& v1) {
+  const unsigned a0 = static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_ptr_t)p0));
+  const unsigned a1 = static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_ptr_t)p1));
+  asm volatile(
+      "ds_read_b128 %0, %2\n\t"
+      "ds_read_b128 %1, %3\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v0), "=&v"(v1)
+      : "v"(a0), "v"(a1)
+      : "memory");
+}
 
 // LDS-only barrier: waits for this wave's LDS traffic, not for global loads.
 __device__ __forceinline__ void lds_barrier() {
@@ -156,7 +179,7 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
   constexpr int kThreads = C::kThreads, RPP = C::kRowsPerPass;
   constexpr int LA = C::kLoadsA, LB = C::kLoadsB, TM = C::TM, TN = C::TN;
   __shared__ u32x4 lds_a[2][C::BM * kChunksPerRow];
-  __shared__ u32x4 lds_b[2][C::BW * kChunksPerRow];
+  __shared__ u32x4 lds_b[C::NSB][C::BW * kChunksPerRow];
   __shared__ int unit_start[kMaxGroups + 1];
   __shared__ int offs[kMaxGroups + 1];  // copy of offsets[0..E]
   __shared__ int wsum[kThreads / 64];
@@ -216,19 +239,23 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
   // ---- source of a unit: buffer descriptors (wave-uniform, scalar
   // registers) plus 32-bit byte offsets.  An A row (a gathered token) needs a
   // per-thread offset per load pass; a weight row is a uniform row base (the
-  // scalar offset of the load) plus one per-thread term.  Rows are clamped to
-  // rows that exist (a tile's first row always does) so every load is
-  // unconditional; rows and columns past the tile's edge give results the
-  // epilogue never stores.  The descriptors' ranges make any stray offset read
-  // zeros.  perm_src entries are loaded one unit ahead and consumed only when
-  // that unit becomes current, so their latency hides behind a whole unit.
+  // scalar offset of the load) plus one per-thread term.  Every load is
+  // unconditional: an A row past the tile's valid rows gets an offset beyond
+  // the descriptor's range, which returns zeros without a memory access, and
+  // columns past the edge give results the epilogue never stores.  perm_src
+  // entries are loaded one unit ahead and consumed only when that unit becomes
+  // current, so their latency hides behind a whole unit.
   struct Src {
     __amdgpu_buffer_rsrc_t ra, rb0, rb1;  // A rows; W1 (or W2) rows; W3 rows
-    int a_off[LA];                        // per thread, bytes
+    int a_off[LA];                        // per thread, bytes (kOutOfRange: no row)
     int b_row[LB];                        // uniform, bytes: weight row base of each pass
     int b_thr;                            // per thread, bytes
     int nk;                               // K-steps with data
+    int rows;                             // valid A rows of the unit
   };
+  // Above any descriptor range (ranges are clamped to 2^31 - 1 bytes); offsets
+  // are advanced in unsigned arithmetic, so they stay out of range.
+  constexpr unsigned kOutOfRange = 0x80000000u;
   int pend_row[LA];  // prepared unit: group row / token per thread row
   int pend_map[LA];  // prepared unit: perm_src[pend_row] when gathering
   Unit pend;
@@ -237,7 +264,7 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
     const bool gather = pend.routed && a.a_row_map;
     MOE_FOR(i, LA, {
       int r = ld_row + RPP * i;
-      if (r >= pend.valid_rows) r = 0;
+      if (r >= pend.valid_rows) r = 0;  // a row that exists; its offset is replaced below
       pend_row[i] = pend.orow0 + r;
       // branch-free, so the loaded value is not touched until the unit switch
       const int32_t* src = gather ? a.a_row_map + pend_row[i] : a.offsets;
@@ -265,8 +292,10 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
     MOE_FOR(i, LA, {
       int row = gather ? pend_map[i] : pend_row[i];
       if (gather && (row < 0 || row >= a.T)) row = 0;  // malformed permutation: stay in bounds
-      sr.a_off[i] = (row * K + ld_chunk * 8) * 2;
+      sr.a_off[i] = ld_row + RPP * i < pend.valid_rows ? (row * K + ld_chunk * 8) * 2
+                                                       : static_cast<int>(kOutOfRange);
     })
+    sr.rows = pend.valid_rows;
     // weight tile: SwiGLU stage rows [0, BW/2) = W1[n0..], [BW/2, BW) = W3[n0..]
     // (each load pass lies in one half, so one descriptor per pass); down
     // stage rows [0, BW) = W2[n0..]
@@ -276,19 +305,28 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
       if (wrow >= N) wrow = 0;
       sr.b_row[i] = uni(wrow * K * 2);
     })
-    sr.b_thr = (ld_row * K + ld_chunk * 8) * 2;
+    // Register path: thread (ld_row, ld_chunk) loads that logical chunk and
+    // stores it swizzled.  DMA path: lane l of a wave writes physical slot
+    // l % 8 of row ld_row (8 rows per wave and pass), so it loads the logical
+    // chunk that the swizzle puts there (pass offsets are multiples of 64 rows
+    // and leave the swizzle unchanged).
+    const int b_chunk = C::DMAB ? (ld_chunk ^ ((ld_row >> 1) & (kChunksPerRow - 1))) : ld_chunk;
+    sr.b_thr = (ld_row * K + b_chunk * 8) * 2;
     sr.nk = pend.nk;
     return sr;
   };
 
+  // A K-step in flight: A rows in registers (and the weight rows too unless
+  // they go straight to LDS).
   struct Slice {
-    u32x4 a[LA], b[LB];
+    u32x4 a[LA], b[C::DMAB ? 1 : LB];
+    int rows;  // valid A rows of the unit the slice belongs to (uniform)
   };
   // Loads K-step f of the current source (f < steps0) or step f - steps0 of
   // the next one, chosen by a uniform test (scalar selects, no branches, so
   // the K-loop stays straight-line).  A step at or past nk (the padding step
   // of an odd count) reloads the last slice and is never multiplied.
-  auto load2 = [&](Slice& sl, const Src& c0, const Src& c1, int steps0, int f)
+  auto load2 = [&](Slice& sl, const Src& c0, const Src& c1, int steps0, int f, int bstage)
       __attribute__((always_inline)) {
     const bool nxt = f >= steps0;
     const int j = nxt ? f - steps0 : f;
@@ -298,20 +336,38 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
     const __amdgpu_buffer_rsrc_t rb0 = nxt ? c1.rb0 : c0.rb0;
     const __amdgpu_buffer_rsrc_t rb1 = nxt ? c1.rb1 : c0.rb1;
     const int bt = (nxt ? c1.b_thr : c0.b_thr) + kb;
+    sl.rows = nxt ? c1.rows : c0.rows;
     MOE_FOR(i, LA, {
-      const int ao = (nxt ? c1.a_off[i] : c0.a_off[i]) + kb;
-      sl.a[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, ao, 0, 0));
+      const unsigned ao = static_cast<unsigned>(nxt ? c1.a_off[i] : c0.a_off[i]) + kb;
+      sl.a[i] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, static_cast<int>(ao), 0, 0));
     })
     MOE_FOR(i, LB, {
       constexpr bool up = kSwiGLU && RPP * i >= C::BW / 2;
       const int br = nxt ? c1.b_row[i] : c0.b_row[i];
-      sl.b[i] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(up ? rb1 : rb0, bt, br, 0));
+      if constexpr (C::DMAB) {
+        // 64 lanes x 16 bytes land at consecutive LDS slots: rows
+        // RPP*i + 8*wave .. +8 of the stage
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            up ? rb1 : rb0,
+            (lds_ptr_t)&lds_b[bstage][(RPP * i + 8 * wave) * kChunksPerRow],
+            16, bt, br, 0, 0);
+      } else {
+        sl.b[i] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(up ? rb1 : rb0, bt, br, 0));
+      }
     })
   };
-  auto stash = [&](const Slice& sl, int buf) __attribute__((always_inline)) {
-    MOE_FOR(i, LA, { lds_a[buf][swz(ld_row + RPP * i, ld_chunk)] = sl.a[i]; })
-    MOE_FOR(i, LB, { lds_b[buf][swz(ld_row + RPP * i, ld_chunk)] = sl.b[i]; })
+  auto stash = [&](const Slice& sl, int buf, int bstage) __attribute__((always_inline)) {
+    // A passes wholly past the valid rows are not stored.  A pass spans whole
+    // 32-row MFMA tiles, so every tile the MFMAs read was stored from this
+    // unit (rows past the valid ones as zeros) and the others are skipped.
+    MOE_FOR(i, LA, {
+      if (RPP * i < sl.rows) lds_a[buf][swz(ld_row + RPP * i, ld_chunk)] = sl.a[i];
+    })
+    if constexpr (!C::DMAB) {
+      MOE_FOR(i, LB, { lds_b[bstage][swz(ld_row + RPP * i, ld_chunk)] = sl.b[i]; })
+    }
   };
 
   // Accumulators: acc[tm][tn], rows wm*BM/WM + 32*tm, weight-tile rows
@@ -328,7 +384,7 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
     return wn * (C::BW / C::WN) + 32 * tn;
   };
 
-  auto mma = [&](int buf, int mrows) __attribute__((always_inline)) {
+  auto mma = [&](int buf, int bstage, int mrows) __attribute__((always_inline)) {
     // mrows: 32-row tiles of this wave that hold valid rows (0..TM)
     if (mrows <= 0) return;
 #pragma unroll
@@ -337,9 +393,22 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
       const int fr = lane & 31;
       bf16x8 af[TM], bfr[TN];
       MOE_FOR(i, TM, {
-        af[i] = __builtin_bit_cast(bf16x8, lds_a[buf][swz(wm * (C::BM / C::WM) + 32 * i + fr, ch)]);
+        if (i < mrows)
+          af[i] = __builtin_bit_cast(bf16x8, lds_a[buf][swz(wm * (C::BM / C::WM) + 32 * i + fr, ch)]);
       })
-      MOE_FOR(j, TN, { bfr[j] = __builtin_bit_cast(bf16x8, lds_b[buf][swz(brow(j) + fr, ch)]); })
+      if constexpr (C::DMAB) {
+        // The compiler would put a full vmcnt(0) before any LDS read of a
+        // buffer that DMA writes, which drains the prefetched loads; vm_wait
+        // already orders these reads after the DMA, so they are issued in asm.
+        static_assert(TN == 2, "two weight fragments per sub-step");
+        u32x4 b0, b1;
+        lds_read2_b128(&lds_b[bstage][swz(brow(0) + fr, ch)], &lds_b[bstage][swz(brow(1) + fr, ch)],
+                       b0, b1);
+        bfr[0] = __builtin_bit_cast(bf16x8, b0);
+        bfr[1] = __builtin_bit_cast(bf16x8, b1);
+      } else {
+        MOE_FOR(j, TN, { bfr[j] = __builtin_bit_cast(bf16x8, lds_b[bstage][swz(brow(j) + fr, ch)]); })
+      }
       MOE_FOR(i, TM, {
         if (i < mrows) {
           MOE_FOR(j, TN, {
@@ -385,71 +454,67 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
   // fetcher stays two steps ahead, running into the next unit during the last
   // two steps of the current one.  The unit after the last one is the last
   // one again: its loads are valid and never used.
+  //
+  // Weight tiles through registers: two LDS buffers, step k in buffer k % 2.
+  // Weight tiles by LDS DMA: three LDS stages, step k in stage k % 3; the
+  // stage written at step k (for step k + 2) was last read at step k - 1,
+  // before the barrier that ends it.  At the end of step k the loads of
+  // step k + 1 must have landed: the compiler waits for its A registers
+  // before the store to LDS, and vm_wait waits for the DMA, which the
+  // compiler does not track -- after it, this thread issued only the LA + LB
+  // loads of step k + 2 (any extra younger memory operation makes the wait
+  // stricter, not weaker).
   auto next_of = [&](int u) __attribute__((always_inline)) {
     return u + G < total_units ? u + G : u;
   };
+  auto vm_wait = [&]() __attribute__((always_inline)) {
+    if constexpr (C::DMAB) {
+      constexpr int n = LA + LB;  // < 64, the vmcnt field
+      static_assert(n < 16, "vmcnt immediate below");
+      __builtin_amdgcn_s_waitcnt(0x0F70 | n);  // vmcnt(n); lgkmcnt, expcnt unconstrained
+    }
+  };
+  auto stage_after = [](int st, int d) __attribute__((always_inline)) {
+    st += d;
+    return st >= C::NSB ? st - C::NSB : st;
+  };
   Slice r0, r1;
-  if constexpr (C::XU) {
-    prepare(lb);
-    Src cur = source_of_pending();
-    Unit cu = pend;
-    prepare(next_of(lb));
-    load2(r0, cur, cur, 1 << 30, 0);
-    load2(r1, cur, cur, 1 << 30, 1);
-    stash(r0, 0);
-    lds_barrier();
-    for (int u = lb; u < total_units; u += G) {
-      const Src nxt = source_of_pending();
-      const Unit nu = pend;
-      prepare(next_of(next_of(u)));
-      const int steps = cur.nk + (cur.nk & 1);
-      // 32-row tiles of this wave with valid rows
-      int mrows = (cu.valid_rows - wm * (C::BM / C::WM) + 31) / 32;
-      mrows = mrows < 0 ? 0 : (mrows > TM ? TM : mrows);
-      zero_acc();
-      for (int kt = 0; kt < steps; kt += 2) {
-        load2(r0, cur, nxt, steps, kt + 2);
-        mma(0, mrows);
-        stash(r1, 1);
-        lds_barrier();
-        load2(r1, cur, nxt, steps, kt + 3);
-        mma(1, kt + 1 < cur.nk ? mrows : 0);
-        stash(r0, 0);
-        lds_barrier();
-      }
-      epilogue(cu);
-      cur = nxt;
-      cu = nu;
-    }
-  } else {
-    // Units are long (many K-steps): the pipeline restarts at each unit and
-    // only the perm_src lookups run one unit ahead.
-    prepare(lb);
-    for (int u = lb; u < total_units; u += G) {
-      const Src cur = source_of_pending();
-      const Unit cu = pend;
-      prepare(next_of(u));
-      const int steps = cur.nk + (cur.nk & 1);
-      int mrows = (cu.valid_rows - wm * (C::BM / C::WM) + 31) / 32;
-      mrows = mrows < 0 ? 0 : (mrows > TM ? TM : mrows);
-      load2(r0, cur, cur, 1 << 30, 0);
-      load2(r1, cur, cur, 1 << 30, 1);
-      lds_barrier();  // the previous unit's last LDS reads are done
-      stash(r0, 0);
+  int cs = 0;  // weight stage of the current step
+  prepare(lb);
+  Src cur = source_of_pending();
+  Unit cu = pend;
+  prepare(next_of(lb));
+  load2(r0, cur, cur, 1 << 30, 0, 0);
+  load2(r1, cur, cur, 1 << 30, 1, 1 % C::NSB);
+  stash(r0, 0, 0);
+  vm_wait();
+  lds_barrier();
+  for (int u = lb; u < total_units; u += G) {
+    const Src nxt = source_of_pending();
+    const Unit nu = pend;
+    prepare(next_of(next_of(u)));
+    const int steps = cur.nk + (cur.nk & 1);
+    // 32-row tiles of this wave with valid rows
+    int mrows = (cu.valid_rows - wm * (C::BM / C::WM) + 31) / 32;
+    mrows = mrows < 0 ? 0 : (mrows > TM ? TM : mrows);
+    zero_acc();
+    for (int kt = 0; kt < steps; kt += 2) {
+      const int c1 = stage_after(cs, 1);
+      load2(r0, cur, nxt, steps, kt + 2, stage_after(cs, 2));
+      mma(0, cs, mrows);
+      stash(r1, 1, c1);
+      vm_wait();
       lds_barrier();
-      zero_acc();
-      for (int kt = 0; kt < steps; kt += 2) {
-        load2(r0, cur, cur, 1 << 30, kt + 2 < steps ? kt + 2 : steps - 1);
-        mma(0, mrows);
-        stash(r1, 1);
-        lds_barrier();
-        load2(r1, cur, cur, 1 << 30, kt + 3 < steps ? kt + 3 : steps - 1);
-        mma(1, kt + 1 < cur.nk ? mrows : 0);
-        stash(r0, 0);
-        lds_barrier();
-      }
-      epilogue(cu);
+      load2(r1, cur, nxt, steps, kt + 3, stage_after(c1, 2));
+      mma(1, c1, kt + 1 < cur.nk ? mrows : 0);
+      cs = stage_after(c1, 1);
+      stash(r0, 0, cs);
+      vm_wait();
+      lds_barrier();
     }
+    epilogue(cu);
+    cur = nxt;
+    cu = nu;
   }
 }
 
