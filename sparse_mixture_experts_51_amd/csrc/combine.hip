@@ -9,56 +9,67 @@
 
 namespace moe {
 
-// One wave per token; each lane owns 16-byte (8 x bf16) column chunks.
+// One thread per (token, 16-byte column chunk), flattened so that a wave
+// reads 1 KB runs of each row whatever d is, and tokens x chunks threads keep
+// the chip busy even for a handful of tokens.
 // out[t] = bf16(residual[t] + y_shared[t] + sum_j g[t,j] * y_perm[pos[t,j]]),
 // fp32 accumulation, slots in order.  Rows outside [0, T*k) are skipped.
+template <typename Index>
 __global__ __launch_bounds__(256) void combine_kernel(
     const uint16_t* __restrict__ y_perm, const uint16_t* __restrict__ y_shared,
     const float* __restrict__ gate, const int32_t* __restrict__ pos,
-    const uint16_t* __restrict__ residual, uint16_t* __restrict__ out, int64_t T, int d, int k) {
-  const int lane = threadIdx.x & 63;
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const int chunks = d / 8;
-  const int64_t nrows = T * k;
-  for (int c = lane; c < chunks; c += kWave) {
-    float acc[8];
+    const uint16_t* __restrict__ residual, uint16_t* __restrict__ out, Index T, int d, int k) {
+  const Index chunks = static_cast<Index>(d / 8);
+  const Index i = static_cast<Index>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= T * chunks) return;
+  const Index t = i / chunks;
+  const Index c = i - t * chunks;
+  const int64_t nrows = static_cast<int64_t>(T) * k;
+  float acc[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-    float v[8];
-    if (residual) {
-      bf16x8_to_f32(reinterpret_cast<const uint4*>(residual + t * d)[c], v);
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+  float v[8];
+  const int64_t row_t = static_cast<int64_t>(t) * d + static_cast<int64_t>(c) * 8;
+  if (residual) {
+    bf16x8_to_f32(*reinterpret_cast<const uint4*>(residual + row_t), v);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += v[i];
-    }
-    if (y_shared) {
-      bf16x8_to_f32(reinterpret_cast<const uint4*>(y_shared + t * d)[c], v);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += v[i];
-    }
-    for (int j = 0; j < k; ++j) {
-      const int row = pos[t * k + j];
-      if (row < 0 || row >= nrows) continue;
-      const float g = gate[t * k + j];
-      bf16x8_to_f32(reinterpret_cast<const uint4*>(y_perm + static_cast<int64_t>(row) * d)[c], v);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = fmaf(g, v[i], acc[i]);
-    }
-    uint4 o;
-    o.x = pack_bf16x2(acc[0], acc[1]);
-    o.y = pack_bf16x2(acc[2], acc[3]);
-    o.z = pack_bf16x2(acc[4], acc[5]);
-    o.w = pack_bf16x2(acc[6], acc[7]);
-    reinterpret_cast<uint4*>(out + t * d)[c] = o;
+    for (int e = 0; e < 8; ++e) acc[e] += v[e];
   }
+  if (y_shared) {
+    bf16x8_to_f32(*reinterpret_cast<const uint4*>(y_shared + row_t), v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += v[e];
+  }
+  const int64_t slot0 = static_cast<int64_t>(t) * k;
+  for (int j = 0; j < k; ++j) {
+    const int row = pos[slot0 + j];
+    if (row < 0 || row >= nrows) continue;
+    const float g = gate[slot0 + j];
+    bf16x8_to_f32(*reinterpret_cast<const uint4*>(y_perm + static_cast<int64_t>(row) * d +
+                                                  static_cast<int64_t>(c) * 8), v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = fmaf(g, v[e], acc[e]);
+  }
+  uint4 o;
+  o.x = pack_bf16x2(acc[0], acc[1]);
+  o.y = pack_bf16x2(acc[2], acc[3]);
+  o.z = pack_bf16x2(acc[4], acc[5]);
+  o.w = pack_bf16x2(acc[6], acc[7]);
+  *reinterpret_cast<uint4*>(out + row_t) = o;
 }
 
 hipError_t launch_combine(const uint16_t* y_perm, const uint16_t* y_shared, const float* gate,
                           const int32_t* pos, const uint16_t* residual, uint16_t* out,
                           int64_t T, int d, int k, hipStream_t s) {
-  const int64_t nblk = (T + 3) / 4;
-  hipLaunchKernelGGL(combine_kernel, dim3(static_cast<unsigned>(nblk)), dim3(256), 0, s, y_perm,
-                     y_shared, gate, pos, residual, out, T, d, k);
+  const int64_t n = T * (d / 8);
+  const int64_t nblk = (n + 255) / 256;
+  if (n + 256 < (int64_t{1} << 31)) {
+    hipLaunchKernelGGL(combine_kernel<int32_t>, dim3(static_cast<unsigned>(nblk)), dim3(256), 0,
+                       s, y_perm, y_shared, gate, pos, residual, out, static_cast<int32_t>(T), d, k);
+  } else {
+    hipLaunchKernelGGL(combine_kernel<int64_t>, dim3(static_cast<unsigned>(nblk)), dim3(256), 0,
+                       s, y_perm, y_shared, gate, pos, residual, out, T, d, k);
+  }
   return hipGetLastError();
 }
 

@@ -422,32 +422,87 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
     }
   };
 
+  // SiLU(gate) * up in fp32 (v_rcp_f32 for the quotient).
+  auto swiglu = [](float ga, float up) __attribute__((always_inline)) {
+    return ga * __builtin_amdgcn_rcpf(1.0f + __expf(-ga)) * up;
+  };
+  // 32x32 accumulator layout: lane holds column (lane & 31), rows
+  // (v/4)*8 + (lane/32)*4 + v%4 for v = 0..15.
+  const int col_l = lane & 31;
+  const int row_l = (lane >> 5) * 4;
   auto epilogue = [&](const Unit& cu) __attribute__((always_inline)) {
-    // 32x32 accumulator layout: lane holds column (lane & 31), rows
-    // (v/4)*8 + (lane/32)*4 + v%4 for v = 0..15.
-    const int col_l = lane & 31;
-    const int row_l = (lane >> 5) * 4;
     uint16_t* cbase = cu.routed ? a.c_routed : a.c_shared;
-    MOE_FOR(i, TM, {
-      MOE_FOR(v, 16, {
-        const int r = wm * (C::BM / C::WM) + 32 * i + (v >> 2) * 8 + row_l + (v & 3);
-        if (r < cu.valid_rows) {
-          uint16_t* orow = cbase + (static_cast<int64_t>(cu.orow0) + r) * cu.N;
+    constexpr int kCols = kSwiGLU ? C::BW / 2 : C::BW;
+    constexpr bool kViaLds =
+        !C::DMAB && (C::BM * kChunksPerRow * 16 + C::BW * kChunksPerRow * 16) / (kCols * 2) >= C::BM;
+    if constexpr (kViaLds) {
+      // Through LDS: each lane's column values go into the idle half of the
+      // double buffer (buffer 1, free since the barrier after the last
+      // K-step), then whole rows leave as 16-byte stores.  Rows are COLS
+      // bf16 wide; the 16-byte chunk q of row r sits at chunk q ^ (r & 4),
+      // so the two rows one 2-byte write instruction covers (r and r + 4)
+      // hit different banks.  Rows [0, kHalfRows) live in lds_a[1], the rest
+      // in lds_b[1].  Tiles that do not fit there store straight from the
+      // accumulators (below).
+      constexpr int COLS = kCols;
+      constexpr int RB = COLS * 2;
+      constexpr int kHalfRows = C::BM * kChunksPerRow * 16 / RB;
+      auto cbyte = [&](int r, int byte) __attribute__((always_inline)) {
+        unsigned char* h = r < kHalfRows ? reinterpret_cast<unsigned char*>(&lds_a[1][0])
+                                         : reinterpret_cast<unsigned char*>(&lds_b[1][0]);
+        const int rr = r < kHalfRows ? r : r - kHalfRows;
+        return h + rr * RB + (((byte >> 4) ^ (r & 4)) << 4) + (byte & 15);
+      };
+      MOE_FOR(i, TM, {
+        MOE_FOR(v, 16, {
+          const int r = wm * (C::BM / C::WM) + 32 * i + (v >> 2) * 8 + row_l + (v & 3);
           if (kSwiGLU) {
             MOE_FOR(j, TN / 2, {
-              const float ga = acc[i][j][v], up = acc[i][j + TN / 2][v];
-              const float hval = ga / (1.0f + __expf(-ga)) * up;
-              orow[cu.n0 + wn * HC + 32 * j + col_l] = f32_to_bf16(hval);
+              const int c = wn * HC + 32 * j + col_l;
+              *reinterpret_cast<uint16_t*>(cbyte(r, 2 * c)) =
+                  f32_to_bf16(swiglu(acc[i][j][v], acc[i][j + TN / 2][v]));
             })
           } else {
             MOE_FOR(j, TN, {
-              const int c = cu.n0 + wn * (C::BW / C::WN) + 32 * j + col_l;
-              if (c < cu.N) orow[c] = f32_to_bf16(acc[i][j][v]);
+              const int c = wn * (C::BW / C::WN) + 32 * j + col_l;
+              *reinterpret_cast<uint16_t*>(cbyte(r, 2 * c)) = f32_to_bf16(acc[i][j][v]);
             })
           }
-        }
+        })
       })
-    })
+      lds_barrier();
+      constexpr int kChunks = C::BM * COLS / 8;
+      const int ncols = cu.N - cu.n0 < COLS ? cu.N - cu.n0 : COLS;
+      for (int idx = tid; idx < kChunks; idx += kThreads) {
+        const int r = idx / (COLS / 8), q = idx % (COLS / 8);
+        if (r < cu.valid_rows && q * 8 < ncols) {
+          const u32x4 val = *reinterpret_cast<const u32x4*>(cbyte(r, q * 16));
+          *reinterpret_cast<u32x4*>(cbase + (static_cast<int64_t>(cu.orow0) + r) * cu.N + cu.n0 +
+                                    q * 8) = val;
+        }
+      }
+      lds_barrier();  // buffer 1 is stashed into during the next unit's first step
+    } else {
+      MOE_FOR(i, TM, {
+        MOE_FOR(v, 16, {
+          const int r = wm * (C::BM / C::WM) + 32 * i + (v >> 2) * 8 + row_l + (v & 3);
+          if (r < cu.valid_rows) {
+            uint16_t* orow = cbase + (static_cast<int64_t>(cu.orow0) + r) * cu.N;
+            if (kSwiGLU) {
+              MOE_FOR(j, TN / 2, {
+                orow[cu.n0 + wn * HC + 32 * j + col_l] =
+                    f32_to_bf16(swiglu(acc[i][j][v], acc[i][j + TN / 2][v]));
+              })
+            } else {
+              MOE_FOR(j, TN, {
+                const int c = cu.n0 + wn * (C::BW / C::WN) + 32 * j + col_l;
+                if (c < cu.N) orow[c] = f32_to_bf16(acc[i][j][v]);
+              })
+            }
+          }
+        })
+      })
+    }
   };
 
   // ---- software pipeline.  Each unit runs an even number of K-steps; the
