@@ -42,7 +42,7 @@ Workspace carve_workspace(void* base, int64_t T, int d, int E, int k, int H, int
     return base ? static_cast<char*>(base) + o : nullptr;
   };
   const int64_t nblk = (T + kPermTokens - 1) / kPermTokens;
-  const int nsplit = seq_splits(T, S);
+  const int nsplit = seq_partials_capacity(T, S);
   const int64_t nseq = S > 0 ? T / S : 0;
   w.scores = reinterpret_cast<float*>(take(sizeof(float) * T * E));
   w.tok_sum = reinterpret_cast<double*>(take(sizeof(double) * (S > 0 ? T : 0)));
@@ -136,7 +136,12 @@ moe_status moe_route(const moe_shape* shape, const uint16_t* x, const float* w_r
   const int64_t T = shape->tokens;
   const int d = shape->d_model, E = shape->n_experts, k = shape->top_k, S = shape->seq_len;
   const bool stats = S > 0 && seq_balance != nullptr;
-  hipError_t e = moe::launch_router_scores(x, w_router, w.scores, T, d, E, s);
+  bool fused = false;
+  hipError_t e = moe::launch_route_fused(x, w_router, bias, topk_idx, topk_gate, margin, w.seq_p,
+                                         w.seq_cnt, stats ? seq_balance : nullptr, alpha, T, d, E,
+                                         k, S, s, &fused);
+  if (e != hipSuccess || fused) return hip_status(e);
+  e = moe::launch_router_scores(x, w_router, w.scores, T, d, E, s);
   if (e == hipSuccess)
     e = moe::launch_select(w.scores, bias, topk_idx, topk_gate, margin, stats ? w.tok_sum : nullptr,
                            T, E, k, s);

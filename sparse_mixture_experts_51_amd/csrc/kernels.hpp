@@ -25,6 +25,8 @@ struct Workspace {
 constexpr int kPermTokens = 256;  // tokens per block of the permutation kernels
 
 int seq_splits(int64_t T, int S);
+// Balance-statistic partials per sequence that the workspace holds.
+int seq_partials_capacity(int64_t T, int S);
 Workspace carve_workspace(void* base, int64_t T, int d, int E, int k, int H, int Hs, int S);
 
 // Number of compute units of the current device (cached per device).
@@ -32,6 +34,12 @@ int device_cus();
 
 hipError_t launch_router_scores(const uint16_t* x, const float* w_router, float* scores,
                                 int64_t T, int d, int E, hipStream_t s);
+// Router, selection and balance statistic in one pass when one block can hold
+// all experts (E <= 64); *done is false when the shape takes the general path.
+hipError_t launch_route_fused(const uint16_t* x, const float* w_router, const float* bias,
+                              int32_t* idx, float* gate, float* margin, double* seq_p,
+                              int32_t* seq_cnt, float* seq_out, float alpha, int64_t T, int d,
+                              int E, int k, int S, hipStream_t s, bool* done);
 hipError_t launch_select(const float* scores, const float* bias, int32_t* idx, float* gate,
                          float* margin, double* tok_sum, int64_t T, int E, int k, hipStream_t s);
 hipError_t launch_seq_balance(const float* scores, const double* tok_sum, const int32_t* idx,

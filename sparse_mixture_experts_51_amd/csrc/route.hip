@@ -42,9 +42,11 @@ __device__ __forceinline__ void route_lds_barrier() {
 // prefetched into registers while this one is multiplied.  Every (token,
 // expert) logit is one fp32 fmaf chain over d in ascending order.
 template <int EPT, int TPT>
-__global__ __launch_bounds__(kRouteThreads) void router_scores_kernel(
-    const uint16_t* __restrict__ x, const float* __restrict__ w_router,
-    float* __restrict__ scores, int64_t T, int d, int E, int BE, int KC) {
+__device__ __forceinline__ void router_logits_tile(const uint16_t* __restrict__ x,
+                                                   const float* __restrict__ w_router, int64_t T,
+                                                   int d, int E, int BE, int KC,
+                                                   unsigned char* lds_raw,
+                                                   float (&acc)[TPT][EPT]) {
   const int TPR = BE / EPT;
   const int rows = kRouteThreads / TPR;
   const int BT = rows * TPT;
@@ -55,7 +57,6 @@ __global__ __launch_bounds__(kRouteThreads) void router_scores_kernel(
   const int64_t t0 = static_cast<int64_t>(blockIdx.x / n_eblk) * BT;
   const int nchunks = d / KC;
 
-  extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
   const int xrow = KC * 2 + 16, wrow = KC * EPT * 4 + 16;  // padded row strides (bytes)
   const int bufbytes = BT * xrow + TPR * wrow;
   auto xs = [&](int b) { return lds_raw + b * bufbytes; };
@@ -141,7 +142,6 @@ __global__ __launch_bounds__(kRouteThreads) void router_scores_kernel(
     }
   };
 
-  float acc[TPT][EPT];
 #pragma unroll
   for (int i = 0; i < TPT; ++i)
 #pragma unroll
@@ -182,7 +182,25 @@ __global__ __launch_bounds__(kRouteThreads) void router_scores_kernel(
       route_lds_barrier();
     }
   }
+}
 
+// Affinity score: the logistic function evaluated in fp64, rounded once.
+__device__ __forceinline__ float sigmoid_score(float logit) {
+  return static_cast<float>(1.0 / (1.0 + exp(-static_cast<double>(logit))));
+}
+
+template <int EPT, int TPT>
+__global__ __launch_bounds__(kRouteThreads) void router_scores_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ w_router,
+    float* __restrict__ scores, int64_t T, int d, int E, int BE, int KC) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+  float acc[TPT][EPT];
+  router_logits_tile<EPT, TPT>(x, w_router, T, d, E, BE, KC, lds_raw, acc);
+  const int TPR = BE / EPT;
+  const int tx = threadIdx.x % TPR, ty = threadIdx.x / TPR;
+  const int n_eblk = (E + BE - 1) / BE;
+  const int e0 = (blockIdx.x % n_eblk) * BE;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x / n_eblk) * ((kRouteThreads / TPR) * TPT);
 #pragma unroll
   for (int i = 0; i < TPT; ++i) {
     const int64_t t = t0 + ty * TPT + i;
@@ -190,9 +208,7 @@ __global__ __launch_bounds__(kRouteThreads) void router_scores_kernel(
 #pragma unroll
     for (int j = 0; j < EPT; ++j) {
       const int e = e0 + tx * EPT + j;
-      if (e < E)
-        scores[t * E + e] =
-            static_cast<float>(1.0 / (1.0 + exp(-static_cast<double>(acc[i][j]))));
+      if (e < E) scores[t * E + e] = sigmoid_score(acc[i][j]);
     }
   }
 }
@@ -209,7 +225,7 @@ struct RouterCfg {
   size_t lds;
 };
 
-static RouterCfg router_cfg(int64_t T, int d, int E, int want_blocks) {
+static RouterCfg router_cfg(int64_t T, int d, int E, int want_blocks, bool whole_e = false) {
   // Largest per-thread tile that still gives one block per CU (with few
   // tokens, trade tile size for blocks: each (token, expert) chain is serial
   // over d, so parallelism is bounded by T*E lanes).  A chunk of d is the
@@ -223,6 +239,7 @@ static RouterCfg router_cfg(int64_t T, int d, int E, int want_blocks) {
   for (int ti = 0; ti < 3; ++ti) {
     for (int bi = 0; bi < 4; ++bi) {
       const int BE = be_list[bi] < Emax ? be_list[bi] : Emax;
+      if (whole_e && BE != Emax) continue;  // one block holds all experts of its tokens
       const int EPT = ept_of(BE) > BE ? BE : ept_of(BE);
       const int TPR = BE / EPT;
       const int TPT = tpt_list[ti];
@@ -274,6 +291,85 @@ hipError_t launch_router_scores(const uint16_t* x, const float* w_router, float*
   return hipErrorInvalidValue;
 }
 
+template <int EPL>
+__device__ __forceinline__ double select_token(const float* srow, const float* __restrict__ bias,
+                                               int lane, int G, int E, int k,
+                                               int32_t* __restrict__ idx_row,
+                                               float* __restrict__ gate_row, float* margin_out,
+                                               double* tok_sum_out);
+
+// Fused routing for E <= 64, where one block holds all experts of its BT
+// tokens: logits and scores (as router_scores_kernel), then selection,
+// gates and margin from the scores kept in LDS (as select_kernel), and --
+// with the balance statistic -- the block's partial sums for its sequence:
+// P_e = sum over its tokens, in token order, of s[t,e] / sum_j s[t,j] (fp64)
+// and the choice counts, at partial index blockIdx.x (a block lies inside one
+// sequence, so seq_final_kernel adds S / BT partials per sequence).
+template <int EPT, int TPT>
+__global__ __launch_bounds__(kRouteThreads) void router_fused_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ w_router,
+    const float* __restrict__ bias, int32_t* __restrict__ idx, float* __restrict__ gate,
+    float* __restrict__ margin, double* __restrict__ seq_p, int32_t* __restrict__ seq_cnt,
+    int64_t T, int d, int E, int k, int BE, int KC, int G) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+  float acc[TPT][EPT];
+  router_logits_tile<EPT, TPT>(x, w_router, T, d, E, BE, KC, lds_raw, acc);
+  const int TPR = BE / EPT;
+  const int tx = threadIdx.x % TPR, ty = threadIdx.x / TPR;
+  const int BT = (kRouteThreads / TPR) * TPT;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * BT;
+  float* sc = reinterpret_cast<float*>(lds_raw);                     // [BT][E]
+  double* tsum = reinterpret_cast<double*>(lds_raw + ((BT * E * 4 + 15) & ~15));  // [BT]
+  __syncthreads();  // every wave is done reading the staged x and W_r
+#pragma unroll
+  for (int i = 0; i < TPT; ++i)
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      const int e = tx * EPT + j;
+      if (e < E) sc[(ty * TPT + i) * E + e] = sigmoid_score(acc[i][j]);
+    }
+  __syncthreads();
+  const int lane = threadIdx.x % G, grp = threadIdx.x / G, ngrp = kRouteThreads / G;
+  for (int tl = grp; tl < BT; tl += ngrp) {
+    const int64_t t = t0 + tl;
+    if (t >= T) continue;  // whole group skips together
+    const double ts = select_token<1>(sc + tl * E, bias, lane, G, E, k, idx + t * k, gate + t * k,
+                                      margin ? margin + t : nullptr, nullptr);
+    if (lane == 0) tsum[tl] = ts;
+  }
+  if (!seq_p) return;
+  // Partials: thread (e, lane l of L = 256 / E) sums s/sum(s) over the tokens
+  // l, l + L, ... in order; the L lane sums are then added in lane order.
+  // Counts: one LDS atomic per (token, slot) of this block.
+  double* part = tsum + BT;                                  // [256]
+  int* cnt = reinterpret_cast<int*>(part + kRouteThreads);   // [E]
+  for (int e = threadIdx.x; e < E; e += kRouteThreads) cnt[e] = 0;
+  __syncthreads();  // tsum, cnt and this block's idx rows are complete
+  const int nt = (T - t0) < BT ? static_cast<int>(T - t0) : BT;
+  for (int i = threadIdx.x; i < nt * k; i += kRouteThreads) {
+    const int e = idx[t0 * k + i];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  }
+  const int L = kRouteThreads / E;
+  {
+    const int e = threadIdx.x % E, l = threadIdx.x / E;
+    double pe = 0.0;
+    if (l < L)
+      for (int tl = l; tl < nt; tl += L) {
+        const double tot = tsum[tl];
+        pe += (tot == 0.0) ? 1.0 / E : static_cast<double>(sc[tl * E + e]) / tot;
+      }
+    part[threadIdx.x] = pe;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kRouteThreads) {
+    double pe = 0.0;
+    for (int l = 0; l < L; ++l) pe += part[l * E + e];
+    seq_p[static_cast<int64_t>(blockIdx.x) * E + e] = pe;
+    seq_cnt[static_cast<int64_t>(blockIdx.x) * E + e] = cnt[e];
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Top-k selection and gates
 
@@ -285,16 +381,11 @@ __device__ __forceinline__ uint64_t pack_key(float key, int e) {
 }
 
 template <int EPL>
-__global__ __launch_bounds__(256) void select_kernel(
-    const float* __restrict__ scores, const float* __restrict__ bias, int32_t* __restrict__ idx,
-    float* __restrict__ gate, float* __restrict__ margin, double* __restrict__ tok_sum,
-    int64_t T, int E, int k, int G) {
-  const int lane = threadIdx.x % G;
-  const int grp = threadIdx.x / G;
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * (256 / G) + grp;
-  if (t >= T) return;  // whole group leaves together
-  const float* srow = scores + t * E;
-
+__device__ __forceinline__ double select_token(const float* srow, const float* __restrict__ bias,
+                                               int lane, int G, int E, int k,
+                                               int32_t* __restrict__ idx_row,
+                                               float* __restrict__ gate_row, float* margin_out,
+                                               double* tok_sum_out) {
   uint64_t pk[EPL];
   double ssum = 0.0;
 #pragma unroll
@@ -338,14 +429,26 @@ __global__ __launch_bounds__(256) void select_kernel(
   float sum = 0.0f;
   for (int j = 0; j < k; ++j) sum += __shfl(s_mine, j, G);
   if (lane < k) {
-    idx[t * k + lane] = my_e;
-    gate[t * k + lane] = (sum == 0.0f) ? 1.0f / static_cast<float>(k) : s_mine / sum;
+    idx_row[lane] = my_e;
+    gate_row[lane] = (sum == 0.0f) ? 1.0f / static_cast<float>(k) : s_mine / sum;
   }
-  if (lane == 0 && margin) margin[t] = (k < E) ? kth - next : __builtin_inff();
-  if (tok_sum) {
-    for (int off = G >> 1; off > 0; off >>= 1) ssum += __shfl_xor(ssum, off, G);
-    if (lane == 0) tok_sum[t] = ssum;
-  }
+  if (lane == 0 && margin_out) *margin_out = (k < E) ? kth - next : __builtin_inff();
+  for (int off = G >> 1; off > 0; off >>= 1) ssum += __shfl_xor(ssum, off, G);
+  if (lane == 0 && tok_sum_out) *tok_sum_out = ssum;
+  return ssum;
+}
+
+template <int EPL>
+__global__ __launch_bounds__(256) void select_kernel(
+    const float* __restrict__ scores, const float* __restrict__ bias, int32_t* __restrict__ idx,
+    float* __restrict__ gate, float* __restrict__ margin, double* __restrict__ tok_sum,
+    int64_t T, int E, int k, int G) {
+  const int lane = threadIdx.x % G;
+  const int grp = threadIdx.x / G;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * (256 / G) + grp;
+  if (t >= T) return;  // whole group leaves together
+  select_token<EPL>(scores + t * E, bias, lane, G, E, k, idx + t * k, gate + t * k,
+                    margin ? margin + t : nullptr, tok_sum ? tok_sum + t : nullptr);
 }
 
 hipError_t launch_select(const float* scores, const float* bias, int32_t* idx, float* gate,
@@ -459,6 +562,52 @@ hipError_t launch_seq_balance(const float* scores, const double* tok_sum, const 
   hipLaunchKernelGGL(seq_final_kernel, dim3(static_cast<unsigned>(nseq)), dim3(256), 0, s, seq_p,
                      seq_cnt, out, alpha, E, k, S, nsplit);
   return hipGetLastError();
+}
+
+int seq_partials_capacity(int64_t T, int S) {
+  if (S <= 0) return 0;
+  const int a = seq_splits(T, S);
+  const int b = S / 16 > 0 ? S / 16 : 1;  // the fused path's blocks hold >= 16 tokens
+  return a > b ? a : b;
+}
+
+hipError_t launch_route_fused(const uint16_t* x, const float* w_router, const float* bias,
+                              int32_t* idx, float* gate, float* margin, double* seq_p,
+                              int32_t* seq_cnt, float* seq_out, float alpha, int64_t T, int d,
+                              int E, int k, int S, hipStream_t s, bool* done) {
+  *done = false;
+  if (E > 64) return hipSuccess;
+  const RouterCfg c = router_cfg(T, d, E, device_cus(), true);
+  if (c.blocks <= 0 || c.BE < E) return hipSuccess;
+  const int TPR = c.BE / c.EPT;
+  const int BT = (kRouteThreads / TPR) * c.TPT;
+  const bool stats = seq_out != nullptr && S > 0;
+  if (stats && (S % BT != 0 || S / BT > seq_partials_capacity(T, S))) return hipSuccess;
+  const int G = next_pow2(E);
+  // scores [BT][E] f32, tok sums [BT] f64, lane partials [256] f64, counts [E] i32
+  const size_t tail = static_cast<size_t>(((BT * E * 4 + 15) & ~15) + BT * 8 + kRouteThreads * 8 +
+                                          E * 4);
+  const size_t lds = c.lds > tail ? c.lds : tail;
+#define MOE_FUSED_CASE(ep, tp)                                                                  \
+  if (c.EPT == ep && c.TPT == tp) {                                                             \
+    hipLaunchKernelGGL((router_fused_kernel<ep, tp>), dim3(static_cast<unsigned>(c.blocks)),     \
+                       dim3(kRouteThreads), lds, s, x, w_router, bias, idx, gate, margin,        \
+                       stats ? seq_p : nullptr, seq_cnt, T, d, E, k, c.BE, c.KC, G);             \
+  } else
+  MOE_FUSED_CASE(4, 4) MOE_FUSED_CASE(4, 2) MOE_FUSED_CASE(4, 1)
+  MOE_FUSED_CASE(2, 4) MOE_FUSED_CASE(2, 2) MOE_FUSED_CASE(2, 1)
+  MOE_FUSED_CASE(1, 4) MOE_FUSED_CASE(1, 2) MOE_FUSED_CASE(1, 1)
+  { return hipErrorInvalidValue; }
+#undef MOE_FUSED_CASE
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  if (stats) {
+    hipLaunchKernelGGL(seq_final_kernel, dim3(static_cast<unsigned>(T / S)), dim3(256), 0, s, seq_p,
+                       seq_cnt, seq_out, alpha, E, k, S, S / BT);
+    err = hipGetLastError();
+  }
+  *done = err == hipSuccess;
+  return err;
 }
 
 }  // namespace moe
