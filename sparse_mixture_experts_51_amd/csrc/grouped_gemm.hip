@@ -47,7 +47,8 @@ constexpr int kChunksPerRow = kBK / 8;       // 16-byte chunks per tile row
 constexpr int kMaxGroups = 1025;
 typedef __attribute__((address_space(3))) void* lds_ptr_t;  // LDS address (DMA destination)
 
-template <int BM_, int BW_, int WM_, int WN_, int BPC_, bool DMAB_>
+template <int BM_, int BW_, int WM_, int WN_, int BPC_, bool DMAB_, bool DMAA_ = false,
+          int NSA_ = 2>
 struct TileCfg {
   static constexpr int BM = BM_;     // rows per unit
   static constexpr int BW = BW_;     // weight rows per unit
@@ -55,7 +56,9 @@ struct TileCfg {
   static constexpr int WN = WN_;     // waves along the weight tile
   static constexpr int BPC = BPC_;   // blocks per CU
   static constexpr bool DMAB = DMAB_;  // weight tiles go from memory straight to LDS
-  static constexpr int NSB = DMAB ? 3 : 2;  // LDS buffers of the weight tile
+  static constexpr bool DMAA = DMAA_;  // A tiles too (then two stages, one step ahead)
+  static constexpr int NSA = DMAA ? NSA_ : 2;          // LDS buffers (stages) of the A tile
+  static constexpr int NSB = DMAA ? NSA : (DMAB ? 3 : 2);  // ... and of the weight tile
   static constexpr int kThreads = 64 * WM * WN;
   static constexpr int kRowsPerPass = kThreads / kChunksPerRow;
   static constexpr int kLoadsA = BM / kRowsPerPass;
@@ -64,9 +67,11 @@ struct TileCfg {
   static constexpr int TN = BW / WN / 32;  // 32-column MFMA tiles per wave
   static_assert(BM % kRowsPerPass == 0 && BW % (2 * kRowsPerPass) == 0, "load passes");
   static_assert(TN % 2 == 0, "SwiGLU pairs gate and up tiles inside a wave");
+  static_assert(!DMAA || (DMAB && TM % 2 == 0), "A by DMA implies weights by DMA");
 };
 using kStream = TileCfg<192, 256, 2, 4, 1, true>;
 using kCompute = TileCfg<128, 128, 2, 2, 2, false>;
+using kBig = TileCfg<256, 128, 4, 2, 1, true, true, 3>;
 
 // XOR swizzle of the 16-byte chunks of a 128-byte row.  gfx950's LDS has 64
 // four-byte banks (256 bytes per clock), so a 16-byte-per-lane access is
@@ -105,6 +110,48 @@ __device__ __forceinline__ void lds_read2_b128(const u32x4* p0, const u32x4* p1,
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(v0), "=&v"(v1)
       : "v"(a0), "v"(a1)
+      : "memory");
+}
+
+// 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at
+// dst + 16 * l (dst is wave-uniform).
+__device__ __forceinline__ void dma_b128(__amdgpu_buffer_rsrc_t rsrc, void* dst, int voffset,
+                                         int soffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)dst, 16, voffset, soffset, 0, 0);
+}
+
+// Six 16-byte LDS reads under one wait (the fragments of one MFMA sub-step
+// of a 4x2 tile), complete on return like lds_read2_b128.
+__device__ __forceinline__ void lds_read6_b128(const u32x4* const (&p)[6], u32x4 (&v)[6]) {
+  unsigned a[6];
+#pragma unroll
+  for (int i = 0; i < 6; ++i) a[i] = static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_ptr_t)p[i]));
+  asm volatile(
+      "ds_read_b128 %0, %6\n\t"
+      "ds_read_b128 %1, %7\n\t"
+      "ds_read_b128 %2, %8\n\t"
+      "ds_read_b128 %3, %9\n\t"
+      "ds_read_b128 %4, %10\n\t"
+      "ds_read_b128 %5, %11\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5])
+      : "memory");
+}
+
+// Four 16-byte LDS reads under one wait (a 2x2 tile's sub-step fragments).
+__device__ __forceinline__ void lds_read4_b128(const u32x4* const (&p)[4], u32x4 (&v)[4]) {
+  unsigned a[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a[i] = static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_ptr_t)p[i]));
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %5\n\t"
+      "ds_read_b128 %2, %6\n\t"
+      "ds_read_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
       : "memory");
 }
 
@@ -178,7 +225,7 @@ template <class C, bool kSwiGLU>
 __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(GroupedGemmArgs a) {
   constexpr int kThreads = C::kThreads, RPP = C::kRowsPerPass;
   constexpr int LA = C::kLoadsA, LB = C::kLoadsB, TM = C::TM, TN = C::TN;
-  __shared__ u32x4 lds_a[2][C::BM * kChunksPerRow];
+  __shared__ u32x4 lds_a[C::NSA][C::BM * kChunksPerRow];  // buffers or DMA stages
   __shared__ u32x4 lds_b[C::NSB][C::BW * kChunksPerRow];
   __shared__ int unit_start[kMaxGroups + 1];
   __shared__ int offs[kMaxGroups + 1];  // copy of offsets[0..E]
@@ -186,7 +233,7 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = uni(tid >> 6);  // wave-uniform, so tile choices stay scalar
   const int wm = wave / C::WN, wn = wave % C::WN;
   const int E = a.E;
   const bool has_shared = a.w_shared != nullptr;
@@ -289,10 +336,13 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
         kSwiGLU ? (routed ? a.w3_routed + static_cast<int64_t>(g) * N * K : a.w3_shared) : w0;
     sr.rb0 = rsrc(w0, wbytes);
     sr.rb1 = rsrc(w1, wbytes);
+    // A by DMA: lane l writes physical chunk l % 8 of its row, so it loads the
+    // logical chunk the swizzle puts there (as for the weights below).
+    const int a_chunk = C::DMAA ? (ld_chunk ^ ((ld_row >> 1) & (kChunksPerRow - 1))) : ld_chunk;
     MOE_FOR(i, LA, {
       int row = gather ? pend_map[i] : pend_row[i];
       if (gather && (row < 0 || row >= a.T)) row = 0;  // malformed permutation: stay in bounds
-      sr.a_off[i] = ld_row + RPP * i < pend.valid_rows ? (row * K + ld_chunk * 8) * 2
+      sr.a_off[i] = ld_row + RPP * i < pend.valid_rows ? (row * K + a_chunk * 8) * 2
                                                        : static_cast<int>(kOutOfRange);
     })
     sr.rows = pend.valid_rows;
@@ -319,7 +369,7 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
   // A K-step in flight: A rows in registers (and the weight rows too unless
   // they go straight to LDS).
   struct Slice {
-    u32x4 a[LA], b[C::DMAB ? 1 : LB];
+    u32x4 a[C::DMAA ? 1 : LA], b[C::DMAB ? 1 : LB];
     int rows;  // valid A rows of the unit the slice belongs to (uniform)
   };
   // Loads K-step f of the current source (f < steps0) or step f - steps0 of
@@ -337,21 +387,20 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
     const __amdgpu_buffer_rsrc_t rb1 = nxt ? c1.rb1 : c0.rb1;
     const int bt = (nxt ? c1.b_thr : c0.b_thr) + kb;
     sl.rows = nxt ? c1.rows : c0.rows;
-    MOE_FOR(i, LA, {
-      const unsigned ao = static_cast<unsigned>(nxt ? c1.a_off[i] : c0.a_off[i]) + kb;
-      sl.a[i] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, static_cast<int>(ao), 0, 0));
-    })
+    if constexpr (!C::DMAA) {
+      MOE_FOR(i, LA, {
+        const unsigned ao = static_cast<unsigned>(nxt ? c1.a_off[i] : c0.a_off[i]) + kb;
+        sl.a[i] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, static_cast<int>(ao), 0, 0));
+      })
+    }
     MOE_FOR(i, LB, {
       constexpr bool up = kSwiGLU && RPP * i >= C::BW / 2;
       const int br = nxt ? c1.b_row[i] : c0.b_row[i];
       if constexpr (C::DMAB) {
         // 64 lanes x 16 bytes land at consecutive LDS slots: rows
         // RPP*i + 8*wave .. +8 of the stage
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            up ? rb1 : rb0,
-            (lds_ptr_t)&lds_b[bstage][(RPP * i + 8 * wave) * kChunksPerRow],
-            16, bt, br, 0, 0);
+        dma_b128(up ? rb1 : rb0, &lds_b[bstage][(RPP * i + 8 * wave) * kChunksPerRow], bt, br);
       } else {
         sl.b[i] = __builtin_bit_cast(
             u32x4, __builtin_amdgcn_raw_buffer_load_b128(up ? rb1 : rb0, bt, br, 0));
@@ -362,9 +411,11 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
     // A passes wholly past the valid rows are not stored.  A pass spans whole
     // 32-row MFMA tiles, so every tile the MFMAs read was stored from this
     // unit (rows past the valid ones as zeros) and the others are skipped.
-    MOE_FOR(i, LA, {
-      if (RPP * i < sl.rows) lds_a[buf][swz(ld_row + RPP * i, ld_chunk)] = sl.a[i];
-    })
+    if constexpr (!C::DMAA) {
+      MOE_FOR(i, LA, {
+        if (RPP * i < sl.rows) lds_a[buf][swz(ld_row + RPP * i, ld_chunk)] = sl.a[i];
+      })
+    }
     if constexpr (!C::DMAB) {
       MOE_FOR(i, LB, { lds_b[bstage][swz(ld_row + RPP * i, ld_chunk)] = sl.b[i]; })
     }
@@ -422,6 +473,80 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
     }
   };
 
+  // All-DMA tiles: K-step f of source c (the last step again past nk) goes
+  // into LDS stage `stage` -- A passes wholly past the valid rows are skipped
+  // (their tiles are never multiplied) -- with the K offset in the scalar
+  // offset of each load.
+  auto issue = [&](const Src& c, int f, int stage) __attribute__((always_inline)) {
+    const int kb = (f < c.nk ? f : c.nk - 1) * (kBK * 2);
+    MOE_FOR(i, LA, {
+      // with more than two stages the wait counts every load, so passes past
+      // the valid rows are issued too (out-of-range offsets, no memory access)
+      if (C::NSA > 2 || RPP * i < c.rows)
+        dma_b128(c.ra, &lds_a[stage][(RPP * i + 8 * wave) * kChunksPerRow], c.a_off[i], kb);
+    })
+    MOE_FOR(i, LB, {
+      constexpr bool up = kSwiGLU && RPP * i >= C::BW / 2;
+      dma_b128(up ? c.rb1 : c.rb0, &lds_b[stage][(RPP * i + 8 * wave) * kChunksPerRow], c.b_thr,
+               c.b_row[i] + kb);
+    })
+  };
+  // MFMAs on an all-DMA stage; every fragment read is in asm (see mma).
+  auto mma_dma = [&](int stage, int mrows) __attribute__((always_inline)) {
+    if (mrows <= 0) return;
+#pragma unroll
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+      const int ch = 2 * ks + (lane >> 5);
+      const int fr = lane & 31;
+      bf16x8 af[TM], bfr[TN];
+      const int r0 = wm * (C::BM / C::WM) + fr;
+      if (TM == 2 && TN == 2 && mrows == 2) {
+        const u32x4* const ptr[4] = {
+            &lds_a[stage][swz(r0, ch)], &lds_a[stage][swz(r0 + 32, ch)],
+            &lds_b[stage][swz(brow(0) + fr, ch)], &lds_b[stage][swz(brow(1) + fr, ch)]};
+        u32x4 v[4];
+        lds_read4_b128(ptr, v);
+        af[0] = __builtin_bit_cast(bf16x8, v[0]);
+        af[TM > 1 ? 1 : 0] = __builtin_bit_cast(bf16x8, v[1]);
+        bfr[0] = __builtin_bit_cast(bf16x8, v[2]);
+        bfr[1] = __builtin_bit_cast(bf16x8, v[3]);
+      } else if (TM == 4 && TN == 2 && mrows == 4) {
+        // the common case: all fragments under one wait
+        const u32x4* const ptr[6] = {
+            &lds_a[stage][swz(r0, ch)], &lds_a[stage][swz(r0 + 32, ch)],
+            &lds_a[stage][swz(r0 + 64, ch)], &lds_a[stage][swz(r0 + 96, ch)],
+            &lds_b[stage][swz(brow(0) + fr, ch)], &lds_b[stage][swz(brow(1) + fr, ch)]};
+        u32x4 v[6];
+        lds_read6_b128(ptr, v);
+        MOE_FOR(i, TM, { af[i] = __builtin_bit_cast(bf16x8, v[i < 4 ? i : 0]); })
+        bfr[0] = __builtin_bit_cast(bf16x8, v[4]);
+        bfr[1] = __builtin_bit_cast(bf16x8, v[5]);
+      } else {
+        u32x4 v0, v1;
+        MOE_FOR(i2, TM / 2, {
+          if (2 * i2 < mrows) {
+            lds_read2_b128(&lds_a[stage][swz(r0 + 64 * i2, ch)],
+                           &lds_a[stage][swz(r0 + 64 * i2 + 32, ch)], v0, v1);
+            af[2 * i2] = __builtin_bit_cast(bf16x8, v0);
+            af[2 * i2 + 1] = __builtin_bit_cast(bf16x8, v1);
+          }
+        })
+        lds_read2_b128(&lds_b[stage][swz(brow(0) + fr, ch)], &lds_b[stage][swz(brow(1) + fr, ch)],
+                       v0, v1);
+        bfr[0] = __builtin_bit_cast(bf16x8, v0);
+        bfr[1] = __builtin_bit_cast(bf16x8, v1);
+      }
+      MOE_FOR(i, TM, {
+        if (i < mrows) {
+          MOE_FOR(j, TN, {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          })
+        }
+      })
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
   // SiLU(gate) * up in fp32 (v_rcp_f32 for the quotient).
   auto swiglu = [](float ga, float up) __attribute__((always_inline)) {
     return ga * __builtin_amdgcn_rcpf(1.0f + __expf(-ga)) * up;
@@ -430,58 +555,78 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
   // (v/4)*8 + (lane/32)*4 + v%4 for v = 0..15.
   const int col_l = lane & 31;
   const int row_l = (lane >> 5) * 4;
-  auto epilogue = [&](const Unit& cu) __attribute__((always_inline)) {
+  auto epilogue = [&](const Unit& cu, int fs) __attribute__((always_inline)) {
     uint16_t* cbase = cu.routed ? a.c_routed : a.c_shared;
     constexpr int kCols = kSwiGLU ? C::BW / 2 : C::BW;
-    constexpr bool kViaLds =
-        !C::DMAB && (C::BM * kChunksPerRow * 16 + C::BW * kChunksPerRow * 16) / (kCols * 2) >= C::BM;
+    constexpr int RB = kCols * 2;                                // bytes per output row
+    constexpr int kRowsA = C::BM * kChunksPerRow * 16 / RB;     // rows that fit in lds_a[fs]
+    constexpr int kRowsB = C::BW * kChunksPerRow * 16 / RB;     // ... and then in lds_b[fs]
+    constexpr int kWaveRows = C::BM / C::WM;
+    constexpr int kPassRows = ((kRowsA + kRowsB) / kWaveRows) * kWaveRows;
+    constexpr bool kViaLds = (!C::DMAB || C::DMAA) && kPassRows > 0;
     if constexpr (kViaLds) {
-      // Through LDS: each lane's column values go into the idle half of the
-      // double buffer (buffer 1, free since the barrier after the last
-      // K-step), then whole rows leave as 16-byte stores.  Rows are COLS
-      // bf16 wide; the 16-byte chunk q of row r sits at chunk q ^ (r & 4),
-      // so the two rows one 2-byte write instruction covers (r and r + 4)
-      // hit different banks.  Rows [0, kHalfRows) live in lds_a[1], the rest
-      // in lds_b[1].  Tiles that do not fit there store straight from the
-      // accumulators (below).
-      constexpr int COLS = kCols;
-      constexpr int RB = COLS * 2;
-      constexpr int kHalfRows = C::BM * kChunksPerRow * 16 / RB;
+      // Through LDS: the lanes' column values go into the idle LDS buffer
+      // (index fs, free since the barrier after the last K-step), then whole
+      // rows leave as 16-byte stores -- in passes of kPassRows rows when the
+      // tile is larger than the buffer.  The 16-byte chunk q of (pass-
+      // relative) row r sits at chunk q ^ (r & 4), so the two rows one 2-byte
+      // write instruction covers (r and r + 4) hit different banks.
       auto cbyte = [&](int r, int byte) __attribute__((always_inline)) {
-        unsigned char* h = r < kHalfRows ? reinterpret_cast<unsigned char*>(&lds_a[1][0])
-                                         : reinterpret_cast<unsigned char*>(&lds_b[1][0]);
-        const int rr = r < kHalfRows ? r : r - kHalfRows;
+        unsigned char* h = r < kRowsA ? reinterpret_cast<unsigned char*>(&lds_a[fs][0])
+                                      : reinterpret_cast<unsigned char*>(&lds_b[fs][0]);
+        const int rr = r < kRowsA ? r : r - kRowsA;
         return h + rr * RB + (((byte >> 4) ^ (r & 4)) << 4) + (byte & 15);
       };
-      MOE_FOR(i, TM, {
-        MOE_FOR(v, 16, {
-          const int r = wm * (C::BM / C::WM) + 32 * i + (v >> 2) * 8 + row_l + (v & 3);
-          if (kSwiGLU) {
-            MOE_FOR(j, TN / 2, {
-              const int c = wn * HC + 32 * j + col_l;
-              *reinterpret_cast<uint16_t*>(cbyte(r, 2 * c)) =
-                  f32_to_bf16(swiglu(acc[i][j][v], acc[i][j + TN / 2][v]));
-            })
-          } else {
-            MOE_FOR(j, TN, {
-              const int c = wn * (C::BW / C::WN) + 32 * j + col_l;
-              *reinterpret_cast<uint16_t*>(cbyte(r, 2 * c)) = f32_to_bf16(acc[i][j][v]);
-            })
-          }
-        })
-      })
-      lds_barrier();
-      constexpr int kChunks = C::BM * COLS / 8;
-      const int ncols = cu.N - cu.n0 < COLS ? cu.N - cu.n0 : COLS;
-      for (int idx = tid; idx < kChunks; idx += kThreads) {
-        const int r = idx / (COLS / 8), q = idx % (COLS / 8);
-        if (r < cu.valid_rows && q * 8 < ncols) {
-          const u32x4 val = *reinterpret_cast<const u32x4*>(cbyte(r, q * 16));
-          *reinterpret_cast<u32x4*>(cbase + (static_cast<int64_t>(cu.orow0) + r) * cu.N + cu.n0 +
-                                    q * 8) = val;
+      // Write side: a 32-row tile never straddles the two regions (kRowsA is a
+      // multiple of 32), its rows' (r & 4) is the lane's row_l, so one base
+      // per tile plus the lane's column offset leaves only immediates per
+      // value.
+      static_assert(kRowsA % 32 == 0, "tiles stay in one region");
+      auto tile_base = [&](int r_tile, int cbyte_off) __attribute__((always_inline)) {
+        unsigned char* h = r_tile < kRowsA ? reinterpret_cast<unsigned char*>(&lds_a[fs][0])
+                                           : reinterpret_cast<unsigned char*>(&lds_b[fs][0]);
+        const int rr = r_tile < kRowsA ? r_tile : r_tile - kRowsA;
+        return h + (rr + row_l) * RB + ((((cbyte_off >> 4) ^ row_l)) << 4) + (cbyte_off & 15);
+      };
+      constexpr int kPasses = (C::BM + kPassRows - 1) / kPassRows;
+      const int ncols = cu.N - cu.n0 < kCols ? cu.N - cu.n0 : kCols;
+      MOE_FOR(p, kPasses, {
+        const int r_lo = p * kPassRows;
+        if (wm * kWaveRows >= r_lo && wm * kWaveRows < r_lo + kPassRows) {
+          MOE_FOR(i, TM, {
+            const int r_tile = wm * kWaveRows + 32 * i - r_lo;
+            if (kSwiGLU) {
+              MOE_FOR(j, TN / 2, {
+                unsigned char* base = tile_base(r_tile, 2 * (wn * HC + 32 * j + col_l));
+                MOE_FOR(v, 16, {
+                  *reinterpret_cast<uint16_t*>(base + ((v >> 2) * 8 + (v & 3)) * RB) =
+                      f32_to_bf16(swiglu(acc[i][j][v], acc[i][j + TN / 2][v]));
+                })
+              })
+            } else {
+              MOE_FOR(j, TN, {
+                unsigned char* base = tile_base(r_tile, 2 * (wn * (C::BW / C::WN) + 32 * j + col_l));
+                MOE_FOR(v, 16, {
+                  *reinterpret_cast<uint16_t*>(base + ((v >> 2) * 8 + (v & 3)) * RB) =
+                      f32_to_bf16(acc[i][j][v]);
+                })
+              })
+            }
+          })
         }
-      }
-      lds_barrier();  // buffer 1 is stashed into during the next unit's first step
+        lds_barrier();
+        constexpr int kPr = (C::BM - p * kPassRows) < kPassRows ? (C::BM - p * kPassRows) : kPassRows;
+        constexpr int kChunks = kPr * kCols / 8;
+        for (int idx = tid; idx < kChunks; idx += kThreads) {
+          const int r = idx / (kCols / 8), q = idx % (kCols / 8);
+          if (r_lo + r < cu.valid_rows && q * 8 < ncols) {
+            const u32x4 val = *reinterpret_cast<const u32x4*>(cbyte(r, q * 16));
+            *reinterpret_cast<u32x4*>(cbase + (static_cast<int64_t>(cu.orow0) + r_lo + r) * cu.N +
+                                      cu.n0 + q * 8) = val;
+          }
+        }
+        lds_barrier();  // the buffer is reused by the next pass or the next unit
+      })
     } else {
       MOE_FOR(i, TM, {
         MOE_FOR(v, 16, {
@@ -533,12 +678,50 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
     st += d;
     return st >= C::NSB ? st - C::NSB : st;
   };
-  Slice r0, r1;
   int cs = 0;  // weight stage of the current step
   prepare(lb);
   Src cur = source_of_pending();
   Unit cu = pend;
   prepare(next_of(lb));
+  if constexpr (C::DMAA) {
+    // All-DMA tiles in NS stages, D = NS - 1 steps ahead: the DMA of step
+    // k + D (running into the next unit's first steps) is issued at step k
+    // into the stage that step k - 1 read, before the barrier that ended it.
+    // At the end of step k this thread waits until only the loads of steps
+    // k + 2 .. k + D (LA + LB each) may still be in flight, so step k + 1 has
+    // landed; the barrier then makes every wave's part visible.  Every group
+    // has at least D K-steps (the launcher checks), so the first D steps of a
+    // unit never reach past the next unit.
+    constexpr int NS = C::NSA, D = NS - 1;
+    constexpr int kAhead = (D - 1) * (LA + LB);
+    static_assert(kAhead < 64, "vmcnt range");
+    auto st = [](int x) __attribute__((always_inline)) { return x >= NS ? x - NS : x; };
+    MOE_FOR(f, D, { issue(cur, f, f); })
+    __builtin_amdgcn_s_waitcnt(0x0F70 | ((kAhead & 15) | ((kAhead >> 4) << 14)));
+    lds_barrier();
+    for (int u = lb; u < total_units; u += G) {
+      const Src nxt = source_of_pending();
+      const Unit nu = pend;
+      prepare(next_of(next_of(u)));
+      int mrows = (cu.valid_rows - wm * (C::BM / C::WM) + 31) / 32;
+      mrows = mrows < 0 ? 0 : (mrows > TM ? TM : mrows);
+      zero_acc();
+      for (int kt = 0; kt < cur.nk; ++kt) {
+        const int f = kt + D;
+        if (f < cur.nk) issue(cur, f, st(cs + D));
+        else issue(nxt, f - cur.nk, st(cs + D));
+        mma_dma(cs, mrows);
+        __builtin_amdgcn_s_waitcnt(0x0F70 | ((kAhead & 15) | ((kAhead >> 4) << 14)));
+        lds_barrier();
+        cs = st(cs + 1);
+      }
+      epilogue(cu, st(cs + D));  // the stage the last step read
+      cur = nxt;
+      cu = nu;
+    }
+    return;
+  }
+  Slice r0, r1;
   load2(r0, cur, cur, 1 << 30, 0, 0);
   load2(r1, cur, cur, 1 << 30, 1, 1 % C::NSB);
   stash(r0, 0, 0);
@@ -567,7 +750,7 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
       vm_wait();
       lds_barrier();
     }
-    epilogue(cu);
+    epilogue(cu, 1);
     cur = nxt;
     cu = nu;
   }
@@ -591,11 +774,23 @@ static bool streaming_shape(const GroupedGemmArgs& a) {
   return rows_per_expert > 64 && rows_per_expert <= 256 && weight_bytes > (int64_t{1} << 30);
 }
 
+// Groups of many rows (hundreds per expert and more): the 256x128 all-DMA
+// tile moves a third fewer bytes per MFMA than 128x128, holds no tile data
+// in registers and runs one step ahead.
+static bool big_groups(const GroupedGemmArgs& a) {
+  constexpr int kMinK = kBK * (kBig::NSA - 1);  // each unit at least D K-steps long
+  if (a.K_r < kMinK || (a.w_shared && a.K_s < kMinK)) return false;
+  return a.T * a.top_k / (a.E > 0 ? a.E : 1) >= 512;
+}
+
 template <bool kSwiGLU>
 static hipError_t launch_gemm(const GroupedGemmArgs& a, hipStream_t s) {
   if (streaming_shape(a)) {
     hipLaunchKernelGGL((grouped_gemm_kernel<kStream, kSwiGLU>), dim3(persistent_grid<kStream>()),
                        dim3(kStream::kThreads), 0, s, a);
+  } else if (big_groups(a)) {
+    hipLaunchKernelGGL((grouped_gemm_kernel<kBig, kSwiGLU>), dim3(persistent_grid<kBig>()),
+                       dim3(kBig::kThreads), 0, s, a);
   } else {
     hipLaunchKernelGGL((grouped_gemm_kernel<kCompute, kSwiGLU>), dim3(persistent_grid<kCompute>()),
                        dim3(kCompute::kThreads), 0, s, a);

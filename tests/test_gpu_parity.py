@@ -142,6 +142,11 @@ FFN_CASES = {
     "v3_dims_T16": custom(tokens=16, d_model=7168, n_experts=16, top_k=4, hidden=2048,
                           shared_hidden=2048, cfg_id=114, w_std=0.006, router_std=0.006,
                           bias_range=0.01),
+    # hundreds of rows per expert (the 256x256 tile), ragged row tails
+    "big_ragged_T3001": custom(tokens=3001, n_experts=8, top_k=4, cfg_id=115),
+    # ... with partial column tiles (H = 320, d = 448) and odd K-step counts
+    "big_H320_d448": custom(tokens=2500, d_model=448, n_experts=8, top_k=4, hidden=320,
+                            shared_hidden=192, cfg_id=116),
 }
 
 
