@@ -226,7 +226,7 @@ struct RouterCfg {
 };
 
 static RouterCfg router_cfg(int64_t T, int d, int E, int want_blocks, bool whole_e = false) {
-  // Largest per-thread tile that still gives one block per CU (with few
+  // Largest per-thread tile that still gives want_blocks blocks (with few
   // tokens, trade tile size for blocks: each (token, expert) chain is serial
   // over d, so parallelism is bounded by T*E lanes).  A chunk of d is the
   // whole of d when x and W_r tiles fit the LDS budget; else 64- or 32-wide
@@ -280,7 +280,9 @@ static hipError_t launch_scores_cfg(const uint16_t* x, const float* w, float* sc
 
 hipError_t launch_router_scores(const uint16_t* x, const float* w_router, float* scores,
                                 int64_t T, int d, int E, hipStream_t s) {
-  const RouterCfg pick = router_cfg(T, d, E, device_cus());
+  // two blocks per CU: with one, each SIMD holds a single wave and the LDS
+  // latency of the operand reads is exposed
+  const RouterCfg pick = router_cfg(T, d, E, 2 * device_cus());
 #define MOE_SCORES_CASE(e, t)                                               \
   if (pick.EPT == e && pick.TPT == t)                                       \
     return launch_scores_cfg<e, t>(x, w_router, scores, T, d, E, pick, s);
