@@ -162,7 +162,7 @@ def main():
     stacked = L > 1
     ev = []  # (start, end) events around every moe_grouped_ffn in the timed region
 
-    def step(i, timed):
+    def step(i, timed, counts_out=None):
         x = xs[i % n_x]
         for l in range(L):
             b, p = bufs[l], params[l]
@@ -171,6 +171,8 @@ def main():
                           b["margin"], b["seq_balance"], 1e-4, ws, stream)
             moe.moe_permute(shape, b["topk_idx"], b["counts"], b["offsets"], b["perm_src"],
                             b["pos"], None, None, ws, stream)
+            if counts_out is not None:
+                counts_out.append(b["counts"].cpu().numpy())
             if timed:
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
@@ -190,6 +192,9 @@ def main():
     for i in range(args.warmup):
         step(i, False)
     torch.cuda.synchronize()
+    # the bias moves every step, and with it the set of experts that receive
+    # rows; keep the starting biases to replay the timed steps afterwards
+    bias0 = [params[l]["bias"].clone() for l in range(L)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     t_start.record(stream)
@@ -201,7 +206,15 @@ def main():
     tokens_per_s = wl.tokens * L / (ms * 1e-3)
 
     ffn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-    counts = [bufs[l]["counts"].cpu().numpy() for l in range(L)]
+    # Algorithmic bytes per moe_grouped_ffn launch, averaged over the same
+    # launches the events timed: replay the timed steps (untimed, from the
+    # same biases) and read every layer's counts.
+    for l in range(L):
+        params[l]["bias"].copy_(bias0[l])
+    counts = []
+    for i in range(args.steps):
+        step(args.warmup + i, False, counts)
+    torch.cuda.synchronize()
     algo = ffn_algorithmic(wl, counts)
     flops = float(np.mean([f for f, _ in algo]))
     byts = float(np.mean([b for _, b in algo]))
