@@ -41,7 +41,8 @@ Workspace carve_workspace(void* base, int64_t T, int d, int E, int k, int H, int
     off = align_up(off + bytes);
     return base ? static_cast<char*>(base) + o : nullptr;
   };
-  const int64_t nblk = (T + kPermTokens - 1) / kPermTokens;
+  const int tb = perm_block_tokens(T);
+  const int64_t nblk = (T + tb - 1) / tb;
   const int nsplit = seq_partials_capacity(T, S);
   const int64_t nseq = S > 0 ? T / S : 0;
   w.scores = reinterpret_cast<float*>(take(sizeof(float) * T * E));

@@ -23,6 +23,7 @@ struct Workspace {
 };
 
 constexpr int kPermTokens = 256;  // tokens per block of the permutation kernels
+int perm_block_tokens(int64_t T);
 
 int seq_splits(int64_t T, int S);
 // Balance-statistic partials per sequence that the workspace holds.

@@ -7,11 +7,11 @@
 // reads ("190行JAX复刻DeepSeek V3" (openai-hub.com), section
 // 最有价值的实验:无辅助损失均衡真的有效).
 //
-// Three kernels over blocks of kPermTokens tokens:
+// Three kernels over blocks of TB = 256 tokens:
 //   count:   LDS-privatised histogram of the block's k*tokens choices
 //   scan:    one block; per expert a running sum over token blocks gives each
 //            block's first row, and a block-wide scan over experts gives offsets
-//   scatter: the block's choices as an LDS bitmap [E][kPermTokens bits]; the
+//   scatter: the block's choices as an LDS bitmap [E][TB bits]; the
 //            rank of (t, e) among earlier tokens of the block choosing e is a
 //            popcount, so rows inside a group are in ascending token order
 //            without sorting.  Optionally copies x rows into x_perm.
@@ -45,12 +45,13 @@ __device__ int block_exclusive_scan_1024(int v, int* total) {
   return wsum[w] + inc - v;
 }
 
-__global__ __launch_bounds__(kPermTokens) void perm_count_kernel(
+template <int TB>
+__global__ __launch_bounds__(TB) void perm_count_kernel(
     const int32_t* __restrict__ idx, int32_t* __restrict__ blk_cnt, int64_t T, int E, int k) {
   extern __shared__ int32_t cnt[];  // [E]
-  for (int e = threadIdx.x; e < E; e += kPermTokens) cnt[e] = 0;
+  for (int e = threadIdx.x; e < E; e += TB) cnt[e] = 0;
   __syncthreads();
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * kPermTokens + threadIdx.x;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * TB + threadIdx.x;
   if (t < T) {
     for (int j = 0; j < k; ++j) {
       const int e = idx[t * k + j];
@@ -58,7 +59,7 @@ __global__ __launch_bounds__(kPermTokens) void perm_count_kernel(
     }
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += kPermTokens)
+  for (int e = threadIdx.x; e < E; e += TB)
     blk_cnt[static_cast<int64_t>(blockIdx.x) * E + e] = cnt[e];
 }
 
@@ -85,9 +86,10 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(
   if (e == 0) offsets[E] = total;
 }
 
-// Exclusive scan of one int per thread over a kPermTokens-thread block.
-__device__ int block_exclusive_scan_256(int v, int* total) {
-  __shared__ int wsum[kPermTokens / 64];
+// Exclusive scan of one int per thread over a TB-thread block.
+template <int TB>
+__device__ int block_exclusive_scan(int v, int* total) {
+  __shared__ int wsum[TB / 64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   int inc = v;
   for (int off = 1; off < 64; off <<= 1) {
@@ -97,7 +99,7 @@ __device__ int block_exclusive_scan_256(int v, int* total) {
   if (lane == 63) wsum[w] = inc;
   __syncthreads();
   int base = 0, tot = 0;
-  for (int i = 0; i < kPermTokens / 64; ++i) {
+  for (int i = 0; i < TB / 64; ++i) {
     base += i < w ? wsum[i] : 0;
     tot += wsum[i];
   }
@@ -109,37 +111,52 @@ __device__ int block_exclusive_scan_256(int v, int* total) {
 // fused_scan: the block derives its own first rows (and block 0 the counts and
 // offsets) from the per-block count table, which is small enough for LDS;
 // otherwise blk_base comes from perm_scan_kernel.
-__global__ __launch_bounds__(kPermTokens) void perm_scatter_kernel(
+template <int TB>
+__global__ __launch_bounds__(TB) void perm_scatter_kernel(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ blk_cnt,
     const int32_t* __restrict__ blk_base, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src, int32_t* __restrict__ pos,
     const uint16_t* __restrict__ x, uint16_t* __restrict__ x_perm, int64_t T, int d, int E, int k,
     int nblk, int fused_scan) {
-  constexpr int W = kPermTokens / 32;  // 32-bit words per expert row of the bitmap
-  extern __shared__ uint32_t bits[];   // [E][W], rows [kPermTokens * k], base [E] (fused)
+  constexpr int W = TB / 32;         // 32-bit words per expert row of the bitmap
+  extern __shared__ uint32_t bits[];  // [E][W], rows [TB * k], base [E], total [E] (fused)
   int32_t* rows = reinterpret_cast<int32_t*>(bits + E * W);
-  int32_t* base = rows + kPermTokens * k;
-  for (int i = threadIdx.x; i < E * W; i += kPermTokens) bits[i] = 0;
+  int32_t* base = rows + TB * k;
+  int32_t* etot = base + E;
+  for (int i = threadIdx.x; i < E * W; i += TB) bits[i] = 0;
   if (fused_scan) {
-    // expert chunk per thread: e in [c0, c0 + per)
-    const int per = (E + kPermTokens - 1) / kPermTokens;
-    const int c0 = threadIdx.x * per;
-    int tot_local = 0;
-    for (int e = c0; e < c0 + per && e < E; ++e) {
+    // Per expert e: rows in blocks before this one, and in all blocks.  L
+    // lanes share an expert (block b2 to lane b2 mod L); lane partial sums
+    // are combined with shuffles inside groups of L consecutive lanes.
+    const int L = E >= TB ? 1 : TB / E;  // power of two when E divides TB
+    const int Lp = (L & (L - 1)) == 0 ? L : 1;
+    const int l = threadIdx.x % Lp;
+    for (int e = threadIdx.x / Lp; e < E; e += TB / Lp) {
       int before = 0, total = 0;
-      for (int b2 = 0; b2 < nblk; ++b2) {
+      for (int b2 = l; b2 < nblk; b2 += Lp) {
         const int c = blk_cnt[static_cast<int64_t>(b2) * E + e];
         before += b2 < static_cast<int>(blockIdx.x) ? c : 0;
         total += c;
       }
-      base[e] = before;       // rows before this block, inside expert e
-      rows[e] = total;        // expert e's load (rows[] is reused below)
-      tot_local += total;
+      for (int off = Lp >> 1; off > 0; off >>= 1) {
+        before += __shfl_xor(before, off, Lp);
+        total += __shfl_xor(total, off, Lp);
+      }
+      if (l == 0) {
+        base[e] = before;
+        etot[e] = total;
+      }
     }
+    __syncthreads();
+    // exclusive scan of the totals over experts: offsets
+    const int per = (E + TB - 1) / TB;
+    const int c0 = threadIdx.x * per;
+    int tot_local = 0;
+    for (int e = c0; e < c0 + per && e < E; ++e) tot_local += etot[e];
     int all;
-    int run = block_exclusive_scan_256(tot_local, &all);
+    int run = block_exclusive_scan<TB>(tot_local, &all);
     for (int e = c0; e < c0 + per && e < E; ++e) {
-      const int total = rows[e];
+      const int total = etot[e];
       base[e] += run;
       if (blockIdx.x == 0) {
         counts[e] = total;
@@ -150,7 +167,7 @@ __global__ __launch_bounds__(kPermTokens) void perm_scatter_kernel(
     if (blockIdx.x == 0 && threadIdx.x == 0) offsets[E] = all;
   }
   __syncthreads();
-  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kPermTokens;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * TB;
   const int64_t t = t0 + threadIdx.x;
   const int word = threadIdx.x / 32, bit = threadIdx.x % 32;
   if (t < T) {
@@ -176,10 +193,10 @@ __global__ __launch_bounds__(kPermTokens) void perm_scatter_kernel(
   }
   if (x_perm == nullptr) return;
   __syncthreads();
-  const int64_t ntok = (T - t0) < kPermTokens ? (T - t0) : kPermTokens;
+  const int64_t ntok = (T - t0) < TB ? (T - t0) : TB;
   const int chunks = d / 8;
   const int64_t work = ntok * k * chunks;
-  for (int64_t c = threadIdx.x; c < work; c += kPermTokens) {
+  for (int64_t c = threadIdx.x; c < work; c += TB) {
     const int64_t p = c / chunks;
     const int ch = static_cast<int>(c % chunks);
     const int row = rows[p];
@@ -190,40 +207,47 @@ __global__ __launch_bounds__(kPermTokens) void perm_scatter_kernel(
   }
 }
 
-hipError_t launch_permute(const int32_t* idx, int32_t* counts, int32_t* offsets,
-                          int32_t* perm_src, int32_t* pos, const uint16_t* x, uint16_t* x_perm,
-                          int32_t* blk_cnt, int32_t* blk_base, int64_t T, int d, int E, int k,
-                          hipStream_t s) {
-  const int nblk = static_cast<int>((T + kPermTokens - 1) / kPermTokens);
+template <int TB>
+static hipError_t launch_permute_tb(const int32_t* idx, int32_t* counts, int32_t* offsets,
+                                    int32_t* perm_src, int32_t* pos, const uint16_t* x,
+                                    uint16_t* x_perm, int32_t* blk_cnt, int32_t* blk_base,
+                                    int64_t T, int d, int E, int k, hipStream_t s) {
+  const int nblk = static_cast<int>((T + TB - 1) / TB);
   hipError_t err;
-  if (nblk > 0) {
-    hipLaunchKernelGGL(perm_count_kernel, dim3(nblk), dim3(kPermTokens), sizeof(int32_t) * E, s,
-                       idx, blk_cnt, T, E, k);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
-  }
   if (nblk == 0) {
     hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, s, blk_cnt, blk_base, counts,
                        offsets, nblk, E);
     return hipGetLastError();
   }
+  hipLaunchKernelGGL((perm_count_kernel<TB>), dim3(nblk), dim3(TB), sizeof(int32_t) * E, s, idx,
+                     blk_cnt, T, E, k);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
   // Small count tables are summed by every scatter block itself (one launch
   // fewer); large ones go through the single-block scan.
-  const size_t lds_base = sizeof(uint32_t) * E * (kPermTokens / 32) +
-                          sizeof(int32_t) * kPermTokens * (k > 1 ? k : 1);
-  const size_t lds_fused = lds_base + sizeof(int32_t) * E;
-  const int fused = nblk > 0 && static_cast<int64_t>(nblk) * E <= 16384 &&
-                    lds_fused <= 64 * 1024 && kPermTokens * (k > 1 ? k : 1) >= E;
+  const size_t lds_base = sizeof(uint32_t) * E * (TB / 32) + sizeof(int32_t) * TB * (k > 1 ? k : 1);
+  const size_t lds_fused = lds_base + 2 * sizeof(int32_t) * E;
+  const int fused = static_cast<int64_t>(nblk) * E <= 16384 && lds_fused <= 64 * 1024;
   if (!fused) {
     hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, s, blk_cnt, blk_base, counts,
                        offsets, nblk, E);
     err = hipGetLastError();
-    if (err != hipSuccess || nblk == 0) return err;
+    if (err != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(perm_scatter_kernel, dim3(nblk), dim3(kPermTokens), fused ? lds_fused : lds_base,
+  hipLaunchKernelGGL((perm_scatter_kernel<TB>), dim3(nblk), dim3(TB), fused ? lds_fused : lds_base,
                      s, idx, blk_cnt, blk_base, counts, offsets, perm_src, pos, x, x_perm, T, d, E,
                      k, nblk, fused);
   return hipGetLastError();
+}
+
+int perm_block_tokens(int64_t) { return kPermTokens; }
+
+hipError_t launch_permute(const int32_t* idx, int32_t* counts, int32_t* offsets,
+                          int32_t* perm_src, int32_t* pos, const uint16_t* x, uint16_t* x_perm,
+                          int32_t* blk_cnt, int32_t* blk_base, int64_t T, int d, int E, int k,
+                          hipStream_t s) {
+  return launch_permute_tb<kPermTokens>(idx, counts, offsets, perm_src, pos, x, x_perm, blk_cnt,
+                                        blk_base, T, d, E, k, s);
 }
 
 }  // namespace moe
