@@ -17,24 +17,32 @@
 // one expert stay in that XCD's L2.  Every block rebuilds the unit table from
 // offsets[] (no host round trip).
 //
-// Two tile configurations:
-//   kStream  BM = 256, BW = 128, 8 waves, 1 block/CU.  For weight-streaming
-//            shapes (few rows per expert, weights far beyond the caches): one
-//            unit covers all rows of an expert, so each weight byte is read
-//            from HBM once (two 128-row m-tiles streaming the same weights
-//            drift apart and both miss L2).
-//   kCompute BM = BW = 128, 4 waves, 2 blocks/CU.  For shapes whose weights
-//            stay in L2/MALL and whose groups have thousands of rows: more,
-//            smaller units keep every CU busy.
+// Three tile configurations:
+//   kStream  BM = 192, BW = 256, 8 waves, 1 block/CU.  For weight-streaming
+//            shapes (about 64 to 256 rows per expert, weights far beyond the
+//            caches): one unit covers all rows of a typical expert, so each
+//            weight byte is read from HBM once (two m-tiles streaming the same
+//            weights drift apart and both miss L2).  Weight tiles go from
+//            memory straight to LDS (three stages).
+//   kCompute BM = BW = 128, 4 waves, 2 blocks/CU.  For few rows per expert
+//            (decode) and small models: more, smaller units keep every CU
+//            busy and two blocks per CU keep more weight bytes in flight.
+//   kBig     BM = 256, BW = 128, 8 waves, 1 block/CU, A and weight tiles both
+//            by LDS DMA in three stages.  For hundreds of rows per expert.
 //
 // Pipeline.  A block's units run as an outer loop; each unit's K-loop (64 of
-// K per step, an odd step count padded by one MFMA-free step) is
-// straight-line code.  The fetcher runs two steps ahead of the MFMAs and
-// crosses into the next unit during the last two steps, choosing the source
-// with scalar selects.  Loads are buffer loads (uniform descriptor + 32-bit
-// offset) into registers, stored to one of two XOR-swizzled LDS buffers.
+// K per step; with register-staged A an odd step count is padded by one
+// MFMA-free step) is straight-line code apart from uniform branches.  The
+// fetcher runs two steps ahead of the MFMAs and crosses into the next unit
+// during the last steps of the current one, choosing the source with scalar
+// selects.  Loads are buffer loads (uniform descriptor + 32-bit offset); the
+// loads of one step are spread over the four MFMA sub-steps of the step two
+// earlier, so that a full memory queue stalls one wave briefly instead of
+// holding all its MFMAs back.  Tiles sit in XOR-swizzled LDS buffers.
 // Barriers are raw s_barrier after an LDS-only wait: __syncthreads() would
-// also drain the in-flight global loads.
+// also drain the in-flight global loads.  The epilogue stages the output
+// tile in the LDS buffers no load in flight writes and leaves it as 16-byte
+// row stores.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -375,9 +383,13 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
   // Loads K-step f of the current source (f < steps0) or step f - steps0 of
   // the next one, chosen by a uniform test (scalar selects, no branches, so
   // the K-loop stays straight-line).  A step at or past nk (the padding step
-  // of an odd count) reloads the last slice and is never multiplied.
-  auto load2 = [&](Slice& sl, const Src& c0, const Src& c1, int steps0, int f, int bstage)
-      __attribute__((always_inline)) {
+  // of an odd count) reloads the last slice and is never multiplied.  With
+  // part P in 0..3 only loads i (A passes first, then weight passes) with
+  // i % 4 == P are issued, so that a step's loads can be spread over the four
+  // MFMA sub-steps; P < 0 issues them all.
+  auto load2 = [&](Slice& sl, const Src& c0, const Src& c1, int steps0, int f, int bstage,
+                   auto part_c) __attribute__((always_inline)) {
+    constexpr int P = decltype(part_c)::value;
     const bool nxt = f >= steps0;
     const int j = nxt ? f - steps0 : f;
     const int nk = nxt ? c1.nk : c0.nk;
@@ -389,12 +401,15 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
     sl.rows = nxt ? c1.rows : c0.rows;
     if constexpr (!C::DMAA) {
       MOE_FOR(i, LA, {
-        const unsigned ao = static_cast<unsigned>(nxt ? c1.a_off[i] : c0.a_off[i]) + kb;
-        sl.a[i] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, static_cast<int>(ao), 0, 0));
+        if constexpr (P < 0 || i % 4 == P) {
+          const unsigned ao = static_cast<unsigned>(nxt ? c1.a_off[i] : c0.a_off[i]) + kb;
+          sl.a[i] = __builtin_bit_cast(
+              u32x4, __builtin_amdgcn_raw_buffer_load_b128(ra, static_cast<int>(ao), 0, 0));
+        }
       })
     }
     MOE_FOR(i, LB, {
+      if constexpr (P >= 0 && (LA + i) % 4 != P) return;
       constexpr bool up = kSwiGLU && RPP * i >= C::BW / 2;
       const int br = nxt ? c1.b_row[i] : c0.b_row[i];
       if constexpr (C::DMAB) {
@@ -421,7 +436,7 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
     }
   };
 
-  // Accumulators: acc[tm][tn], rows wm*BM/WM + 32*tm, weight-tile rows
+  // Accumulators: acc[tm][tn], rows tile_row(tm) .. +31, weight-tile rows
   // SwiGLU: tn < TN/2 gate rows wn*HC + 32*tn, tn >= TN/2 the up rows of the
   // same h columns (BW/2 further); down: rows wn*BW/WN + 32*tn.
   constexpr int HC = C::BW / 2 / C::WN;  // h columns per wave (SwiGLU)
@@ -429,23 +444,34 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
   auto zero_acc = [&]() __attribute__((always_inline)) {
     MOE_FOR(i, TM, { MOE_FOR(j, TN, { acc[i][j] = f32x16{}; }) })
   };
+  // 32-row MFMA tiles are dealt to the WM wave rows in turn (tile i of wave
+  // row wm starts at row 32 * (wm + WM * i)), so a unit with fewer valid rows
+  // than BM still spreads its MFMAs over every wave instead of leaving the
+  // waves of the last rows idle at the barrier.
+  auto tile_row = [&](int i) __attribute__((always_inline)) { return 32 * (wm + C::WM * i); };
+  // tiles of this wave that hold valid rows (0..TM)
+  auto valid_tiles = [&](int valid_rows) __attribute__((always_inline)) {
+    const int m = ((valid_rows + 31) / 32 - wm + C::WM - 1) / C::WM;
+    return m < 0 ? 0 : (m > TM ? TM : m);
+  };
   auto brow = [&](int tn) __attribute__((always_inline)) {
     if (kSwiGLU)
       return tn < TN / 2 ? wn * HC + 32 * tn : C::BW / 2 + wn * HC + 32 * (tn - TN / 2);
     return wn * (C::BW / C::WN) + 32 * tn;
   };
 
-  auto mma = [&](int buf, int bstage, int mrows) __attribute__((always_inline)) {
+  // after(integral_constant<int, ks>) runs after the MFMAs of sub-step ks
+  // (also when the wave has no valid tiles).
+  auto mma = [&](int buf, int bstage, int mrows, auto&& after) __attribute__((always_inline)) {
     // mrows: 32-row tiles of this wave that hold valid rows (0..TM)
-    if (mrows <= 0) return;
-#pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
+    MOE_FOR(ks, kBK / 16, {
+     if (mrows > 0) {
       const int ch = 2 * ks + (lane >> 5);
       const int fr = lane & 31;
       bf16x8 af[TM], bfr[TN];
       MOE_FOR(i, TM, {
         if (i < mrows)
-          af[i] = __builtin_bit_cast(bf16x8, lds_a[buf][swz(wm * (C::BM / C::WM) + 32 * i + fr, ch)]);
+          af[i] = __builtin_bit_cast(bf16x8, lds_a[buf][swz(tile_row(i) + fr, ch)]);
       })
       if constexpr (C::DMAB) {
         // The compiler would put a full vmcnt(0) before any LDS read of a
@@ -467,42 +493,49 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
           })
         }
       })
+     }
+      after(ks_c);
       // Keep each sub-step's fragment reads next to its MFMAs: hoisting them
       // all costs registers and spills the in-flight slices.
       __builtin_amdgcn_sched_barrier(0);
-    }
+    })
   };
 
   // All-DMA tiles: K-step f of source c (the last step again past nk) goes
   // into LDS stage `stage` -- A passes wholly past the valid rows are skipped
   // (their tiles are never multiplied) -- with the K offset in the scalar
   // offset of each load.
-  auto issue = [&](const Src& c, int f, int stage) __attribute__((always_inline)) {
+  // Part P (0..3, or all with P < 0) as in load2.
+  auto issue = [&](const Src& c, int f, int stage, auto part_c) __attribute__((always_inline)) {
+    constexpr int P = decltype(part_c)::value;
     const int kb = (f < c.nk ? f : c.nk - 1) * (kBK * 2);
     MOE_FOR(i, LA, {
+      if constexpr (P >= 0 && i % 4 != P) return;
       // with more than two stages the wait counts every load, so passes past
       // the valid rows are issued too (out-of-range offsets, no memory access)
       if (C::NSA > 2 || RPP * i < c.rows)
         dma_b128(c.ra, &lds_a[stage][(RPP * i + 8 * wave) * kChunksPerRow], c.a_off[i], kb);
     })
     MOE_FOR(i, LB, {
+      if constexpr (P >= 0 && (LA + i) % 4 != P) return;
       constexpr bool up = kSwiGLU && RPP * i >= C::BW / 2;
       dma_b128(up ? c.rb1 : c.rb0, &lds_b[stage][(RPP * i + 8 * wave) * kChunksPerRow], c.b_thr,
                c.b_row[i] + kb);
     })
   };
   // MFMAs on an all-DMA stage; every fragment read is in asm (see mma).
-  auto mma_dma = [&](int stage, int mrows) __attribute__((always_inline)) {
-    if (mrows <= 0) return;
-#pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
+  // after(integral_constant<int, ks>) runs after the MFMAs of sub-step ks.
+  auto mma_dma = [&](int stage, int mrows, auto&& after) __attribute__((always_inline)) {
+    MOE_FOR(ks, kBK / 16, {
+     if (mrows > 0) {
       const int ch = 2 * ks + (lane >> 5);
       const int fr = lane & 31;
       bf16x8 af[TM], bfr[TN];
-      const int r0 = wm * (C::BM / C::WM) + fr;
+      const int r0 = tile_row(0) + fr;
+      constexpr int kTs = 32 * C::WM;  // row stride between a wave's tiles
       if (TM == 2 && TN == 2 && mrows == 2) {
         const u32x4* const ptr[4] = {
-            &lds_a[stage][swz(r0, ch)], &lds_a[stage][swz(r0 + 32, ch)],
+            &lds_a[stage][swz(r0, ch)], &lds_a[stage][swz(r0 + kTs, ch)],
             &lds_b[stage][swz(brow(0) + fr, ch)], &lds_b[stage][swz(brow(1) + fr, ch)]};
         u32x4 v[4];
         lds_read4_b128(ptr, v);
@@ -513,8 +546,8 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
       } else if (TM == 4 && TN == 2 && mrows == 4) {
         // the common case: all fragments under one wait
         const u32x4* const ptr[6] = {
-            &lds_a[stage][swz(r0, ch)], &lds_a[stage][swz(r0 + 32, ch)],
-            &lds_a[stage][swz(r0 + 64, ch)], &lds_a[stage][swz(r0 + 96, ch)],
+            &lds_a[stage][swz(r0, ch)], &lds_a[stage][swz(r0 + kTs, ch)],
+            &lds_a[stage][swz(r0 + 2 * kTs, ch)], &lds_a[stage][swz(r0 + 3 * kTs, ch)],
             &lds_b[stage][swz(brow(0) + fr, ch)], &lds_b[stage][swz(brow(1) + fr, ch)]};
         u32x4 v[6];
         lds_read6_b128(ptr, v);
@@ -525,8 +558,8 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
         u32x4 v0, v1;
         MOE_FOR(i2, TM / 2, {
           if (2 * i2 < mrows) {
-            lds_read2_b128(&lds_a[stage][swz(r0 + 64 * i2, ch)],
-                           &lds_a[stage][swz(r0 + 64 * i2 + 32, ch)], v0, v1);
+            lds_read2_b128(&lds_a[stage][swz(r0 + 2 * kTs * i2, ch)],
+                           &lds_a[stage][swz(r0 + 2 * kTs * i2 + kTs, ch)], v0, v1);
             af[2 * i2] = __builtin_bit_cast(bf16x8, v0);
             af[2 * i2 + 1] = __builtin_bit_cast(bf16x8, v1);
           }
@@ -543,8 +576,10 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
           })
         }
       })
+     }
+      after(ks_c);
       __builtin_amdgcn_sched_barrier(0);
-    }
+    })
   };
 
   // SiLU(gate) * up in fp32 (v_rcp_f32 for the quotient).
@@ -555,36 +590,37 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
   // (v/4)*8 + (lane/32)*4 + v%4 for v = 0..15.
   const int col_l = lane & 31;
   const int row_l = (lane >> 5) * 4;
-  auto epilogue = [&](const Unit& cu, int fs) __attribute__((always_inline)) {
+  // fa, fb: the A buffer and the weight stage that no load in flight writes
+  // (both free since the barrier after the unit's last K-step); mrows: the
+  // wave's tiles with valid rows.
+  auto epilogue = [&](const Unit& cu, int mrows, int fa, int fb) __attribute__((always_inline)) {
     uint16_t* cbase = cu.routed ? a.c_routed : a.c_shared;
     constexpr int kCols = kSwiGLU ? C::BW / 2 : C::BW;
-    constexpr int RB = kCols * 2;                                // bytes per output row
-    constexpr int kRowsA = C::BM * kChunksPerRow * 16 / RB;     // rows that fit in lds_a[fs]
-    constexpr int kRowsB = C::BW * kChunksPerRow * 16 / RB;     // ... and then in lds_b[fs]
-    constexpr int kWaveRows = C::BM / C::WM;
-    constexpr int kPassRows = ((kRowsA + kRowsB) / kWaveRows) * kWaveRows;
-    constexpr bool kViaLds = (!C::DMAB || C::DMAA) && kPassRows > 0;
+    constexpr int RB = kCols * 2;                                       // bytes per output row
+    constexpr int kRowsA = (C::BM * kChunksPerRow * 16 / RB) / 32 * 32;  // whole tiles in lds_a[fa]
+    constexpr int kRowsB = C::BW * kChunksPerRow * 16 / RB;             // rows in lds_b[fb]
+    constexpr int kPassRows = (kRowsA + kRowsB) / 32 * 32;
+    constexpr bool kViaLds = kPassRows > 0;
     if constexpr (kViaLds) {
-      // Through LDS: the lanes' column values go into the idle LDS buffer
-      // (index fs, free since the barrier after the last K-step), then whole
+      // Through LDS: the lanes' column values go into the idle buffers (rows
+      // [0, kRowsA) of a pass in lds_a[fa], the rest in lds_b[fb]), then whole
       // rows leave as 16-byte stores -- in passes of kPassRows rows when the
-      // tile is larger than the buffer.  The 16-byte chunk q of (pass-
+      // tile is larger than the buffers.  The 16-byte chunk q of (pass-
       // relative) row r sits at chunk q ^ (r & 4), so the two rows one 2-byte
       // write instruction covers (r and r + 4) hit different banks.
       auto cbyte = [&](int r, int byte) __attribute__((always_inline)) {
-        unsigned char* h = r < kRowsA ? reinterpret_cast<unsigned char*>(&lds_a[fs][0])
-                                      : reinterpret_cast<unsigned char*>(&lds_b[fs][0]);
+        unsigned char* h = r < kRowsA ? reinterpret_cast<unsigned char*>(&lds_a[fa][0])
+                                      : reinterpret_cast<unsigned char*>(&lds_b[fb][0]);
         const int rr = r < kRowsA ? r : r - kRowsA;
         return h + rr * RB + (((byte >> 4) ^ (r & 4)) << 4) + (byte & 15);
       };
-      // Write side: a 32-row tile never straddles the two regions (kRowsA is a
-      // multiple of 32), its rows' (r & 4) is the lane's row_l, so one base
-      // per tile plus the lane's column offset leaves only immediates per
-      // value.
-      static_assert(kRowsA % 32 == 0, "tiles stay in one region");
+      // Write side: a 32-row tile never straddles the two regions (kRowsA and
+      // kPassRows are multiples of 32), its rows' (r & 4) is the lane's row_l,
+      // so one base per tile plus the lane's column offset leaves only
+      // immediates per value.
       auto tile_base = [&](int r_tile, int cbyte_off) __attribute__((always_inline)) {
-        unsigned char* h = r_tile < kRowsA ? reinterpret_cast<unsigned char*>(&lds_a[fs][0])
-                                           : reinterpret_cast<unsigned char*>(&lds_b[fs][0]);
+        unsigned char* h = r_tile < kRowsA ? reinterpret_cast<unsigned char*>(&lds_a[fa][0])
+                                           : reinterpret_cast<unsigned char*>(&lds_b[fb][0]);
         const int rr = r_tile < kRowsA ? r_tile : r_tile - kRowsA;
         return h + (rr + row_l) * RB + ((((cbyte_off >> 4) ^ row_l)) << 4) + (cbyte_off & 15);
       };
@@ -592,9 +628,9 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
       const int ncols = cu.N - cu.n0 < kCols ? cu.N - cu.n0 : kCols;
       MOE_FOR(p, kPasses, {
         const int r_lo = p * kPassRows;
-        if (wm * kWaveRows >= r_lo && wm * kWaveRows < r_lo + kPassRows) {
-          MOE_FOR(i, TM, {
-            const int r_tile = wm * kWaveRows + 32 * i - r_lo;
+        MOE_FOR(i, TM, {
+          const int r_tile = tile_row(i) - r_lo;
+          if (i < mrows && r_tile >= 0 && r_tile < kPassRows) {
             if (kSwiGLU) {
               MOE_FOR(j, TN / 2, {
                 unsigned char* base = tile_base(r_tile, 2 * (wn * HC + 32 * j + col_l));
@@ -612,8 +648,8 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
                 })
               })
             }
-          })
-        }
+          }
+        })
         lds_barrier();
         constexpr int kPr = (C::BM - p * kPassRows) < kPassRows ? (C::BM - p * kPassRows) : kPassRows;
         constexpr int kChunks = kPr * kCols / 8;
@@ -630,7 +666,7 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
     } else {
       MOE_FOR(i, TM, {
         MOE_FOR(v, 16, {
-          const int r = wm * (C::BM / C::WM) + 32 * i + (v >> 2) * 8 + row_l + (v & 3);
+          const int r = tile_row(i) + (v >> 2) * 8 + row_l + (v & 3);
           if (r < cu.valid_rows) {
             uint16_t* orow = cbase + (static_cast<int64_t>(cu.orow0) + r) * cu.N;
             if (kSwiGLU) {
@@ -696,34 +732,37 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
     constexpr int kAhead = (D - 1) * (LA + LB);
     static_assert(kAhead < 64, "vmcnt range");
     auto st = [](int x) __attribute__((always_inline)) { return x >= NS ? x - NS : x; };
-    MOE_FOR(f, D, { issue(cur, f, f); })
+    MOE_FOR(f, D, { issue(cur, f, f, std::integral_constant<int, -1>{}); })
     __builtin_amdgcn_s_waitcnt(0x0F70 | ((kAhead & 15) | ((kAhead >> 4) << 14)));
     lds_barrier();
     for (int u = lb; u < total_units; u += G) {
       const Src nxt = source_of_pending();
       const Unit nu = pend;
       prepare(next_of(next_of(u)));
-      int mrows = (cu.valid_rows - wm * (C::BM / C::WM) + 31) / 32;
-      mrows = mrows < 0 ? 0 : (mrows > TM ? TM : mrows);
+      const int mrows = valid_tiles(cu.valid_rows);
       zero_acc();
       for (int kt = 0; kt < cur.nk; ++kt) {
+        // step kt + D goes out between the MFMA sub-steps of step kt
         const int f = kt + D;
-        if (f < cur.nk) issue(cur, f, st(cs + D));
-        else issue(nxt, f - cur.nk, st(cs + D));
-        mma_dma(cs, mrows);
+        const int sd = st(cs + D);
+        mma_dma(cs, mrows, [&](auto ks_c) __attribute__((always_inline)) {
+          if (f < cur.nk) issue(cur, f, sd, ks_c);
+          else issue(nxt, f - cur.nk, sd, ks_c);
+        });
         __builtin_amdgcn_s_waitcnt(0x0F70 | ((kAhead & 15) | ((kAhead >> 4) << 14)));
         lds_barrier();
         cs = st(cs + 1);
       }
-      epilogue(cu, st(cs + D));  // the stage the last step read
+      epilogue(cu, mrows, st(cs + D), st(cs + D));  // the stage the last step read
       cur = nxt;
       cu = nu;
     }
     return;
   }
   Slice r0, r1;
-  load2(r0, cur, cur, 1 << 30, 0, 0);
-  load2(r1, cur, cur, 1 << 30, 1, 1 % C::NSB);
+  constexpr std::integral_constant<int, -1> kAll{};
+  load2(r0, cur, cur, 1 << 30, 0, 0, kAll);
+  load2(r1, cur, cur, 1 << 30, 1, 1 % C::NSB, kAll);
   stash(r0, 0, 0);
   vm_wait();
   lds_barrier();
@@ -733,24 +772,30 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
     prepare(next_of(next_of(u)));
     const int steps = cur.nk + (cur.nk & 1);
     // 32-row tiles of this wave with valid rows
-    int mrows = (cu.valid_rows - wm * (C::BM / C::WM) + 31) / 32;
-    mrows = mrows < 0 ? 0 : (mrows > TM ? TM : mrows);
+    const int mrows = valid_tiles(cu.valid_rows);
     zero_acc();
     for (int kt = 0; kt < steps; kt += 2) {
       const int c1 = stage_after(cs, 1);
-      load2(r0, cur, nxt, steps, kt + 2, stage_after(cs, 2));
-      mma(0, cs, mrows);
+      // the loads of step kt + 2 go out between the MFMA sub-steps of step kt
+      const int s2 = stage_after(cs, 2);
+      mma(0, cs, mrows, [&](auto ks_c) __attribute__((always_inline)) {
+        load2(r0, cur, nxt, steps, kt + 2, s2, ks_c);
+      });
       stash(r1, 1, c1);
       vm_wait();
       lds_barrier();
-      load2(r1, cur, nxt, steps, kt + 3, stage_after(c1, 2));
-      mma(1, c1, kt + 1 < cur.nk ? mrows : 0);
+      const int s3 = stage_after(c1, 2);
+      mma(1, c1, kt + 1 < cur.nk ? mrows : 0, [&](auto ks_c) __attribute__((always_inline)) {
+        load2(r1, cur, nxt, steps, kt + 3, s3, ks_c);
+      });
       cs = stage_after(c1, 1);
       stash(r0, 0, cs);
       vm_wait();
       lds_barrier();
     }
-    epilogue(cu, 1);
+    // buffer 0 holds the next unit's first A slice, stage cs its first weight
+    // slice and, with three stages, stage cs + 1 its second
+    epilogue(cu, mrows, 1, stage_after(cs, C::NSB - 1));
     cur = nxt;
     cu = nu;
   }
