@@ -163,6 +163,31 @@ __device__ __forceinline__ void lds_read4_b128(const u32x4* const (&p)[4], u32x4
       : "memory");
 }
 
+// The epilogue's LDS traffic is written in asm too: the compiler cannot tell
+// its buffers from those that LDS DMA is filling and would otherwise drain
+// every load in flight before the first access.  A 2-byte write at p + OFF
+// (completed by the lgkmcnt(0) of the barrier that follows it) ...
+template <int OFF>
+__device__ __forceinline__ void lds_write_b16(void* p, uint16_t v) {
+  const unsigned a = static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_ptr_t)p));
+  asm volatile("ds_write_b16 %0, %1 offset:%2"
+               :
+               : "v"(a), "v"(static_cast<unsigned>(v)), "i"(OFF)
+               : "memory");
+}
+// ... and a 16-byte read, complete on return.
+__device__ __forceinline__ u32x4 lds_read_b128(const void* p) {
+  const unsigned a = static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_ptr_t)p));
+  u32x4 v;
+  asm volatile(
+      "ds_read_b128 %0, %1\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v)
+      : "v"(a)
+      : "memory");
+  return v;
+}
+
 // LDS-only barrier: waits for this wave's LDS traffic, not for global loads.
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt unconstrained
@@ -298,8 +323,11 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
   // unconditional: an A row past the tile's valid rows gets an offset beyond
   // the descriptor's range, which returns zeros without a memory access, and
   // columns past the edge give results the epilogue never stores.  perm_src
-  // entries are loaded one unit ahead and consumed only when that unit becomes
-  // current, so their latency hides behind a whole unit.
+  // entries are loaded a unit ahead (pend_map) and copied to map_ready during
+  // the first K-step of the current unit, where the compiler's wait for them
+  // counts exactly the loads issued since; at the unit switch, where its count
+  // would have to cover every K-loop trip, it would drain the prefetched
+  // tiles of the next unit.
   struct Src {
     __amdgpu_buffer_rsrc_t ra, rb0, rb1;  // A rows; W1 (or W2) rows; W3 rows
     int a_off[LA];                        // per thread, bytes (kOutOfRange: no row)
@@ -312,7 +340,8 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
   // are advanced in unsigned arithmetic, so they stay out of range.
   constexpr unsigned kOutOfRange = 0x80000000u;
   int pend_row[LA];  // prepared unit: group row / token per thread row
-  int pend_map[LA];  // prepared unit: perm_src[pend_row] when gathering
+  int pend_map[LA];   // prepared unit: perm_src[pend_row] when gathering (in flight)
+  int map_ready[LA];  // the same values once landed (see settle)
   Unit pend;
   auto prepare = [&](int u) __attribute__((always_inline)) {
     pend = decode(u);
@@ -324,6 +353,15 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
       // branch-free, so the loaded value is not touched until the unit switch
       const int32_t* src = gather ? a.a_row_map + pend_row[i] : a.offsets;
       pend_map[i] = *src;
+    })
+  };
+  // The empty asm makes each value a new one defined here, so the compiler
+  // waits for the load at this point and cannot fold the copy away.
+  auto settle = [&]() __attribute__((always_inline)) {
+    MOE_FOR(i, LA, {
+      int v = pend_map[i];
+      asm volatile("" : "+v"(v));
+      map_ready[i] = v;
     })
   };
   constexpr int kRsrcFlags = 0x00020000;  // raw (untyped) buffer
@@ -348,7 +386,7 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
     // logical chunk the swizzle puts there (as for the weights below).
     const int a_chunk = C::DMAA ? (ld_chunk ^ ((ld_row >> 1) & (kChunksPerRow - 1))) : ld_chunk;
     MOE_FOR(i, LA, {
-      int row = gather ? pend_map[i] : pend_row[i];
+      int row = gather ? map_ready[i] : pend_row[i];
       if (gather && (row < 0 || row >= a.T)) row = 0;  // malformed permutation: stay in bounds
       sr.a_off[i] = ld_row + RPP * i < pend.valid_rows ? (row * K + a_chunk * 8) * 2
                                                        : static_cast<int>(kOutOfRange);
@@ -600,6 +638,7 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
     constexpr int kRowsA = (C::BM * kChunksPerRow * 16 / RB) / 32 * 32;  // whole tiles in lds_a[fa]
     constexpr int kRowsB = C::BW * kChunksPerRow * 16 / RB;             // rows in lds_b[fb]
     constexpr int kPassRows = (kRowsA + kRowsB) / 32 * 32;
+    static_assert(27 * RB < 65536, "LDS write offsets fit the 16-bit offset field");
     constexpr bool kViaLds = kPassRows > 0;
     if constexpr (kViaLds) {
       // Through LDS: the lanes' column values go into the idle buffers (rows
@@ -635,16 +674,15 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
               MOE_FOR(j, TN / 2, {
                 unsigned char* base = tile_base(r_tile, 2 * (wn * HC + 32 * j + col_l));
                 MOE_FOR(v, 16, {
-                  *reinterpret_cast<uint16_t*>(base + ((v >> 2) * 8 + (v & 3)) * RB) =
-                      f32_to_bf16(swiglu(acc[i][j][v], acc[i][j + TN / 2][v]));
+                  lds_write_b16<((v >> 2) * 8 + (v & 3)) * RB>(
+                      base, f32_to_bf16(swiglu(acc[i][j][v], acc[i][j + TN / 2][v])));
                 })
               })
             } else {
               MOE_FOR(j, TN, {
                 unsigned char* base = tile_base(r_tile, 2 * (wn * (C::BW / C::WN) + 32 * j + col_l));
                 MOE_FOR(v, 16, {
-                  *reinterpret_cast<uint16_t*>(base + ((v >> 2) * 8 + (v & 3)) * RB) =
-                      f32_to_bf16(acc[i][j][v]);
+                  lds_write_b16<((v >> 2) * 8 + (v & 3)) * RB>(base, f32_to_bf16(acc[i][j][v]));
                 })
               })
             }
@@ -656,7 +694,7 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
         for (int idx = tid; idx < kChunks; idx += kThreads) {
           const int r = idx / (kCols / 8), q = idx % (kCols / 8);
           if (r_lo + r < cu.valid_rows && q * 8 < ncols) {
-            const u32x4 val = *reinterpret_cast<const u32x4*>(cbyte(r, q * 16));
+            const u32x4 val = lds_read_b128(cbyte(r, q * 16));
             *reinterpret_cast<u32x4*>(cbase + (static_cast<int64_t>(cu.orow0) + r_lo + r) * cu.N +
                                       cu.n0 + q * 8) = val;
           }
@@ -716,9 +754,11 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
   };
   int cs = 0;  // weight stage of the current step
   prepare(lb);
+  settle();
   Src cur = source_of_pending();
   Unit cu = pend;
   prepare(next_of(lb));
+  settle();
   if constexpr (C::DMAA) {
     // All-DMA tiles in NS stages, D = NS - 1 steps ahead: the DMA of step
     // k + D (running into the next unit's first steps) is issued at step k
@@ -749,6 +789,7 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
           if (f < cur.nk) issue(cur, f, sd, ks_c);
           else issue(nxt, f - cur.nk, sd, ks_c);
         });
+        if (kt == 0) settle();
         __builtin_amdgcn_s_waitcnt(0x0F70 | ((kAhead & 15) | ((kAhead >> 4) << 14)));
         lds_barrier();
         cs = st(cs + 1);
@@ -781,6 +822,7 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
       mma(0, cs, mrows, [&](auto ks_c) __attribute__((always_inline)) {
         load2(r0, cur, nxt, steps, kt + 2, s2, ks_c);
       });
+      if (kt == 0) settle();
       stash(r1, 1, c1);
       vm_wait();
       lds_barrier();
