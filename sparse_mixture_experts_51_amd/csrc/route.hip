@@ -12,14 +12,16 @@
 // SIMT fp32 GEMM (MFMA would reorder the sums); x and W_r are staged through
 // LDS with a register prefetch of the next d-chunk.  Scores = sigmoid in fp64,
 // rounded once to fp32.
-// Kernel 2 (select): one group of G lanes per token (G = next power of two
-// of E, at most 64).  k+1 rounds of a 64-bit group max over
-// (orderable key << 32 | ~expert) pick the largest key with the lowest index
-// on ties; the (k+1)-th gives the margin.
+// Kernel 2 (select): one group of G lanes per token (G = 16, 32 or 64 as E
+// fits).  k+1 rounds of a 64-bit group max over (orderable key << 32 |
+// ~expert), reduced with DPP lane moves, pick the largest key with the
+// lowest index on ties; the (k+1)-th gives the margin.
 // Kernels 3-4 (seq balance): per-slice partial sums, then one block per
 // sequence reduces them in a fixed order.
 #include "common.hpp"
 #include "kernels.hpp"
+
+#include <type_traits>
 
 namespace moe {
 
@@ -147,9 +149,16 @@ __device__ __forceinline__ void router_logits_tile(const uint16_t* __restrict__ 
 #pragma unroll
     for (int j = 0; j < EPT; ++j) acc[i][j] = 0.0f;
 
+  // Small thread tiles unroll by four chunks of 8 (KC is a multiple of 32) so
+  // that the scheduler can read the next chunks' operands from LDS while the
+  // FMAs of the current one run; they run few waves per SIMD, and nothing
+  // else would hide the LDS latency.  Large tiles have the ILP already and
+  // would spend the registers.
+  constexpr int kUnroll = TPT * EPT <= 2 ? 4 : 1;
   auto compute = [&](int b) {
     const unsigned char* xb = xs(b) + ty * TPT * xrow;
     const unsigned char* wb = ws(b) + tx * wrow;
+#pragma unroll kUnroll
     for (int kk = 0; kk < KC; kk += 8) {
       float xv[TPT][8], wv[8 * EPT];
 #pragma unroll
@@ -218,6 +227,9 @@ static int next_pow2(int v) {
   while (p < v) p <<= 1;
   return p;
 }
+
+// Lanes per token in the selection: 16, 32 or 64 (see group_max).
+static int select_group(int E) { return E <= 16 ? 16 : (E <= 32 ? 32 : 64); }
 
 struct RouterCfg {
   int BE, EPT, TPT, KC;
@@ -293,9 +305,9 @@ hipError_t launch_router_scores(const uint16_t* x, const float* w_router, float*
   return hipErrorInvalidValue;
 }
 
-template <int EPL>
+template <int EPL, int G>
 __device__ __forceinline__ double select_token(const float* srow, const float* __restrict__ bias,
-                                               int lane, int G, int E, int k,
+                                               int lane, int lane64, int E, int k,
                                                int32_t* __restrict__ idx_row,
                                                float* __restrict__ gate_row, float* margin_out,
                                                double* tok_sum_out);
@@ -331,14 +343,21 @@ __global__ __launch_bounds__(kRouteThreads) void router_fused_kernel(
       if (e < E) sc[(ty * TPT + i) * E + e] = sigmoid_score(acc[i][j]);
     }
   __syncthreads();
-  const int lane = threadIdx.x % G, grp = threadIdx.x / G, ngrp = kRouteThreads / G;
-  for (int tl = grp; tl < BT; tl += ngrp) {
-    const int64_t t = t0 + tl;
-    if (t >= T) continue;  // whole group skips together
-    const double ts = select_token<1>(sc + tl * E, bias, lane, G, E, k, idx + t * k, gate + t * k,
-                                      margin ? margin + t : nullptr, nullptr);
-    if (lane == 0) tsum[tl] = ts;
-  }
+  auto select_all = [&](auto g_c) __attribute__((always_inline)) {
+    constexpr int GG = decltype(g_c)::value;
+    const int lane = threadIdx.x % GG, grp = threadIdx.x / GG, ngrp = kRouteThreads / GG;
+    for (int tl = grp; tl < BT; tl += ngrp) {
+      const int64_t t = t0 + tl;
+      if (t >= T) continue;  // whole group skips together
+      const double ts = select_token<1, GG>(sc + tl * E, bias, lane, threadIdx.x & 63, E, k,
+                                            idx + t * k, gate + t * k,
+                                            margin ? margin + t : nullptr, nullptr);
+      if (lane == 0) tsum[tl] = ts;
+    }
+  };
+  if (G == 16) select_all(std::integral_constant<int, 16>{});
+  else if (G == 32) select_all(std::integral_constant<int, 32>{});
+  else select_all(std::integral_constant<int, 64>{});
   if (!seq_p) return;
   // Partials: thread (e, lane l of L = 256 / E) sums s/sum(s) over the tokens
   // l, l + L, ... in order; the L lane sums are then added in lane order.
@@ -382,90 +401,193 @@ __device__ __forceinline__ uint64_t pack_key(float key, int e) {
   return (static_cast<uint64_t>(orderable(key)) << 32) | lo;
 }
 
-template <int EPL>
+// Group reductions of the selection run on DPP lane moves, which stay in the
+// vector ALU (a shuffle through ds_bpermute is an LDS round trip).  A group
+// is one 16-lane DPP row (G = 16), two rows (G = 32) or the wave (G = 64).
+// Row step: quad_perm [1,0,3,2] and [2,3,0,1] (lane xor 1, 2), then row_ror
+// by 12 and 8 (lane i reads lane i + 4, then i + 8, mod 16); after the four
+// steps every lane of a row holds the row's reduction.  Rows are then joined
+// with row_bcast:15 (lane 15 of a row into the next row) and row_bcast:31
+// (lane 31 into rows 2 and 3), which leave the group's result in its last
+// lane (31 or 63); readlane makes it wave-uniform.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), CTRL, ROWS, 0xF, false));
+}
+
+// A candidate: 64-bit key (hi:lo as pack_key) and the unbiased score of its
+// expert, which rides along so that the winners' scores need no lookup.
+struct Cand {
+  uint32_t hi, lo;
+  float s;
+};
+__device__ __forceinline__ void cand_max(Cand& a, const Cand& b) {
+  const bool take = b.hi > a.hi || (b.hi == a.hi && b.lo > a.lo);
+  a.hi = take ? b.hi : a.hi;
+  a.lo = take ? b.lo : a.lo;
+  a.s = take ? b.s : a.s;
+}
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ Cand dpp_cand(const Cand& v) {
+  return Cand{dpp_u32<CTRL, ROWS>(v.hi), dpp_u32<CTRL, ROWS>(v.lo),
+              __uint_as_float(dpp_u32<CTRL, ROWS>(__float_as_uint(v.s)))};
+}
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t u = __double_as_longlong(v);
+  const uint32_t lo = dpp_u32<CTRL, ROWS>(static_cast<uint32_t>(u));
+  const uint32_t hi = dpp_u32<CTRL, ROWS>(static_cast<uint32_t>(u >> 32));
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppRor12 = 0x12C, kDppRor8 = 0x128;
+constexpr int kDppBcast15 = 0x142, kDppBcast31 = 0x143;
+
+// Group maximum, the same in every lane of the group.
+template <int G>
+__device__ __forceinline__ Cand group_max(Cand v, int lane64) {
+  cand_max(v, dpp_cand<kDppXor1>(v));
+  cand_max(v, dpp_cand<kDppXor2>(v));
+  cand_max(v, dpp_cand<kDppRor12>(v));
+  cand_max(v, dpp_cand<kDppRor8>(v));
+  if constexpr (G == 16) {
+    return v;
+  } else {
+    cand_max(v, dpp_cand<kDppBcast15, 0xA>(v));  // rows 1, 3 take rows 0, 2
+    if constexpr (G == 64) cand_max(v, dpp_cand<kDppBcast31, 0xC>(v));
+    auto pick = [&](int src) __attribute__((always_inline)) {
+      return Cand{static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v.hi), src)),
+                  static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v.lo), src)),
+                  __uint_as_float(static_cast<uint32_t>(
+                      __builtin_amdgcn_readlane(static_cast<int>(__float_as_uint(v.s)), src)))};
+    };
+    if constexpr (G == 64) return pick(63);
+    const Cand g0 = pick(31), g1 = pick(63);
+    return lane64 < 32 ? g0 : g1;
+  }
+}
+
+// Group sum (fp64) with the same lane moves; the tree differs from a
+// sequential sum, so the value is compared within a tolerance, never
+// bit-for-bit.
+template <int G>
+__device__ __forceinline__ double group_sum(double v, int lane64) {
+  v += dpp_f64<kDppXor1>(v);
+  v += dpp_f64<kDppXor2>(v);
+  v += dpp_f64<kDppRor12>(v);
+  v += dpp_f64<kDppRor8>(v);
+  if constexpr (G == 16) {
+    return v;
+  } else {
+    // rows 1 and 3 add rows 0 and 2; with G = 64 row 3 then adds row 1
+    const double b15 = dpp_f64<kDppBcast15, 0xA>(v);
+    v = (lane64 & 16) ? v + b15 : v;
+    if constexpr (G == 64) {
+      const double b31 = dpp_f64<kDppBcast31, 0xC>(v);
+      v = (lane64 >= 48) ? v + b31 : v;
+    }
+    auto pick = [&](int src) __attribute__((always_inline)) {
+      const uint64_t u = __double_as_longlong(v);
+      const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u), src));
+      const uint32_t hi =
+          static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(u >> 32), src));
+      return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+    };
+    if constexpr (G == 64) return pick(63);
+    const double g0 = pick(31), g1 = pick(63);
+    return lane64 < 32 ? g0 : g1;
+  }
+}
+
+// Top-k of one token by a group of G lanes (lane = index in the group, lane64
+// = index in the wave); lane i holds experts i, i + G, ... (EPL of them).
+// k + 1 rounds of a group maximum over (orderable key << 32 | ~expert) pick
+// the largest key with the lowest index on ties; the (k+1)-th gives the
+// margin.  The gate sum adds the winners' unbiased scores in slot order.
+template <int EPL, int G>
 __device__ __forceinline__ double select_token(const float* srow, const float* __restrict__ bias,
-                                               int lane, int G, int E, int k,
+                                               int lane, int lane64, int E, int k,
                                                int32_t* __restrict__ idx_row,
                                                float* __restrict__ gate_row, float* margin_out,
                                                double* tok_sum_out) {
-  uint64_t pk[EPL];
+  Cand pk[EPL];
   double ssum = 0.0;
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
     const int e = lane + i * G;
-    pk[i] = 0;  // padding and taken entries
+    pk[i] = Cand{0, 0, 0.0f};  // padding and taken entries
     if (e < E) {
       const float sv = srow[e];
       ssum += static_cast<double>(sv);
-      pk[i] = pack_key(sv + bias[e], e);
+      const uint64_t key = pack_key(sv + bias[e], e);
+      pk[i] = Cand{static_cast<uint32_t>(key >> 32), static_cast<uint32_t>(key), sv};
     }
   }
 
   int my_e = 0;
-  float kth = 0.0f, next = 0.0f;
+  float s_mine = 0.0f, sum = 0.0f, kth = 0.0f, next = 0.0f;
   const int rounds = (k < E) ? k + 1 : k;
   for (int r = 0; r < rounds; ++r) {
-    uint64_t v = pk[0];
+    Cand v = pk[0];
 #pragma unroll
-    for (int i = 1; i < EPL; ++i) v = pk[i] > v ? pk[i] : v;
-    for (int off = G >> 1; off > 0; off >>= 1) {
-      const uint64_t o = __shfl_xor(v, off, G);
-      v = o > v ? o : v;
-    }
-    const int e = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(v));
-    const uint32_t hi = static_cast<uint32_t>(v >> 32);
-    const float key = hi ? from_orderable(hi) : __uint_as_float(0x7FC00000u);
+    for (int i = 1; i < EPL; ++i) cand_max(v, pk[i]);
+    v = group_max<G>(v, lane64);
+    const int e = static_cast<int>(0xFFFFFFFFu - v.lo);
+    const float key = v.hi ? from_orderable(v.hi) : __uint_as_float(0x7FC00000u);
     if (r < k) {
 #pragma unroll
       for (int i = 0; i < EPL; ++i)
-        if (lane + i * G == e) pk[i] = 0;
-      if (lane == r) my_e = e;
+        if (lane + i * G == e) pk[i] = Cand{0, 0, 0.0f};
+      if (lane == r) {
+        my_e = e;
+        s_mine = v.s;
+      }
+      sum += v.s;
       if (r == k - 1) kth = key;
     } else {
       next = key;
     }
   }
 
-  // Gates from the unbiased scores of the winners, summed in slot order.
-  const float s_mine = (lane < k) ? srow[my_e] : 0.0f;
-  float sum = 0.0f;
-  for (int j = 0; j < k; ++j) sum += __shfl(s_mine, j, G);
+  // Gates from the unbiased scores of the winners, normalised over them.
   if (lane < k) {
     idx_row[lane] = my_e;
     gate_row[lane] = (sum == 0.0f) ? 1.0f / static_cast<float>(k) : s_mine / sum;
   }
   if (lane == 0 && margin_out) *margin_out = (k < E) ? kth - next : __builtin_inff();
-  for (int off = G >> 1; off > 0; off >>= 1) ssum += __shfl_xor(ssum, off, G);
+  ssum = group_sum<G>(ssum, lane64);
   if (lane == 0 && tok_sum_out) *tok_sum_out = ssum;
   return ssum;
 }
 
-template <int EPL>
+template <int EPL, int G>
 __global__ __launch_bounds__(256) void select_kernel(
     const float* __restrict__ scores, const float* __restrict__ bias, int32_t* __restrict__ idx,
     float* __restrict__ gate, float* __restrict__ margin, double* __restrict__ tok_sum,
-    int64_t T, int E, int k, int G) {
+    int64_t T, int E, int k) {
+  const int lane64 = threadIdx.x & 63;
   const int lane = threadIdx.x % G;
   const int grp = threadIdx.x / G;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * (256 / G) + grp;
   if (t >= T) return;  // whole group leaves together
-  select_token<EPL>(scores + t * E, bias, lane, G, E, k, idx + t * k, gate + t * k,
-                    margin ? margin + t : nullptr, tok_sum ? tok_sum + t : nullptr);
+  select_token<EPL, G>(scores + t * E, bias, lane, lane64, E, k, idx + t * k, gate + t * k,
+                       margin ? margin + t : nullptr, tok_sum ? tok_sum + t : nullptr);
 }
 
 hipError_t launch_select(const float* scores, const float* bias, int32_t* idx, float* gate,
                          float* margin, double* tok_sum, int64_t T, int E, int k, hipStream_t s) {
-  const int G = next_pow2(E) < 64 ? next_pow2(E) : 64;
+  const int G = select_group(E);
   const int epl = (E + G - 1) / G;
   const int64_t nblk = (T + (256 / G) - 1) / (256 / G);
   const dim3 grid(static_cast<unsigned>(nblk)), block(256);
-#define MOE_SEL_CASE(n)                                                                      \
-  if (epl <= n) {                                                                            \
-    hipLaunchKernelGGL((select_kernel<n>), grid, block, 0, s, scores, bias, idx, gate, margin, \
-                       tok_sum, T, E, k, G);                                                  \
-    return hipGetLastError();                                                                \
+#define MOE_SEL_CASE(n, g)                                                                     \
+  if (epl <= n && G == g) {                                                                    \
+    hipLaunchKernelGGL((select_kernel<n, g>), grid, block, 0, s, scores, bias, idx, gate, margin, \
+                       tok_sum, T, E, k);                                                       \
+    return hipGetLastError();                                                                  \
   }
-  MOE_SEL_CASE(1) MOE_SEL_CASE(2) MOE_SEL_CASE(4) MOE_SEL_CASE(8) MOE_SEL_CASE(16)
+  MOE_SEL_CASE(1, 16) MOE_SEL_CASE(1, 32) MOE_SEL_CASE(1, 64) MOE_SEL_CASE(2, 64)
+  MOE_SEL_CASE(4, 64) MOE_SEL_CASE(8, 64) MOE_SEL_CASE(16, 64)
 #undef MOE_SEL_CASE
   return hipErrorInvalidValue;
 }
@@ -579,13 +701,14 @@ hipError_t launch_route_fused(const uint16_t* x, const float* w_router, const fl
                               int E, int k, int S, hipStream_t s, bool* done) {
   *done = false;
   if (E > 64) return hipSuccess;
-  const RouterCfg c = router_cfg(T, d, E, device_cus(), true);
+  // two blocks per CU: a second wave per SIMD hides the first one's LDS latency
+  const RouterCfg c = router_cfg(T, d, E, 2 * device_cus(), true);
   if (c.blocks <= 0 || c.BE < E) return hipSuccess;
   const int TPR = c.BE / c.EPT;
   const int BT = (kRouteThreads / TPR) * c.TPT;
   const bool stats = seq_out != nullptr && S > 0;
   if (stats && (S % BT != 0 || S / BT > seq_partials_capacity(T, S))) return hipSuccess;
-  const int G = next_pow2(E);
+  const int G = select_group(E);
   // scores [BT][E] f32, tok sums [BT] f64, lane partials [256] f64, counts [E] i32
   const size_t tail = static_cast<size_t>(((BT * E * 4 + 15) & ~15) + BT * 8 + kRouteThreads * 8 +
                                           E * 4);

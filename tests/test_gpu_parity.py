@@ -47,6 +47,15 @@ ROUTE_CASES = {
     "k_equals_E": custom(tokens=100, d_model=64, n_experts=8, top_k=8, cfg_id=97),
     "k1": custom(tokens=300, n_experts=16, top_k=1, cfg_id=98),
     "T1": custom(tokens=1, n_experts=16, top_k=4, cfg_id=99),
+    # two 16-lane rows per token in the selection: separate select kernel
+    # (250-token sequences do not split into whole blocks) and fused routing
+    "E24_k3": custom(tokens=500, seq_len=250, d_model=128, n_experts=24, top_k=3, cfg_id=117,
+                     router_std=0.1),
+    "E24_k3_fused": custom(tokens=512, seq_len=256, d_model=128, n_experts=24, top_k=3,
+                           cfg_id=119, router_std=0.1),
+    # a whole wave per token, one expert per lane
+    "E64_k8": custom(tokens=320, seq_len=160, d_model=128, n_experts=64, top_k=8, cfg_id=118,
+                     router_std=0.1),
 }
 
 
