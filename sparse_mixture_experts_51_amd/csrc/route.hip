@@ -648,23 +648,47 @@ __global__ __launch_bounds__(256) void seq_partial_kernel(
   for (int e = threadIdx.x; e < E; e += 256) seq_cnt[static_cast<int64_t>(blockIdx.x) * E + e] = cnt[e];
 }
 
+// One block per sequence.  Experts are taken 256 / ne lanes at a time (ne =
+// experts of the pass): lane l of expert e adds the partials l, l + L, ... in
+// order, the L lane sums are added in lane order, and the experts' terms
+// f_e * P_e / S are then summed by a tree over the block.  With few splits
+// every lane loads one partial, so the whole kernel is one memory round trip.
 __global__ __launch_bounds__(256) void seq_final_kernel(
     const double* __restrict__ seq_p, const int32_t* __restrict__ seq_cnt, float* __restrict__ out,
     float alpha, int E, int k, int S, int nsplit) {
   __shared__ double part[256];
+  __shared__ int64_t pcnt[256];
   const int q = blockIdx.x;
   double acc = 0.0;
-  for (int e = threadIdx.x; e < E; e += 256) {
+  for (int e0 = 0; e0 < E; e0 += 256) {
+    const int ne = (E - e0) < 256 ? (E - e0) : 256;
+    const int L = 256 / ne;
+    const int e = e0 + threadIdx.x % ne, l = threadIdx.x / ne;
     double p = 0.0;
     int64_t c = 0;
-    for (int sp = 0; sp < nsplit; ++sp) {
-      const int64_t o = (static_cast<int64_t>(q) * nsplit + sp) * E + e;
-      p += seq_p[o];
-      c += seq_cnt[o];
+    if (l < L) {
+      for (int sp = l; sp < nsplit; sp += L) {
+        const int64_t o = (static_cast<int64_t>(q) * nsplit + sp) * E + e;
+        p += seq_p[o];
+        c += seq_cnt[o];
+      }
     }
-    const double f = static_cast<double>(E) / (static_cast<double>(k) * S) * static_cast<double>(c);
-    acc += f * (p / S);
+    __syncthreads();  // the previous pass is done with part / pcnt
+    part[threadIdx.x] = p;
+    pcnt[threadIdx.x] = c;
+    __syncthreads();
+    if (threadIdx.x < ne) {
+      double pe = 0.0;
+      int64_t ce = 0;
+      for (int j = 0; j < L; ++j) {
+        pe += part[j * ne + threadIdx.x];
+        ce += pcnt[j * ne + threadIdx.x];
+      }
+      const double f = static_cast<double>(E) / (static_cast<double>(k) * S) * static_cast<double>(ce);
+      acc += f * (pe / S);
+    }
   }
+  __syncthreads();
   part[threadIdx.x] = acc;
   __syncthreads();
   for (int w = 128; w > 0; w >>= 1) {
