@@ -165,15 +165,11 @@ __device__ __forceinline__ void lds_read4_b128(const u32x4* const (&p)[4], u32x4
 
 // The epilogue's LDS traffic is written in asm too: the compiler cannot tell
 // its buffers from those that LDS DMA is filling and would otherwise drain
-// every load in flight before the first access.  A 2-byte write at p + OFF
+// every load in flight before the first access.  An 8-byte write at p
 // (completed by the lgkmcnt(0) of the barrier that follows it) ...
-template <int OFF>
-__device__ __forceinline__ void lds_write_b16(void* p, uint16_t v) {
+__device__ __forceinline__ void lds_write_b64(void* p, uint64_t v) {
   const unsigned a = static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_ptr_t)p));
-  asm volatile("ds_write_b16 %0, %1 offset:%2"
-               :
-               : "v"(a), "v"(static_cast<unsigned>(v)), "i"(OFF)
-               : "memory");
+  asm volatile("ds_write_b64 %0, %1" : : "v"(a), "v"(v) : "memory");
 }
 // ... and a 16-byte read, complete on return.
 __device__ __forceinline__ u32x4 lds_read_b128(const void* p) {
@@ -186,6 +182,13 @@ __device__ __forceinline__ u32x4 lds_read_b128(const void* p) {
       : "v"(a)
       : "memory");
   return v;
+}
+
+// Two fp32 values to packed bf16 (round to nearest even) in one conversion.
+__device__ __forceinline__ uint32_t bf16x2_bits(float lo, float hi) {
+  typedef float f2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{lo, hi}, b2_t));
 }
 
 // LDS-only barrier: waits for this wave's LDS traffic, not for global loads.
@@ -474,9 +477,10 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
     }
   };
 
-  // Accumulators: acc[tm][tn], rows tile_row(tm) .. +31, weight-tile rows
-  // SwiGLU: tn < TN/2 gate rows wn*HC + 32*tn, tn >= TN/2 the up rows of the
-  // same h columns (BW/2 further); down: rows wn*BW/WN + 32*tn.
+  // Accumulators: acc[tm][tn] pairs token rows tile_row(tm) .. +31 with
+  // weight-tile rows (output columns) -- SwiGLU: tn < TN/2 gate rows
+  // wn*HC + 32*tn, tn >= TN/2 the up rows of the same h columns (BW/2
+  // further); down: rows wn*BW/WN + 32*tn.
   constexpr int HC = C::BW / 2 / C::WN;  // h columns per wave (SwiGLU)
   f32x16 acc[TM][TN];
   auto zero_acc = [&]() __attribute__((always_inline)) {
@@ -527,7 +531,7 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
       MOE_FOR(i, TM, {
         if (i < mrows) {
           MOE_FOR(j, TN, {
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
           })
         }
       })
@@ -610,7 +614,7 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
       MOE_FOR(i, TM, {
         if (i < mrows) {
           MOE_FOR(j, TN, {
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
           })
         }
       })
@@ -624,104 +628,77 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
   auto swiglu = [](float ga, float up) __attribute__((always_inline)) {
     return ga * __builtin_amdgcn_rcpf(1.0f + __expf(-ga)) * up;
   };
-  // 32x32 accumulator layout: lane holds column (lane & 31), rows
-  // (v/4)*8 + (lane/32)*4 + v%4 for v = 0..15.
-  const int col_l = lane & 31;
-  const int row_l = (lane >> 5) * 4;
+  // The MFMAs take the weight fragment as the first operand, so acc holds the
+  // transposed tile: lane l has token row (l & 31) of its 32x32 tile and, for
+  // g = 0..3, the four adjacent output columns 8g + 4(l >> 5) + 0..3 as
+  // values 4g .. 4g+3.
+  const int lrow = lane & 31;
+  const int lcol = (lane >> 5) * 4;
   // fa, fb: the A buffer and the weight stage that no load in flight writes
   // (both free since the barrier after the unit's last K-step); mrows: the
   // wave's tiles with valid rows.
+  //
+  // The output tile goes through those buffers (rows [0, kRowsA) of a pass in
+  // lds_a[fa], the rest in lds_b[fb]) and leaves as 16-byte row stores, in
+  // passes of kPassRows rows when it is larger than the buffers.  A lane
+  // writes its four adjacent columns as one 8-byte word; one write
+  // instruction covers 32 rows at one 16-byte chunk, so chunk q of (pass-
+  // relative) row r sits at chunk q ^ sw(r), which spreads those rows over
+  // all 64 banks (and keeps a row's chunks on distinct banks for the reads).
   auto epilogue = [&](const Unit& cu, int mrows, int fa, int fb) __attribute__((always_inline)) {
     uint16_t* cbase = cu.routed ? a.c_routed : a.c_shared;
     constexpr int kCols = kSwiGLU ? C::BW / 2 : C::BW;
     constexpr int RB = kCols * 2;                                       // bytes per output row
+    constexpr int C16 = RB / 16;                                        // 16-byte chunks per row
     constexpr int kRowsA = (C::BM * kChunksPerRow * 16 / RB) / 32 * 32;  // whole tiles in lds_a[fa]
     constexpr int kRowsB = C::BW * kChunksPerRow * 16 / RB;             // rows in lds_b[fb]
     constexpr int kPassRows = (kRowsA + kRowsB) / 32 * 32;
-    static_assert(27 * RB < 65536, "LDS write offsets fit the 16-bit offset field");
-    constexpr bool kViaLds = kPassRows > 0;
-    if constexpr (kViaLds) {
-      // Through LDS: the lanes' column values go into the idle buffers (rows
-      // [0, kRowsA) of a pass in lds_a[fa], the rest in lds_b[fb]), then whole
-      // rows leave as 16-byte stores -- in passes of kPassRows rows when the
-      // tile is larger than the buffers.  The 16-byte chunk q of (pass-
-      // relative) row r sits at chunk q ^ (r & 4), so the two rows one 2-byte
-      // write instruction covers (r and r + 4) hit different banks.
-      auto cbyte = [&](int r, int byte) __attribute__((always_inline)) {
-        unsigned char* h = r < kRowsA ? reinterpret_cast<unsigned char*>(&lds_a[fa][0])
-                                      : reinterpret_cast<unsigned char*>(&lds_b[fb][0]);
-        const int rr = r < kRowsA ? r : r - kRowsA;
-        return h + rr * RB + (((byte >> 4) ^ (r & 4)) << 4) + (byte & 15);
-      };
-      // Write side: a 32-row tile never straddles the two regions (kRowsA and
-      // kPassRows are multiples of 32), its rows' (r & 4) is the lane's row_l,
-      // so one base per tile plus the lane's column offset leaves only
-      // immediates per value.
-      auto tile_base = [&](int r_tile, int cbyte_off) __attribute__((always_inline)) {
-        unsigned char* h = r_tile < kRowsA ? reinterpret_cast<unsigned char*>(&lds_a[fa][0])
-                                           : reinterpret_cast<unsigned char*>(&lds_b[fb][0]);
-        const int rr = r_tile < kRowsA ? r_tile : r_tile - kRowsA;
-        return h + (rr + row_l) * RB + ((((cbyte_off >> 4) ^ row_l)) << 4) + (cbyte_off & 15);
-      };
-      constexpr int kPasses = (C::BM + kPassRows - 1) / kPassRows;
-      const int ncols = cu.N - cu.n0 < kCols ? cu.N - cu.n0 : kCols;
-      MOE_FOR(p, kPasses, {
-        const int r_lo = p * kPassRows;
-        MOE_FOR(i, TM, {
-          const int r_tile = tile_row(i) - r_lo;
-          if (i < mrows && r_tile >= 0 && r_tile < kPassRows) {
-            if (kSwiGLU) {
-              MOE_FOR(j, TN / 2, {
-                unsigned char* base = tile_base(r_tile, 2 * (wn * HC + 32 * j + col_l));
-                MOE_FOR(v, 16, {
-                  lds_write_b16<((v >> 2) * 8 + (v & 3)) * RB>(
-                      base, f32_to_bf16(swiglu(acc[i][j][v], acc[i][j + TN / 2][v])));
-                })
-              })
-            } else {
-              MOE_FOR(j, TN, {
-                unsigned char* base = tile_base(r_tile, 2 * (wn * (C::BW / C::WN) + 32 * j + col_l));
-                MOE_FOR(v, 16, {
-                  lds_write_b16<((v >> 2) * 8 + (v & 3)) * RB>(base, f32_to_bf16(acc[i][j][v]));
-                })
-              })
-            }
-          }
-        })
-        lds_barrier();
-        constexpr int kPr = (C::BM - p * kPassRows) < kPassRows ? (C::BM - p * kPassRows) : kPassRows;
-        constexpr int kChunks = kPr * kCols / 8;
-        for (int idx = tid; idx < kChunks; idx += kThreads) {
-          const int r = idx / (kCols / 8), q = idx % (kCols / 8);
-          if (r_lo + r < cu.valid_rows && q * 8 < ncols) {
-            const u32x4 val = lds_read_b128(cbyte(r, q * 16));
-            *reinterpret_cast<u32x4*>(cbase + (static_cast<int64_t>(cu.orow0) + r_lo + r) * cu.N +
-                                      cu.n0 + q * 8) = val;
-          }
-        }
-        lds_barrier();  // the buffer is reused by the next pass or the next unit
-      })
-    } else {
+    static_assert(kPassRows > 0 && C16 >= 8 && (C16 & (C16 - 1)) == 0, "output staging layout");
+    auto sw = [](int r) __attribute__((always_inline)) { return C16 >= 16 ? (r & 15) : ((r >> 1) & 7); };
+    auto row_ptr = [&](int r) __attribute__((always_inline)) {
+      return r < kRowsA ? reinterpret_cast<unsigned char*>(&lds_a[fa][0]) + r * RB
+                        : reinterpret_cast<unsigned char*>(&lds_b[fb][0]) + (r - kRowsA) * RB;
+    };
+    constexpr int kPasses = (C::BM + kPassRows - 1) / kPassRows;
+    const int ncols = cu.N - cu.n0 < kCols ? cu.N - cu.n0 : kCols;
+    MOE_FOR(p, kPasses, {
+      const int r_lo = p * kPassRows;
       MOE_FOR(i, TM, {
-        MOE_FOR(v, 16, {
-          const int r = tile_row(i) + (v >> 2) * 8 + row_l + (v & 3);
-          if (r < cu.valid_rows) {
-            uint16_t* orow = cbase + (static_cast<int64_t>(cu.orow0) + r) * cu.N;
-            if (kSwiGLU) {
-              MOE_FOR(j, TN / 2, {
-                orow[cu.n0 + wn * HC + 32 * j + col_l] =
-                    f32_to_bf16(swiglu(acc[i][j][v], acc[i][j + TN / 2][v]));
+        const int r_tile = tile_row(i) - r_lo;
+        if (i < mrows && r_tile >= 0 && r_tile < kPassRows) {
+          // a 32-row tile lies in one region: kRowsA and kPassRows are multiples of 32
+          const int r = r_tile + lrow;
+          unsigned char* row = row_ptr(r);
+          const int s = sw(r);
+          MOE_FOR(j, (kSwiGLU ? TN / 2 : TN), {
+            const int col0 = kSwiGLU ? wn * HC + 32 * j : wn * (C::BW / C::WN) + 32 * j;
+            MOE_FOR(g, 4, {
+              float v[4];
+              MOE_FOR(t, 4, {
+                v[t] = kSwiGLU ? swiglu(acc[i][j][4 * g + t], acc[i][kSwiGLU ? j + TN / 2 : j][4 * g + t])
+                               : acc[i][j][4 * g + t];
               })
-            } else {
-              MOE_FOR(j, TN, {
-                const int c = cu.n0 + wn * (C::BW / C::WN) + 32 * j + col_l;
-                if (c < cu.N) orow[c] = f32_to_bf16(acc[i][j][v]);
-              })
-            }
-          }
-        })
+              const uint64_t w = static_cast<uint64_t>(bf16x2_bits(v[0], v[1])) |
+                                 (static_cast<uint64_t>(bf16x2_bits(v[2], v[3])) << 32);
+              const int q = (col0 >> 3) + g;  // 16-byte chunk of these columns
+              lds_write_b64(row + ((q ^ s) << 4) + lcol * 2, w);
+            })
+          })
+        }
       })
-    }
+      lds_barrier();
+      constexpr int kPr = (C::BM - p * kPassRows) < kPassRows ? (C::BM - p * kPassRows) : kPassRows;
+      constexpr int kChunks = kPr * C16;
+      for (int idx = tid; idx < kChunks; idx += kThreads) {
+        const int r = idx / C16, q = idx % C16;
+        if (r_lo + r < cu.valid_rows && q * 8 < ncols) {
+          const u32x4 val = lds_read_b128(row_ptr(r) + ((q ^ sw(r)) << 4));
+          *reinterpret_cast<u32x4*>(cbase + (static_cast<int64_t>(cu.orow0) + r_lo + r) * cu.N +
+                                    cu.n0 + q * 8) = val;
+        }
+      }
+      lds_barrier();  // the buffers are reused by the next pass or the next unit
+    })
   };
 
   // ---- software pipeline.  Each unit runs an even number of K-steps; the
