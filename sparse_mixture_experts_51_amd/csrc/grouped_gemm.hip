@@ -847,18 +847,44 @@ static bool big_groups(const GroupedGemmArgs& a) {
   return a.T * a.top_k / (a.E > 0 ? a.E : 1) >= 512;
 }
 
+template <class C, bool kSwiGLU>
+static void launch_cfg(const GroupedGemmArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((grouped_gemm_kernel<C, kSwiGLU>), dim3(persistent_grid<C>()), dim3(C::kThreads),
+                     0, s, a);
+}
+
 template <bool kSwiGLU>
 static hipError_t launch_gemm(const GroupedGemmArgs& a, hipStream_t s) {
   if (streaming_shape(a)) {
-    hipLaunchKernelGGL((grouped_gemm_kernel<kStream, kSwiGLU>), dim3(persistent_grid<kStream>()),
-                       dim3(kStream::kThreads), 0, s, a);
-  } else if (big_groups(a)) {
-    hipLaunchKernelGGL((grouped_gemm_kernel<kBig, kSwiGLU>), dim3(persistent_grid<kBig>()),
-                       dim3(kBig::kThreads), 0, s, a);
-  } else {
-    hipLaunchKernelGGL((grouped_gemm_kernel<kCompute, kSwiGLU>), dim3(persistent_grid<kCompute>()),
-                       dim3(kCompute::kThreads), 0, s, a);
+    if (!a.w_shared) {
+      launch_cfg<kStream, kSwiGLU>(a, s);
+      return hipGetLastError();
+    }
+    // The streaming tile would cover the shared expert's T rows in T / BM
+    // units that each stream its whole weight tile again, at the CU time of a
+    // routed unit; the shared expert runs as its own launch instead, with the
+    // tile its row count calls for (and the routed units alone divide evenly
+    // over the grid more often).
+    GroupedGemmArgs routed = a;
+    routed.w_shared = routed.w3_shared = nullptr;
+    routed.a_shared = nullptr;
+    routed.c_shared = nullptr;
+    launch_cfg<kStream, kSwiGLU>(routed, s);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    GroupedGemmArgs shared = a;  // one group: the shared expert's T rows
+    shared.E = 0;
+    shared.w_routed = shared.w3_routed = nullptr;
+    shared.a_routed = nullptr;
+    shared.a_row_map = nullptr;
+    shared.c_routed = nullptr;
+    constexpr int kMinK = kBK * (kBig::NSA - 1);
+    if (a.T >= 512 && a.K_s >= kMinK) launch_cfg<kBig, kSwiGLU>(shared, s);
+    else launch_cfg<kCompute, kSwiGLU>(shared, s);
+    return hipGetLastError();
   }
+  if (big_groups(a)) launch_cfg<kBig, kSwiGLU>(a, s);
+  else launch_cfg<kCompute, kSwiGLU>(a, s);
   return hipGetLastError();
 }
 
