@@ -232,7 +232,8 @@ def main():
     roof["traffic"] = recorded["hbm_bytes_per_launch"] if recorded else None
     if recorded:
         roof["traffic_over_algorithmic"] = roof["traffic"] / byts
-    roof["kernel"] = "moe_grouped_ffn = grouped_gemm_kernel<true> + grouped_gemm_kernel<false>"
+    roof["kernel"] = ("moe_grouped_ffn = every grouped_gemm_kernel launch of one call "
+                      "(SwiGLU and down stages; with streaming tiles the shared expert has its own)")
     roof["ms_per_launch"] = ffn_ms
     roof["algorithmic_flop"] = flops
     roof["algorithmic_bytes"] = byts

@@ -79,11 +79,13 @@ def traffic(fetch_dir: str, write_dir: str) -> dict:
         # the calibration copies are the large ones; other copies are small uploads
         copy = [v for v in copy if v >= 0.5 * max(copy)]
         factor = COPY_BYTES / (sum(copy) / len(copy) * 1024.0)
-        swig = [v for k, lst in d.items() if "grouped_gemm" in k and "true>(" in k for _, v in lst]
-        down = [v for k, lst in d.items() if "grouped_gemm" in k and "false>(" in k for _, v in lst]
-        if not swig or not down:
+        # one FFN call runs each grouped_gemm instance once (the SwiGLU and down
+        # stages, each possibly split into a routed and a shared-expert launch):
+        # per call, the mean dispatch of every instance, summed
+        gemm = {k: [v for _, v in lst] for k, lst in d.items() if "grouped_gemm" in k}
+        if not any("true>(" in k for k in gemm) or not any("false>(" in k for k in gemm):
             raise RuntimeError(f"no grouped_gemm dispatches in the {counter} run")
-        kib = sum(swig) / len(swig) + sum(down) / len(down)
+        kib = sum(sum(v) / len(v) for v in gemm.values())
         res[counter] = {"kib_per_launch": kib, "factor": factor, "bytes_per_launch": kib * 1024 * factor,
                         "copy_kib": sum(copy) / len(copy)}
     return res

@@ -37,6 +37,21 @@ def test_traffic_scales_by_the_calibration_copy(tmp_path):
     assert t["WRITE_SIZE"]["bytes_per_launch"] == pytest.approx(400.0 * 1024)
 
 
+def test_traffic_sums_the_instances_of_one_call(tmp_path):
+    # a call that splits each stage into two kernel instances: per call, the
+    # mean of each instance, summed over the instances
+    big_s = SWIG.replace("128, 128, 2, 2, 2", "256, 128, 4, 2, 1")
+    big_d = DOWN.replace("128, 128, 2, 2, 2", "256, 128, 4, 2, 1")
+    kib = profiling.COPY_BYTES / 1024
+    rows = [("__amd_rocclr_copyBuffer", kib)]
+    for _ in range(3):
+        rows += [(SWIG, 1000.0), (big_s, 100.0), (DOWN, 500.0), (big_d, 50.0)]
+    _write(tmp_path / "f", "FETCH_SIZE", rows)
+    _write(tmp_path / "w", "WRITE_SIZE", rows)
+    t = profiling.traffic(str(tmp_path / "f"), str(tmp_path / "w"))
+    assert t["FETCH_SIZE"]["bytes_per_launch"] == pytest.approx(1650.0 * 1024)
+
+
 def test_traffic_record_is_tied_to_the_gemm_source(tmp_path):
     kib = profiling.COPY_BYTES / 1024
     _write(tmp_path / "f", "FETCH_SIZE", [("__amd_rocclr_copyBuffer", kib), (SWIG, 10.0), (DOWN, 10.0)])
