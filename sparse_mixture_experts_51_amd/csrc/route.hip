@@ -37,10 +37,11 @@ __device__ __forceinline__ void route_lds_barrier() {
 
 // Block tile: BT tokens x BE experts; thread tile: TPT tokens x EPT experts
 // (TPR = BE/EPT threads per token row).  d is walked in chunks of KC.  A
-// chunk's x rows (bf16, [BT][KC]) and W_r columns (fp32, [TPR][KC][EPT]:
-// a thread's EPT experts adjacent) sit in LDS with rows padded by 16 bytes,
-// so the lanes of a wave read distinct banks and one 16-byte LDS read gives a
-// thread 8 values of x or 4 of W.  With more than one chunk, the next chunk is
+// chunk's x rows (converted to fp32 when staged, [BT][KC]: the FMAs then
+// need no conversion, which the BE / EPT threads of a token row would each
+// repeat) and W_r columns (fp32, [TPR][KC][EPT]: a thread's EPT experts
+// adjacent) sit in LDS with rows padded by 16 bytes, so the lanes of a wave
+// read distinct banks; one 16-byte LDS read gives a thread 4 values.  With more than one chunk, the next chunk is
 // prefetched into registers while this one is multiplied.  Every (token,
 // expert) logit is one fp32 fmaf chain over d in ascending order.
 template <int EPT, int TPT>
@@ -59,7 +60,7 @@ __device__ __forceinline__ void router_logits_tile(const uint16_t* __restrict__ 
   const int64_t t0 = static_cast<int64_t>(blockIdx.x / n_eblk) * BT;
   const int nchunks = d / KC;
 
-  const int xrow = KC * 2 + 16, wrow = KC * EPT * 4 + 16;  // padded row strides (bytes)
+  const int xrow = KC * 4 + 16, wrow = KC * EPT * 4 + 16;  // padded row strides (bytes)
   const int bufbytes = BT * xrow + TPR * wrow;
   auto xs = [&](int b) { return lds_raw + b * bufbytes; };
   auto ws = [&](int b) { return lds_raw + b * bufbytes + BT * xrow; };
@@ -117,7 +118,10 @@ __device__ __forceinline__ void router_logits_tile(const uint16_t* __restrict__ 
 #pragma unroll
     for (int p = 0; p < kMaxX; ++p) {
       if (p >= nx) break;
-      *reinterpret_cast<uint4*>(xb + r * xrow + c * 16) = rx[p];
+      float f[8];
+      bf16x8_to_f32(rx[p], f);
+      *reinterpret_cast<float4*>(xb + r * xrow + c * 32) = make_float4(f[0], f[1], f[2], f[3]);
+      *reinterpret_cast<float4*>(xb + r * xrow + c * 32 + 16) = make_float4(f[4], f[5], f[6], f[7]);
       r += x_dr;
       c += x_dc;
       if (c >= CX) { c -= CX; ++r; }
@@ -163,8 +167,10 @@ __device__ __forceinline__ void router_logits_tile(const uint16_t* __restrict__ 
       float xv[TPT][8], wv[8 * EPT];
 #pragma unroll
       for (int i = 0; i < TPT; ++i) {
-        const uint4 q = *reinterpret_cast<const uint4*>(xb + i * xrow + kk * 2);
-        bf16x8_to_f32(q, xv[i]);
+        const float4 q0 = *reinterpret_cast<const float4*>(xb + i * xrow + kk * 4);
+        const float4 q1 = *reinterpret_cast<const float4*>(xb + i * xrow + kk * 4 + 16);
+        xv[i][0] = q0.x; xv[i][1] = q0.y; xv[i][2] = q0.z; xv[i][3] = q0.w;
+        xv[i][4] = q1.x; xv[i][5] = q1.y; xv[i][6] = q1.z; xv[i][7] = q1.w;
       }
 #pragma unroll
       for (int h = 0; h < 2 * EPT; ++h) {
@@ -241,8 +247,8 @@ static RouterCfg router_cfg(int64_t T, int d, int E, int want_blocks, bool whole
   // Largest per-thread tile that still gives want_blocks blocks (with few
   // tokens, trade tile size for blocks: each (token, expert) chain is serial
   // over d, so parallelism is bounded by T*E lanes).  A chunk of d is the
-  // whole of d when x and W_r tiles fit the LDS budget; else 64- or 32-wide
-  // double-buffered chunks.
+  // whole of d when x and W_r tiles fit the LDS budget; else the longest
+  // power-of-two double-buffered chunk that fits.
   const int Emax = next_pow2(E) < 64 ? next_pow2(E) : 64;
   auto ept_of = [](int BE) { return BE >= 64 ? 4 : (BE >= 32 ? 2 : 1); };
   RouterCfg best{0, 0, 0, 0, -1, 0};
@@ -259,7 +265,7 @@ static RouterCfg router_cfg(int64_t T, int d, int E, int want_blocks, bool whole
       if (BT > 256) continue;
       const int64_t blocks = ((T + BT - 1) / BT) * ((E + BE - 1) / BE);
       auto bytes = [&](int KC) {
-        return static_cast<size_t>(BT * (KC * 2 + 16) + TPR * (KC * EPT * 4 + 16));
+        return static_cast<size_t>(BT * (KC * 4 + 16) + TPR * (KC * EPT * 4 + 16));
       };
       auto fits = [&](int KC) {  // at most 8 pieces of x and 8 of W per thread
         return static_cast<int64_t>(BT) * (KC / 8) <= 8 * kRouteThreads &&
@@ -271,7 +277,11 @@ static RouterCfg router_cfg(int64_t T, int d, int E, int want_blocks, bool whole
         KC = d;
         lds = bytes(d);
       } else {
-        KC = (d % 64 == 0 && 2 * bytes(64) <= static_cast<size_t>(kRouteLds) && fits(64)) ? 64 : 32;
+        // the largest power-of-two chunk that divides d and fits twice: long
+        // chunks give the register prefetch of the next one time to land
+        KC = 32;
+        for (int kc = 64; kc < d; kc *= 2)
+          if (d % kc == 0 && 2 * bytes(kc) <= static_cast<size_t>(kRouteLds) && fits(kc)) KC = kc;
         lds = 2 * bytes(KC);
       }
       const RouterCfg c{BE, EPT, TPT, KC, blocks, lds};
