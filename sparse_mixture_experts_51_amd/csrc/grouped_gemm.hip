@@ -234,13 +234,18 @@ struct Unit {
 template <class C, bool kSwiGLU>
 __device__ __forceinline__ Unit decode_unit(const GroupedGemmArgs& a, const int* unit_start,
                                             const int* offs, int ngroups, int u) {
-  int lo = 0, hi = ngroups - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (uni(unit_start[mid]) <= u) lo = mid; else hi = mid - 1;
+  // The group is the last one whose first unit is <= u (unit_start does not
+  // decrease): the lanes of the wave test 64 groups at a time and count the
+  // hits, so the LDS reads are independent instead of a binary search chain.
+  const int lane = threadIdx.x & 63;
+  int below = 0;
+  for (int base = 0; base < ngroups; base += 64) {
+    const int g = base + lane;
+    const bool hit = g < ngroups && unit_start[g] <= u;
+    below += __popcll(__ballot(hit));
   }
   Unit r;
-  r.g = uni(lo);
+  r.g = uni(below - 1);
   r.routed = r.g < a.E;
   const int grow0 = r.routed ? uni(offs[r.g]) : 0;
   const int rows = r.routed ? uni(offs[r.g + 1]) - grow0 : static_cast<int>(a.T);
@@ -346,37 +351,43 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
   int pend_map[LA];   // prepared unit: perm_src[pend_row] when gathering (in flight)
   int map_ready[LA];  // the same values once landed (see settle)
   Unit pend;
-  auto prepare = [&](int u) __attribute__((always_inline)) {
-    pend = decode(u);
-    const bool gather = pend.routed && a.a_row_map;
+  auto prepare_into = [&](int u, Unit& pu, int (&prow)[LA], int (&pmap)[LA])
+      __attribute__((always_inline)) {
+    pu = decode(u);
+    const bool gather = pu.routed && a.a_row_map;
     MOE_FOR(i, LA, {
       int r = ld_row + RPP * i;
-      if (r >= pend.valid_rows) r = 0;  // a row that exists; its offset is replaced below
-      pend_row[i] = pend.orow0 + r;
+      if (r >= pu.valid_rows) r = 0;  // a row that exists; its offset is replaced below
+      prow[i] = pu.orow0 + r;
       // branch-free, so the loaded value is not touched until the unit switch
-      const int32_t* src = gather ? a.a_row_map + pend_row[i] : a.offsets;
-      pend_map[i] = *src;
+      const int32_t* src = gather ? a.a_row_map + prow[i] : a.offsets;
+      pmap[i] = *src;
     })
+  };
+  auto prepare = [&](int u) __attribute__((always_inline)) {
+    prepare_into(u, pend, pend_row, pend_map);
   };
   // The empty asm makes each value a new one defined here, so the compiler
   // waits for the load at this point and cannot fold the copy away.
-  auto settle = [&]() __attribute__((always_inline)) {
+  auto settle_into = [&](const int (&pmap)[LA], int (&ready)[LA]) __attribute__((always_inline)) {
     MOE_FOR(i, LA, {
-      int v = pend_map[i];
+      int v = pmap[i];
       asm volatile("" : "+v"(v));
-      map_ready[i] = v;
+      ready[i] = v;
     })
   };
+  auto settle = [&]() __attribute__((always_inline)) { settle_into(pend_map, map_ready); };
   constexpr int kRsrcFlags = 0x00020000;  // raw (untyped) buffer
   auto rsrc = [](const void* base, int64_t bytes) __attribute__((always_inline)) {
     const int n = bytes < 0x7FFFFFFF ? static_cast<int>(bytes) : 0x7FFFFFFF;
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), n,
                                              kRsrcFlags);
   };
-  auto source_of_pending = [&]() __attribute__((always_inline)) {
+  auto source_of = [&](const Unit& pu, const int (&prow)[LA], const int (&ready)[LA])
+      __attribute__((always_inline)) {
     Src sr;
-    const bool routed = pend.routed;
-    const int K = pend.K, N = pend.N, g = pend.g, n0 = pend.n0;
+    const bool routed = pu.routed;
+    const int K = pu.K, N = pu.N, g = pu.g, n0 = pu.n0;
     const bool gather = routed && a.a_row_map;
     sr.ra = routed ? rsrc(a.a_routed, a.a_routed_bytes) : rsrc(a.a_shared, a.a_shared_bytes);
     const int64_t wbytes = static_cast<int64_t>(N) * K * 2;
@@ -389,12 +400,12 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
     // logical chunk the swizzle puts there (as for the weights below).
     const int a_chunk = C::DMAA ? (ld_chunk ^ ((ld_row >> 1) & (kChunksPerRow - 1))) : ld_chunk;
     MOE_FOR(i, LA, {
-      int row = gather ? map_ready[i] : pend_row[i];
+      int row = gather ? ready[i] : prow[i];
       if (gather && (row < 0 || row >= a.T)) row = 0;  // malformed permutation: stay in bounds
-      sr.a_off[i] = ld_row + RPP * i < pend.valid_rows ? (row * K + a_chunk * 8) * 2
-                                                       : static_cast<int>(kOutOfRange);
+      sr.a_off[i] = ld_row + RPP * i < pu.valid_rows ? (row * K + a_chunk * 8) * 2
+                                                     : static_cast<int>(kOutOfRange);
     })
-    sr.rows = pend.valid_rows;
+    sr.rows = pu.valid_rows;
     // weight tile: SwiGLU stage rows [0, BW/2) = W1[n0..], [BW/2, BW) = W3[n0..]
     // (each load pass lies in one half, so one descriptor per pass); down
     // stage rows [0, BW) = W2[n0..]
@@ -411,8 +422,11 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
     // and leave the swizzle unchanged).
     const int b_chunk = C::DMAB ? (ld_chunk ^ ((ld_row >> 1) & (kChunksPerRow - 1))) : ld_chunk;
     sr.b_thr = (ld_row * K + b_chunk * 8) * 2;
-    sr.nk = pend.nk;
+    sr.nk = pu.nk;
     return sr;
+  };
+  auto source_of_pending = [&]() __attribute__((always_inline)) {
+    return source_of(pend, pend_row, map_ready);
   };
 
   // A K-step in flight: A rows in registers (and the weight rows too unless
@@ -547,19 +561,21 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
   // into LDS stage `stage` -- A passes wholly past the valid rows are skipped
   // (their tiles are never multiplied) -- with the K offset in the scalar
   // offset of each load.
-  // Part P (0..3, or all with P < 0) as in load2.
+  // Part P (0..3, or all with P = -1) as in load2; P = kOnlyA / kOnlyB issues
+  // all A / all weight passes.
+  constexpr int kOnlyA = -2, kOnlyB = -3;
   auto issue = [&](const Src& c, int f, int stage, auto part_c) __attribute__((always_inline)) {
     constexpr int P = decltype(part_c)::value;
     const int kb = (f < c.nk ? f : c.nk - 1) * (kBK * 2);
     MOE_FOR(i, LA, {
-      if constexpr (P >= 0 && i % 4 != P) return;
+      if constexpr (P == kOnlyB || (P >= 0 && i % 4 != P)) return;
       // with more than two stages the wait counts every load, so passes past
       // the valid rows are issued too (out-of-range offsets, no memory access)
       if (C::NSA > 2 || RPP * i < c.rows)
         dma_b128(c.ra, &lds_a[stage][(RPP * i + 8 * wave) * kChunksPerRow], c.a_off[i], kb);
     })
     MOE_FOR(i, LB, {
-      if constexpr (P >= 0 && (LA + i) % 4 != P) return;
+      if constexpr (P == kOnlyA || (P >= 0 && (LA + i) % 4 != P)) return;
       constexpr bool up = kSwiGLU && RPP * i >= C::BW / 2;
       dma_b128(up ? c.rb1 : c.rb0, &lds_b[stage][(RPP * i + 8 * wave) * kChunksPerRow], c.b_thr,
                c.b_row[i] + kb);
@@ -730,12 +746,12 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
     return st >= C::NSB ? st - C::NSB : st;
   };
   int cs = 0;  // weight stage of the current step
-  prepare(lb);
-  settle();
-  Src cur = source_of_pending();
-  Unit cu = pend;
+  // The first two units' perm_src entries are loaded together, so the start
+  // pays one round trip for them.
+  Unit cu;
+  int row0[LA], map0[LA], ready0[LA];
+  prepare_into(lb, cu, row0, map0);
   prepare(next_of(lb));
-  settle();
   if constexpr (C::DMAA) {
     // All-DMA tiles in NS stages, D = NS - 1 steps ahead: the DMA of step
     // k + D (running into the next unit's first steps) is issued at step k
@@ -749,9 +765,22 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
     constexpr int kAhead = (D - 1) * (LA + LB);
     static_assert(kAhead < 64, "vmcnt range");
     auto st = [](int x) __attribute__((always_inline)) { return x >= NS ? x - NS : x; };
-    MOE_FOR(f, D, { issue(cur, f, f, std::integral_constant<int, -1>{}); })
-    __builtin_amdgcn_s_waitcnt(0x0F70 | ((kAhead & 15) | ((kAhead >> 4) << 14)));
+    // The weight passes of the first D steps need no perm_src entry: they go
+    // out first, and the A passes once the entries have landed.  Order: B of
+    // steps 0..D-1, then A of steps 0..D-1, so step 0 has landed when only
+    // the A passes of steps 1..D-1 may still be in flight.
+    {
+      const Src cur_b = source_of(cu, row0, row0);  // weight fields only (A ones unused)
+      MOE_FOR(f, D, { issue(cur_b, f, f, std::integral_constant<int, kOnlyB>{}); })
+    }
+    settle_into(map0, ready0);
+    Src cur = source_of(cu, row0, ready0);
+    MOE_FOR(f, D, { issue(cur, f, f, std::integral_constant<int, kOnlyA>{}); })
+    constexpr int kFirst = (D - 1) * LA;
+    static_assert(kFirst < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | ((kFirst & 15) | ((kFirst >> 4) << 14)));
     lds_barrier();
+    settle();  // free here: those loads are older than the A passes
     for (int u = lb; u < total_units; u += G) {
       const Src nxt = source_of_pending();
       const Unit nu = pend;
@@ -777,6 +806,8 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
     }
     return;
   }
+  settle_into(map0, ready0);
+  Src cur = source_of(cu, row0, ready0);
   Slice r0, r1;
   constexpr std::integral_constant<int, -1> kAll{};
   load2(r0, cur, cur, 1 << 30, 0, 0, kAll);
@@ -784,6 +815,7 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
   stash(r0, 0, 0);
   vm_wait();
   lds_barrier();
+  settle();  // those loads are older than the first two steps' loads
   for (int u = lb; u < total_units; u += G) {
     const Src nxt = source_of_pending();
     const Unit nu = pend;
