@@ -709,8 +709,11 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
         const int r = idx / C16, q = idx % C16;
         if (r_lo + r < cu.valid_rows && q * 8 < ncols) {
           const u32x4 val = lds_read_b128(row_ptr(r) + ((q ^ sw(r)) << 4));
-          *reinterpret_cast<u32x4*>(cbase + (static_cast<int64_t>(cu.orow0) + r_lo + r) * cu.N +
-                                    cu.n0 + q * 8) = val;
+          // non-temporal: the rows are not read again by this kernel, and the
+          // streaming hint leaves the caches to the operands
+          __builtin_nontemporal_store(
+              val, reinterpret_cast<u32x4*>(cbase + (static_cast<int64_t>(cu.orow0) + r_lo + r) * cu.N +
+                                            cu.n0 + q * 8));
         }
       }
       lds_barrier();  // the buffers are reused by the next pass or the next unit
