@@ -40,15 +40,35 @@ __global__ __launch_bounds__(256) void combine_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] += v[e];
   }
+  // Slots in groups of 8: all positions and gates of a group, then all its
+  // rows, are loaded before the first FMA, so the loads overlap instead of
+  // each row waiting for its position; the FMAs still run in slot order.
   const int64_t slot0 = static_cast<int64_t>(t) * k;
-  for (int j = 0; j < k; ++j) {
-    const int row = pos[slot0 + j];
-    if (row < 0 || row >= nrows) continue;
-    const float g = gate[slot0 + j];
-    bf16x8_to_f32(*reinterpret_cast<const uint4*>(y_perm + static_cast<int64_t>(row) * d +
-                                                  static_cast<int64_t>(c) * 8), v);
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    int row[8];
+    float g[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = fmaf(g, v[e], acc[e]);
+    for (int jj = 0; jj < 8; ++jj) {
+      const bool in = j0 + jj < k;
+      row[jj] = in ? pos[slot0 + j0 + jj] : -1;
+      g[jj] = in ? gate[slot0 + j0 + jj] : 0.0f;
+    }
+    u32x4 y[8];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const bool ok = row[jj] >= 0 && row[jj] < nrows;
+      // y_perm rows are read once: the streaming hint keeps them out of the way
+      y[jj] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+                       y_perm + static_cast<int64_t>(row[jj]) * d + static_cast<int64_t>(c) * 8))
+                 : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      if (row[jj] < 0 || row[jj] >= nrows) continue;
+      bf16x8_to_f32(make_uint4(y[jj][0], y[jj][1], y[jj][2], y[jj][3]), v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(g[jj], v[e], acc[e]);
+    }
   }
   uint4 o;
   o.x = pack_bf16x2(acc[0], acc[1]);
