@@ -28,7 +28,9 @@
 //            (decode) and small models: more, smaller units keep every CU
 //            busy and two blocks per CU keep more weight bytes in flight.
 //   kBig     BM = 256, BW = 128, 8 waves, 1 block/CU, A and weight tiles both
-//            by LDS DMA in three stages.  For hundreds of rows per expert.
+//            by LDS DMA in three stages.  For hundreds of rows per expert,
+//            and for the shared expert when the routed experts stream (it
+//            then runs as a launch of its own).
 //
 // Pipeline.  A block's units run as an outer loop; each unit's K-loop (64 of
 // K per step; with register-staged A an odd step count is padded by one
@@ -42,7 +44,7 @@
 // Barriers are raw s_barrier after an LDS-only wait: __syncthreads() would
 // also drain the in-flight global loads.  The epilogue stages the output
 // tile in the LDS buffers no load in flight writes and leaves it as 16-byte
-// row stores.
+// non-temporal row stores.
 #include "common.hpp"
 #include "kernels.hpp"
 
