@@ -615,32 +615,37 @@ int seq_splits(int64_t T, int S) {
   return static_cast<int>(sp);
 }
 
+constexpr int kSeqThreads = 1024;
+
 // grid (nseq * nsplit): each block walks a slice of one sequence.  Thread
 // (token lane tl, expert e) sums s[t,e]/tok_sum[t] in fp64 over the slice's
 // tokens t = a + tl, a + tl + L, ...; the L lanes of an expert are then added
 // in lane order (deterministic).  Choices are counted with LDS atomics.
-__global__ __launch_bounds__(256) void seq_partial_kernel(
+// 1024 threads give several lanes per expert even for 256 experts, and the
+// unrolled token loop keeps several loads in flight per lane.
+__global__ __launch_bounds__(kSeqThreads) void seq_partial_kernel(
     const float* __restrict__ scores, const double* __restrict__ tok_sum,
     const int32_t* __restrict__ idx, double* __restrict__ seq_p, int32_t* __restrict__ seq_cnt,
     int E, int k, int S, int nsplit) {
   extern __shared__ int32_t cnt[];               // [E]
-  __shared__ double part[256];
+  __shared__ double part[kSeqThreads];
   const int q = blockIdx.x / nsplit, sp = blockIdx.x % nsplit;
   const int64_t a = static_cast<int64_t>(q) * S + static_cast<int64_t>(S) * sp / nsplit;
   const int64_t b = static_cast<int64_t>(q) * S + static_cast<int64_t>(S) * (sp + 1) / nsplit;
-  for (int e = threadIdx.x; e < E; e += 256) cnt[e] = 0;
+  for (int e = threadIdx.x; e < E; e += kSeqThreads) cnt[e] = 0;
   __syncthreads();
-  for (int64_t i = a * k + threadIdx.x; i < b * k; i += 256) {
+  for (int64_t i = a * k + threadIdx.x; i < b * k; i += kSeqThreads) {
     const int e = idx[i];
     if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
   }
   const double inv_e = 1.0 / E;
-  for (int e0 = 0; e0 < E; e0 += 256) {
-    const int ne = (E - e0) < 256 ? (E - e0) : 256;
-    const int L = 256 / ne;  // token lanes per expert
+  for (int e0 = 0; e0 < E; e0 += kSeqThreads) {
+    const int ne = (E - e0) < kSeqThreads ? (E - e0) : kSeqThreads;
+    const int L = kSeqThreads / ne;  // token lanes per expert
     const int e = e0 + threadIdx.x % ne, tl = threadIdx.x / ne;
     double p = 0.0;
     if (tl < L) {
+#pragma unroll 4
       for (int64_t t = a + tl; t < b; t += L) {
         const double tot = tok_sum[t];
         p += (tot == 0.0) ? inv_e : static_cast<double>(scores[t * E + e]) / tot;
@@ -655,28 +660,31 @@ __global__ __launch_bounds__(256) void seq_partial_kernel(
     }
     __syncthreads();
   }
-  for (int e = threadIdx.x; e < E; e += 256) seq_cnt[static_cast<int64_t>(blockIdx.x) * E + e] = cnt[e];
+  for (int e = threadIdx.x; e < E; e += kSeqThreads) seq_cnt[static_cast<int64_t>(blockIdx.x) * E + e] = cnt[e];
 }
 
-// One block per sequence.  Experts are taken 256 / ne lanes at a time (ne =
-// experts of the pass): lane l of expert e adds the partials l, l + L, ... in
-// order, the L lane sums are added in lane order, and the experts' terms
-// f_e * P_e / S are then summed by a tree over the block.  With few splits
-// every lane loads one partial, so the whole kernel is one memory round trip.
-__global__ __launch_bounds__(256) void seq_final_kernel(
+// One block per sequence.  Experts are taken NT / ne lanes at a time
+// (ne = experts of the pass): lane l of expert e adds the partials l, l + L,
+// ... in order (unrolled, so several loads are in flight), the L lane sums
+// are added in lane order, and the experts' terms f_e * P_e / S are then
+// summed by a tree over the block.  NT = 256 serves the fused path's few
+// experts and splits; long sequences of many experts take 1024.
+template <int NT>
+__global__ __launch_bounds__(NT) void seq_final_kernel(
     const double* __restrict__ seq_p, const int32_t* __restrict__ seq_cnt, float* __restrict__ out,
     float alpha, int E, int k, int S, int nsplit) {
-  __shared__ double part[256];
-  __shared__ int64_t pcnt[256];
+  __shared__ double part[NT];
+  __shared__ int64_t pcnt[NT];
   const int q = blockIdx.x;
   double acc = 0.0;
-  for (int e0 = 0; e0 < E; e0 += 256) {
-    const int ne = (E - e0) < 256 ? (E - e0) : 256;
-    const int L = 256 / ne;
+  for (int e0 = 0; e0 < E; e0 += NT) {
+    const int ne = (E - e0) < NT ? (E - e0) : NT;
+    const int L = NT / ne;
     const int e = e0 + threadIdx.x % ne, l = threadIdx.x / ne;
     double p = 0.0;
     int64_t c = 0;
     if (l < L) {
+#pragma unroll 4
       for (int sp = l; sp < nsplit; sp += L) {
         const int64_t o = (static_cast<int64_t>(q) * nsplit + sp) * E + e;
         p += seq_p[o];
@@ -701,7 +709,7 @@ __global__ __launch_bounds__(256) void seq_final_kernel(
   __syncthreads();
   part[threadIdx.x] = acc;
   __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
+  for (int w = NT / 2; w > 0; w >>= 1) {
     if (threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
     __syncthreads();
   }
@@ -713,12 +721,13 @@ hipError_t launch_seq_balance(const float* scores, const double* tok_sum, const 
                               int64_t T, int E, int k, int S, hipStream_t s) {
   const int nsplit = seq_splits(T, S);
   const int64_t nseq = T / S;
-  hipLaunchKernelGGL(seq_partial_kernel, dim3(static_cast<unsigned>(nseq * nsplit)), dim3(256),
-                     sizeof(int32_t) * E, s, scores, tok_sum, idx, seq_p, seq_cnt, E, k, S, nsplit);
+  hipLaunchKernelGGL(seq_partial_kernel, dim3(static_cast<unsigned>(nseq * nsplit)),
+                     dim3(kSeqThreads), sizeof(int32_t) * E, s, scores, tok_sum, idx, seq_p, seq_cnt,
+                     E, k, S, nsplit);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(seq_final_kernel, dim3(static_cast<unsigned>(nseq)), dim3(256), 0, s, seq_p,
-                     seq_cnt, out, alpha, E, k, S, nsplit);
+  hipLaunchKernelGGL(seq_final_kernel<kSeqThreads>, dim3(static_cast<unsigned>(nseq)),
+                     dim3(kSeqThreads), 0, s, seq_p, seq_cnt, out, alpha, E, k, S, nsplit);
   return hipGetLastError();
 }
 
@@ -761,7 +770,7 @@ hipError_t launch_route_fused(const uint16_t* x, const float* w_router, const fl
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (stats) {
-    hipLaunchKernelGGL(seq_final_kernel, dim3(static_cast<unsigned>(T / S)), dim3(256), 0, s, seq_p,
+    hipLaunchKernelGGL(seq_final_kernel<256>, dim3(static_cast<unsigned>(T / S)), dim3(256), 0, s, seq_p,
                        seq_cnt, seq_out, alpha, E, k, S, S / BT);
     err = hipGetLastError();
   }
