@@ -18,12 +18,15 @@
 // offsets[] (no host round trip).
 //
 // Three tile configurations:
-//   kStream  BM = 192, BW = 256, 8 waves, 1 block/CU.  For weight-streaming
-//            shapes (about 64 to 256 rows per expert, weights far beyond the
-//            caches): one unit covers all rows of a typical expert, so each
-//            weight byte is read from HBM once (two m-tiles streaming the same
-//            weights drift apart and both miss L2).  Weight tiles go from
-//            memory straight to LDS (three stages).
+//   kStream  BM = 192, BW = 256, 8 MFMA waves plus 4 loader waves, 1
+//            block/CU.  For weight-streaming shapes (about 64 to 256 rows per
+//            expert, weights far beyond the caches): one unit covers all rows
+//            of a typical expert, so each weight byte is read from HBM once
+//            (two m-tiles streaming the same weights drift apart and both
+//            miss L2).  Weight tiles go from memory straight to LDS (three
+//            stages).  The loader waves issue every tile load: under a full
+//            memory queue a load instruction waits to issue, and a wave that
+//            also runs MFMAs would hold them back meanwhile.
 //   kCompute BM = BW = 128, 4 waves, 2 blocks/CU.  For few rows per expert
 //            (decode) and small models: more, smaller units keep every CU
 //            busy and two blocks per CU keep more weight bytes in flight.
@@ -37,10 +40,10 @@
 // MFMA-free step) is straight-line code apart from uniform branches.  The
 // fetcher runs two steps ahead of the MFMAs and crosses into the next unit
 // during the last steps of the current one, choosing the source with scalar
-// selects.  Loads are buffer loads (uniform descriptor + 32-bit offset); the
-// loads of one step are spread over the four MFMA sub-steps of the step two
-// earlier, so that a full memory queue stalls one wave briefly instead of
-// holding all its MFMAs back.  Tiles sit in XOR-swizzled LDS buffers.
+// selects.  Loads are buffer loads (uniform descriptor + 32-bit offset); in
+// the tiles without loader waves the loads of one step are spread over the
+// four MFMA sub-steps of the step two earlier, so that a full memory queue
+// stalls one wave briefly instead of holding all its MFMAs back.  Tiles sit in XOR-swizzled LDS buffers.
 // Barriers are raw s_barrier after an LDS-only wait: __syncthreads() would
 // also drain the in-flight global loads.  The epilogue stages the output
 // tile in the LDS buffers no load in flight writes and leaves it as 16-byte
@@ -58,7 +61,7 @@ constexpr int kMaxGroups = 1025;
 typedef __attribute__((address_space(3))) void* lds_ptr_t;  // LDS address (DMA destination)
 
 template <int BM_, int BW_, int WM_, int WN_, int BPC_, bool DMAB_, bool DMAA_ = false,
-          int NSA_ = 2>
+          int NSA_ = 2, int PW_ = 0>
 struct TileCfg {
   static constexpr int BM = BM_;     // rows per unit
   static constexpr int BW = BW_;     // weight rows per unit
@@ -69,8 +72,11 @@ struct TileCfg {
   static constexpr bool DMAA = DMAA_;  // A tiles too (then two stages, one step ahead)
   static constexpr int NSA = DMAA ? NSA_ : 2;          // LDS buffers (stages) of the A tile
   static constexpr int NSB = DMAA ? NSA : (DMAB ? 3 : 2);  // ... and of the weight tile
-  static constexpr int kThreads = 64 * WM * WN;
-  static constexpr int kRowsPerPass = kThreads / kChunksPerRow;
+  static constexpr int PW = PW_;     // loader waves (0: the MFMA waves load their own tiles)
+  static constexpr int kThreads = 64 * WM * WN;        // MFMA threads
+  static constexpr int kAllThreads = kThreads + 64 * PW;
+  static constexpr int kLoaders = PW > 0 ? 64 * PW : kThreads;  // threads that issue tile loads
+  static constexpr int kRowsPerPass = kLoaders / kChunksPerRow;
   static constexpr int kLoadsA = BM / kRowsPerPass;
   static constexpr int kLoadsB = BW / kRowsPerPass;
   static constexpr int TM = BM / WM / 32;  // 32-row MFMA tiles per wave
@@ -78,8 +84,9 @@ struct TileCfg {
   static_assert(BM % kRowsPerPass == 0 && BW % (2 * kRowsPerPass) == 0, "load passes");
   static_assert(TN % 2 == 0, "SwiGLU pairs gate and up tiles inside a wave");
   static_assert(!DMAA || (DMAB && TM % 2 == 0), "A by DMA implies weights by DMA");
+  static_assert(PW == 0 || (DMAB && !DMAA), "loader waves: A through registers, weights by DMA");
 };
-using kStream = TileCfg<192, 256, 2, 4, 1, true>;
+using kStream = TileCfg<192, 256, 2, 4, 1, true, false, 2, 4>;
 using kCompute = TileCfg<128, 128, 2, 2, 2, false>;
 using kBig = TileCfg<256, 128, 4, 2, 1, true, true, 3>;
 
@@ -265,14 +272,14 @@ __device__ __forceinline__ Unit decode_unit(const GroupedGemmArgs& a, const int*
 }
 
 template <class C, bool kSwiGLU>
-__global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(GroupedGemmArgs a) {
+__global__ __launch_bounds__(C::kAllThreads, C::BPC) void grouped_gemm_kernel(GroupedGemmArgs a) {
   constexpr int kThreads = C::kThreads, RPP = C::kRowsPerPass;
   constexpr int LA = C::kLoadsA, LB = C::kLoadsB, TM = C::TM, TN = C::TN;
   __shared__ u32x4 lds_a[C::NSA][C::BM * kChunksPerRow];  // buffers or DMA stages
   __shared__ u32x4 lds_b[C::NSB][C::BW * kChunksPerRow];
   __shared__ int unit_start[kMaxGroups + 1];
   __shared__ int offs[kMaxGroups + 1];  // copy of offsets[0..E]
-  __shared__ int wsum[kThreads / 64];
+  __shared__ int wsum[C::kAllThreads / 64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -285,8 +292,8 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
 
   // ---- unit table: units of group g start at unit_start[g]
   {
-    constexpr int kPer = (kMaxGroups + kThreads - 1) / kThreads;
-    const int per = (ngroups + kThreads - 1) / kThreads;
+    constexpr int kPer = (kMaxGroups + C::kAllThreads - 1) / C::kAllThreads;
+    const int per = (ngroups + C::kAllThreads - 1) / C::kAllThreads;
     int local[kPer];
     int sum = 0;
     for (int i = 0; i < per; ++i) {
@@ -303,7 +310,7 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
       sum += u;
     }
     int total;
-    int run = block_scan<kThreads>(sum, &total, wsum);
+    int run = block_scan<C::kAllThreads>(sum, &total, wsum);
     for (int i = 0; i < per; ++i) {
       const int g = tid * per + i;
       if (g < ngroups) unit_start[g] = run;
@@ -323,8 +330,12 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
     return decode_unit<C, kSwiGLU>(a, unit_start, offs, ngroups, u);
   };
 
-  const int ld_row = tid / kChunksPerRow;  // 0..RPP-1
-  const int ld_chunk = tid % kChunksPerRow;
+  // loader thread geometry (the loader waves follow the MFMA waves)
+  const bool loader = C::PW == 0 || wave >= C::WM * C::WN;
+  const int ltid = C::PW > 0 ? tid - kThreads : tid;
+  const int lwave = C::PW > 0 ? wave - C::WM * C::WN : wave;
+  const int ld_row = ltid / kChunksPerRow;  // 0..RPP-1
+  const int ld_chunk = ltid % kChunksPerRow;
 
   // ---- source of a unit: buffer descriptors (wave-uniform, scalar
   // registers) plus 32-bit byte offsets.  An A row (a gathered token) needs a
@@ -472,7 +483,7 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
       if constexpr (C::DMAB) {
         // 64 lanes x 16 bytes land at consecutive LDS slots: rows
         // RPP*i + 8*wave .. +8 of the stage
-        dma_b128(up ? rb1 : rb0, &lds_b[bstage][(RPP * i + 8 * wave) * kChunksPerRow], bt, br);
+        dma_b128(up ? rb1 : rb0, &lds_b[bstage][(RPP * i + 8 * lwave) * kChunksPerRow], bt, br);
       } else {
         sl.b[i] = __builtin_bit_cast(
             u32x4, __builtin_amdgcn_raw_buffer_load_b128(up ? rb1 : rb0, bt, br, 0));
@@ -574,12 +585,12 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
       // with more than two stages the wait counts every load, so passes past
       // the valid rows are issued too (out-of-range offsets, no memory access)
       if (C::NSA > 2 || RPP * i < c.rows)
-        dma_b128(c.ra, &lds_a[stage][(RPP * i + 8 * wave) * kChunksPerRow], c.a_off[i], kb);
+        dma_b128(c.ra, &lds_a[stage][(RPP * i + 8 * lwave) * kChunksPerRow], c.a_off[i], kb);
     })
     MOE_FOR(i, LB, {
       if constexpr (P == kOnlyA || (P >= 0 && (LA + i) % 4 != P)) return;
       constexpr bool up = kSwiGLU && RPP * i >= C::BW / 2;
-      dma_b128(up ? c.rb1 : c.rb0, &lds_b[stage][(RPP * i + 8 * wave) * kChunksPerRow], c.b_thr,
+      dma_b128(up ? c.rb1 : c.rb0, &lds_b[stage][(RPP * i + 8 * lwave) * kChunksPerRow], c.b_thr,
                c.b_row[i] + kb);
     })
   };
@@ -663,21 +674,21 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
   // instruction covers 32 rows at one 16-byte chunk, so chunk q of (pass-
   // relative) row r sits at chunk q ^ sw(r), which spreads those rows over
   // all 64 banks (and keeps a row's chunks on distinct banks for the reads).
+  constexpr int kCols = kSwiGLU ? C::BW / 2 : C::BW;
+  constexpr int RB = kCols * 2;                                       // bytes per output row
+  constexpr int C16 = RB / 16;                                        // 16-byte chunks per row
+  constexpr int kRowsA = (C::BM * kChunksPerRow * 16 / RB) / 32 * 32;  // whole tiles in lds_a[fa]
+  constexpr int kRowsB = C::BW * kChunksPerRow * 16 / RB;             // rows in lds_b[fb]
+  constexpr int kPassRows = (kRowsA + kRowsB) / 32 * 32;
+  constexpr int kPasses = (C::BM + kPassRows - 1) / kPassRows;
+  static_assert(kPassRows > 0 && C16 >= 8 && (C16 & (C16 - 1)) == 0, "output staging layout");
   auto epilogue = [&](const Unit& cu, int mrows, int fa, int fb) __attribute__((always_inline)) {
     uint16_t* cbase = cu.routed ? a.c_routed : a.c_shared;
-    constexpr int kCols = kSwiGLU ? C::BW / 2 : C::BW;
-    constexpr int RB = kCols * 2;                                       // bytes per output row
-    constexpr int C16 = RB / 16;                                        // 16-byte chunks per row
-    constexpr int kRowsA = (C::BM * kChunksPerRow * 16 / RB) / 32 * 32;  // whole tiles in lds_a[fa]
-    constexpr int kRowsB = C::BW * kChunksPerRow * 16 / RB;             // rows in lds_b[fb]
-    constexpr int kPassRows = (kRowsA + kRowsB) / 32 * 32;
-    static_assert(kPassRows > 0 && C16 >= 8 && (C16 & (C16 - 1)) == 0, "output staging layout");
     auto sw = [](int r) __attribute__((always_inline)) { return C16 >= 16 ? (r & 15) : ((r >> 1) & 7); };
     auto row_ptr = [&](int r) __attribute__((always_inline)) {
       return r < kRowsA ? reinterpret_cast<unsigned char*>(&lds_a[fa][0]) + r * RB
                         : reinterpret_cast<unsigned char*>(&lds_b[fb][0]) + (r - kRowsA) * RB;
     };
-    constexpr int kPasses = (C::BM + kPassRows - 1) / kPassRows;
     const int ncols = cu.N - cu.n0 < kCols ? cu.N - cu.n0 : kCols;
     MOE_FOR(p, kPasses, {
       const int r_lo = p * kPassRows;
@@ -751,6 +762,32 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
     return st >= C::NSB ? st - C::NSB : st;
   };
   int cs = 0;  // weight stage of the current step
+  if constexpr (C::PW > 0) {
+    if (!loader) {
+      // MFMA waves: the loader waves fill A buffer k % 2 and weight stage
+      // k % 3 for step k and hit the same barriers (one per K-step, two per
+      // epilogue pass), so these waves issue no global load in the K-loop.
+      Unit cu = decode(lb);
+      lds_barrier();  // step 0 has landed
+      for (int u = lb; u < total_units; u += G) {
+        const Unit nu = decode(next_of(u));
+        const int steps = cu.nk + (cu.nk & 1);
+        const int mrows = valid_tiles(cu.valid_rows);
+        zero_acc();
+        for (int kt = 0; kt < steps; kt += 2) {
+          const int c1 = stage_after(cs, 1);
+          mma(0, cs, mrows, [](auto) {});
+          lds_barrier();
+          mma(1, c1, kt + 1 < cu.nk ? mrows : 0, [](auto) {});
+          cs = stage_after(c1, 1);
+          lds_barrier();
+        }
+        epilogue(cu, mrows, 1, stage_after(cs, C::NSB - 1));
+        cu = nu;
+      }
+      return;
+    }
+  }
   // The first two units' perm_src entries are loaded together, so the start
   // pays one round trip for them.
   Unit cu;
@@ -828,22 +865,31 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
     const int steps = cur.nk + (cur.nk & 1);
     // 32-row tiles of this wave with valid rows
     const int mrows = valid_tiles(cu.valid_rows);
-    zero_acc();
+    if constexpr (C::PW == 0) zero_acc();
     for (int kt = 0; kt < steps; kt += 2) {
       const int c1 = stage_after(cs, 1);
       // the loads of step kt + 2 go out between the MFMA sub-steps of step kt
+      // (all at once from a loader wave)
       const int s2 = stage_after(cs, 2);
-      mma(0, cs, mrows, [&](auto ks_c) __attribute__((always_inline)) {
-        load2(r0, cur, nxt, steps, kt + 2, s2, ks_c);
-      });
+      if constexpr (C::PW > 0) {
+        load2(r0, cur, nxt, steps, kt + 2, s2, kAll);
+      } else {
+        mma(0, cs, mrows, [&](auto ks_c) __attribute__((always_inline)) {
+          load2(r0, cur, nxt, steps, kt + 2, s2, ks_c);
+        });
+      }
       if (kt == 0) settle();
       stash(r1, 1, c1);
       vm_wait();
       lds_barrier();
       const int s3 = stage_after(c1, 2);
-      mma(1, c1, kt + 1 < cur.nk ? mrows : 0, [&](auto ks_c) __attribute__((always_inline)) {
-        load2(r1, cur, nxt, steps, kt + 3, s3, ks_c);
-      });
+      if constexpr (C::PW > 0) {
+        load2(r1, cur, nxt, steps, kt + 3, s3, kAll);
+      } else {
+        mma(1, c1, kt + 1 < cur.nk ? mrows : 0, [&](auto ks_c) __attribute__((always_inline)) {
+          load2(r1, cur, nxt, steps, kt + 3, s3, ks_c);
+        });
+      }
       cs = stage_after(c1, 1);
       stash(r0, 0, cs);
       vm_wait();
@@ -851,10 +897,18 @@ __global__ __launch_bounds__(C::kThreads, C::BPC) void grouped_gemm_kernel(Group
     }
     // buffer 0 holds the next unit's first A slice, stage cs its first weight
     // slice and, with three stages, stage cs + 1 its second
-    epilogue(cu, mrows, 1, stage_after(cs, C::NSB - 1));
+    if constexpr (C::PW > 0) {
+      for (int p = 0; p < kPasses; ++p) {  // the MFMA waves' epilogue barriers
+        lds_barrier();
+        lds_barrier();
+      }
+    } else {
+      epilogue(cu, mrows, 1, stage_after(cs, C::NSB - 1));
+    }
     cur = nxt;
     cu = nu;
   }
+  if constexpr (C::PW > 0) __builtin_amdgcn_s_waitcnt(0x0F70);  // no DMA left in flight
 }
 
 template <class C>
@@ -886,7 +940,7 @@ static bool big_groups(const GroupedGemmArgs& a) {
 
 template <class C, bool kSwiGLU>
 static void launch_cfg(const GroupedGemmArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((grouped_gemm_kernel<C, kSwiGLU>), dim3(persistent_grid<C>()), dim3(C::kThreads),
+  hipLaunchKernelGGL((grouped_gemm_kernel<C, kSwiGLU>), dim3(persistent_grid<C>()), dim3(C::kAllThreads),
                      0, s, a);
 }
 

@@ -336,8 +336,21 @@ def test_v3_full_size(name, v3_weights):
     sample = sample[same[sample]]
     out = sampled_outputs(x, p, sample, ref["idx"], ref["gate"])
     check_bf16_close(g["out"][sample], out, f"{name}.out[sampled {len(sample)} tokens]")
-    # y_perm rows of the sampled tokens against the oracle's own expert outputs
     assert g["y_perm"].shape == (wl.tokens * wl.top_k, wl.d_model)
+    # every row of the largest, the smallest and a median expert group (each
+    # group is one m-tile of the weight-streaming tile at prefill), so that
+    # all of a tile's row passes and output columns are compared
+    counts = g["counts"]
+    used = np.nonzero(counts)[0]
+    order = used[np.argsort(counts[used], kind="stable")]
+    xb = bits(x)
+    for e in sorted({int(order[-1]), int(order[0]), int(order[len(order) // 2])}):
+        lo, hi = int(g["offsets"][e]), int(g["offsets"][e + 1])
+        rows = g["perm_src"][lo:hi]
+        ref_e = oracle.grouped_ffn(xb[rows], np.arange(hi - lo, dtype=np.int32),
+                                   np.array([0, hi - lo], np.int32), bits(p["w1"][e])[None],
+                                   bits(p["w3"][e])[None], bits(p["w2"][e])[None])
+        check_bf16_close(g["y_perm"][lo:hi], ref_e["y_perm"], f"{name}.y_perm[expert {e}, {hi - lo} rows]")
 
 
 def test_mini_train_stacked_layers_teacher_forced():
