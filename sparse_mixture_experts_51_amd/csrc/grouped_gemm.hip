@@ -192,6 +192,28 @@ __device__ __forceinline__ u32x4 lds_read_b128(const void* p) {
       : "memory");
   return v;
 }
+// N 16-byte LDS reads, in groups of six, four, two and one under one wait each.
+template <int N, int I = 0>
+__device__ __forceinline__ void lds_read_n(const u32x4* const (&p)[N], u32x4 (&v)[N]) {
+  if constexpr (N - I >= 6) {
+    const u32x4* const q[6] = {p[I], p[I + 1], p[I + 2], p[I + 3], p[I + 4], p[I + 5]};
+    u32x4 w[6];
+    lds_read6_b128(q, w);
+    for (int i = 0; i < 6; ++i) v[I + i] = w[i];
+    lds_read_n<N, I + 6>(p, v);
+  } else if constexpr (N - I >= 4) {
+    const u32x4* const q[4] = {p[I], p[I + 1], p[I + 2], p[I + 3]};
+    u32x4 w[4];
+    lds_read4_b128(q, w);
+    for (int i = 0; i < 4; ++i) v[I + i] = w[i];
+    lds_read_n<N, I + 4>(p, v);
+  } else if constexpr (N - I >= 2) {
+    lds_read2_b128(p[I], p[I + 1], v[I], v[I + 1]);
+    lds_read_n<N, I + 2>(p, v);
+  } else if constexpr (N - I == 1) {
+    v[I] = lds_read_b128(p[I]);
+  }
+}
 
 // Two fp32 values to packed bf16 (round to nearest even) in one conversion.
 __device__ __forceinline__ uint32_t bf16x2_bits(float lo, float hi) {
@@ -718,16 +740,38 @@ __global__ __launch_bounds__(C::kAllThreads, C::BPC) void grouped_gemm_kernel(Gr
       lds_barrier();
       constexpr int kPr = (C::BM - p * kPassRows) < kPassRows ? (C::BM - p * kPassRows) : kPassRows;
       constexpr int kChunks = kPr * C16;
-      for (int idx = tid; idx < kChunks; idx += kThreads) {
-        const int r = idx / C16, q = idx % C16;
+      auto store_chunk = [&](int r, int q, const u32x4& val) __attribute__((always_inline)) {
         if (r_lo + r < cu.valid_rows && q * 8 < ncols) {
-          const u32x4 val = lds_read_b128(row_ptr(r) + ((q ^ sw(r)) << 4));
           // non-temporal: the rows are not read again by this kernel, and the
           // streaming hint leaves the caches to the operands
           __builtin_nontemporal_store(
               val, reinterpret_cast<u32x4*>(cbase + (static_cast<int64_t>(cu.orow0) + r_lo + r) * cu.N +
                                             cu.n0 + q * 8));
         }
+      };
+      if constexpr (C::PW > 0) {
+        // the loader waves leave no registers for batches
+        for (int idx = tid; idx < kChunks; idx += kThreads) {
+          const int r = idx / C16, q = idx % C16;
+          if (r_lo + r < cu.valid_rows && q * 8 < ncols)
+            store_chunk(r, q, lds_read_b128(row_ptr(r) + ((q ^ sw(r)) << 4)));
+        }
+      } else {
+        // all of a thread's chunks are read under one wait, then stored
+        static_assert(kChunks % kThreads == 0, "whole chunks per thread");
+        constexpr int kIter = kChunks / kThreads;
+        const u32x4* src[kIter];
+        u32x4 val[kIter];
+        MOE_FOR(it, kIter, {
+          const int idx = tid + it * kThreads;
+          const int r = idx / C16, q = idx % C16;
+          src[it] = reinterpret_cast<const u32x4*>(row_ptr(r) + ((q ^ sw(r)) << 4));
+        })
+        lds_read_n<kIter>(src, val);
+        MOE_FOR(it, kIter, {
+          const int idx = tid + it * kThreads;
+          store_chunk(idx / C16, idx % C16, val[it]);
+        })
       }
       lds_barrier();  // the buffers are reused by the next pass or the next unit
     })
