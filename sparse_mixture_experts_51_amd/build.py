@@ -22,7 +22,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["route.hip", "permute.hip", "grouped_gemm.hip", "combine.hip", "api.cpp"]
-HEADERS = ["common.hpp", "kernels.hpp"]
+HEADERS = ["common.hpp", "gemm_common.hpp", "kernels.hpp"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
