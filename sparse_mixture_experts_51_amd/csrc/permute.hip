@@ -127,8 +127,10 @@ __global__ __launch_bounds__(TB) void perm_scatter_kernel(
   if (fused_scan) {
     // Per expert e: rows in blocks before this one, and in all blocks.  L
     // lanes share an expert (block b2 to lane b2 mod L); lane partial sums
-    // are combined with shuffles inside groups of L consecutive lanes.
-    const int L = E >= TB ? 1 : TB / E;  // power of two when E divides TB
+    // are combined with shuffles inside groups of L consecutive lanes, which
+    // must lie in one wave (at most 64 lanes, also when E < TB / 64).
+    int L = E >= TB ? 1 : TB / E;  // power of two when E divides TB
+    if (L > kWave) L = kWave;
     const int Lp = (L & (L - 1)) == 0 ? L : 1;
     const int l = threadIdx.x % Lp;
     for (int e = threadIdx.x / Lp; e < E; e += TB / Lp) {

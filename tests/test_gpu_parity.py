@@ -110,26 +110,33 @@ def test_route_nan_token_and_bias_only_moves_choice():
 
 PERM_CASES = [(2048, 16, 4), (1000, 16, 4), (4096, 256, 8), (300, 1024, 32), (1, 8, 2),
               (777, 8, 2), (64, 256, 8)]
+# every case with and without the x_perm copy, plus the mini model's shape, a
+# single expert and eight choices per token without it
+PERM_RUNS = ([(T, E, k, True) for T, E, k in PERM_CASES] + [(T, E, k, False) for T, E, k in PERM_CASES]
+             + [(8192, 16, 4, False), (500, 1, 1, False), (3000, 16, 8, False)])
 
 
-@pytest.mark.parametrize("T,E,k", PERM_CASES)
-def test_permute_matches_oracle(T, E, k):
-    say(f"[permute] T={T} E={E} k={k}")
+@pytest.mark.parametrize("T,E,k,gather", PERM_RUNS)
+def test_permute_matches_oracle(T, E, k, gather):
+    say(f"[permute] T={T} E={E} k={k} x_perm={gather}")
     gen = torch.Generator().manual_seed(T * 131 + E)
     idx = torch.stack([torch.randperm(E, generator=gen)[:k] for _ in range(T)]).to(torch.int32)
     d = 128
     shape = moe.Shape(T, d, E, k, 64, 0, 0)
-    bufs = moe.alloc_buffers(shape, DEV, x_perm=True)
+    bufs = moe.alloc_buffers(shape, DEV, x_perm=gather)
     x = torch.randn(T, d, device=DEV).to(torch.bfloat16)
     idx_d = idx.to(DEV)
+    bufs["perm_src"].fill_(-7)
+    bufs["pos"].fill_(-7)
     moe.moe_permute(shape, idx_d, bufs["counts"], bufs["offsets"], bufs["perm_src"], bufs["pos"],
-                    x, bufs["x_perm"], bufs["workspace"])
+                    x if gather else None, bufs["x_perm"] if gather else None, bufs["workspace"])
     torch.cuda.synchronize()
     ref = oracle.permute(idx.numpy(), E)
     for key in ("counts", "offsets", "perm_src", "pos"):
         assert np.array_equal(host(bufs[key]), ref[key]), key
-    xp = bits(bufs["x_perm"])
-    assert np.array_equal(xp, bits(x)[ref["perm_src"]])
+    if gather:
+        xp = bits(bufs["x_perm"])
+        assert np.array_equal(xp, bits(x)[ref["perm_src"]])
 
 
 def test_permute_zero_tokens_writes_zero_loads():
