@@ -17,7 +17,7 @@
 // one expert stay in that XCD's L2.  Every block rebuilds the unit table from
 // offsets[] (no host round trip).
 //
-// Three tile configurations:
+// Four tile configurations:
 //   kStream  BM = 192, BW = 256, 8 MFMA waves plus 4 loader waves, 1
 //            block/CU.  For weight-streaming shapes (about 64 to 256 rows per
 //            expert, weights far beyond the caches): one unit covers all rows
@@ -31,9 +31,12 @@
 //            (decode) and small models: more, smaller units keep every CU
 //            busy and two blocks per CU keep more weight bytes in flight.
 //   kBig     BM = 256, BW = 128, 8 waves, 1 block/CU, A and weight tiles both
-//            by LDS DMA in three stages.  For hundreds of rows per expert,
-//            and for the shared expert when the routed experts stream (it
-//            then runs as a launch of its own).
+//            by LDS DMA in three stages.  For hundreds of rows per expert.
+//   kBigL    kBig plus 4 loader waves that issue the DMA, so the MFMA waves
+//            read fragments with plain LDS loads the compiler schedules.  For
+//            the shared expert when the routed experts stream (it then runs
+//            as a launch of its own, with long K): 10% faster there, no gain
+//            on the mini model's six K-steps per unit.
 //
 // Pipeline.  A block's units run as an outer loop; each unit's K-loop (64 of
 // K per step; with register-staged A an odd step count is padded by one
@@ -84,11 +87,12 @@ struct TileCfg {
   static_assert(BM % kRowsPerPass == 0 && BW % (2 * kRowsPerPass) == 0, "load passes");
   static_assert(TN % 2 == 0, "SwiGLU pairs gate and up tiles inside a wave");
   static_assert(!DMAA || (DMAB && TM % 2 == 0), "A by DMA implies weights by DMA");
-  static_assert(PW == 0 || (DMAB && !DMAA), "loader waves: A through registers, weights by DMA");
+  static_assert(PW == 0 || DMAB, "loader waves: weights by DMA");
 };
 using kStream = TileCfg<192, 256, 2, 4, 1, true, false, 2, 4>;
 using kCompute = TileCfg<128, 128, 2, 2, 2, false>;
 using kBig = TileCfg<256, 128, 4, 2, 1, true, true, 3>;
+using kBigL = TileCfg<256, 128, 4, 2, 1, true, true, 3, 4>;  // kBig with loader waves
 
 // XOR swizzle of the 16-byte chunks of a 128-byte row.  gfx950's LDS has 64
 // four-byte banks (256 bytes per clock), so a 16-byte-per-lane access is
@@ -524,6 +528,29 @@ __global__ __launch_bounds__(C::kAllThreads, C::BPC) void grouped_gemm_kernel(Gr
     })
   };
 
+  // MFMA waves of loader-wave tiles issue no DMA, so their fragment reads are
+  // plain LDS loads the compiler schedules freely (no drain before them).
+  auto mma_plain = [&](int abuf, int bstage, int mrows) __attribute__((always_inline)) {
+    MOE_FOR(ks, kBK / 16, {
+      if (mrows > 0) {
+        const int ch = 2 * ks + (lane >> 5);
+        const int fr = lane & 31;
+        bf16x8 af[TM], bfr[TN];
+        MOE_FOR(i, TM, {
+          if (i < mrows) af[i] = __builtin_bit_cast(bf16x8, lds_a[abuf][swz(tile_row(i) + fr, ch)]);
+        })
+        MOE_FOR(j, TN, { bfr[j] = __builtin_bit_cast(bf16x8, lds_b[bstage][swz(brow(j) + fr, ch)]); })
+        MOE_FOR(i, TM, {
+          if (i < mrows) {
+            MOE_FOR(j, TN, {
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+            })
+          }
+        })
+      }
+    })
+  };
+
   // SiLU(gate) * up in fp32 (v_rcp_f32 for the quotient).
   auto swiglu = [](float ga, float up) __attribute__((always_inline)) {
     return ga * __builtin_amdgcn_rcpf(1.0f + __expf(-ga)) * up;
@@ -598,7 +625,7 @@ __global__ __launch_bounds__(C::kAllThreads, C::BPC) void grouped_gemm_kernel(Gr
                                             cu.n0 + q * 8));
         }
       };
-      if constexpr (C::PW > 0) {
+      if constexpr (C::PW > 0 && TM * TN > 4) {
         // the loader waves leave no registers for batches
         for (int idx = tid; idx < kChunks; idx += kThreads) {
           const int r = idx / C16, q = idx % C16;
@@ -656,6 +683,28 @@ __global__ __launch_bounds__(C::kAllThreads, C::BPC) void grouped_gemm_kernel(Gr
   };
   int cs = 0;  // weight stage of the current step
   if constexpr (C::PW > 0) {
+    if (!loader && C::DMAA) {
+      // MFMA waves of an all-DMA tile: the loader waves fill stage k % NS
+      // (A and weights) for step k and hit the same barriers (one per K-step,
+      // two per epilogue pass).
+      constexpr int NS = C::NSA, D = NS - 1;
+      auto st = [](int x) __attribute__((always_inline)) { return x >= NS ? x - NS : x; };
+      Unit cu = decode(lb);
+      lds_barrier();  // step 0 has landed
+      for (int u = lb; u < total_units; u += G) {
+        const Unit nu = decode(next_of(u));
+        const int mrows = valid_tiles(cu.valid_rows);
+        zero_acc();
+        for (int kt = 0; kt < cu.nk; ++kt) {
+          mma_plain(cs, cs, mrows);
+          lds_barrier();
+          cs = st(cs + 1);
+        }
+        epilogue(cu, mrows, st(cs + D), st(cs + D));  // the stage the last step read
+        cu = nu;
+      }
+      return;
+    }
     if (!loader) {
       // MFMA waves: the loader waves fill A buffer k % 2 and weight stage
       // k % 3 for step k and hit the same barriers (one per K-step, two per
@@ -723,19 +772,33 @@ __global__ __launch_bounds__(C::kAllThreads, C::BPC) void grouped_gemm_kernel(Gr
       const int mrows = valid_tiles(cu.valid_rows);
       zero_acc();
       for (int kt = 0; kt < cur.nk; ++kt) {
-        // step kt + D goes out between the MFMA sub-steps of step kt
+        // step kt + D goes out between the MFMA sub-steps of step kt (all at
+        // once from a loader wave)
         const int f = kt + D;
         const int sd = st(cs + D);
-        mma_dma(cs, mrows, [&](auto ks_c) __attribute__((always_inline)) {
-          if (f < cur.nk) issue(cur, f, sd, ks_c);
-          else issue(nxt, f - cur.nk, sd, ks_c);
-        });
+        if constexpr (C::PW > 0) {
+          constexpr std::integral_constant<int, -1> kAllParts{};
+          if (f < cur.nk) issue(cur, f, sd, kAllParts);
+          else issue(nxt, f - cur.nk, sd, kAllParts);
+        } else {
+          mma_dma(cs, mrows, [&](auto ks_c) __attribute__((always_inline)) {
+            if (f < cur.nk) issue(cur, f, sd, ks_c);
+            else issue(nxt, f - cur.nk, sd, ks_c);
+          });
+        }
         if (kt == 0) settle();
         __builtin_amdgcn_s_waitcnt(0x0F70 | ((kAhead & 15) | ((kAhead >> 4) << 14)));
         lds_barrier();
         cs = st(cs + 1);
       }
-      epilogue(cu, mrows, st(cs + D), st(cs + D));  // the stage the last step read
+      if constexpr (C::PW > 0) {
+        for (int p = 0; p < kPasses; ++p) {  // the MFMA waves' epilogue barriers
+          lds_barrier();
+          lds_barrier();
+        }
+      } else {
+        epilogue(cu, mrows, st(cs + D), st(cs + D));  // the stage the last step read
+      }
       cur = nxt;
       cu = nu;
     }
@@ -862,8 +925,8 @@ static hipError_t launch_gemm(const GroupedGemmArgs& a, hipStream_t s) {
     shared.a_routed = nullptr;
     shared.a_row_map = nullptr;
     shared.c_routed = nullptr;
-    constexpr int kMinK = kBK * (kBig::NSA - 1);
-    if (a.T >= 512 && a.K_s >= kMinK) launch_cfg<kBig, kSwiGLU>(shared, s);
+    constexpr int kMinK = kBK * (kBigL::NSA - 1);
+    if (a.T >= 512 && a.K_s >= kMinK) launch_cfg<kBigL, kSwiGLU>(shared, s);
     else launch_cfg<kCompute, kSwiGLU>(shared, s);
     return hipGetLastError();
   }

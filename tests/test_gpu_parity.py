@@ -358,6 +358,13 @@ def test_v3_full_size(name, v3_weights):
                                    np.array([0, hi - lo], np.int32), bits(p["w1"][e])[None],
                                    bits(p["w3"][e])[None], bits(p["w2"][e])[None])
         check_bf16_close(g["y_perm"][lo:hi], ref_e["y_perm"], f"{name}.y_perm[expert {e}, {hi - lo} rows]")
+    # shared-expert rows spread over all of its m-tiles (at prefill it runs as
+    # a launch of its own)
+    if wl.shared_hidden:
+        rows = np.unique(np.linspace(0, wl.tokens - 1, 16).astype(int))
+        shared = tuple(bits(p[n]) for n in ("ws1", "ws3", "ws2"))
+        ysh = np.stack([oracle.expert_ffn(xb[t], *shared) for t in rows])
+        check_bf16_close(g["y_shared"][rows], ysh, f"{name}.y_shared[{len(rows)} rows]")
 
 
 def test_mini_train_stacked_layers_teacher_forced():
