@@ -672,9 +672,10 @@ __global__ __launch_bounds__(C::kAllThreads, C::BPC) void grouped_gemm_kernel(Gr
   };
   auto vm_wait = [&]() __attribute__((always_inline)) {
     if constexpr (C::DMAB) {
-      constexpr int n = LA + LB;  // < 64, the vmcnt field
-      static_assert(n < 16, "vmcnt immediate below");
-      __builtin_amdgcn_s_waitcnt(0x0F70 | n);  // vmcnt(n); lgkmcnt, expcnt unconstrained
+      constexpr int n = LA + LB;
+      static_assert(n < 64, "vmcnt range");
+      // vmcnt(n) (low bits 3:0, high bits 15:14); lgkmcnt, expcnt unconstrained
+      __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
     }
   };
   auto stage_after = [](int st, int d) __attribute__((always_inline)) {
