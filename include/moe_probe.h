@@ -1,0 +1,32 @@
+/* moe_probe.h -- the HBM read probe of libmoe_probe.so, a measurement aid
+ * kept apart from the MoE interface in moe.h.
+ *
+ * It gives the achievable HBM read rate that the measurements report beside
+ * the 8 TB/s specification: one block per compute unit streams 1 MiB pieces
+ * of a buffer into LDS by LDS DMA, 32 KiB per step in a three-stage ring --
+ * the access pattern of the grouped GEMM's weight stream, without MFMAs.
+ */
+#ifndef MOE_PROBE_H_
+#define MOE_PROBE_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Reads the `bytes` bytes at device address `buf` once, enqueued on `stream`
+ * (a hipStream_t as void*; NULL = the default stream) without synchronising.
+ *   buf    device memory, 16-byte aligned, owned by the caller
+ *   bytes  a positive multiple of 1 MiB
+ *   sink   device memory of at least one uint32_t per compute unit; the kernel
+ *          writes it only if a folded checksum of the data hits one fixed value
+ * Returns 0 when the launch was enqueued, 1 on unusable sizes, a NULL pointer
+ * or a failed launch (nothing is enqueued then). */
+int moe_probe_hbm_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_PROBE_H_ */

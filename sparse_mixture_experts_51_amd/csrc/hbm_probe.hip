@@ -1,0 +1,76 @@
+// hbm_probe.hip -- the achievable HBM read rate, for the measurements (a
+// library of its own, libmoe_probe.so, next to libmoe.so; not part of the
+// MoE interface).
+//
+// One block per CU streams whole 1 MiB pieces of a buffer, 32 KiB per step,
+// straight into a three-stage LDS ring by LDS DMA, two steps ahead -- the
+// access pattern of the grouped GEMM's weight stream without its MFMAs.
+// Each thread folds one word of every landed stage into a per-block value so
+// that the loads have a consumer.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+constexpr int kThreads = 512;
+constexpr int kStep = 32 * 1024;      // bytes per step
+constexpr int kPiece = 1024 * 1024;   // bytes per unit of work
+constexpr int kStages = 3;
+constexpr int kPasses = kStep / (kThreads * 16);  // 16-byte DMA per thread and pass
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__global__ __launch_bounds__(kThreads) void hbm_read_kernel(const unsigned char* __restrict__ buf,
+                                                            int pieces, uint32_t* __restrict__ sink) {
+  __shared__ u32x4 ring[kStages][kStep / 16];
+  const int tid = threadIdx.x, wave = tid >> 6;
+  constexpr int kSteps = kPiece / kStep;
+  uint32_t acc = 0;
+  for (int p = blockIdx.x; p < pieces; p += gridDim.x) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned char*>(buf) + static_cast<int64_t>(p) * kPiece, static_cast<short>(0), kPiece,
+        0x00020000);
+    // step s into stage st: pass i covers bytes [i * 8 KiB, (i + 1) * 8 KiB)
+    // of the step, lane l of wave w the 16 bytes at (w * 64 + l) * 16
+    auto issue = [&](int s, int st) {
+#pragma unroll
+      for (int i = 0; i < kPasses; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)&ring[st][i * kThreads + wave * 64], 16,
+                                                 tid * 16, s * kStep + i * kThreads * 16, 0, 0);
+    };
+    issue(0, 0);
+    issue(1, 1);
+    for (int s = 0; s < kSteps; ++s) {
+      const int f = s + 2;
+      issue(f < kSteps ? f : kSteps - 1, f % kStages);  // past the end: the last step again
+      // all but the newest step's kPasses loads have landed, so step s + 1 has
+      __builtin_amdgcn_s_waitcnt(0x0F70 | kPasses);
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      acc ^= ring[s % kStages][tid][0];
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) before the stage is reused
+      __builtin_amdgcn_s_barrier();
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): nothing in flight into the ring
+    __builtin_amdgcn_s_barrier();
+  }
+  if (acc == 0x9E3779B9u) sink[blockIdx.x] = acc;  // keeps the reads; practically never stored
+}
+
+}  // namespace
+
+// Reads `bytes` (a multiple of 1 MiB, at most 2^31 MiB) at `buf` once.  `sink`
+// holds one word per CU and is normally left untouched.  Returns 0, or 1 if
+// the sizes are unusable or the launch fails.
+extern "C" int moe_probe_hbm_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
+  if (!buf || !sink || bytes <= 0 || bytes % kPiece != 0) return 1;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 1;
+  const int64_t pieces = bytes / kPiece;
+  if (pieces > 0x7FFFFFFF) return 1;
+  hipLaunchKernelGGL(hbm_read_kernel, dim3(cus), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const unsigned char*>(buf), static_cast<int>(pieces), sink);
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}

@@ -139,6 +139,20 @@ def test_permute_matches_oracle(T, E, k, gather):
         assert np.array_equal(xp, bits(x)[ref["perm_src"]])
 
 
+def test_hbm_probe_reads_and_leaves_the_sink():
+    import ctypes
+
+    from sparse_mixture_experts_51_amd import build
+    P = ctypes.CDLL(build.PROBE_LIB)
+    P.moe_probe_hbm_read.restype = ctypes.c_int
+    P.moe_probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    buf = torch.ones(8 << 20, dtype=torch.bfloat16, device=DEV)  # 16 MiB
+    sink = torch.full((4096,), 7, dtype=torch.int32, device=DEV)
+    assert P.moe_probe_hbm_read(buf.data_ptr(), 16 << 20, sink.data_ptr(), None) == 0
+    torch.cuda.synchronize()
+    assert torch.all(sink == 7)
+
+
 def test_permute_zero_tokens_writes_zero_loads():
     shape = moe.Shape(0, 64, 16, 4, 64, 0, 0)
     bufs = moe.alloc_buffers(shape, DEV)
