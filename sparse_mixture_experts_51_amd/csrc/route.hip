@@ -300,8 +300,110 @@ static hipError_t launch_scores_cfg(const uint16_t* x, const float* w, float* sc
   return hipGetLastError();
 }
 
+// Router scores on the fp32 matrix cores, for many tokens.  The fp32 MFMA
+// with K = 1 (v_mfma_f32_16x16x1_4b_f32) adds one product per output per
+// instruction with a single rounding, so a chain of them over d ascending is
+// the same fmaf chain as in router_logits_tile, bit for bit, at twice the
+// rate of the non-packed vector FMA.  The instruction holds four 16x16
+// blocks: block b takes its 16 rows from A lanes 16b..16b+15 and its 16
+// columns from B lanes 16b..16b+15, and element i of lane l is row
+// 4 (l / 16) + i % 4, column l % 16 of block i / 4.  A wave puts the same 16
+// tokens in every block's rows and 64 experts (16 per block) in the columns:
+// 16 tokens x 64 experts per wave, one instruction per index of d.  A block of
+// four waves (64 tokens) stages x as fp32 and W_r transposed to
+// [expert][index of d] in LDS, in chunks of 128 of d.
+constexpr int kMfTok = 64;     // tokens per block (16 per wave)
+constexpr int kMfExp = 64;     // experts per block
+constexpr int kMfKC = 128;     // d per staged chunk
+constexpr int kMfRow = kMfKC + 4;  // LDS row in floats (16-byte pad)
+
+__global__ __launch_bounds__(256) void router_scores_mfma_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ w_router, float* __restrict__ scores,
+    int64_t T, int d, int E) {
+  __shared__ float xs[2][kMfTok * kMfRow];
+  __shared__ float wt[2][kMfExp * kMfRow];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kMfTok;
+  const int e0 = blockIdx.y * kMfExp;
+  // staging: x piece p (8 values) = row p / 16, cols 8 (p % 16); W piece q
+  // (4 experts of one index of d) = index q / 16, experts 4 (q % 16)
+  constexpr int kXP = kMfTok * kMfKC / 8 / 256;  // x pieces per thread (4)
+  constexpr int kWP = kMfKC * kMfExp / 4 / 256;  // W pieces per thread (8)
+  uint4 px[kXP];
+  float4 pw[kWP];
+  auto fetch = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < kXP; ++i) {
+      const int p = tid + 256 * i;
+      const int64_t t = t0 + p / 16;
+      px[i] = t < T ? *reinterpret_cast<const uint4*>(x + t * d + c * kMfKC + (p % 16) * 8)
+                    : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < kWP; ++i) {
+      const int q = tid + 256 * i;
+      pw[i] = *reinterpret_cast<const float4*>(w_router + static_cast<int64_t>(c * kMfKC + q / 16) * E + e0 +
+                                               (q % 16) * 4);
+    }
+  };
+  auto stash = [&](int b) {
+#pragma unroll
+    for (int i = 0; i < kXP; ++i) {
+      const int p = tid + 256 * i;
+      float f[8];
+      bf16x8_to_f32(px[i], f);
+      float* dst = &xs[b][(p / 16) * kMfRow + (p % 16) * 8];
+      *reinterpret_cast<float4*>(dst) = make_float4(f[0], f[1], f[2], f[3]);
+      *reinterpret_cast<float4*>(dst + 4) = make_float4(f[4], f[5], f[6], f[7]);
+    }
+#pragma unroll
+    for (int i = 0; i < kWP; ++i) {
+      const int q = tid + 256 * i;
+      const int kk = q / 16, e = (q % 16) * 4;
+      wt[b][(e + 0) * kMfRow + kk] = pw[i].x;
+      wt[b][(e + 1) * kMfRow + kk] = pw[i].y;
+      wt[b][(e + 2) * kMfRow + kk] = pw[i].z;
+      wt[b][(e + 3) * kMfRow + kk] = pw[i].w;
+    }
+  };
+  f32x16 acc = {};
+  const int nch = d / kMfKC;
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  for (int c = 0; c < nch; ++c) {
+    if (c + 1 < nch) fetch(c + 1);  // in flight during the MFMAs below
+    const float* xr = &xs[c & 1][(16 * wave + (lane & 15)) * kMfRow];  // A: token lane % 16
+    const float* wr = &wt[c & 1][lane * kMfRow];                      // B: expert lane
+#pragma unroll 8
+    for (int k = 0; k < kMfKC; k += 4) {
+      const float4 a4 = *reinterpret_cast<const float4*>(xr + k);
+      const float4 b4 = *reinterpret_cast<const float4*>(wr + k);
+      acc = __builtin_amdgcn_mfma_f32_16x16x1f32(a4.x, b4.x, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x1f32(a4.y, b4.y, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x1f32(a4.z, b4.z, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x1f32(a4.w, b4.w, acc, 0, 0, 0);
+    }
+    if (c + 1 < nch) stash((c + 1) & 1);  // the buffers step c - 1 read
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t t = t0 + 16 * wave + 4 * (lane / 16) + (i % 4);
+    const int e = e0 + 16 * (i / 4) + (lane % 16);
+    if (t < T) scores[t * E + e] = sigmoid_score(acc[i]);
+  }
+}
+
 hipError_t launch_router_scores(const uint16_t* x, const float* w_router, float* scores,
                                 int64_t T, int d, int E, hipStream_t s) {
+  if (T >= 1024 && E % kMfExp == 0 && d % kMfKC == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0 &&
+      (reinterpret_cast<uintptr_t>(w_router) & 15) == 0) {
+    const dim3 grid(static_cast<unsigned>((T + kMfTok - 1) / kMfTok), static_cast<unsigned>(E / kMfExp));
+    hipLaunchKernelGGL(router_scores_mfma_kernel, grid, dim3(256), 0, s, x, w_router, scores, T, d, E);
+    return hipGetLastError();
+  }
   // two blocks per CU: with one, each SIMD holds a single wave and the LDS
   // latency of the operand reads is exposed
   const RouterCfg pick = router_cfg(T, d, E, 2 * device_cus());

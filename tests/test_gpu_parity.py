@@ -56,6 +56,12 @@ ROUTE_CASES = {
     # a whole wave per token, one expert per lane
     "E64_k8": custom(tokens=320, seq_len=160, d_model=128, n_experts=64, top_k=8, cfg_id=118,
                      router_std=0.1),
+    # logits on the fp32 matrix cores (many tokens, E a multiple of 64): a
+    # ragged last block of tokens, and the V3 expert count
+    "mfma_T1100_E128": custom(tokens=1100, seq_len=550, d_model=256, n_experts=128, top_k=8,
+                              cfg_id=120, router_std=0.1),
+    "mfma_T2048_E256": custom(tokens=2048, seq_len=1024, d_model=384, n_experts=256, top_k=8,
+                              cfg_id=121, router_std=0.05),
 }
 
 
