@@ -11,7 +11,8 @@ resident in HBM before the timed region.  Prints ONE JSON line.
 value = tokens x layers / second (each token counted once per MoE layer
 forward).  The roofline object covers the dominant kernel pair -- the grouped
 expert GEMMs of moe_grouped_ffn -- timed live with HIP events on the stream
-they are launched on.  cpu_baseline times the CPU oracle on a bounded token
+they are launched on, around one layer's call per timed step (layers in
+turn; an event record costs a few microseconds of stream time).  cpu_baseline times the CPU oracle on a bounded token
 sample of the same workload.
 """
 from __future__ import annotations
@@ -193,7 +194,7 @@ def main():
     bufs = [moe.alloc_buffers(shape, dev) for _ in range(L)]
     stream = torch.cuda.current_stream()
     stacked = L > 1
-    ev = []  # (start, end) events around every moe_grouped_ffn in the timed region
+    ev = []  # (start, end) events around one moe_grouped_ffn per timed step (layers in turn)
 
     def step(i, timed, counts_out=None):
         x = xs[i % n_x]
@@ -206,14 +207,18 @@ def main():
                             b["pos"], None, None, ws, stream)
             if counts_out is not None:
                 counts_out.append(b["counts"].cpu().numpy())
-            if timed:
+            # one layer's FFN per step is timed with events (layers in turn):
+            # each event record costs a few microseconds of stream time, so
+            # timing every layer would inflate the step it measures
+            ffn_timed = timed and l == i % L
+            if ffn_timed:
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
             moe.moe_grouped_ffn(shape, x, None, b["perm_src"], b["offsets"], p["w1"], p["w3"],
                                 p["w2"], p.get("ws1"), p.get("ws3"), p.get("ws2"), b["y_perm"],
                                 b["y_shared"], ws, stream)
-            if timed:
+            if ffn_timed:
                 e1.record(stream)
                 ev.append((e0, e1))
             moe.moe_combine(shape, b["y_perm"], b["y_shared"], b["topk_gate"], b["pos"],
