@@ -26,7 +26,8 @@
 namespace moe {
 
 constexpr int kRouteThreads = 256;
-constexpr int kRouteLds = 64 * 1024;  // LDS budget of one router block
+constexpr int kRouteLds = 64 * 1024;       // LDS budget of one router block (two per CU)
+constexpr int kRouteLdsOne = 160 * 1024;   // ... when there are no more blocks than CUs
 
 // LDS-only barrier: waits for this wave's LDS traffic, not for global loads,
 // so the next chunk's loads stay in flight across it.
@@ -264,6 +265,9 @@ static RouterCfg router_cfg(int64_t T, int d, int E, int want_blocks, bool whole
       const int BT = (kRouteThreads / TPR) * TPT;
       if (BT > 256) continue;
       const int64_t blocks = ((T + BT - 1) / BT) * ((E + BE - 1) / BE);
+      // few blocks (few tokens): one per CU, and all of its LDS for longer
+      // chunks of d -- fewer chunk barriers and load round trips
+      const size_t budget = blocks <= device_cus() ? kRouteLdsOne : kRouteLds;
       auto bytes = [&](int KC) {
         return static_cast<size_t>(BT * (KC * 4 + 16) + TPR * (KC * EPT * 4 + 16));
       };
@@ -273,7 +277,7 @@ static RouterCfg router_cfg(int64_t T, int d, int E, int want_blocks, bool whole
       };
       int KC;
       size_t lds;
-      if (bytes(d) <= static_cast<size_t>(kRouteLds) && fits(d)) {
+      if (bytes(d) <= budget && fits(d)) {
         KC = d;
         lds = bytes(d);
       } else {
@@ -281,7 +285,7 @@ static RouterCfg router_cfg(int64_t T, int d, int E, int want_blocks, bool whole
         // chunks give the register prefetch of the next one time to land
         KC = 32;
         for (int kc = 64; kc < d; kc *= 2)
-          if (d % kc == 0 && 2 * bytes(kc) <= static_cast<size_t>(kRouteLds) && fits(kc)) KC = kc;
+          if (d % kc == 0 && 2 * bytes(kc) <= budget && fits(kc)) KC = kc;
         lds = 2 * bytes(KC);
       }
       const RouterCfg c{BE, EPT, TPT, KC, blocks, lds};
@@ -295,6 +299,12 @@ static RouterCfg router_cfg(int64_t T, int d, int E, int want_blocks, bool whole
 template <int EPT, int TPT>
 static hipError_t launch_scores_cfg(const uint16_t* x, const float* w, float* sc, int64_t T, int d,
                                     int E, const RouterCfg& c, hipStream_t s) {
+  if (c.lds > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&router_scores_kernel<EPT, TPT>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             static_cast<int>(c.lds));
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((router_scores_kernel<EPT, TPT>), dim3(static_cast<unsigned>(c.blocks)),
                      dim3(kRouteThreads), c.lds, s, x, w, sc, T, d, E, c.BE, c.KC);
   return hipGetLastError();
@@ -860,6 +870,12 @@ hipError_t launch_route_fused(const uint16_t* x, const float* w_router, const fl
   const size_t lds = c.lds > tail ? c.lds : tail;
 #define MOE_FUSED_CASE(ep, tp)                                                                  \
   if (c.EPT == ep && c.TPT == tp) {                                                             \
+    if (lds > 64 * 1024) {                                                                      \
+      const hipError_t ae = hipFuncSetAttribute(                                                \
+          reinterpret_cast<const void*>(&router_fused_kernel<ep, tp>),                          \
+          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));                   \
+      if (ae != hipSuccess) return ae;                                                          \
+    }                                                                                           \
     hipLaunchKernelGGL((router_fused_kernel<ep, tp>), dim3(static_cast<unsigned>(c.blocks)),     \
                        dim3(kRouteThreads), lds, s, x, w_router, bias, idx, gate, margin,        \
                        stats ? seq_p : nullptr, seq_cnt, T, d, E, k, c.BE, c.KC, G);             \
