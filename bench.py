@@ -11,9 +11,11 @@ resident in HBM before the timed region.  Prints ONE JSON line.
 value = tokens x layers / second (each token counted once per MoE layer
 forward).  The roofline object covers the dominant kernel pair -- the grouped
 expert GEMMs of moe_grouped_ffn -- timed live with HIP events on the stream
-they are launched on, around one layer's call per timed step (layers in
-turn; an event record costs a few microseconds of stream time).  cpu_baseline times the CPU oracle on a bounded token
-sample of the same workload.
+they are launched on, around one layer's call in every fifth timed step
+(layers in turn; an event record costs a few microseconds of stream time).
+By default 20 warm-up steps and 100 timed steps: the clocks settle within
+the warm-up.  cpu_baseline times the CPU oracle on a bounded token sample of
+the same workload.
 """
 from __future__ import annotations
 
@@ -34,12 +36,14 @@ PEAK_HBM_GBS = 8000.0
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target wall time of the CPU oracle sample")
+    ap.add_argument("--ffn-events-every", type=int, default=5,
+                    help="time one layer's moe_grouped_ffn with HIP events in every N-th timed step")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain device copy of 1 GiB (counter calibration)")
     return ap.parse_args()
@@ -207,10 +211,10 @@ def main():
                             b["pos"], None, None, ws, stream)
             if counts_out is not None:
                 counts_out.append(b["counts"].cpu().numpy())
-            # one layer's FFN per step is timed with events (layers in turn):
-            # each event record costs a few microseconds of stream time, so
-            # timing every layer would inflate the step it measures
-            ffn_timed = timed and l == i % L
+            # one layer's FFN in every N-th step is timed with events (layers
+            # in turn): each event record costs a few microseconds of stream
+            # time, so timing every layer would inflate the step it measures
+            ffn_timed = timed and i % args.ffn_events_every == 0 and l == (i // args.ffn_events_every) % L
             if ffn_timed:
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
