@@ -50,8 +50,10 @@ def parse():
 
 
 def hbm_read_probe():
-    """Achievable HBM read rate: moe_probe_hbm_read (libmoe_probe.so) over
-    8 GiB, best of four passes, GB/s.  It streams like the GEMM's weights."""
+    """Achievable HBM read rate over 8 GiB, best of four passes, GB/s, for each
+    probe of libmoe_probe.so: moe_probe_hbm_read (LDS DMA, the streamed
+    weights' pattern) and moe_probe_hbm_read_nt (non-temporal register loads,
+    the register path's pattern)."""
     import ctypes
 
     import torch
@@ -61,25 +63,28 @@ def hbm_read_probe():
     if not os.path.exists(_build.PROBE_LIB):
         raise SystemExit(f"{_build.PROBE_LIB} is missing: run the build first")
     P = ctypes.CDLL(_build.PROBE_LIB)
-    P.moe_probe_hbm_read.restype = ctypes.c_int
-    P.moe_probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
     nbytes = 8 << 30
     buf = torch.ones(nbytes // 2, dtype=torch.bfloat16, device="cuda:0")
     sink = torch.zeros(4096, dtype=torch.int32, device="cuda:0")
     stream = torch.cuda.current_stream()
-    best = 0.0
-    for _ in range(4):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        if P.moe_probe_hbm_read(buf.data_ptr(), nbytes, sink.data_ptr(), stream.cuda_stream) != 0:
-            raise RuntimeError("moe_probe_hbm_read failed")
-        e1.record(stream)
-        torch.cuda.synchronize()
-        best = max(best, nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    out = {}
+    for key, name in (("dma", "moe_probe_hbm_read"), ("nt", "moe_probe_hbm_read_nt")):
+        fn = getattr(P, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+        best = 0.0
+        for _ in range(4):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            if fn(buf.data_ptr(), nbytes, sink.data_ptr(), stream.cuda_stream) != 0:
+                raise RuntimeError(f"{name} failed")
+            e1.record(stream)
+            torch.cuda.synchronize()
+            best = max(best, nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+        out[key] = best
     del buf, sink
-    torch.cuda.empty_cache()
-    return best
+    return out
 
 
 def ffn_algorithmic(wl, counts_per_layer):
@@ -283,10 +288,14 @@ def main():
     roof["hbm_frac"] = byts / t_s / 1e9 / PEAK_HBM_GBS
     # time at the spec roofline (the slower of MFMA and HBM) over measured time
     roof["attainable_frac"] = max(flops / (PEAK_BF16_TFLOPS * 1e12), byts / (PEAK_HBM_GBS * 1e9)) / t_s
-    probe = hbm_read_probe()
+    probes = hbm_read_probe()
+    probe = max(probes.values())
     roof["hbm_read_probe_gbs"] = probe
-    roof["hbm_read_probe"] = ("moe_probe_hbm_read: 8 GiB streamed by LDS DMA, 32 KiB steps, one block "
-                              "per CU, best of four passes")
+    roof["hbm_read_probe_dma_gbs"] = probes["dma"]
+    roof["hbm_read_probe_nt_gbs"] = probes["nt"]
+    roof["hbm_read_probe"] = ("the faster of two reads of 8 GiB, best of four passes each: "
+                              "moe_probe_hbm_read (LDS DMA, 32 KiB steps, one block per CU) and "
+                              "moe_probe_hbm_read_nt (non-temporal 16-byte register loads)")
     roof["hbm_frac_of_probe"] = byts / t_s / 1e9 / probe
 
     line = {

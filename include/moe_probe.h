@@ -2,9 +2,11 @@
  * kept apart from the MoE interface in moe.h.
  *
  * It gives the achievable HBM read rate that the measurements report beside
- * the 8 TB/s specification: one block per compute unit streams 1 MiB pieces
- * of a buffer into LDS by LDS DMA, 32 KiB per step in a three-stage ring --
- * the access pattern of the grouped GEMM's weight stream, without MFMAs.
+ * the 8 TB/s specification, read two ways: by LDS DMA (one block per compute
+ * unit streams 1 MiB pieces of a buffer into LDS, 32 KiB per step in a
+ * three-stage ring -- the access pattern of the grouped GEMM's streamed
+ * weights, without MFMAs) and by non-temporal 16-byte register loads (the
+ * pattern of its register-path weight loads).
  */
 #ifndef MOE_PROBE_H_
 #define MOE_PROBE_H_
@@ -24,6 +26,12 @@ extern "C" {
  * Returns 0 when the launch was enqueued, 1 on unusable sizes, a NULL pointer
  * or a failed launch (nothing is enqueued then). */
 int moe_probe_hbm_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
+
+/* As moe_probe_hbm_read, with non-temporal register loads: eight blocks of 256
+ * threads per compute unit, each thread with eight 16-byte loads in flight.
+ * Same arguments, ownership and return values; `buf` must be 16-byte aligned
+ * (else 1, nothing enqueued). */
+int moe_probe_hbm_read_nt(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

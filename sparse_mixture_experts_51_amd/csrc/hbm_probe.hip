@@ -1,12 +1,16 @@
 // hbm_probe.hip -- the achievable HBM read rate, for the measurements (a
 // library of its own, libmoe_probe.so, next to libmoe.so; not part of the
-// MoE interface).
+// MoE interface).  Two ways of reading:
 //
-// One block per CU streams whole 1 MiB pieces of a buffer, 32 KiB per step,
-// straight into a three-stage LDS ring by LDS DMA, two steps ahead -- the
-// access pattern of the grouped GEMM's weight stream without its MFMAs.
-// Each thread folds one word of every landed stage into a per-block value so
-// that the loads have a consumer.
+// - LDS DMA: one block per CU streams whole 1 MiB pieces of a buffer, 32 KiB
+//   per step, straight into a three-stage LDS ring, two steps ahead -- the
+//   access pattern of the grouped GEMM's streamed weights without its MFMAs.
+// - Non-temporal register loads: eight blocks of 256 threads per CU, each
+//   thread with eight 16-byte loads in flight, grid-strided -- the pattern of
+//   the register-path weight loads.
+//
+// Each thread folds what it read into a per-thread value so that the loads
+// have a consumer.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -57,6 +61,36 @@ __global__ __launch_bounds__(kThreads) void hbm_read_kernel(const unsigned char*
   if (acc == 0x9E3779B9u) sink[blockIdx.x] = acc;  // keeps the reads; practically never stored
 }
 
+constexpr int kNtThreads = 256;
+constexpr int kNtBlocksPerCu = 8;
+constexpr int kNtInFlight = 8;  // 16-byte loads per thread per trip
+
+__global__ __launch_bounds__(kNtThreads) void hbm_read_nt_kernel(const u32x4* __restrict__ buf, int64_t n16,
+                                                                uint32_t* __restrict__ sink) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kNtThreads * kNtInFlight;
+  uint32_t acc = 0;
+  for (int64_t base = static_cast<int64_t>(blockIdx.x) * kNtThreads * kNtInFlight + threadIdx.x; base < n16;
+       base += stride) {
+    u32x4 v[kNtInFlight];
+#pragma unroll
+    for (int u = 0; u < kNtInFlight; ++u) {
+      const int64_t i = base + static_cast<int64_t>(u) * kNtThreads;
+      v[u] = i < n16 ? __builtin_nontemporal_load(buf + i) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < kNtInFlight; ++u) acc ^= v[u][0] ^ v[u][3];
+  }
+  if (acc == 0x9E3779B9u) sink[blockIdx.x / kNtBlocksPerCu] = acc;  // practically never stored
+}
+
+int compute_units(int* cus) {
+  int dev = 0;
+  return hipGetDevice(&dev) == hipSuccess &&
+                 hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && *cus > 0
+             ? 0
+             : 1;
+}
+
 }  // namespace
 
 // Reads `bytes` (a multiple of 1 MiB, at most 2^31 MiB) at `buf` once.  `sink`
@@ -64,13 +98,23 @@ __global__ __launch_bounds__(kThreads) void hbm_read_kernel(const unsigned char*
 // the sizes are unusable or the launch fails.
 extern "C" int moe_probe_hbm_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
   if (!buf || !sink || bytes <= 0 || bytes % kPiece != 0) return 1;
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return 1;
+  int cus = 0;
+  if (compute_units(&cus) != 0) return 1;
   const int64_t pieces = bytes / kPiece;
   if (pieces > 0x7FFFFFFF) return 1;
   hipLaunchKernelGGL(hbm_read_kernel, dim3(cus), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
                      static_cast<const unsigned char*>(buf), static_cast<int>(pieces), sink);
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+// The same contract with non-temporal register loads (kNtBlocksPerCu blocks
+// per CU; `sink` again holds one word per CU).
+extern "C" int moe_probe_hbm_read_nt(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
+  if (!buf || !sink || bytes <= 0 || bytes % kPiece != 0 || (reinterpret_cast<uintptr_t>(buf) & 15) != 0)
+    return 1;
+  int cus = 0;
+  if (compute_units(&cus) != 0) return 1;
+  hipLaunchKernelGGL(hbm_read_nt_kernel, dim3(cus * kNtBlocksPerCu), dim3(kNtThreads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const u32x4*>(buf), bytes / 16, sink);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }

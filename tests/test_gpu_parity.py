@@ -150,13 +150,16 @@ def test_hbm_probe_reads_and_leaves_the_sink():
 
     from sparse_mixture_experts_51_amd import build
     P = ctypes.CDLL(build.PROBE_LIB)
-    P.moe_probe_hbm_read.restype = ctypes.c_int
-    P.moe_probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
     buf = torch.ones(8 << 20, dtype=torch.bfloat16, device=DEV)  # 16 MiB
     sink = torch.full((4096,), 7, dtype=torch.int32, device=DEV)
-    assert P.moe_probe_hbm_read(buf.data_ptr(), 16 << 20, sink.data_ptr(), None) == 0
-    torch.cuda.synchronize()
-    assert torch.all(sink == 7)
+    for name in ("moe_probe_hbm_read", "moe_probe_hbm_read_nt"):
+        say(f"[probe] {name} over 16 MiB")
+        fn = getattr(P, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+        assert fn(buf.data_ptr(), 16 << 20, sink.data_ptr(), None) == 0
+        torch.cuda.synchronize()
+        assert torch.all(sink == 7), name
 
 
 def test_permute_zero_tokens_writes_zero_loads():
