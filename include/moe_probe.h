@@ -2,11 +2,11 @@
  * kept apart from the MoE interface in moe.h.
  *
  * It gives the achievable HBM read rate that the measurements report beside
- * the 8 TB/s specification, read two ways: by LDS DMA (one block per compute
- * unit streams 1 MiB pieces of a buffer into LDS, 32 KiB per step in a
- * three-stage ring -- the access pattern of the grouped GEMM's streamed
- * weights, without MFMAs) and by non-temporal 16-byte register loads (the
- * pattern of its register-path weight loads).
+ * the 8 TB/s specification, read two ways, both with the non-temporal hint:
+ * by LDS DMA (one block per compute unit streams 1 MiB pieces of a buffer
+ * into LDS, 32 KiB per step in a three-stage ring -- the access pattern of
+ * the grouped GEMM's streamed weights, without MFMAs) and by 16-byte register
+ * loads (the pattern of its register-path weight loads).
  */
 #ifndef MOE_PROBE_H_
 #define MOE_PROBE_H_

@@ -44,10 +44,12 @@ __device__ __forceinline__ void lds_read2_b128(const u32x4* p0, const u32x4* p1,
 }
 
 // 16 bytes per lane from a buffer straight into LDS: lane l's bytes land at
-// dst + 16 * l (dst is wave-uniform).
+// dst + 16 * l (dst is wave-uniform).  kPolicy is the load's cache-policy
+// operand (on gfx950 bit 1 is the non-temporal hint).
+template <int kPolicy = 0>
 __device__ __forceinline__ void dma_b128(__amdgpu_buffer_rsrc_t rsrc, void* dst, int voffset,
                                          int soffset) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)dst, 16, voffset, soffset, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)dst, 16, voffset, soffset, 0, kPolicy);
 }
 
 // Six 16-byte LDS reads under one wait (the fragments of one MFMA sub-step

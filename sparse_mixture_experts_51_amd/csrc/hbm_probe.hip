@@ -3,8 +3,9 @@
 // MoE interface).  Two ways of reading:
 //
 // - LDS DMA: one block per CU streams whole 1 MiB pieces of a buffer, 32 KiB
-//   per step, straight into a three-stage LDS ring, two steps ahead -- the
-//   access pattern of the grouped GEMM's streamed weights without its MFMAs.
+//   per step, straight into a three-stage LDS ring, two steps ahead, with the
+//   non-temporal hint -- the access pattern of the grouped GEMM's streamed
+//   weights without its MFMAs.
 // - Non-temporal register loads: eight blocks of 256 threads per CU, each
 //   thread with eight 16-byte loads in flight, grid-strided -- the pattern of
 //   the register-path weight loads.
@@ -20,6 +21,7 @@ constexpr int kThreads = 512;
 constexpr int kStep = 32 * 1024;      // bytes per step
 constexpr int kPiece = 1024 * 1024;   // bytes per unit of work
 constexpr int kStages = 3;
+constexpr int kPolicyNT = 2;  // cache-policy operand: bit 1 is the non-temporal hint on gfx950
 constexpr int kPasses = kStep / (kThreads * 16);  // 16-byte DMA per thread and pass
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -40,7 +42,7 @@ __global__ __launch_bounds__(kThreads) void hbm_read_kernel(const unsigned char*
 #pragma unroll
       for (int i = 0; i < kPasses; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)&ring[st][i * kThreads + wave * 64], 16,
-                                                 tid * 16, s * kStep + i * kThreads * 16, 0, 0);
+                                                 tid * 16, s * kStep + i * kThreads * 16, 0, kPolicyNT);
     };
     issue(0, 0);
     issue(1, 1);
