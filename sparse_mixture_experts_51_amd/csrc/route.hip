@@ -357,25 +357,27 @@ __global__ __launch_bounds__(256) void router_scores_mfma_kernel(
                                                (q % 16) * 4);
     }
   };
+  auto stash_x = [&](int b, int i) __attribute__((always_inline)) {
+    const int p = tid + 256 * i;
+    float f[8];
+    bf16x8_to_f32(px[i], f);
+    float* dst = &xs[b][(p / 16) * kMfRow + (p % 16) * 8];
+    *reinterpret_cast<float4*>(dst) = make_float4(f[0], f[1], f[2], f[3]);
+    *reinterpret_cast<float4*>(dst + 4) = make_float4(f[4], f[5], f[6], f[7]);
+  };
+  auto stash_w = [&](int b, int i) __attribute__((always_inline)) {
+    const int q = tid + 256 * i;
+    const int kk = q / 16, e = (q % 16) * 4;
+    wt[b][(e + 0) * kMfRow + kk] = pw[i].x;
+    wt[b][(e + 1) * kMfRow + kk] = pw[i].y;
+    wt[b][(e + 2) * kMfRow + kk] = pw[i].z;
+    wt[b][(e + 3) * kMfRow + kk] = pw[i].w;
+  };
   auto stash = [&](int b) {
 #pragma unroll
-    for (int i = 0; i < kXP; ++i) {
-      const int p = tid + 256 * i;
-      float f[8];
-      bf16x8_to_f32(px[i], f);
-      float* dst = &xs[b][(p / 16) * kMfRow + (p % 16) * 8];
-      *reinterpret_cast<float4*>(dst) = make_float4(f[0], f[1], f[2], f[3]);
-      *reinterpret_cast<float4*>(dst + 4) = make_float4(f[4], f[5], f[6], f[7]);
-    }
+    for (int i = 0; i < kXP; ++i) stash_x(b, i);
 #pragma unroll
-    for (int i = 0; i < kWP; ++i) {
-      const int q = tid + 256 * i;
-      const int kk = q / 16, e = (q % 16) * 4;
-      wt[b][(e + 0) * kMfRow + kk] = pw[i].x;
-      wt[b][(e + 1) * kMfRow + kk] = pw[i].y;
-      wt[b][(e + 2) * kMfRow + kk] = pw[i].z;
-      wt[b][(e + 3) * kMfRow + kk] = pw[i].w;
-    }
+    for (int i = 0; i < kWP; ++i) stash_w(b, i);
   };
   f32x16 acc = {};
   const int nch = d / kMfKC;
@@ -386,16 +388,29 @@ __global__ __launch_bounds__(256) void router_scores_mfma_kernel(
     if (c + 1 < nch) fetch(c + 1);  // in flight during the MFMAs below
     const float* xr = &xs[c & 1][(16 * wave + (lane & 15)) * kMfRow];  // A: token lane % 16
     const float* wr = &wt[c & 1][lane * kMfRow];                      // B: expert lane
-#pragma unroll 8
-    for (int k = 0; k < kMfKC; k += 4) {
-      const float4 a4 = *reinterpret_cast<const float4*>(xr + k);
-      const float4 b4 = *reinterpret_cast<const float4*>(wr + k);
-      acc = __builtin_amdgcn_mfma_f32_16x16x1f32(a4.x, b4.x, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x1f32(a4.y, b4.y, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x1f32(a4.z, b4.z, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_16x16x1f32(a4.w, b4.w, acc, 0, 0, 0);
+    const bool more = c + 1 < nch;
+    const int nb = (c + 1) & 1;  // the buffers step c - 1 read
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+#pragma unroll
+      for (int k = 16 * g; k < 16 * g + 16; k += 4) {
+        const float4 a4 = *reinterpret_cast<const float4*>(xr + k);
+        const float4 b4 = *reinterpret_cast<const float4*>(wr + k);
+        acc = __builtin_amdgcn_mfma_f32_16x16x1f32(a4.x, b4.x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x1f32(a4.y, b4.y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x1f32(a4.z, b4.z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x1f32(a4.w, b4.w, acc, 0, 0, 0);
+      }
+      // the next chunk goes to LDS in the issue slots that the dependent
+      // MFMA chain leaves, in the second half (its loads have landed by then)
+      if (more) {
+        if (g == 4) { stash_x(nb, 0); stash_x(nb, 1); }
+        if (g == 5) { stash_x(nb, 2); stash_x(nb, 3); }
+        if (g == 6) { stash_w(nb, 0); stash_w(nb, 1); stash_w(nb, 2); stash_w(nb, 3); }
+        if (g == 7) { stash_w(nb, 4); stash_w(nb, 5); stash_w(nb, 6); stash_w(nb, 7); }
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (c + 1 < nch) stash((c + 1) & 1);  // the buffers step c - 1 read
     __syncthreads();
   }
 #pragma unroll
