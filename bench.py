@@ -171,6 +171,9 @@ def cpu_baseline(wl, target_s: float):
 
 def main():
     args = parse()
+    if args.steps < 1 or args.warmup < 0 or args.ffn_events_every < 1:
+        print("bench.py needs --steps >= 1, --warmup >= 0 and --ffn-events-every >= 1", file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no "
               "multi-GPU path", file=sys.stderr)
