@@ -14,7 +14,9 @@
 //   scatter: the block's choices as an LDS bitmap [E][TB bits]; the
 //            rank of (t, e) among earlier tokens of the block choosing e is a
 //            popcount, so rows inside a group are in ascending token order
-//            without sorting.  Optionally copies x rows into x_perm.
+//            without sorting.
+// and, when x_perm is asked for, a gather of x rows into it over the whole
+// chip (the scatter's few blocks would copy them on a few CUs).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -116,12 +118,10 @@ __global__ __launch_bounds__(TB) void perm_scatter_kernel(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ blk_cnt,
     const int32_t* __restrict__ blk_base, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src, int32_t* __restrict__ pos,
-    const uint16_t* __restrict__ x, uint16_t* __restrict__ x_perm, int64_t T, int d, int E, int k,
-    int nblk, int fused_scan) {
+    int64_t T, int E, int k, int nblk, int fused_scan) {
   constexpr int W = TB / 32;         // 32-bit words per expert row of the bitmap
-  extern __shared__ uint32_t bits[];  // [E][W], rows [TB * k], base [E], total [E] (fused)
-  int32_t* rows = reinterpret_cast<int32_t*>(bits + E * W);
-  int32_t* base = rows + TB * k;
+  extern __shared__ uint32_t bits[];  // [E][W], base [E], total [E] (fused)
+  int32_t* base = reinterpret_cast<int32_t*>(bits + E * W);
   int32_t* etot = base + E;
   for (int i = threadIdx.x; i < E * W; i += TB) bits[i] = 0;
   if (fused_scan) {
@@ -190,22 +190,30 @@ __global__ __launch_bounds__(TB) void perm_scatter_kernel(
         perm_src[row] = static_cast<int32_t>(t);
       }
       pos[t * k + j] = row;
-      rows[threadIdx.x * k + j] = row;
     }
   }
-  if (x_perm == nullptr) return;
-  __syncthreads();
-  const int64_t ntok = (T - t0) < TB ? (T - t0) : TB;
+}
+
+// x_perm[r] = x[perm_src[r]] for the rows r < offsets[E] that the scatter
+// filled: 16 bytes per thread and trip, consecutive threads along a row,
+// grid-strided.  A source index outside [0, T) (malformed choices) leaves its
+// row untouched.
+__global__ __launch_bounds__(256) void perm_gather_kernel(const uint16_t* __restrict__ x,
+                                                          const int32_t* __restrict__ perm_src,
+                                                          const int32_t* __restrict__ offsets,
+                                                          uint16_t* __restrict__ x_perm, int64_t T,
+                                                          int d, int E, int64_t nrows) {
   const int chunks = d / 8;
-  const int64_t work = ntok * k * chunks;
-  for (int64_t c = threadIdx.x; c < work; c += TB) {
-    const int64_t p = c / chunks;
-    const int ch = static_cast<int>(c % chunks);
-    const int row = rows[p];
-    if (row < 0) continue;
-    const int64_t tok = t0 + p / k;
-    reinterpret_cast<uint4*>(x_perm + static_cast<int64_t>(row) * d)[ch] =
-        reinterpret_cast<const uint4*>(x + tok * d)[ch];
+  const int64_t filled = offsets[E];
+  const int64_t rows = filled < nrows ? filled : nrows;
+  const int64_t work = rows * chunks;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < work; i += stride) {
+    const int64_t r = i / chunks;
+    const int c = static_cast<int>(i - r * chunks);
+    const int64_t t = perm_src[r];
+    if (t < 0 || t >= T) continue;
+    reinterpret_cast<uint4*>(x_perm + r * d)[c] = reinterpret_cast<const uint4*>(x + t * d)[c];
   }
 }
 
@@ -227,7 +235,7 @@ static hipError_t launch_permute_tb(const int32_t* idx, int32_t* counts, int32_t
   if (err != hipSuccess) return err;
   // Small count tables are summed by every scatter block itself (one launch
   // fewer); large ones go through the single-block scan.
-  const size_t lds_base = sizeof(uint32_t) * E * (TB / 32) + sizeof(int32_t) * TB * (k > 1 ? k : 1);
+  const size_t lds_base = sizeof(uint32_t) * E * (TB / 32);
   const size_t lds_fused = lds_base + 2 * sizeof(int32_t) * E;
   const int fused = static_cast<int64_t>(nblk) * E <= 16384 && lds_fused <= 64 * 1024;
   if (!fused) {
@@ -237,8 +245,14 @@ static hipError_t launch_permute_tb(const int32_t* idx, int32_t* counts, int32_t
     if (err != hipSuccess) return err;
   }
   hipLaunchKernelGGL((perm_scatter_kernel<TB>), dim3(nblk), dim3(TB), fused ? lds_fused : lds_base,
-                     s, idx, blk_cnt, blk_base, counts, offsets, perm_src, pos, x, x_perm, T, d, E,
-                     k, nblk, fused);
+                     s, idx, blk_cnt, blk_base, counts, offsets, perm_src, pos, T, E, k, nblk, fused);
+  err = hipGetLastError();
+  if (err != hipSuccess || x_perm == nullptr) return err;
+  const int64_t nrows = T * k;
+  const int64_t blocks = (nrows * (d / 8) + 255) / 256;
+  const unsigned grid = static_cast<unsigned>(blocks < 65536 ? blocks : 65536);
+  hipLaunchKernelGGL(perm_gather_kernel, dim3(grid > 0 ? grid : 1), dim3(256), 0, s, x, perm_src, offsets,
+                     x_perm, T, d, E, nrows);
   return hipGetLastError();
 }
 
