@@ -145,6 +145,44 @@ def test_permute_matches_oracle(T, E, k, gather):
         assert np.array_equal(xp, bits(x)[ref["perm_src"]])
 
 
+def test_permute_skips_malformed_choices_and_gathers_the_rest():
+    """Choices outside [0, E) (only a malformed caller produces them) are left
+    out of the loads, offsets and rows; every other row is placed and copied.
+    Checked by properties, with no oracle call: the oracle is never fed such
+    input."""
+    T, E, k, d = 700, 16, 4, 128
+    say(f"[permute] malformed choices T={T} E={E} k={k} x_perm=True")
+    gen = torch.Generator().manual_seed(4242)
+    idx = torch.stack([torch.randperm(E, generator=gen)[:k] for _ in range(T)]).to(torch.int32)
+    bad = torch.rand(T, k, generator=gen) < 0.07
+    idx[bad] = torch.where(torch.rand(T, k, generator=gen) < 0.5, -1, E + 3).to(torch.int32)[bad]
+    shape = moe.Shape(T, d, E, k, 64, 0, 0)
+    bufs = moe.alloc_buffers(shape, DEV, x_perm=True)
+    x = torch.randn(T, d, device=DEV).to(torch.bfloat16)
+    bufs["x_perm"].fill_(0)
+    moe.moe_permute(shape, idx.to(DEV), bufs["counts"], bufs["offsets"], bufs["perm_src"], bufs["pos"],
+                    x, bufs["x_perm"], bufs["workspace"])
+    torch.cuda.synchronize()
+    ids = idx.numpy()
+    valid = (ids >= 0) & (ids < E)
+    counts, offsets = host(bufs["counts"]), host(bufs["offsets"])
+    assert np.array_equal(counts, np.bincount(ids[valid], minlength=E))
+    assert offsets[0] == 0 and np.array_equal(np.diff(offsets), counts) and offsets[E] == valid.sum()
+    pos, src = host(bufs["pos"]), host(bufs["perm_src"])
+    assert np.all(pos[~valid] == -1)
+    n = int(offsets[E])
+    assert sorted(pos[valid].tolist()) == list(range(n))  # a bijection onto the filled rows
+    for t, j in zip(*np.nonzero(valid)):
+        e, r = ids[t, j], pos[t, j]
+        assert src[r] == t and offsets[e] <= r < offsets[e + 1]
+    for e in range(E):  # ascending tokens inside each group
+        seg = src[offsets[e]:offsets[e + 1]]
+        assert np.all(np.diff(seg) > 0)
+    xp, xb = bits(bufs["x_perm"]), bits(x)
+    assert np.array_equal(xp[:n], xb[src[:n]])
+    assert not xp[n:].any()  # rows past the filled ones are not written
+
+
 def test_hbm_probe_reads_and_leaves_the_sink():
     import ctypes
 
