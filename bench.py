@@ -8,14 +8,27 @@ the workload, moe_route -> moe_permute -> moe_grouped_ffn -> moe_combine
 moe_update_bias for every layer.  Inputs are seeded synthetic tensors already
 resident in HBM before the timed region.  Prints ONE JSON line.
 
+The default workload is the DeepSeek-V3-shaped prefill layer (4096 tokens,
+d_model 7168, 256 routed experts top-8 plus one shared expert, expert hidden
+2048); the mini-model and decode workloads are behind --workload.
+
 value = tokens x layers / second (each token counted once per MoE layer
-forward).  The roofline object covers the dominant kernel pair -- the grouped
-expert GEMMs of moe_grouped_ffn -- timed live with HIP events on the stream
-they are launched on, around one layer's call in every fifth timed step
-(layers in turn; an event record costs a few microseconds of stream time).
-By default 20 warm-up steps and 100 timed steps: the clocks settle within
-the warm-up.  cpu_baseline times the CPU oracle on a bounded token sample of
-the same workload.
+forward).  The roofline object covers the dominant kernel group -- the
+grouped expert GEMMs of moe_grouped_ffn -- timed live with HIP events on the
+stream they are launched on, around one layer's call in the first timed step
+and every fifth one after it (layers in turn; an event record costs a few
+microseconds of stream time).  moe_update_bias is timed the same way in those
+steps and reported on its own.  By default 20 warm-up steps and 100 timed
+steps: the clocks settle within the warm-up.
+
+Workloads of one batch (the prefill and decode layers, which stand for
+inference) route every step with the same, frozen bias, so each step does
+the same work; the bias update still runs every step, into a training copy
+of the bias that routing does not read.  Multi-step training workloads (the
+stacked mini layers) route with the live bias.
+
+cpu_baseline times the CPU oracle on a bounded token sample of the same
+workload, on this host's cores.
 """
 from __future__ import annotations
 
@@ -102,14 +115,29 @@ def ffn_algorithmic(wl, counts_per_layer):
     return out
 
 
-def cpu_baseline(wl, target_s: float):
+def cpu_model() -> str:
+    """The host CPU's model name (first "model name" line of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, target_s: float, params_dev=None, x_dev=None):
     """The CPU oracle, as it stands, on a bounded sample of the workload.
 
     Mini shapes: whole layer passes over all tokens (layer i % L of step
     i // L) until the timed oracle work reaches target_s.  V3 shapes (22.5 GB
     of experts): the first n tokens are routed on the host, only the experts
-    they chose are drawn, and the oracle's expert FFN and combine run for
-    them.  Weight generation is outside the timed part."""
+    they chose are copied to the host (from the device copies the GPU path
+    uses: the same seeded draws), and the oracle's expert FFN and combine run
+    for them.  Copies and weight draws are outside the timed part.  Threads:
+    the CPUs this process may use, capped at 16 (one GPU's share of a GPU
+    host)."""
     import numpy as np
     import torch
 
@@ -117,6 +145,11 @@ def cpu_baseline(wl, target_s: float):
     from sparse_mixture_experts_51_amd import workloads
 
     threads = oracle.default_threads()
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        affinity = os.cpu_count() or 1
+    host = {"cores": threads, "cpu_model": cpu_model(), "cpus_available": affinity}
     if wl.n_experts * wl.hidden * wl.d_model * 6 <= (1 << 31):
         hp = {}
         done, dt = 0, 0.0
@@ -131,25 +164,26 @@ def cpu_baseline(wl, target_s: float):
             oracle.layer(xb, hp[l], wl.top_k, seq_len=wl.seq_len, nthreads=threads)
             dt += time.perf_counter() - t0
             done += 1
-        return {"value": done * wl.tokens / dt, "unit": "tokens/s", "cores": threads,
+        return {"value": done * wl.tokens / dt, "unit": "tokens/s", **host,
                 "kind": "oracle",
                 "sample": f"{done} layer passes over all {wl.tokens} tokens of {wl.name} (route, "
                           f"balance statistic, permute, grouped FFN, combine), fp64 oracle, "
                           f"{dt:.1f} s on {threads} threads; counts tokens x layers per second"}
 
     import concurrent.futures as cf
-    xb = oracle.as_bf16_bits(workloads.tokens(wl, 0, "cpu"))
-    w_r = workloads.router(wl, 0, "cpu").numpy()
-    b = workloads.bias(wl, 0, "cpu").numpy()
-    sh = {k: oracle.as_bf16_bits(v) for k, v in workloads.shared_weights(wl, 0, "cpu").items()}
+    if params_dev is None:
+        params_dev = workloads.layer_params(wl, 0, "cpu")
+    xb = oracle.as_bf16_bits(workloads.tokens(wl, 0, "cpu") if x_dev is None else x_dev)
+    w_r = params_dev["w_router"].cpu().numpy()
+    b = params_dev["bias"].cpu().numpy()
+    sh = {k: oracle.as_bf16_bits(params_dev[k]) for k in ("ws1", "ws3", "ws2") if k in params_dev}
     cache = {}
     n = 4
     while True:
         r = oracle.route(xb[:n], w_r, b, wl.top_k, threads)
         for e in np.unique(r["idx"]):
             if e not in cache:
-                ew = workloads.one_expert(wl, int(e), 0, "cpu")
-                cache[e] = tuple(oracle.as_bf16_bits(ew[k]) for k in ("w1", "w3", "w2"))
+                cache[e] = tuple(oracle.as_bf16_bits(params_dev[k][int(e)]) for k in ("w1", "w3", "w2"))
         t0 = time.perf_counter()
         r = oracle.route(xb[:n], w_r, b, wl.top_k, threads)
         jobs = [(t, j) for t in range(n) for j in range(wl.top_k)]
@@ -163,7 +197,7 @@ def cpu_baseline(wl, target_s: float):
         if dt >= target_s / 2 or n >= min(64, wl.tokens):
             break
         n = min(64, wl.tokens, n * 2)
-    return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": n / dt, "unit": "tokens/s", **host, "kind": "oracle",
             "sample": f"first {n} of {wl.tokens} tokens of {wl.name}: routed on the host, then "
                       f"expert FFN of their {wl.top_k} chosen experts plus the shared expert and "
                       f"the combine, fp64 oracle, {dt:.1f} s on {threads} threads"}
@@ -184,6 +218,11 @@ def main():
 
     from sparse_mixture_experts_51_amd import moe, profiling, workloads
 
+    name = args.workload or workloads.DEFAULT_BENCH_WORKLOAD
+    if name not in workloads.WORKLOADS:
+        print(f"unknown workload {name!r}; one of {sorted(workloads.WORKLOADS)}", file=sys.stderr)
+        sys.exit(2)
+
     if args.calibrate_copy:
         # a plain device-to-device copy of profiling.COPY_BYTES bytes, three times
         src = torch.empty(profiling.COPY_BYTES, dtype=torch.uint8, device="cuda:0").fill_(1)
@@ -193,11 +232,12 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    name = args.workload or workloads.DEFAULT_BENCH_WORKLOAD
     wl = workloads.WORKLOADS[name]
     dev = "cuda:0"
     torch.cuda.set_device(0)
     moe.load()
+    # achievable HBM read rate first, outside the timed region
+    probes = hbm_read_probe()
     shape = moe.Shape.of(wl)
     L = wl.layers
     params = [workloads.layer_params(wl, l, dev) for l in range(L)]
@@ -206,10 +246,16 @@ def main():
     bufs = [moe.alloc_buffers(shape, dev) for _ in range(L)]
     stream = torch.cuda.current_stream()
     stacked = L > 1
-    ev = []  # (start, end) events around one moe_grouped_ffn per timed step (layers in turn)
+    # one batch (inference-shaped): route with a frozen bias, update a training copy
+    frozen = wl.steps == 1
+    train_bias = [params[l]["bias"].clone() if frozen else params[l]["bias"] for l in range(L)]
+    ev = []   # (start, end) events around one moe_grouped_ffn per timed step (layers in turn)
+    evb = []  # (start, end) events around the bias updates of the same steps
 
     def step(i, timed, counts_out=None):
+        """Step i; timed = index among the timed steps, or None."""
         x = xs[i % n_x]
+        events = timed is not None and timed % args.ffn_events_every == 0
         for l in range(L):
             b, p = bufs[l], params[l]
             ws = b["workspace"]
@@ -219,10 +265,10 @@ def main():
                             b["pos"], None, None, ws, stream)
             if counts_out is not None:
                 counts_out.append(b["counts"].cpu().numpy())
-            # one layer's FFN in every N-th step is timed with events (layers
-            # in turn): each event record costs a few microseconds of stream
-            # time, so timing every layer would inflate the step it measures
-            ffn_timed = timed and i % args.ffn_events_every == 0 and l == (i // args.ffn_events_every) % L
+            # one layer's FFN in every N-th timed step is timed with events
+            # (layers in turn): each event record costs a few microseconds of
+            # stream time, so timing every layer would inflate the step it measures
+            ffn_timed = events and l == (timed // args.ffn_events_every) % L
             if ffn_timed:
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
@@ -236,26 +282,35 @@ def main():
             moe.moe_combine(shape, b["y_perm"], b["y_shared"], b["topk_gate"], b["pos"],
                             x if stacked else None, b["out"], stream)
             x = b["out"]
+        if events:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
         for l in range(L):
-            moe.moe_update_bias(shape, bufs[l]["counts"], params[l]["bias"], 1e-3, stream)
+            moe.moe_update_bias(shape, bufs[l]["counts"], train_bias[l], 1e-3, stream)
+        if events:
+            e1.record(stream)
+            evb.append((e0, e1))
 
     for i in range(args.warmup):
-        step(i, False)
+        step(i, None)
     torch.cuda.synchronize()
-    # the bias moves every step, and with it the set of experts that receive
-    # rows; keep the starting biases to replay the timed steps afterwards
+    # the live bias moves every step, and with it the set of experts that
+    # receive rows; keep the starting biases to replay the timed steps afterwards
     bias0 = [params[l]["bias"].clone() for l in range(L)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     t_start.record(stream)
     for i in range(args.steps):
-        step(args.warmup + i, True)
+        step(args.warmup + i, i)
     t_end.record(stream)
     torch.cuda.synchronize()
     ms = t_start.elapsed_time(t_end) / args.steps
     tokens_per_s = wl.tokens * L / (ms * 1e-3)
 
-    ffn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    ffn_times = [a.elapsed_time(b) for a, b in ev]
+    ffn_ms = float(np.mean(ffn_times))
+    bias_ms = float(np.mean([a.elapsed_time(b) for a, b in evb]))
     # Algorithmic bytes per moe_grouped_ffn launch, averaged over the same
     # launches the events timed: replay the timed steps (untimed, from the
     # same biases) and read every layer's counts.
@@ -263,7 +318,7 @@ def main():
         params[l]["bias"].copy_(bias0[l])
     counts = []
     for i in range(args.steps):
-        step(args.warmup + i, False, counts)
+        step(args.warmup + i, None, counts)
     torch.cuda.synchronize()
     algo = ffn_algorithmic(wl, counts)
     flops = float(np.mean([f for f, _ in algo]))
@@ -281,17 +336,22 @@ def main():
     recorded = profiling.load_traffic(os.path.join(ROOT, "profiles"), wl.name)
     roof["traffic"] = recorded["hbm_bytes_per_launch"] if recorded else None
     if recorded:
+        # counter traffic also holds the h round trip, which the algorithmic
+        # bytes leave out
         roof["traffic_over_algorithmic"] = roof["traffic"] / byts
+        roof["h_round_trip_bytes"] = 2.0 * 2 * (wl.tokens * wl.top_k * wl.hidden
+                                                + wl.tokens * wl.shared_hidden)
     roof["kernel"] = ("moe_grouped_ffn = every grouped_gemm_kernel launch of one call "
                       "(SwiGLU and down stages; with streaming tiles the shared expert has its own)")
     roof["ms_per_launch"] = ffn_ms
+    roof["ms_per_launch_median"] = float(np.median(ffn_times))
+    roof["launches_timed"] = len(ffn_times)
     roof["algorithmic_flop"] = flops
     roof["algorithmic_bytes"] = byts
     roof["mfma_frac"] = flops / t_s / 1e12 / PEAK_BF16_TFLOPS
     roof["hbm_frac"] = byts / t_s / 1e9 / PEAK_HBM_GBS
     # time at the spec roofline (the slower of MFMA and HBM) over measured time
     roof["attainable_frac"] = max(flops / (PEAK_BF16_TFLOPS * 1e12), byts / (PEAK_HBM_GBS * 1e9)) / t_s
-    probes = hbm_read_probe()
     probe = max(probes.values())
     roof["hbm_read_probe_gbs"] = probe
     roof["hbm_read_probe_dma_gbs"] = probes["dma"]
@@ -310,11 +370,14 @@ def main():
                    "seq_len": wl.seq_len, "d_model": wl.d_model, "n_experts": wl.n_experts,
                    "top_k": wl.top_k, "hidden": wl.hidden, "shared_hidden": wl.shared_hidden,
                    "value_counts": "tokens x layers per second",
+                   "routing_bias": "frozen (inference); the update runs into a training copy"
+                                   if frozen else "live (updated every step)",
                    "parallelism": "none (1 GPU)"},
+        "update_bias_ms_per_step": bias_ms,
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, params[0], xs[0])
     print(json.dumps(line), flush=True)
 
 

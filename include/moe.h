@@ -15,7 +15,10 @@
  *     synchronises: each call only enqueues kernels on `stream` (a
  *     hipStream_t passed as void*; NULL means the default stream) and returns.
  *   - bf16 arrays are passed as uint16_t bit patterns.  Layouts are
- *     row-major and contiguous.
+ *     row-major and contiguous.  Every bf16 array must start on a 16-byte
+ *     boundary (the kernels move 16-byte chunks); a misaligned one returns
+ *     MOE_ERR_INVALID_ARGUMENT.  The workspace must start on a 256-byte
+ *     boundary (else MOE_ERR_WORKSPACE).
  *   - Arguments are checked on the host before anything is enqueued.  A bad
  *     argument returns MOE_ERR_INVALID_ARGUMENT (or MOE_ERR_UNSUPPORTED for a
  *     legal shape this build does not handle, MOE_ERR_WORKSPACE for a too

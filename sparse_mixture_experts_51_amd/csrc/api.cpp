@@ -184,8 +184,9 @@ moe_status moe_grouped_ffn(const moe_shape* shape, const uint16_t* x, const uint
   if (!x || !perm_src || !offsets || !w1 || !w3 || !w2 || !y_perm) return MOE_ERR_INVALID_ARGUMENT;
   if (shared != (ws1 && ws3 && ws2 && y_shared)) return MOE_ERR_INVALID_ARGUMENT;
   if (!shared && (ws1 || ws3 || ws2 || y_shared)) return MOE_ERR_INVALID_ARGUMENT;
-  const void* ptrs[] = {x, x_perm ? x_perm : x, w1, w3, w2, ws1 ? ws1 : w1, ws3 ? ws3 : w1,
-                        ws2 ? ws2 : w1};
+  // the GEMMs load and store 16-byte chunks of every bf16 array
+  const void* ptrs[] = {x,      x_perm ? x_perm : x, w1, w3, w2, ws1 ? ws1 : w1, ws3 ? ws3 : w1,
+                        ws2 ? ws2 : w1, y_perm, y_shared ? y_shared : y_perm};
   for (const void* p : ptrs)
     if (!aligned16(p)) return MOE_ERR_INVALID_ARGUMENT;
   if ((st = check_ws(shape, workspace, workspace_bytes)) != MOE_OK) return st;

@@ -6,12 +6,17 @@
 // which experts win but not their gate scores; sequence-wise balance loss
 // with weight 1e-4).
 //
-// Kernel 1 (router_scores): logits by an fp32 FMA chain over d in ascending
-// order, one chain per (token, expert) register, so every logit is the same
-// bit pattern on any hardware that does IEEE fused multiply-add.  This is a
-// SIMT fp32 GEMM (MFMA would reorder the sums); x and W_r are staged through
-// LDS with a register prefetch of the next d-chunk.  Scores = sigmoid in fp64,
-// rounded once to fp32.
+// Kernel 1 (router scores): logits by an fp32 FMA chain over d in ascending
+// order, so every logit is the same bit pattern on any hardware that does
+// IEEE fused multiply-add.  Two forms compute that same chain:
+//   - router_scores_kernel / router_fused_kernel: a SIMT fp32 GEMM, one chain
+//     per (token, expert) register, x and W_r staged through LDS with a
+//     register prefetch of the next d-chunk;
+//   - router_scores_mfma_kernel (many tokens, E a multiple of 64): the fp32
+//     matrix cores with K = 1 (v_mfma_f32_16x16x1_4b_f32).  One instruction
+//     adds one product to each output and rounds once, so a chain of them
+//     over d ascending is the fmaf chain; a wider K would reorder the sums.
+// Scores = sigmoid in fp64, rounded once to fp32.
 // Kernel 2 (select): one group of G lanes per token (G = 16, 32 or 64 as E
 // fits).  k+1 rounds of a 64-bit group max over (orderable key << 32 |
 // ~expert), reduced with DPP lane moves, pick the largest key with the

@@ -98,7 +98,7 @@ WORKLOADS = {
         "DeepSeek-V3-shaped decode step, 64 independent tokens"),
 }
 
-DEFAULT_BENCH_WORKLOAD = "mini_train_8192x6"
+DEFAULT_BENCH_WORKLOAD = "v3_prefill_4096"
 
 
 def _gen(device, seed: int) -> torch.Generator:

@@ -164,6 +164,12 @@ def test_grouped_ffn_argument_checks(L):
         moe.MOE_ERR_INVALID_ARGUMENT
     assert L.moe_grouped_ffn(ctypes.byref(s), *ok_args, fake(20), need - 256, None) == \
         moe.MOE_ERR_WORKSPACE
+    # misaligned outputs: the GEMM epilogue writes 16-byte chunks of y_perm and y_shared
+    for i in (10, 11):
+        args = list(ok_args)
+        args[i] = ctypes.c_void_p(A + 0x100000 * (i + 1) + 8)
+        assert L.moe_grouped_ffn(ctypes.byref(s), *args, fake(20), need, None) == \
+            moe.MOE_ERR_INVALID_ARGUMENT, i
 
 
 def test_combine_and_bias_argument_checks(L):

@@ -23,3 +23,22 @@ def test_unusable_step_counts_are_refused():
         r = run_bench(*args)
         assert r.returncode == 2, args
         assert r.stdout == "", args
+
+
+def test_unknown_workload_is_refused():
+    r = run_bench("--workload", "no_such_workload")
+    assert r.returncode == 2
+    assert "unknown workload" in r.stderr
+    assert r.stdout == ""
+
+
+def test_first_timed_step_always_records_events():
+    """Events go around the FFN of timed steps 0, N, 2N, ..., so any --steps
+    and --warmup give at least one timing (no empty mean, no NaN)."""
+    import ast
+    src = open(os.path.join(ROOT, "bench.py")).read()
+    tree = ast.parse(src)
+    step = next(n for n in ast.walk(tree) if isinstance(n, ast.FunctionDef) and n.name == "step")
+    text = ast.get_source_segment(src, step)
+    assert "timed % args.ffn_events_every == 0" in text
+    assert "step(args.warmup + i, i)" in src

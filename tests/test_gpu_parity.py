@@ -118,8 +118,13 @@ PERM_CASES = [(2048, 16, 4), (1000, 16, 4), (4096, 256, 8), (300, 1024, 32), (1,
               (777, 8, 2), (64, 256, 8)]
 # every case with and without the x_perm copy, plus the mini model's shape, a
 # single expert and eight choices per token without it
+# count tables of more than 16384 (block, expert) entries go through the
+# separate single-block scan kernel instead of the scan inside the scatter:
+# 79 token blocks x 256 experts and 20 x 1024
+PERM_SCAN_CASES = [(20000, 256, 8), (5000, 1024, 8)]
 PERM_RUNS = ([(T, E, k, True) for T, E, k in PERM_CASES] + [(T, E, k, False) for T, E, k in PERM_CASES]
-             + [(8192, 16, 4, False), (500, 1, 1, False), (3000, 16, 8, False)])
+             + [(8192, 16, 4, False), (500, 1, 1, False), (3000, 16, 8, False)]
+             + [(T, E, k, g) for T, E, k in PERM_SCAN_CASES for g in (True, False)])
 
 
 @pytest.mark.parametrize("T,E,k,gather", PERM_RUNS)
@@ -284,8 +289,14 @@ def test_combine_matches_oracle_with_residual():
             mag += np.abs(f32(bits(ys)).astype(np.float64))
         if r is not None:
             mag += np.abs(f32(bits(r)).astype(np.float64))
-        # both sides round once to bf16; before rounding they differ by the fp32
-        # accumulation error, at most (k+2) * 2^-24 * sum|terms|
+        # Both sides round once to bf16.  Before rounding they differ by the
+        # GPU's fp32 accumulation error, at most (k+2) * 2^-24 * sum|terms|
+        # (k+2 rounded additions, each off by at most 2^-24 of a partial sum
+        # no larger than sum|terms|); two roundings of values that close land
+        # at most one bf16 ulp (<= 2^-7 |ref|) apart.  Asserted:
+        #   |gpu - ref| <= 2^-7 |ref| + 2 (k+3) 2^-24 sum|terms|
+        # i.e. twice (2^-8 |ref| + (k+3) 2^-24 sum|terms|), the accumulation
+        # term with one spare rounding and a factor 2 of headroom.
         bound = np.abs(rr) * 2.0 ** -8 + (k + 3) * 2.0 ** -24 * mag + 1e-30
         assert np.all(np.abs(g - rr) <= 2 * bound)
         assert (g == rr).mean() > 0.99
