@@ -29,7 +29,9 @@
  *     still writes zero counts and offsets.
  *   - Outputs must not overlap inputs (except `bias` in moe_update_bias).
  *   - Calls are stateless and thread-safe; calls that share a workspace must
- *     be ordered (same stream, or synchronised).
+ *     be ordered (same stream, or synchronised).  The one exception is
+ *     moe_permute_noalloc, whose static per-GPU scratch is shared by all its
+ *     calls on that GPU (see there).
  *
  * Supported shapes: 1 <= E <= 1024, 1 <= k <= min(E, 32), d, H and Hs
  * multiples of 64, T*(k+1) < 2^31.  When seq_len > 0 it must divide T.
@@ -49,7 +51,8 @@ typedef enum moe_status {
   MOE_ERR_INVALID_ARGUMENT = 1,
   MOE_ERR_UNSUPPORTED = 2,
   MOE_ERR_WORKSPACE = 3,
-  MOE_ERR_HIP = 4
+  MOE_ERR_HIP = 4,
+  MOE_ERR_SCRATCH_LIMIT = 5 /* moe_permute_noalloc: shape beyond its static scratch */
 } moe_status;
 
 /* Layer shape.
@@ -131,6 +134,23 @@ moe_status moe_route(const moe_shape* shape, const uint16_t* x, const float* w_r
 moe_status moe_permute(const moe_shape* shape, const int32_t* topk_idx, int32_t* counts,
                        int32_t* offsets, int32_t* perm_src, int32_t* pos, const uint16_t* x,
                        uint16_t* x_perm, void* workspace, size_t workspace_bytes, void* stream);
+
+/* moe_permute without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments (minus the workspace), results, checks
+ * and error codes as moe_permute.  Its per-block count and first-row tables
+ * live in a static 2 MiB device array of the library, one per GPU, held
+ * until the process ends; the call allocates nothing.  Limit: the two tables
+ * take 2 * 4 * ceil(T/256) * E bytes (each rounded up to 256), at most 2 MiB,
+ * i.e. about T * E <= 67 million (T <= 262144 at E = 256); a larger shape
+ * returns MOE_ERR_SCRATCH_LIMIT and nothing is enqueued.  The array of the
+ * current device (hipGetDevice) is used, so `stream` must belong to that
+ * device.  Every call on one GPU shares that array: calls that may overlap
+ * on one GPU (different streams, or threads without ordering) race and must
+ * be serialised by the caller. */
+moe_status moe_permute_noalloc(const moe_shape* shape, const int32_t* topk_idx, int32_t* counts,
+                               int32_t* offsets, int32_t* perm_src, int32_t* pos,
+                               const uint16_t* x, uint16_t* x_perm, void* stream);
 
 /* Expert feed-forward networks over the expert groups, plus the shared
  * expert on every token (steps: grouped GEMM 1 with SwiGLU, grouped GEMM 2).

@@ -8,6 +8,7 @@
 #include <algorithm>
 #include <atomic>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/moe.h"
 #include "kernels.hpp"
@@ -97,6 +98,40 @@ moe_status check_ws(const moe_shape* s, void* ws, size_t bytes) {
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// ---- static scratch of moe_permute_noalloc
+// The per-block count and first-row tables of the permutation, for callers
+// that cannot allocate.  In host code `scratch` names a host-side stand-in,
+// not device memory: kernels get the device address that hipGetSymbolAddress
+// returns for the current device (each device holds its own copy).
+constexpr size_t kScratchBytes = size_t{2} << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];
+
+// Device address of this device's scratch, looked up once per device.
+moe_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+// Bytes of the permutation tables (the same carve-up as the workspace's).
+size_t permute_table_bytes(int64_t T, int E) {
+  const int tb = moe::perm_block_tokens(T);
+  const int64_t nblk = (T + tb - 1) / tb;
+  const size_t one = (sizeof(int32_t) * nblk * E + 255) / 256 * 256;
+  return 2 * one;
+}
+
 bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
 
 }  // namespace
@@ -110,6 +145,8 @@ const char* moe_status_str(int status) {
     case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: shape outside what this build handles";
     case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing, too small or misaligned";
     case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP launch failed";
+    case MOE_ERR_SCRATCH_LIMIT:
+      return "MOE_ERR_SCRATCH_LIMIT: shape needs more than the 2 MiB static scratch";
     default: return "unknown moe_status";
   }
 }
@@ -167,6 +204,29 @@ moe_status moe_permute(const moe_shape* shape, const int32_t* topk_idx, int32_t*
   // T == 0 still defines counts = 0 and offsets = 0: the kernels handle it.
   return hip_status(moe::launch_permute(topk_idx, counts, offsets, perm_src, pos, x, x_perm,
                                         w.blk_cnt, w.blk_base, shape->tokens, shape->d_model,
+                                        shape->n_experts, shape->top_k,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_permute_noalloc(const moe_shape* shape, const int32_t* topk_idx, int32_t* counts,
+                               int32_t* offsets, int32_t* perm_src, int32_t* pos,
+                               const uint16_t* x, uint16_t* x_perm, void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!counts || !offsets) return MOE_ERR_INVALID_ARGUMENT;
+  if (shape->tokens > 0 && (!topk_idx || !perm_src || !pos)) return MOE_ERR_INVALID_ARGUMENT;
+  if ((x == nullptr) != (x_perm == nullptr)) return MOE_ERR_INVALID_ARGUMENT;
+  if (x_perm && (!aligned16(x) || !aligned16(x_perm))) return MOE_ERR_INVALID_ARGUMENT;
+  const size_t need = permute_table_bytes(shape->tokens, shape->n_experts);
+  if (need > kScratchBytes) return MOE_ERR_SCRATCH_LIMIT;
+  void* base = nullptr;
+  if ((st = scratch_of_current_device(&base)) != MOE_OK) return st;
+  // the count kernel writes every count-table entry and the scan (when it
+  // runs) every first-row entry before they are read: nothing is cleared
+  int32_t* blk_cnt = static_cast<int32_t*>(base);
+  int32_t* blk_base = reinterpret_cast<int32_t*>(static_cast<unsigned char*>(base) + need / 2);
+  return hip_status(moe::launch_permute(topk_idx, counts, offsets, perm_src, pos, x, x_perm,
+                                        blk_cnt, blk_base, shape->tokens, shape->d_model,
                                         shape->n_experts, shape->top_k,
                                         static_cast<hipStream_t>(stream)));
 }

@@ -23,9 +23,10 @@ MOE_ERR_INVALID_ARGUMENT = 1
 MOE_ERR_UNSUPPORTED = 2
 MOE_ERR_WORKSPACE = 3
 MOE_ERR_HIP = 4
+MOE_ERR_SCRATCH_LIMIT = 5
 
 EXPORTED = ("moe_status_str", "moe_workspace_bytes", "moe_route", "moe_permute",
-            "moe_grouped_ffn", "moe_combine", "moe_update_bias")
+            "moe_permute_noalloc", "moe_grouped_ffn", "moe_combine", "moe_update_bias")
 
 
 class MoeError(RuntimeError):
@@ -83,6 +84,7 @@ def load() -> ctypes.CDLL:
     L.moe_workspace_bytes.argtypes = [S, ctypes.POINTER(ctypes.c_size_t)]
     L.moe_route.argtypes = [S, P, P, P, P, P, P, P, ctypes.c_float, P, ctypes.c_size_t, P]
     L.moe_permute.argtypes = [S, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    L.moe_permute_noalloc.argtypes = [S, P, P, P, P, P, P, P, P]
     L.moe_grouped_ffn.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     L.moe_combine.argtypes = [S, P, P, P, P, P, P, P]
     L.moe_update_bias.argtypes = [S, P, P, ctypes.c_float, P]
@@ -135,6 +137,13 @@ def moe_permute(shape: Shape, topk_idx, counts, offsets, perm_src, pos, x=None, 
     _ok(load().moe_permute(ctypes.byref(shape.c()), _p(topk_idx), _p(counts), _p(offsets),
                            _p(perm_src), _p(pos), _p(x), _p(x_perm), wp, wn, _s(stream)),
         "moe_permute")
+
+
+def moe_permute_noalloc(shape: Shape, topk_idx, counts, offsets, perm_src, pos, x=None,
+                        x_perm=None, stream=None):
+    _ok(load().moe_permute_noalloc(ctypes.byref(shape.c()), _p(topk_idx), _p(counts),
+                                   _p(offsets), _p(perm_src), _p(pos), _p(x), _p(x_perm),
+                                   _s(stream)), "moe_permute_noalloc")
 
 
 def moe_grouped_ffn(shape: Shape, x, x_perm, perm_src, offsets, w1, w3, w2, ws1, ws3, ws2,

@@ -184,8 +184,28 @@ def test_combine_and_bias_argument_checks(L):
         moe.MOE_ERR_INVALID_ARGUMENT
 
 
+def test_permute_noalloc_argument_checks_and_scratch_limit(L):
+    """moe_permute_noalloc checks like moe_permute and refuses shapes beyond its
+    2 MiB static scratch before touching the GPU."""
+    s = shape().c()
+    base = [fake(j) for j in range(5)]
+    for i in range(5):
+        args = list(base)
+        args[i] = None
+        assert L.moe_permute_noalloc(ctypes.byref(s), *args, None, None, None) == \
+            moe.MOE_ERR_INVALID_ARGUMENT
+    assert L.moe_permute_noalloc(ctypes.byref(s), *base, fake(6), None, None) == \
+        moe.MOE_ERR_INVALID_ARGUMENT
+    # two tables of 4 * ceil(T/256) * E bytes: 2 x 4 MiB here
+    big = shape(tokens=1 << 20, n_experts=256, top_k=8, seq_len=0, d_model=64, hidden=64,
+                shared_hidden=0).c()
+    assert L.moe_permute_noalloc(ctypes.byref(big), *base, None, None, None) == \
+        moe.MOE_ERR_SCRATCH_LIMIT
+    assert moe.status_str(moe.MOE_ERR_SCRATCH_LIMIT).startswith("MOE_ERR_SCRATCH_LIMIT")
+
+
 def test_status_strings(L):
-    for code in range(5):
+    for code in range(6):
         assert moe.status_str(code).startswith("MOE_")
     assert moe.status_str(99) == "unknown moe_status"
 
