@@ -37,9 +37,10 @@
 //            by LDS DMA in three stages.  For hundreds of rows per expert.
 //   kBigL    kBig plus 4 loader waves that issue the DMA, so the MFMA waves
 //            read fragments with plain LDS loads the compiler schedules.  For
-//            the shared expert when the routed experts stream (it then runs
-//            as a launch of its own, with long K): 10% faster there, no gain
-//            on the mini model's six K-steps per unit.
+//            long K: the shared expert when the routed experts stream (it then
+//            runs as a launch of its own; 10% faster than kBig there) and
+//            groups of hundreds of rows at d = 7168 (4% faster); no gain on
+//            the mini model's six K-steps per unit.
 //
 // Pipeline.  A block's units run as an outer loop; each unit's K-loop (64 of
 // K per step; with register-staged A an odd step count is padded by one
@@ -901,6 +902,7 @@ static bool streaming_shape(const GroupedGemmArgs& a) {
 // Groups of many rows (hundreds per expert and more): the 256x128 all-DMA
 // tile moves a third fewer bytes per MFMA than 128x128, holds no tile data
 // in registers and runs one step ahead.
+constexpr int kLongK = 1024;  // reduction length from which the loader-wave form is used
 static bool big_groups(const GroupedGemmArgs& a) {
   constexpr int kMinK = kBK * (kBig::NSA - 1);  // each unit at least D K-steps long
   if (a.K_r < kMinK || (a.w_shared && a.K_s < kMinK)) return false;
@@ -943,8 +945,15 @@ static hipError_t launch_gemm(const GroupedGemmArgs& a, hipStream_t s) {
     else launch_cfg<kCompute, kSwiGLU>(shared, s);
     return hipGetLastError();
   }
-  if (big_groups(a)) launch_cfg<kBig, kSwiGLU>(a, s);
-  else launch_cfg<kCompute, kSwiGLU>(a, s);
+  // With long K the loader-wave form pays off (about 1024 rows per expert at
+  // d = 7168, H = 2048: FFN 3.54 -> 3.39 ms, bit-identical); the mini model's
+  // four to six K-steps per unit gain nothing from it.
+  if (big_groups(a)) {
+    if (a.K_r >= kLongK && (!a.w_shared || a.K_s >= kLongK)) launch_cfg<kBigL, kSwiGLU>(a, s);
+    else launch_cfg<kBig, kSwiGLU>(a, s);
+  } else {
+    launch_cfg<kCompute, kSwiGLU>(a, s);
+  }
   return hipGetLastError();
 }
 

@@ -96,6 +96,14 @@ WORKLOADS = {
         "v3_decode_64", 5, 4, 64, 0, 7168, 256, 8, 2048, 2048, 1, 1,
         1.0, 0.006, 0.006, "uniform", 0.01, 0.0,
         "DeepSeek-V3-shaped decode step, 64 independent tokens"),
+    # The grouped-FFN shape one GPU holds under 8-way expert parallelism of the
+    # V3 layer (32 of the 256 experts, about 1024 rows each, the shared expert
+    # on the GPU's own 4096 tokens), built as a layer of 32 experts with top-8
+    # routing over 4096 tokens: the matrix-core-bound regime of the layer.
+    "v3_local32_4096": Workload(
+        "v3_local32_4096", 6, 6, 4096, 4096, 7168, 32, 8, 2048, 2048, 1, 1,
+        1.0, 0.006, 0.006, "uniform", 0.01, 0.0,
+        "V3 dims, 32 local experts top-8 over 4096 tokens (~1024 rows per expert)"),
 }
 
 DEFAULT_BENCH_WORKLOAD = "v3_prefill_4096"

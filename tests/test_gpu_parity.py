@@ -395,11 +395,22 @@ def v3_weights():
 
 @pytest.mark.parametrize("name", ["v3_prefill_4096", "v3_decode_64"])
 def test_v3_full_size(name, v3_weights):
+    full_size_check(name, v3_weights)
+
+
+def test_v3_local32_full_size():
+    """The matrix-core-bound shape (about 1024 rows per expert)."""
+    wl = workloads.WORKLOADS["v3_local32_4096"]
+    say("[v3] drawing the 32 experts of v3_local32_4096 on the GPU")
+    p = workloads.layer_params(wl, 0, DEV)
+    full_size_check(wl.name, p)
+
+
+def full_size_check(name, p):
     wl = workloads.WORKLOADS[name]
     shape = moe.Shape.of(wl)
     say(f"[v3] {name} T={wl.tokens}")
     x = workloads.tokens(wl, 0, DEV)
-    p = v3_weights
     bufs = run_layer(shape, x, p)
     g = gpu_host(bufs)
     ref = oracle.route(bits(x), host(p["w_router"]), host(p["bias"]), wl.top_k)
