@@ -86,6 +86,8 @@ def _declare(L):
     L.oracle_dense_masked.restype = None
     L.oracle_update_bias.argtypes = [I64, I32, I32, P, P, ctypes.c_float]
     L.oracle_update_bias.restype = None
+    L.oracle_rmsnorm.argtypes = [I64, I32, P, P, ctypes.c_double, P]
+    L.oracle_rmsnorm.restype = None
 
 
 def default_threads() -> int:
@@ -280,6 +282,26 @@ def update_bias(counts, bias, T: int, k: int, gamma: float = 1e-3) -> np.ndarray
     b = np.array(bias, dtype=np.float32, copy=True)
     lib().oracle_update_bias(T, b.shape[0], k, _p(c), _p(b), ctypes.c_float(gamma))
     return b
+
+
+def rmsnorm(x_bits, gain, eps: float = 1e-6) -> np.ndarray:
+    """RMSNorm of every row of x (bf16 bits [T, d]) with fp32 gain [d] -> bf16 bits."""
+    x = _c(x_bits, np.uint16)
+    g = _c(gain, np.float32)
+    T, d = x.shape
+    out = np.empty((T, d), np.uint16)
+    lib().oracle_rmsnorm(T, d, _p(x), _p(g), float(eps), _p(out))
+    return out
+
+
+def block(x_bits, params: dict, k: int, seq_len: int = 0, alpha: float = 1e-4,
+          eps: float = 1e-6, nthreads: int | None = None) -> dict:
+    """One pre-norm residual block: x + MoE(RMSNorm(x)); returns layer()'s
+    dict for the normalised input, plus "xn" (the norm's output)."""
+    xn = rmsnorm(x_bits, params["norm"], eps)
+    res = layer(xn, params, k, seq_len, alpha, residual=x_bits, nthreads=nthreads)
+    res["xn"] = xn
+    return res
 
 
 def layer(x_bits, params: dict, k: int, seq_len: int = 0, alpha: float = 1e-4,

@@ -494,6 +494,33 @@ void oracle_dense_masked(int64_t T, int d, int E, int k, int H, int Hs, const ui
 }
 
 /* ------------------------------------------------------------------ */
+/* RMSNorm before the MoE in a pre-norm residual block                 */
+/* ------------------------------------------------------------------ */
+
+/* The model's layers are pure functions over arrays, RMSNorm among them
+ * ([ZH] section "纯JAX"也需要打一个小星号), and the MoE sits in a residual
+ * Transformer block ([ZH] section 先说结论).  READING (the pages give
+ * neither the formula's constants nor the placement): a pre-norm block
+ * x_next = x + MoE(RMSNorm(x)), with
+ *   out[t,i] = bf16( x[t,i] / sqrt(mean_j x[t,j]^2 + eps) * g[i] )
+ * evaluated in fp64 and rounded once to bf16; g is the norm's learned fp32
+ * gain, eps is passed in (1e-6 in the workloads). */
+void oracle_rmsnorm(int64_t T, int d, const uint16_t* x, const float* g, double eps,
+                    uint16_t* out) {
+  for (int64_t t = 0; t < T; ++t) {
+    const uint16_t* xr = x + (size_t)t * d;
+    double ss = 0.0;
+    for (int i = 0; i < d; ++i) {
+      double v = (double)bf16_to_f32(xr[i]);
+      ss += v * v;
+    }
+    double r = 1.0 / sqrt(ss / (double)d + eps);
+    for (int i = 0; i < d; ++i)
+      out[(size_t)t * d + i] = f64_to_bf16((double)bf16_to_f32(xr[i]) * r * (double)g[i]);
+  }
+}
+
+/* ------------------------------------------------------------------ */
 /* Bias update (step a11)                                              */
 /* ------------------------------------------------------------------ */
 

@@ -454,3 +454,74 @@ def test_bias_update_balanced_is_noop(oracle_lib):
     b = np.linspace(-0.3, 0.3, 16).astype(np.float32)
     out = oracle_lib.update_bias(np.full(16, 128, np.int32), b, 512, 4)
     assert np.array_equal(out, b)
+
+
+# ---------------------------------------------------------------- RMSNorm
+
+def test_rmsnorm_hand_example(oracle_lib):
+    g = gold("hand_rmsnorm_d4.json")
+    out = oracle_lib.rmsnorm(bf16_bits([g["x"]]), np.array(g["gain"], np.float32), g["eps"])
+    assert out[0].tolist() == g["out_bits"]
+
+
+def test_rmsnorm_constant_rows_give_the_gain(oracle_lib):
+    # a constant row c has rms |c|: each output is sign(c) * g_i exactly
+    d = 64
+    gain = np.array([0.5, 2.0, -1.0, 1.5] * (d // 4), np.float32)
+    x = bf16_bits([[3.0] * d, [-0.25] * d, [1e-3] * d])
+    out = oracle_lib.bf16_bits_to_f32(oracle_lib.rmsnorm(x, gain, 0.0))
+    assert np.array_equal(out[0], gain)
+    assert np.array_equal(out[1], -gain)
+    assert np.array_equal(out[2], gain)
+
+
+def test_rmsnorm_scale_invariance_and_gain_index(oracle_lib):
+    rng = np.random.default_rng(7)
+    T, d = 9, 384
+    xf = rng.standard_normal((T, d)).astype(np.float32)
+    x = bf16_bits(xf)
+    ones = np.ones(d, np.float32)
+    base = oracle_lib.rmsnorm(x, ones, 0.0)
+    # scaling a row by a power of two changes nothing (eps = 0)
+    x8 = bf16_bits(oracle_lib.bf16_bits_to_f32(x) * 8.0)
+    assert np.array_equal(oracle_lib.rmsnorm(x8, ones, 0.0), base)
+    # a power-of-two gain per column scales exactly that column
+    gain = (2.0 ** (np.arange(d) % 3 - 1)).astype(np.float32)
+    scaled = oracle_lib.bf16_bits_to_f32(oracle_lib.rmsnorm(x, gain, 0.0))
+    assert np.array_equal(scaled, oracle_lib.bf16_bits_to_f32(base) * gain)
+    # rows are independent: permuting rows permutes the outputs
+    perm = rng.permutation(T)
+    assert np.array_equal(oracle_lib.rmsnorm(x[perm], ones, 0.0), base[perm])
+    # the output's mean square is 1 within one bf16 rounding per element
+    o = oracle_lib.bf16_bits_to_f32(base).astype(np.float64)
+    assert np.all(np.abs((o ** 2).mean(axis=1) - 1.0) < 2 * 2.0 ** -8)
+
+
+def test_rmsnorm_eps_and_zero_row(oracle_lib):
+    d = 128
+    x = bf16_bits([[0.0] * d, [1e-4] * d])
+    out = oracle_lib.bf16_bits_to_f32(oracle_lib.rmsnorm(x, np.ones(d, np.float32), 1e-6))
+    assert np.all(out[0] == 0.0)  # no NaN from 0/0
+    # eps enters under the root: 1e-4 / sqrt(1e-8 + 1e-6) = 0.0995037...
+    expect = 1e-4 / math.sqrt(1e-8 + 1e-6)
+    assert np.all(np.abs(out[1] - expect) <= 2.0 ** -8 * expect)
+    assert not np.allclose(out[1], 1.0)  # eps = 0 would give 1
+
+
+def test_block_with_zero_experts_is_the_residual(oracle_lib):
+    """x + MoE(RMSNorm(x)) with every expert weight zero returns x itself: the
+    residual is the block's input, not its normalised input."""
+    rng = np.random.default_rng(3)
+    T, d, E, k, H = 40, 64, 8, 2, 64
+    x = bf16_bits(rng.standard_normal((T, d)))
+    p = {"norm": (1 + 0.1 * rng.standard_normal(d)).astype(np.float32),
+         "w_router": (0.1 * rng.standard_normal((d, E))).astype(np.float32),
+         "bias": np.zeros(E, np.float32),
+         "w1": np.zeros((E, H, d), np.uint16), "w3": np.zeros((E, H, d), np.uint16),
+         "w2": np.zeros((E, d, H), np.uint16), "ws1": np.zeros((H, d), np.uint16),
+         "ws3": np.zeros((H, d), np.uint16), "ws2": np.zeros((d, H), np.uint16)}
+    r = oracle_lib.block(x, p, k)
+    assert np.array_equal(r["out"], x)
+    assert np.array_equal(r["xn"], oracle_lib.rmsnorm(x, p["norm"], 1e-6))
+    # routing saw the normalised input
+    assert np.array_equal(r["idx"], oracle_lib.route(r["xn"], p["w_router"], p["bias"], k)["idx"])
