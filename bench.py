@@ -4,7 +4,8 @@
 
 A step is one pass of the whole hot path over one batch: for every layer of
 the workload, moe_route -> moe_permute -> moe_grouped_ffn -> moe_combine
-(the combine also adds the residual stream of stacked layers), then
+(the combine also adds the residual stream of stacked layers; pre-norm block
+workloads run moe_rmsnorm first and route the normalised rows), then
 moe_update_bias for every layer.  Inputs are seeded synthetic tensors already
 resident in HBM before the timed region.  Prints ONE JSON line.
 
@@ -161,13 +162,17 @@ def cpu_baseline(wl, target_s: float, params_dev=None, x_dev=None):
                          for k, v in p.items()}
             xb = oracle.as_bf16_bits(workloads.tokens(wl, st, "cpu"))
             t0 = time.perf_counter()
-            oracle.layer(xb, hp[l], wl.top_k, seq_len=wl.seq_len, nthreads=threads)
+            if wl.norm:
+                oracle.block(xb, hp[l], wl.top_k, seq_len=wl.seq_len, nthreads=threads)
+            else:
+                oracle.layer(xb, hp[l], wl.top_k, seq_len=wl.seq_len, nthreads=threads)
             dt += time.perf_counter() - t0
             done += 1
         return {"value": done * wl.tokens / dt, "unit": "tokens/s", **host,
                 "kind": "oracle",
-                "sample": f"{done} layer passes over all {wl.tokens} tokens of {wl.name} (route, "
-                          f"balance statistic, permute, grouped FFN, combine), fp64 oracle, "
+                "sample": f"{done} layer passes over all {wl.tokens} tokens of {wl.name} ("
+                          f"{'RMSNorm, ' if wl.norm else ''}route, balance statistic, permute, "
+                          f"grouped FFN, combine), fp64 oracle, "
                           f"{dt:.1f} s on {threads} threads; counts tokens x layers per second"}
 
     import concurrent.futures as cf
@@ -273,7 +278,11 @@ def main():
         for l in range(L):
             b, p = bufs[l], params[l]
             ws = b["workspace"]
-            moe.moe_route(shape, x, p["w_router"], p["bias"], b["topk_idx"], b["topk_gate"],
+            xin = x
+            if wl.norm:  # pre-norm block: the MoE sees RMSNorm(x), the residual is x
+                moe.moe_rmsnorm(shape, x, p["norm"], 1e-6, b["xn"], stream)
+                xin = b["xn"]
+            moe.moe_route(shape, xin, p["w_router"], p["bias"], b["topk_idx"], b["topk_gate"],
                           b["margin"], b["seq_balance"], 1e-4, ws, stream)
             moe.moe_permute(shape, b["topk_idx"], b["counts"], b["offsets"], b["perm_src"],
                             b["pos"], None, None, ws, stream)
@@ -287,14 +296,14 @@ def main():
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
-            moe.moe_grouped_ffn(shape, x, None, b["perm_src"], b["offsets"], p["w1"], p["w3"],
+            moe.moe_grouped_ffn(shape, xin, None, b["perm_src"], b["offsets"], p["w1"], p["w3"],
                                 p["w2"], p.get("ws1"), p.get("ws3"), p.get("ws2"), b["y_perm"],
                                 b["y_shared"], ws, stream)
             if ffn_timed:
                 e1.record(stream)
                 ev.append((e0, e1))
             moe.moe_combine(shape, b["y_perm"], b["y_shared"], b["topk_gate"], b["pos"],
-                            x if stacked else None, b["out"], stream)
+                            x if stacked or wl.norm else None, b["out"], stream)
             x = b["out"]
         if events:
             e0 = torch.cuda.Event(enable_timing=True)

@@ -1,9 +1,11 @@
 /*
  * moe.h -- C ABI of libmoe.so: the DeepSeekMoE layer forward on gfx950.
  *
- * Five calls make one layer forward, in this order, on one HIP stream:
+ * Four calls make one layer forward, in this order, on one HIP stream:
  *   moe_route -> moe_permute -> moe_grouped_ffn -> moe_combine
- * and, once per training step and layer, moe_update_bias.
+ * and, once per training step and layer, moe_update_bias.  In a pre-norm
+ * residual block moe_rmsnorm comes first and the block's input is
+ * moe_combine's residual.
  *
  * Pages cited (title, then section):
  *   [ZH] "190行JAX复刻DeepSeek V3" (openai-hub.com news)
@@ -184,6 +186,21 @@ moe_status moe_grouped_ffn(const moe_shape* shape, const uint16_t* x, const uint
  *   topk_gate [T, k] fp32, pos [T, k] int32 (in); out [T, d] bf16 (out)   */
 moe_status moe_combine(const moe_shape* shape, const uint16_t* y_perm, const uint16_t* y_shared,
                        const float* topk_gate, const int32_t* pos, const uint16_t* residual,
+                       uint16_t* out, void* stream);
+
+/* RMSNorm of the token rows, the input of the MoE in a pre-norm residual
+ * block x_next = x + MoE(RMSNorm(x)): for every row t,
+ *   out[t,i] = bf16( x[t,i] / sqrt(mean_j x[t,j]^2 + eps) * gain[i] )
+ * with the mean of squares accumulated in fp32.  The pages list RMSNorm among
+ * the model's functions ([ZH] "纯JAX"也需要打一个小星号) and place the MoE in a
+ * residual Transformer block ([ZH] 先说结论); the pre-norm placement is a
+ * stated reading.  The block's residual add is moe_combine's `residual`.
+ * Only shape->tokens and shape->d_model are used (the shape is checked as
+ * for the other calls).
+ *   x [T, d] bf16 (in); gain [d] fp32 (in, 16-byte aligned); out [T, d] bf16
+ *   (out, must not overlap x); eps >= 0 and finite (else
+ *   MOE_ERR_INVALID_ARGUMENT; 1e-6 in the workloads)                   */
+moe_status moe_rmsnorm(const moe_shape* shape, const uint16_t* x, const float* gain, float eps,
                        uint16_t* out, void* stream);
 
 /* Auxiliary-loss-free balancing (step: bias update), once per step and layer:

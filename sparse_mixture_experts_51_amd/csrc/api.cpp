@@ -314,6 +314,18 @@ moe_status moe_combine(const moe_shape* shape, const uint16_t* y_perm, const uin
                                         static_cast<hipStream_t>(stream)));
 }
 
+moe_status moe_rmsnorm(const moe_shape* shape, const uint16_t* x, const float* gain, float eps,
+                       uint16_t* out, void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!(eps >= 0.0f) || eps > 3.0e38f) return MOE_ERR_INVALID_ARGUMENT;  // also rejects NaN
+  if (shape->tokens == 0) return MOE_OK;
+  if (!x || !gain || !out) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(x) || !aligned16(gain) || !aligned16(out)) return MOE_ERR_INVALID_ARGUMENT;
+  return hip_status(moe::launch_rmsnorm(x, gain, eps, out, shape->tokens, shape->d_model,
+                                        static_cast<hipStream_t>(stream)));
+}
+
 moe_status moe_update_bias(const moe_shape* shape, const int32_t* counts, float* bias,
                            float gamma, void* stream) {
   moe_status st = check_shape(shape);

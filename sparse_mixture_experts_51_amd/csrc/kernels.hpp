@@ -80,6 +80,8 @@ hipError_t launch_gemm_down(const GroupedGemmArgs& a, hipStream_t s);
 hipError_t launch_combine(const uint16_t* y_perm, const uint16_t* y_shared, const float* gate,
                           const int32_t* pos, const uint16_t* residual, uint16_t* out,
                           int64_t T, int d, int k, hipStream_t s);
+hipError_t launch_rmsnorm(const uint16_t* x, const float* gain, float eps, uint16_t* out,
+                          int64_t T, int d, hipStream_t s);
 hipError_t launch_update_bias(const int32_t* counts, float* bias, float gamma, int64_t T, int E,
                               int k, hipStream_t s);
 

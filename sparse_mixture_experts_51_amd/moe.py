@@ -26,7 +26,8 @@ MOE_ERR_HIP = 4
 MOE_ERR_SCRATCH_LIMIT = 5
 
 EXPORTED = ("moe_status_str", "moe_workspace_bytes", "moe_route", "moe_permute",
-            "moe_permute_noalloc", "moe_grouped_ffn", "moe_combine", "moe_update_bias")
+            "moe_permute_noalloc", "moe_grouped_ffn", "moe_combine", "moe_rmsnorm",
+            "moe_update_bias")
 
 
 class MoeError(RuntimeError):
@@ -87,6 +88,7 @@ def load() -> ctypes.CDLL:
     L.moe_permute_noalloc.argtypes = [S, P, P, P, P, P, P, P, P]
     L.moe_grouped_ffn.argtypes = [S, P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     L.moe_combine.argtypes = [S, P, P, P, P, P, P, P]
+    L.moe_rmsnorm.argtypes = [S, P, P, ctypes.c_float, P, P]
     L.moe_update_bias.argtypes = [S, P, P, ctypes.c_float, P]
     for name in EXPORTED[1:]:
         getattr(L, name).restype = ctypes.c_int
@@ -159,6 +161,11 @@ def moe_combine(shape: Shape, y_perm, y_shared, topk_gate, pos, residual, out, s
                            _p(pos), _p(residual), _p(out), _s(stream)), "moe_combine")
 
 
+def moe_rmsnorm(shape: Shape, x, gain, eps: float, out, stream=None):
+    _ok(load().moe_rmsnorm(ctypes.byref(shape.c()), _p(x), _p(gain), ctypes.c_float(eps), _p(out),
+                           _s(stream)), "moe_rmsnorm")
+
+
 def moe_update_bias(shape: Shape, counts, bias, gamma: float = 1e-3, stream=None):
     _ok(load().moe_update_bias(ctypes.byref(shape.c()), _p(counts), _p(bias),
                                ctypes.c_float(gamma), _s(stream)), "moe_update_bias")
@@ -186,6 +193,7 @@ def alloc_buffers(shape: Shape, device="cuda", x_perm: bool = False) -> dict:
         "y_perm": torch.empty((T * k, d), dtype=b16, device=device),
         "y_shared": torch.empty((T, d), dtype=b16, device=device) if shape.shared_hidden else None,
         "out": torch.empty((T, d), dtype=b16, device=device),
+        "xn": torch.empty((T, d), dtype=b16, device=device),  # RMSNorm output of a block
         "workspace": torch.empty((max(ws_bytes, 256),), dtype=torch.uint8, device=device),
     }
 
@@ -205,3 +213,10 @@ def layer_forward(shape: Shape, x, params: dict, bufs: dict, residual=None, alph
     moe_combine(shape, bufs["y_perm"], bufs["y_shared"], bufs["topk_gate"], bufs["pos"], residual,
                 bufs["out"], stream)
     return bufs["out"]
+
+
+def block_forward(shape: Shape, x, params: dict, bufs: dict, eps: float = 1e-6,
+                  alpha: float = 1e-4, stream=None):
+    """Pre-norm residual block: out = x + MoE(RMSNorm(x)), all on one stream."""
+    moe_rmsnorm(shape, x, params["norm"], eps, bufs["xn"], stream)
+    return layer_forward(shape, bufs["xn"], params, bufs, residual=x, alpha=alpha, stream=stream)

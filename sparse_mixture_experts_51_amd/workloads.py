@@ -41,6 +41,7 @@ ROLE_WS1 = 6
 ROLE_WS3 = 7
 ROLE_WS2 = 8
 ROLE_IMBALANCE = 9
+ROLE_NORM = 10
 
 
 def seed_of(cfg: int, layer: int, role: int, expert: int = -1, step: int = 0) -> int:
@@ -68,6 +69,7 @@ class Workload:
     bias_range: float
     imbalance: float     # 0: none; else half-width c of the per-expert logit offsets
     description: str = ""
+    norm: bool = False   # pre-norm residual block: x + MoE(RMSNorm(x))
 
     @property
     def rows(self) -> int:
@@ -104,6 +106,15 @@ WORKLOADS = {
         "v3_local32_4096", 6, 6, 4096, 4096, 7168, 32, 8, 2048, 2048, 1, 1,
         1.0, 0.006, 0.006, "uniform", 0.01, 0.0,
         "V3 dims, 32 local experts top-8 over 4096 tokens (~1024 rows per expert)"),
+    # The pages' small configuration: 4 layers, 8 experts, top-2 routing and a
+    # 128-token context (190行JAX复刻DeepSeek V3, section 如何在Mac上复现), as
+    # pre-norm residual blocks over 32 sequences; d_model and the expert
+    # sizes are the mini model's (the pages do not give them).
+    "small_block_4096x4": Workload(
+        "small_block_4096x4", 7, 7, 4096, 128, 384, 8, 2, 256, 256, 4, 10,
+        1.0, 0.02, 0.02, "uniform", 0.05, 0.0,
+        "small configuration: 4 pre-norm blocks, 8 experts top-2, 32 seqs x 128 tokens",
+        norm=True),
 }
 
 DEFAULT_BENCH_WORKLOAD = "v3_prefill_4096"
@@ -202,8 +213,17 @@ def shared_weights(wl: Workload, layer: int = 0, device="cpu") -> dict:
     }
 
 
+def norm_gain(wl: Workload, layer: int = 0, device="cpu") -> torch.Tensor:
+    """RMSNorm gain [d] fp32, N(1, 0.1^2): the spread of a trained gain, so
+    that a gain applied to the wrong column shows."""
+    g = normal((wl.d_model,), 0.1, seed_of(wl.weight_cfg_id, layer, ROLE_NORM), device)
+    return g.add_(1.0)
+
+
 def layer_params(wl: Workload, layer: int = 0, device="cpu") -> dict:
     p = {"w_router": router(wl, layer, device), "bias": bias(wl, layer, device)}
+    if wl.norm:
+        p["norm"] = norm_gain(wl, layer, device)
     p.update(expert_weights(wl, layer, device))
     p.update(shared_weights(wl, layer, device))
     return p

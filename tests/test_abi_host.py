@@ -204,6 +204,28 @@ def test_permute_noalloc_argument_checks_and_scratch_limit(L):
     assert moe.status_str(moe.MOE_ERR_SCRATCH_LIMIT).startswith("MOE_ERR_SCRATCH_LIMIT")
 
 
+def test_rmsnorm_argument_checks(L):
+    s = shape().c()
+    f = ctypes.c_float
+    for i in range(3):
+        args = [fake(0), fake(1), fake(2)]
+        args[i] = None
+        assert L.moe_rmsnorm(ctypes.byref(s), args[0], args[1], f(1e-6), args[2], None) == \
+            moe.MOE_ERR_INVALID_ARGUMENT
+    for eps in (-1.0, float("nan"), float("inf")):
+        assert L.moe_rmsnorm(ctypes.byref(s), fake(0), fake(1), f(eps), fake(2), None) == \
+            moe.MOE_ERR_INVALID_ARGUMENT, eps
+    for i in range(3):  # every array 16-byte aligned
+        args = [fake(0), fake(1), fake(2)]
+        args[i] = ctypes.c_void_p(A + 0x100000 * (i + 1) + 4)
+        assert L.moe_rmsnorm(ctypes.byref(s), args[0], args[1], f(1e-6), args[2], None) == \
+            moe.MOE_ERR_INVALID_ARGUMENT, i
+    z = shape(tokens=0, seq_len=0).c()
+    assert L.moe_rmsnorm(ctypes.byref(z), None, None, f(1e-6), None, None) == moe.MOE_OK
+    assert L.moe_rmsnorm(ctypes.byref(shape(d_model=100).c()), fake(0), fake(1), f(1e-6), fake(2),
+                         None) == moe.MOE_ERR_UNSUPPORTED
+
+
 def test_status_strings(L):
     for code in range(6):
         assert moe.status_str(code).startswith("MOE_")

@@ -302,6 +302,88 @@ def test_combine_matches_oracle_with_residual():
         assert (g == rr).mean() > 0.99
 
 
+def bf16_ulp_diff(a_bits, b_bits):
+    """Distance in bf16 steps between two arrays of finite bf16 bit patterns."""
+    def key(b):
+        b = np.asarray(b).astype(np.int64)
+        return np.where(b & 0x8000, -(b & 0x7FFF), b)
+    return np.abs(key(a_bits) - key(b_bits))
+
+
+# (T, d): one chunk per lane and less (d = 64, 384), 2, 4, 8 and 16 chunks per
+# lane in registers (d = 1024 ... 8192, the V3 width among them), and the
+# re-reading path (d = 16384); ragged row counts against four rows per block
+NORM_CASES = [(1000, 384), (33, 64), (5, 1024), (4096, 7168), (7, 8192), (3, 16384), (1, 128)]
+
+
+@pytest.mark.parametrize("T,d", NORM_CASES)
+def test_rmsnorm_matches_oracle(T, d):
+    say(f"[rmsnorm] T={T} d={d}")
+    gen = torch.Generator(device=DEV).manual_seed(T * 7 + d)
+    x = torch.randn(T, d, device=DEV, generator=gen).to(torch.bfloat16)
+    if T > 2:
+        x[1] = 0.0      # a zero row: eps keeps it finite
+        x[2] = -0.375   # a constant row
+    gain = 1.0 + 0.3 * torch.randn(d, device=DEV, generator=gen)
+    out = torch.empty_like(x)
+    shape = moe.Shape(T, d, 8, 2, 64, 0, 0)
+    moe.moe_rmsnorm(shape, x, gain, 1e-6, out)
+    torch.cuda.synchronize()
+    ref = oracle.rmsnorm(bits(x), host(gain), 1e-6)
+    g = bits(out)
+    diff = bf16_ulp_diff(g, ref)
+    # fp32 sum and product against the oracle's fp64: the roundings to bf16
+    # may differ by one step where the value lies within ~2^-23 of a midpoint
+    say(f"  max bf16 steps {diff.max()}, differing elements {(diff > 0).mean():.2e}")
+    assert diff.max() <= 1
+    assert (diff > 0).mean() < 1e-3
+    if T > 2:
+        assert not (g[1] & 0x7FFF).any()  # +-0 (a negative gain gives -0)
+
+
+def test_small_config_blocks_teacher_forced():
+    """The pages' small configuration (4 layers, 8 experts, top-2, 128-token
+    sequences) as pre-norm residual blocks, two steps with the bias update in
+    between.  Each layer's oracle input is the GPU's layer input (teacher
+    forcing); the norm, routing, loads and bias are compared exactly (the
+    norm to one bf16 step), the block outputs on sampled tokens."""
+    wl = workloads.WORKLOADS["small_block_4096x4"]
+    shape = moe.Shape.of(wl)
+    params = [workloads.layer_params(wl, l, DEV) for l in range(wl.layers)]
+    bufs = [moe.alloc_buffers(shape, DEV) for _ in range(wl.layers)]
+    sample = np.arange(0, wl.tokens, 37)
+    for step in range(2):
+        x = workloads.tokens(wl, step, DEV)
+        for l in range(wl.layers):
+            say(f"[small] step {step} layer {l}")
+            b_before = host(params[l]["bias"]).copy()
+            moe.block_forward(shape, x, params[l], bufs[l])
+            torch.cuda.synchronize()
+            g = gpu_host(bufs[l])
+            hp = host_params(params[l])
+            hp["bias"] = b_before
+            xb = bits(x)
+            xn_ref = oracle.rmsnorm(xb, hp["norm"], 1e-6)
+            assert bf16_ulp_diff(g["xn"], xn_ref).max() <= 1
+            # routing on the GPU's normalised rows, exact
+            ref = oracle.route(g["xn"], hp["w_router"], b_before, wl.top_k)
+            check_routing(g, ref, f"step{step}.layer{l}")
+            pm = oracle.permute(g["topk_idx"], wl.n_experts)
+            for key in ("counts", "offsets", "perm_src", "pos"):
+                assert np.array_equal(g[key], pm[key]), key
+            L = oracle.seq_balance(ref["scores"], g["topk_idx"], wl.seq_len, 1e-4)
+            assert np.abs(g["seq_balance"] - L).max() / np.abs(L).max() <= 1e-5
+            lo = oracle.layer(g["xn"][sample], hp, wl.top_k, residual=xb[sample])
+            check_bf16_close(g["out"][sample], lo["out"], f"step{step}.layer{l}.out")
+            x = bufs[l]["out"].clone()
+        for l in range(wl.layers):
+            b_before = host(params[l]["bias"]).copy()
+            moe.moe_update_bias(shape, bufs[l]["counts"], params[l]["bias"], 1e-3)
+            torch.cuda.synchronize()
+            ref_b = oracle.update_bias(host(bufs[l]["counts"]), b_before, wl.tokens, wl.top_k)
+            assert np.array_equal(host(params[l]["bias"]), ref_b)
+
+
 def test_update_bias_matches_oracle_bit_exact():
     for T, E, k in ((8192, 16, 4), (4096, 256, 8), (10, 1000, 3)):
         gen = torch.Generator().manual_seed(E)
