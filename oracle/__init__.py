@@ -88,6 +88,13 @@ def _declare(L):
     L.oracle_update_bias.restype = None
     L.oracle_rmsnorm.argtypes = [I64, I32, P, P, ctypes.c_double, P]
     L.oracle_rmsnorm.restype = None
+    L.oracle_moe_backward.argtypes = [I64, I32, I32, I32, I32, I32, I32, ctypes.c_double,
+                                      P, P, P, P, P, P, P, P, P, P, I32, P, P, P, P, P, P, P, P,
+                                      I32]
+    L.oracle_moe_backward.restype = None
+    L.oracle_moe_forward_f64.argtypes = [I64, I32, I32, I32, I32, I32, I32, ctypes.c_double,
+                                         P, P, P, P, P, P, P, P, P, P, P]
+    L.oracle_moe_forward_f64.restype = None
 
 
 def default_threads() -> int:
@@ -282,6 +289,69 @@ def update_bias(counts, bias, T: int, k: int, gamma: float = 1e-3) -> np.ndarray
     b = np.array(bias, dtype=np.float32, copy=True)
     lib().oracle_update_bias(T, b.shape[0], k, _p(c), _p(b), ctypes.c_float(gamma))
     return b
+
+
+def _f64(a) -> np.ndarray:
+    """bf16 bit patterns (uint16 / int16) or real numbers -> fp64 array."""
+    a = np.asarray(a)
+    if a.dtype in (np.uint16, np.int16):
+        a = bf16_bits_to_f32(a.view(np.uint16))
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _bwd_weights(params: dict, H: int, d: int):
+    w = [_f64(params[n]) for n in ("w1", "w3", "w2")]
+    if params.get("ws1") is not None:
+        ws = [_f64(params[n]) for n in ("ws1", "ws3", "ws2")]
+    else:
+        ws = [None, None, None]
+    return w, ws
+
+
+def layer_backward(x, params: dict, idx, dout, seq_len: int = 0, alpha: float = 1e-4,
+                   round_storage: bool = True, nthreads: int | None = None) -> dict:
+    """Gradient of sum_t <dout[t], out[t]> + sum_b L_b with respect to x, the
+    router and the expert weights, the choice of experts `idx` held fixed
+    (fp64 results).  x and dout: bf16 bits or reals; params as for layer()."""
+    xd, dd = _f64(x), _f64(dout)
+    wr = _f64(params["w_router"])
+    ix = _c(idx, np.int32)
+    T, d = xd.shape
+    E = wr.shape[1]
+    k = ix.shape[1]
+    (w1, w3, w2), (ws1, ws3, ws2) = _bwd_weights(params, 0, d)
+    H = w1.shape[1]
+    Hs = ws1.shape[0] if ws1 is not None else 0
+    out = {"dx": np.empty((T, d)), "dw_router": np.empty((d, E)),
+           "dw1": np.empty_like(w1), "dw3": np.empty_like(w3), "dw2": np.empty_like(w2),
+           "dws1": np.empty_like(ws1) if Hs else None, "dws3": np.empty_like(ws3) if Hs else None,
+           "dws2": np.empty_like(ws2) if Hs else None}
+    lib().oracle_moe_backward(T, d, E, k, H, Hs, seq_len, float(alpha), _p(xd), _p(wr), _p(ix),
+                              _p(w1), _p(w3), _p(w2), _p(ws1), _p(ws3), _p(ws2), _p(dd),
+                              int(bool(round_storage)), _p(out["dx"]), _p(out["dw_router"]),
+                              _p(out["dw1"]), _p(out["dw3"]), _p(out["dw2"]), _p(out["dws1"]),
+                              _p(out["dws3"]), _p(out["dws2"]), nthreads or default_threads())
+    return out
+
+
+def forward_f64(x, params: dict, idx, seq_len: int = 0, alpha: float = 1e-4):
+    """The layer in fp64 with the choice of experts held fixed and nothing
+    rounded (no residual): returns (out [T,d], sum of the balance statistic)."""
+    xd = _f64(x)
+    wr = _f64(params["w_router"])
+    ix = _c(idx, np.int32)
+    T, d = xd.shape
+    E = wr.shape[1]
+    k = ix.shape[1]
+    (w1, w3, w2), (ws1, ws3, ws2) = _bwd_weights(params, 0, d)
+    H = w1.shape[1]
+    Hs = ws1.shape[0] if ws1 is not None else 0
+    out = np.empty((T, d))
+    lb = ctypes.c_double(0.0)
+    lib().oracle_moe_forward_f64(T, d, E, k, H, Hs, seq_len, float(alpha), _p(xd), _p(wr),
+                                 _p(ix), _p(w1), _p(w3), _p(w2), _p(ws1), _p(ws3), _p(ws2),
+                                 _p(out), ctypes.byref(lb))
+    return out, lb.value
 
 
 def rmsnorm(x_bits, gain, eps: float = 1e-6) -> np.ndarray:

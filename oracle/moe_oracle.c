@@ -521,6 +521,307 @@ void oracle_rmsnorm(int64_t T, int d, const uint16_t* x, const float* g, double 
 }
 
 /* ------------------------------------------------------------------ */
+/* Backward of the layer (training)                                    */
+/* ------------------------------------------------------------------ */
+
+/* The pages' workload is training: the model is trained for 12000 steps with
+ * AdamW ([ZH] section 如何在Mac上复现), on a loss that adds the small
+ * sequence-wise balance loss to the language-model loss ([ZH] section
+ * 多Token预测也被保留了), while the per-expert bias stays outside the loss and
+ * only moves the choice of experts ([ZH] section 最有价值的实验).
+ *
+ * With the choice of experts held fixed (it is piecewise constant), the
+ * layer's output out[t] = r[t] + ys[t] + sum_j g[t,j] y[t,j] and the balance
+ * statistic sum_b L_b are smooth functions of x and the weights.  For an
+ * upstream gradient dout this computes the gradient of
+ *   L = sum_t <dout[t], out[t]> + sum_b L_b
+ * with respect to x, W_r and every expert weight, by the chain rule written
+ * out step by step (the residual r passes dout through and is left to the
+ * caller; the bias has no gradient).
+ *
+ * round_storage = 0: everything in fp64, no rounding -- the exact gradient of
+ * the fp64 layer (oracle_moe_forward_f64), which finite differences pin.
+ * round_storage = 1: the values the GPU path stores in bf16 or fp32 are
+ * rounded at the same points (scores, keys and gates as in the forward;
+ * h, y, dy = g * dout, dh, da, dc and each row's input gradient in bf16),
+ * so that a comparison measures accumulation order only. */
+
+static double sigm64(double v) { return 1.0 / (1.0 + exp(-v)); }
+static double keep_bf16(double v, int round) {
+  return round ? (double)bf16_to_f32(f64_to_bf16(v)) : v;
+}
+
+/* Scores and gates of every token, at the precision round_storage asks for. */
+static void bwd_scores(int64_t T, int d, int E, int k, const double* x, const double* wr,
+                       const int32_t* idx, int round, double* s, double* g, double* gsum) {
+  for (int64_t t = 0; t < T; ++t) {
+    for (int e = 0; e < E; ++e) {
+      if (round) {
+        float acc = 0.0f;
+        for (int i = 0; i < d; ++i)
+          acc = fmaf((float)x[(size_t)t * d + i], (float)wr[(size_t)i * E + e], acc);
+        s[(size_t)t * E + e] = (double)sigmoid_score(acc);
+      } else {
+        double acc = 0.0;
+        for (int i = 0; i < d; ++i) acc += x[(size_t)t * d + i] * wr[(size_t)i * E + e];
+        s[(size_t)t * E + e] = sigm64(acc);
+      }
+    }
+    double sum;
+    if (round) {
+      float fs = 0.0f;
+      for (int j = 0; j < k; ++j) fs += (float)s[(size_t)t * E + idx[t * k + j]];
+      sum = fs;
+    } else {
+      sum = 0.0;
+      for (int j = 0; j < k; ++j) sum += s[(size_t)t * E + idx[t * k + j]];
+    }
+    gsum[t] = sum;
+    for (int j = 0; j < k; ++j) {
+      double sj = s[(size_t)t * E + idx[t * k + j]];
+      double gj = sum == 0.0 ? 1.0 / k : sj / sum;
+      g[t * k + j] = round ? (double)(float)gj : gj;
+    }
+  }
+}
+
+typedef struct {
+  int64_t T;
+  int d, E, k, H, Hs, round;
+  const double *x, *w1, *w3, *w2, *ws1, *ws3, *ws2, *dout, *g;
+  const int32_t* idx;
+  double *dw1, *dw3, *dw2, *dws1, *dws3, *dws2;
+  double* dxrow; /* [T, k+1, d]: input gradient of each routed row, then the shared row */
+  double* dg;    /* [T, k]: <dout, y> of each routed row */
+} bwd_ctx;
+
+/* One expert (group < E) or the shared expert (group == E) over all of its
+ * rows: recompute a = x W1^T, c = x W3^T, h = silu(a) c and y = h W2^T, then
+ *   dy = gate * dout,  dg = <dout, y>,  dh = dy W2,
+ *   da = dh * c * silu'(a),  dc = dh * silu(a),  silu'(a) = s(a) (1 + a (1 - s(a))),
+ *   dW2 += dy^T h,  dW1 += da^T x,  dW3 += dc^T x,  dx_row = da W1 + dc W3.
+ * Only this group writes its weight gradients, so groups run in parallel. */
+static void bwd_group(void* p, int64_t grp) {
+  bwd_ctx* c = (bwd_ctx*)p;
+  const int d = c->d, k = c->k, rd = c->round;
+  const int shared = grp == c->E;
+  const int H = shared ? c->Hs : c->H;
+  if (shared && H == 0) return;
+  const size_t wo = shared ? 0 : (size_t)grp * H * d;
+  const double* W1 = (shared ? c->ws1 : c->w1) + wo;
+  const double* W3 = (shared ? c->ws3 : c->w3) + wo;
+  const double* W2 = (shared ? c->ws2 : c->w2) + wo;
+  double* dW1 = (shared ? c->dws1 : c->dw1) + wo;
+  double* dW3 = (shared ? c->dws3 : c->dw3) + wo;
+  double* dW2 = (shared ? c->dws2 : c->dw2) + wo;
+  double* a = (double*)malloc(sizeof(double) * H);
+  double* cc = (double*)malloc(sizeof(double) * H);
+  double* hv = (double*)malloc(sizeof(double) * H);
+  double* dh = (double*)malloc(sizeof(double) * H);
+  double* da = (double*)malloc(sizeof(double) * H);
+  double* dc = (double*)malloc(sizeof(double) * H);
+  double* dy = (double*)malloc(sizeof(double) * d);
+  for (int64_t t = 0; t < c->T; ++t) {
+    int slot = -1;
+    if (shared) {
+      slot = k;
+    } else {
+      for (int j = 0; j < k; ++j)
+        if (c->idx[t * k + j] == (int)grp) slot = j;
+      if (slot < 0) continue;
+    }
+    const double* xr = c->x + (size_t)t * d;
+    const double* dor = c->dout + (size_t)t * d;
+    const double gate = shared ? 1.0 : c->g[t * k + slot];
+    for (int h = 0; h < H; ++h) {
+      double s1 = 0.0, s3 = 0.0;
+      for (int i = 0; i < d; ++i) {
+        s1 += xr[i] * W1[(size_t)h * d + i];
+        s3 += xr[i] * W3[(size_t)h * d + i];
+      }
+      a[h] = s1;
+      cc[h] = s3;
+      hv[h] = keep_bf16(s1 * sigm64(s1) * s3, rd);
+    }
+    if (!shared) {
+      double dot = 0.0;
+      for (int o = 0; o < d; ++o) {
+        double y = 0.0;
+        for (int h = 0; h < H; ++h) y += hv[h] * W2[(size_t)o * H + h];
+        dot += dor[o] * keep_bf16(y, rd);
+      }
+      c->dg[t * k + slot] = dot;
+    }
+    for (int o = 0; o < d; ++o) dy[o] = keep_bf16(gate * dor[o], rd);
+    for (int h = 0; h < H; ++h) {
+      double acc = 0.0;
+      for (int o = 0; o < d; ++o) acc += dy[o] * W2[(size_t)o * H + h];
+      dh[h] = keep_bf16(acc, rd);
+    }
+    for (int o = 0; o < d; ++o)
+      for (int h = 0; h < H; ++h) dW2[(size_t)o * H + h] += dy[o] * hv[h];
+    for (int h = 0; h < H; ++h) {
+      double sg = sigm64(a[h]);
+      da[h] = keep_bf16(dh[h] * cc[h] * sg * (1.0 + a[h] * (1.0 - sg)), rd);
+      dc[h] = keep_bf16(dh[h] * a[h] * sg, rd);
+      for (int i = 0; i < d; ++i) {
+        dW1[(size_t)h * d + i] += da[h] * xr[i];
+        dW3[(size_t)h * d + i] += dc[h] * xr[i];
+      }
+    }
+    double* dxo = c->dxrow + ((size_t)t * (k + 1) + slot) * d;
+    for (int i = 0; i < d; ++i) {
+      double acc = 0.0;
+      for (int h = 0; h < H; ++h) acc += da[h] * W1[(size_t)h * d + i] + dc[h] * W3[(size_t)h * d + i];
+      dxo[i] = keep_bf16(acc, rd);
+    }
+  }
+  free(a); free(cc); free(hv); free(dh); free(da); free(dc); free(dy);
+}
+
+/* Gradient of L with respect to x [T,d], W_r [d,E] and the expert weights
+ * (layouts as in the forward), all fp64 and overwritten.  x and the weights
+ * are fp64 values (bf16 or fp32 numbers widened, or arbitrary reals for the
+ * finite-difference pins); idx is the choice of experts to hold fixed.  The
+ * balance term: per sequence b of S tokens, with p[t,i] = s[t,i] / Z_t and
+ * Z_t = sum_e s[t,e], L_b = alpha sum_i f_i P_i, P_i = mean_t p[t,i] and
+ * f_i = E/(kS) #{t in b choosing i}; so dL_b/ds[t,m] = alpha/S (f_m -
+ * sum_i f_i p[t,i]) / Z_t.  The gates g_j = s_j / sum_j' s_j' give
+ * dL/ds_m = (dg_m - sum_j dg_j g_j) / sum for a chosen m.  Then dlogit =
+ * ds s (1 - s), dx += dlogit W_r^T and dW_r = x^T dlogit. */
+void oracle_moe_backward(int64_t T, int d, int E, int k, int H, int Hs, int S, double alpha,
+                         const double* x, const double* wr, const int32_t* idx, const double* w1,
+                         const double* w3, const double* w2, const double* ws1, const double* ws3,
+                         const double* ws2, const double* dout, int round_storage, double* dx,
+                         double* dwr, double* dw1, double* dw3, double* dw2, double* dws1,
+                         double* dws3, double* dws2, int nthreads) {
+  double* s = (double*)calloc((size_t)T * E, sizeof(double));
+  double* g = (double*)calloc((size_t)T * k, sizeof(double));
+  double* gsum = (double*)calloc((size_t)T, sizeof(double));
+  double* ds = (double*)calloc((size_t)T * E, sizeof(double));
+  double* dg = (double*)calloc((size_t)T * k, sizeof(double));
+  double* dxrow = (double*)calloc((size_t)T * (k + 1) * d, sizeof(double));
+  memset(dw1, 0, sizeof(double) * (size_t)E * H * d);
+  memset(dw3, 0, sizeof(double) * (size_t)E * H * d);
+  memset(dw2, 0, sizeof(double) * (size_t)E * H * d);
+  if (Hs) {
+    memset(dws1, 0, sizeof(double) * (size_t)Hs * d);
+    memset(dws3, 0, sizeof(double) * (size_t)Hs * d);
+    memset(dws2, 0, sizeof(double) * (size_t)Hs * d);
+  }
+  bwd_scores(T, d, E, k, x, wr, idx, round_storage, s, g, gsum);
+  bwd_ctx c = {T, d, E, k, H, Hs, round_storage, x, w1, w3, w2, ws1, ws3, ws2, dout, g, idx,
+               dw1, dw3, dw2, dws1, dws3, dws2, dxrow, dg};
+  parallel_for(E + 1, nthreads, bwd_group, &c);
+  /* gates */
+  for (int64_t t = 0; t < T; ++t) {
+    if (gsum[t] == 0.0) continue; /* g = 1/k: constant */
+    double gs = 0.0;
+    for (int j = 0; j < k; ++j) gs += dg[t * k + j] * g[t * k + j];
+    for (int j = 0; j < k; ++j) ds[(size_t)t * E + idx[t * k + j]] += (dg[t * k + j] - gs) / gsum[t];
+  }
+  /* sequence balance term */
+  if (S > 0) {
+    double* f = (double*)malloc(sizeof(double) * E);
+    for (int64_t b0 = 0; b0 + S <= T; b0 += S) {
+      for (int i = 0; i < E; ++i) f[i] = 0.0;
+      for (int64_t t = b0; t < b0 + S; ++t)
+        for (int j = 0; j < k; ++j) f[idx[t * k + j]] += (double)E / ((double)k * S);
+      for (int64_t t = b0; t < b0 + S; ++t) {
+        double Z = 0.0;
+        for (int i = 0; i < E; ++i) Z += s[(size_t)t * E + i];
+        if (Z == 0.0) continue;
+        double q = 0.0;
+        for (int i = 0; i < E; ++i) q += f[i] * s[(size_t)t * E + i] / Z;
+        for (int m = 0; m < E; ++m) ds[(size_t)t * E + m] += alpha / S * (f[m] - q) / Z;
+      }
+    }
+    free(f);
+  }
+  /* sigmoid, router, and the input gradient */
+  memset(dwr, 0, sizeof(double) * (size_t)d * E);
+  for (int64_t t = 0; t < T; ++t) {
+    for (int i = 0; i < d; ++i) {
+      double acc = 0.0;
+      for (int j = 0; j <= k; ++j) acc += dxrow[((size_t)t * (k + 1) + j) * d + i];
+      dx[(size_t)t * d + i] = acc;
+    }
+    for (int e = 0; e < E; ++e) {
+      double se = s[(size_t)t * E + e];
+      double dl = ds[(size_t)t * E + e] * se * (1.0 - se);
+      if (dl == 0.0) continue;
+      for (int i = 0; i < d; ++i) {
+        dx[(size_t)t * d + i] += dl * wr[(size_t)i * E + e];
+        dwr[(size_t)i * E + e] += x[(size_t)t * d + i] * dl;
+      }
+    }
+  }
+  free(s); free(g); free(gsum); free(ds); free(dg); free(dxrow);
+}
+
+/* The fp64 layer with the choice of experts held fixed and nothing rounded:
+ * out[t] = sum_j g[t,j] y[t,j] + ys[t] (no residual), and *loss_bal =
+ * sum_b L_b -- the function whose gradient oracle_moe_backward with
+ * round_storage = 0 computes (checked against finite differences). */
+void oracle_moe_forward_f64(int64_t T, int d, int E, int k, int H, int Hs, int S, double alpha,
+                            const double* x, const double* wr, const int32_t* idx,
+                            const double* w1, const double* w3, const double* w2,
+                            const double* ws1, const double* ws3, const double* ws2, double* out,
+                            double* loss_bal) {
+  double* s = (double*)calloc((size_t)T * E, sizeof(double));
+  double* g = (double*)calloc((size_t)T * k, sizeof(double));
+  double* gsum = (double*)calloc((size_t)T, sizeof(double));
+  int hmax = H > Hs ? H : Hs;
+  double* hv = (double*)malloc(sizeof(double) * (hmax > 0 ? hmax : 1));
+  bwd_scores(T, d, E, k, x, wr, idx, 0, s, g, gsum);
+  for (int64_t t = 0; t < T; ++t) {
+    const double* xr = x + (size_t)t * d;
+    for (int o = 0; o < d; ++o) out[(size_t)t * d + o] = 0.0;
+    for (int j = 0; j <= k; ++j) {
+      const int shared = j == k;
+      if (shared && !Hs) continue;
+      const int Hg = shared ? Hs : H;
+      const size_t wo = shared ? 0 : (size_t)idx[t * k + j] * H * d;
+      const double* W1 = (shared ? ws1 : w1) + wo;
+      const double* W3 = (shared ? ws3 : w3) + wo;
+      const double* W2 = (shared ? ws2 : w2) + wo;
+      const double gate = shared ? 1.0 : g[t * k + j];
+      for (int h = 0; h < Hg; ++h) {
+        double s1 = 0.0, s3 = 0.0;
+        for (int i = 0; i < d; ++i) {
+          s1 += xr[i] * W1[(size_t)h * d + i];
+          s3 += xr[i] * W3[(size_t)h * d + i];
+        }
+        hv[h] = s1 * sigm64(s1) * s3;
+      }
+      for (int o = 0; o < d; ++o) {
+        double y = 0.0;
+        for (int h = 0; h < Hg; ++h) y += hv[h] * W2[(size_t)o * Hg + h];
+        out[(size_t)t * d + o] += gate * y;
+      }
+    }
+  }
+  double lb = 0.0;
+  if (S > 0) {
+    for (int64_t b0 = 0; b0 + S <= T; b0 += S) {
+      for (int i = 0; i < E; ++i) {
+        double f = 0.0, P = 0.0;
+        for (int64_t t = b0; t < b0 + S; ++t) {
+          for (int j = 0; j < k; ++j)
+            if (idx[t * k + j] == i) f += (double)E / ((double)k * S);
+          double Z = 0.0;
+          for (int e = 0; e < E; ++e) Z += s[(size_t)t * E + e];
+          P += (Z == 0.0 ? 1.0 / E : s[(size_t)t * E + i] / Z) / S;
+        }
+        lb += alpha * f * P;
+      }
+    }
+  }
+  *loss_bal = lb;
+  free(s); free(g); free(gsum); free(hv);
+}
+
+/* ------------------------------------------------------------------ */
 /* Bias update (step a11)                                              */
 /* ------------------------------------------------------------------ */
 

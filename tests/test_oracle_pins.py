@@ -525,3 +525,106 @@ def test_block_with_zero_experts_is_the_residual(oracle_lib):
     assert np.array_equal(r["xn"], oracle_lib.rmsnorm(x, p["norm"], 1e-6))
     # routing saw the normalised input
     assert np.array_equal(r["idx"], oracle_lib.route(r["xn"], p["w_router"], p["bias"], k)["idx"])
+
+
+# ---------------------------------------------------------------- backward
+
+def _bwd_case(seed, T=6, d=8, E=4, k=2, H=4, Hs=4, scale=0.5):
+    rng = np.random.default_rng(seed)
+    p = {"w_router": rng.standard_normal((d, E)) * scale,
+         "w1": rng.standard_normal((E, H, d)) * scale, "w3": rng.standard_normal((E, H, d)) * scale,
+         "w2": rng.standard_normal((E, d, H)) * scale}
+    if Hs:
+        p.update({"ws1": rng.standard_normal((Hs, d)) * scale,
+                  "ws3": rng.standard_normal((Hs, d)) * scale,
+                  "ws2": rng.standard_normal((d, Hs)) * scale})
+    x = rng.standard_normal((T, d))
+    idx = np.array([rng.permutation(E)[:k] for _ in range(T)], np.int32)
+    dout = rng.standard_normal((T, d))
+    return p, x, idx, dout
+
+
+@pytest.mark.parametrize("S,alpha,Hs", [(3, 0.3, 4), (0, 0.0, 4), (6, 1.0, 0)])
+def test_backward_matches_finite_differences(oracle_lib, S, alpha, Hs):
+    """The exact fp64 gradient against central differences of the fp64 layer
+    (choice of experts fixed): every input and weight, with and without the
+    balance term and the shared expert."""
+    p, x, idx, dout = _bwd_case(11 + S, Hs=Hs)
+    g = oracle_lib.layer_backward(x, p, idx, dout, S, alpha, round_storage=False)
+
+    def loss(xx, pp):
+        o, lb = oracle_lib.forward_f64(xx, pp, idx, S, alpha)
+        return float((dout * o).sum() + lb)
+
+    eps = 1e-6
+    for name, key in [("x", "dx"), ("w_router", "dw_router"), ("w1", "dw1"), ("w3", "dw3"),
+                      ("w2", "dw2")] + ([("ws1", "dws1"), ("ws3", "dws3"), ("ws2", "dws2")] if Hs else []):
+        base = x if name == "x" else p[name]
+        num = np.zeros_like(base)
+        for ii in np.ndindex(base.shape):
+            plus, minus = base.copy(), base.copy()
+            plus[ii] += eps
+            minus[ii] -= eps
+            if name == "x":
+                num[ii] = (loss(plus, p) - loss(minus, p)) / (2 * eps)
+            else:
+                num[ii] = (loss(x, {**p, name: plus}) - loss(x, {**p, name: minus})) / (2 * eps)
+        err = np.abs(num - g[key]).max() / max(np.abs(num).max(), 1e-30)
+        assert err < 1e-6, (name, err)
+
+
+def test_backward_unchosen_experts_get_no_gradient(oracle_lib):
+    """The pages' dense formulation weights unchosen experts by zero, so their
+    weights get exactly zero gradient; chosen ones do not."""
+    p, x, idx, dout = _bwd_case(5, T=5, E=6, k=2)
+    idx[:] = np.array([0, 3], np.int32)  # experts 1, 2, 4, 5 never chosen
+    g = oracle_lib.layer_backward(x, p, idx, dout, 0, 0.0, round_storage=False)
+    for key in ("dw1", "dw3", "dw2"):
+        for e in (1, 2, 4, 5):
+            assert not g[key][e].any(), (key, e)
+        for e in (0, 3):
+            assert np.abs(g[key][e]).max() > 0, (key, e)
+
+
+def test_backward_linear_in_dout_and_balance_alone(oracle_lib):
+    p, x, idx, dout = _bwd_case(9, T=8, E=4, k=2)
+    _, _, _, dout2 = _bwd_case(10, T=8, E=4, k=2)
+    a = oracle_lib.layer_backward(x, p, idx, dout, 0, 0.0, round_storage=False)
+    b = oracle_lib.layer_backward(x, p, idx, dout2, 0, 0.0, round_storage=False)
+    c = oracle_lib.layer_backward(x, p, idx, dout + dout2, 0, 0.0, round_storage=False)
+    for key in ("dx", "dw_router", "dw1", "dw2", "dws3"):
+        assert np.allclose(c[key], a[key] + b[key], rtol=1e-12, atol=1e-12), key
+    # no upstream gradient and no balance term: nothing; with the balance
+    # term alone, only the router (and x through it) receives a gradient
+    z = oracle_lib.layer_backward(x, p, idx, np.zeros_like(dout), 4, 0.0, round_storage=False)
+    assert not any(z[key].any() for key in ("dx", "dw_router", "dw1", "dws2"))
+    bal = oracle_lib.layer_backward(x, p, idx, np.zeros_like(dout), 4, 0.5, round_storage=False)
+    assert bal["dw_router"].any() and bal["dx"].any()
+    assert not any(bal[key].any() for key in ("dw1", "dw3", "dw2", "dws1", "dws3", "dws2"))
+
+
+def test_backward_forward_f64_is_the_layer(oracle_lib):
+    """The fp64 layer the gradient is taken of is the forward oracle without
+    its bf16 storage points: on bf16 inputs the two agree within bf16 error."""
+    import torch
+    rng = np.random.default_rng(21)
+    T, d, E, k, H = 64, 64, 8, 2, 64
+    xb = bf16_bits(rng.standard_normal((T, d)))
+    bf = lambda a: bf16_bits(a)  # noqa: E731
+    p = {"w_router": (0.2 * rng.standard_normal((d, E))).astype(np.float32),
+         "bias": np.zeros(E, np.float32),
+         "w1": bf(0.1 * rng.standard_normal((E, H, d))), "w3": bf(0.1 * rng.standard_normal((E, H, d))),
+         "w2": bf(0.1 * rng.standard_normal((E, d, H))), "ws1": bf(0.1 * rng.standard_normal((H, d))),
+         "ws3": bf(0.1 * rng.standard_normal((H, d))), "ws2": bf(0.1 * rng.standard_normal((d, H)))}
+    ref = oracle_lib.layer(xb, p, k)
+    o64, _ = oracle_lib.forward_f64(xb, p, ref["idx"])
+    out = oracle_lib.bf16_bits_to_f32(ref["out"]).astype(np.float64)
+    assert np.abs(out - o64).max() <= 2e-2 * np.abs(o64).max()
+    assert np.linalg.norm(out - o64) / np.linalg.norm(o64) < 1e-2
+    # ... and the rounded backward stays within bf16 error of the exact one
+    dout = bf16_bits(rng.standard_normal((T, d)))
+    g0 = oracle_lib.layer_backward(xb, p, ref["idx"], dout, 0, 0.0, round_storage=False)
+    g1 = oracle_lib.layer_backward(xb, p, ref["idx"], dout, 0, 0.0, round_storage=True)
+    for key in ("dx", "dw_router", "dw1", "dw2", "dws1"):
+        rel = np.linalg.norm(g1[key] - g0[key]) / np.linalg.norm(g0[key])
+        assert rel < 2e-2, (key, rel)
