@@ -211,6 +211,76 @@ moe_status moe_rmsnorm(const moe_shape* shape, const uint16_t* x, const float* g
 moe_status moe_update_bias(const moe_shape* shape, const int32_t* counts, float* bias,
                            float gamma, void* stream);
 
+/* ---- Backward (training) --------------------------------------------------
+ * The pages' workload is training (12000 AdamW steps, [ZH] 如何在Mac上复现) on
+ * a loss that adds the small sequence-wise balance loss ([ZH] 多Token预测也被保
+ * 留了); the per-expert bias stays out of the loss and gets no gradient ([ZH]
+ * 最有价值的实验).  With the forward's choice of experts held fixed, three calls
+ * give the gradient of  sum_t <dout[t], out[t]> + sum_b L_b  with respect to
+ * the layer's input and every weight, in this order on one stream:
+ *   moe_combine_backward -> moe_grouped_ffn_backward -> moe_route_backward
+ * They read the forward's results (choices, gates, offsets, perm_src, pos,
+ * x_perm -- moe_permute must have materialised it -- and y_perm) and a
+ * workspace of moe_backward_workspace_bytes().  Input gradients are bf16,
+ * weight gradients fp32 (the master weights are fp32, [VI] Những gì có trong
+ * 190 dòng code).  Conventions as above (device pointers, 16-byte aligned
+ * bf16 arrays, checks before launch, no allocation). */
+
+/* Bytes of device workspace for the three backward calls (256-aligned). */
+moe_status moe_backward_workspace_bytes(const moe_shape* shape, size_t* bytes);
+
+/* Through the combine out = r + y_shared + sum_j g_j y_perm[pos[t,j]]:
+ *   dy_perm[pos[t,j]] = bf16( topk_gate[t,j] * dout[t] )   (expert-grouped rows)
+ *   dgate[t,j]        = <dout[t], y_perm[pos[t,j]]>          (fp32)
+ * The shared expert's and the residual's gradient is dout itself.
+ *   dout [T, d], y_perm [T*k, d] bf16 (in); topk_gate [T, k] fp32, pos [T, k]
+ *   int32 (in); dy_perm [T*k, d] bf16, dgate [T, k] fp32 (out)          */
+moe_status moe_combine_backward(const moe_shape* shape, const uint16_t* dout, const uint16_t* y_perm,
+                                const float* topk_gate, const int32_t* pos, uint16_t* dy_perm,
+                                float* dgate, void* stream);
+
+/* Through the experts, per expert group (rows offsets[e] .. offsets[e+1]-1,
+ * x_perm the gathered inputs, dy_perm from moe_combine_backward) and for the
+ * shared expert on every token (inputs x, upstream gradient dout):
+ *   a, c = x W1^T, x W3^T (recomputed), h = bf16(silu(a) c)
+ *   dh = bf16(dy W2), da = bf16(dh c silu'(a)), dc = bf16(dh silu(a))
+ *   dx_perm (dx_shared) = bf16(da W1 + dc W3)
+ *   dW2 = dy^T h,  dW1 = da^T x,  dW3 = dc^T x   (fp32; zero for an expert
+ *   with no rows: unchosen experts get no gradient)
+ *   x [T, d], x_perm [T*k, d], dy_perm [T*k, d], dout [T, d] bf16 (in);
+ *   offsets [E+1] int32 (in); w1, w3 [E, H, d], w2 [E, d, H], ws1, ws3 [Hs, d],
+ *   ws2 [d, Hs] bf16 (in); dx_perm [T*k, d], dx_shared [T, d] bf16 (out);
+ *   dw1, dw3 [E, H, d], dw2 [E, d, H], dws1, dws3 [Hs, d], dws2 [d, Hs] fp32
+ *   (out).  The shared arguments are NULL iff Hs == 0.                   */
+moe_status moe_grouped_ffn_backward(const moe_shape* shape, const uint16_t* x,
+                                    const uint16_t* x_perm, const int32_t* offsets,
+                                    const uint16_t* w1, const uint16_t* w3, const uint16_t* w2,
+                                    const uint16_t* ws1, const uint16_t* ws3, const uint16_t* ws2,
+                                    const uint16_t* dy_perm, const uint16_t* dout,
+                                    uint16_t* dx_perm, uint16_t* dx_shared, float* dw1, float* dw3,
+                                    float* dw2, float* dws1, float* dws3, float* dws2,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Through the routing: the scores s = sigmoid(x W_r) are recomputed (the
+ * forward's fp32 chain); the gates g_j = s_j / sum s over the chosen experts
+ * give ds_j = (dgate_j - sum_j' dgate_j' g_j') / sum; with shape->seq_len > 0
+ * and alpha > 0 the balance statistic alpha sum_i f_i P_i of each sequence
+ * adds ds_m += alpha/S (f_m - sum_i f_i s_i/Z) / Z (Z = sum_e s_e, f as in
+ * moe_route); dlogit = ds s (1 - s).  Then
+ *   dx[t]     = bf16( d_residual[t] + dx_shared[t] + sum_j dx_perm[pos[t,j]]
+ *                     + sum_e dlogit[t,e] W_r[:,e] )
+ *   dw_router = x^T dlogit  (fp32, [d, E]);  the bias gets no gradient.
+ *   x [T, d] bf16, w_router [d, E] fp32, topk_idx / pos [T, k] int32,
+ *   topk_gate / dgate [T, k] fp32, dx_perm [T*k, d] bf16 (in); dx_shared
+ *   [T, d] bf16 (in; NULL iff Hs == 0); d_residual [T, d] bf16 or NULL (in);
+ *   alpha >= 0; dx [T, d] bf16, dw_router [d, E] fp32 (out)              */
+moe_status moe_route_backward(const moe_shape* shape, const uint16_t* x, const float* w_router,
+                              const int32_t* topk_idx, const float* topk_gate, const float* dgate,
+                              float alpha, const uint16_t* dx_perm, const uint16_t* dx_shared,
+                              const int32_t* pos, const uint16_t* d_residual, uint16_t* dx,
+                              float* dw_router, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -22,7 +22,8 @@ PROBE_LIB = os.path.join(PKG, "libmoe_probe.so")  # HBM read probe of the measur
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["route.hip", "permute.hip", "grouped_gemm.hip", "combine.hip", "norm.hip", "api.cpp"]
+SOURCES = ["route.hip", "permute.hip", "grouped_gemm.hip", "combine.hip", "norm.hip", "bwd_gemm.hip",
+           "bwd.hip", "api.cpp"]
 PROBE_SOURCES = ["hbm_probe.hip"]
 HEADERS = ["common.hpp", "gemm_common.hpp", "kernels.hpp"]
 

@@ -326,6 +326,168 @@ moe_status moe_rmsnorm(const moe_shape* shape, const uint16_t* x, const float* g
                                         static_cast<hipStream_t>(stream)));
 }
 
+// ---- backward
+namespace {
+struct BwdWorkspace {
+  uint16_t *dh, *h, *da, *dc;      // [T*k, H] bf16, expert-grouped rows
+  uint16_t *dhs, *hs, *das, *dcs;  // [T, Hs] bf16, the shared expert
+  float* scores;                   // [T, E]
+  float* freq;                     // [T/S, E]
+  float* dlogit;                   // [T, E]
+  float* dwr_part;                 // [splits, d, E]
+  int splits;
+  size_t total;
+};
+BwdWorkspace carve_bwd(const moe_shape* s, void* base) {
+  BwdWorkspace w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = (off + bytes + 255) / 256 * 256;
+    return base ? static_cast<char*>(base) + o : nullptr;
+  };
+  const int64_t T = s->tokens, rk = T * s->top_k;
+  const int H = s->hidden, Hs = s->shared_hidden, E = s->n_experts, d = s->d_model;
+  w.dh = reinterpret_cast<uint16_t*>(take(2 * rk * H));
+  w.h = reinterpret_cast<uint16_t*>(take(2 * rk * H));
+  w.da = reinterpret_cast<uint16_t*>(take(2 * rk * H));
+  w.dc = reinterpret_cast<uint16_t*>(take(2 * rk * H));
+  w.dhs = reinterpret_cast<uint16_t*>(take(2 * T * Hs));
+  w.hs = reinterpret_cast<uint16_t*>(take(2 * T * Hs));
+  w.das = reinterpret_cast<uint16_t*>(take(2 * T * Hs));
+  w.dcs = reinterpret_cast<uint16_t*>(take(2 * T * Hs));
+  w.scores = reinterpret_cast<float*>(take(4 * T * E));
+  w.freq = reinterpret_cast<float*>(take(4 * (s->seq_len > 0 ? T / s->seq_len : 0) * E));
+  w.dlogit = reinterpret_cast<float*>(take(4 * T * E));
+  w.splits = moe::route_bwd_splits(T);
+  w.dwr_part = reinterpret_cast<float*>(take(4 * static_cast<int64_t>(w.splits) * d * E));
+  w.total = off;
+  return w;
+}
+moe_status check_bwd_ws(const moe_shape* s, void* ws, size_t bytes) {
+  if (!ws || bytes < carve_bwd(s, nullptr).total) return MOE_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) % 256) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+}  // namespace
+
+moe_status moe_backward_workspace_bytes(const moe_shape* shape, size_t* bytes) {
+  if (!bytes) return MOE_ERR_INVALID_ARGUMENT;
+  const moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  *bytes = carve_bwd(shape, nullptr).total;
+  return MOE_OK;
+}
+
+moe_status moe_combine_backward(const moe_shape* shape, const uint16_t* dout, const uint16_t* y_perm,
+                                const float* topk_gate, const int32_t* pos, uint16_t* dy_perm,
+                                float* dgate, void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (shape->tokens == 0) return MOE_OK;
+  if (!dout || !y_perm || !topk_gate || !pos || !dy_perm || !dgate) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(dout) || !aligned16(y_perm) || !aligned16(dy_perm)) return MOE_ERR_INVALID_ARGUMENT;
+  return hip_status(moe::launch_combine_bwd(dout, y_perm, topk_gate, pos, dy_perm, dgate,
+                                            shape->tokens, shape->d_model, shape->top_k,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_grouped_ffn_backward(const moe_shape* shape, const uint16_t* x,
+                                    const uint16_t* x_perm, const int32_t* offsets,
+                                    const uint16_t* w1, const uint16_t* w3, const uint16_t* w2,
+                                    const uint16_t* ws1, const uint16_t* ws3, const uint16_t* ws2,
+                                    const uint16_t* dy_perm, const uint16_t* dout,
+                                    uint16_t* dx_perm, uint16_t* dx_shared, float* dw1, float* dw3,
+                                    float* dw2, float* dws1, float* dws3, float* dws2,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (shape->tokens == 0) return MOE_OK;
+  const bool shared = shape->shared_hidden > 0;
+  if (!x || !x_perm || !offsets || !w1 || !w3 || !w2 || !dy_perm || !dx_perm || !dw1 || !dw3 || !dw2)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (shared != (ws1 && ws3 && ws2 && dout && dx_shared && dws1 && dws3 && dws2))
+    return MOE_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {x, x_perm, w1, w3, w2, dy_perm, dx_perm, dw1, dw3, dw2,
+                        shared ? ws1 : w1, shared ? ws3 : w1, shared ? ws2 : w1,
+                        shared ? dout : x, shared ? dx_shared : dx_perm,
+                        shared ? dws1 : dw1, shared ? dws3 : dw1, shared ? dws2 : dw1};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MOE_ERR_INVALID_ARGUMENT;
+  if ((st = check_bwd_ws(shape, workspace, workspace_bytes)) != MOE_OK) return st;
+  const BwdWorkspace w = carve_bwd(shape, workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t T = shape->tokens;
+  const int d = shape->d_model, E = shape->n_experts, H = shape->hidden, Hs = shape->shared_hidden;
+  hipError_t e = hipSuccess;
+  // one expert's (or the shared expert's) five GEMMs
+  auto run = [&](int groups, const int32_t* offs, int rows, int Hh, const uint16_t* xa,
+                 const uint16_t* dya, const uint16_t* W1, const uint16_t* W3, const uint16_t* W2,
+                 int64_t wstride, uint16_t* dh, uint16_t* h, uint16_t* da, uint16_t* dc,
+                 uint16_t* dxo, float* dW1, float* dW3, float* dW2) {
+    moe::BwdGemmArgs g{};
+    g.groups = groups;
+    g.offsets = offs;
+    g.rows = rows;
+    // dh = dy W2  (W2 [d, H] read as [K, N])
+    g.ragged_k = 0; g.N = Hh; g.K = d; g.K2 = 0;
+    g.a = dya; g.lda = d; g.b = W2; g.ldb = Hh; g.b_gstride = wstride;
+    g.c = dh; g.ldc = Hh;
+    if ((e = moe::launch_bwd_gemm(g, moe::kBwdDgradKM, s)) != hipSuccess) return;
+    // a, c = x W1^T, x W3^T -> h, da, dc
+    moe::BwdGemmArgs r = g;
+    r.N = Hh; r.K = d; r.a = xa; r.lda = d; r.b = W1; r.b2 = W3; r.ldb = d;
+    r.c = nullptr; r.dh = dh; r.h = h; r.da = da; r.dc = dc; r.ld_h = Hh;
+    if ((e = moe::launch_bwd_gemm(r, moe::kBwdRecompute, s)) != hipSuccess) return;
+    // dx = da W1 + dc W3  (W1, W3 [H, d] read as [K, N])
+    moe::BwdGemmArgs x2 = g;
+    x2.N = d; x2.K = Hh; x2.K2 = Hh; x2.a = da; x2.a2 = dc; x2.lda = Hh;
+    x2.b = W1; x2.b2 = W3; x2.ldb = d; x2.c = dxo; x2.ldc = d;
+    if ((e = moe::launch_bwd_gemm(x2, moe::kBwdDgradKM, s)) != hipSuccess) return;
+    // dW2 = dy^T h,  dW1 = da^T x,  dW3 = dc^T x  (K = the group's rows)
+    moe::BwdGemmArgs wg{};
+    wg.groups = groups; wg.offsets = offs; wg.rows = rows; wg.ragged_k = 1;
+    wg.M = d; wg.N = Hh; wg.a = dya; wg.lda = d; wg.b = h; wg.ldb = Hh;
+    wg.c = dW2; wg.ldc = Hh; wg.c_gstride = static_cast<int64_t>(d) * Hh;
+    if ((e = moe::launch_bwd_gemm(wg, moe::kBwdWgrad, s)) != hipSuccess) return;
+    wg.M = Hh; wg.N = d; wg.a = da; wg.lda = Hh; wg.b = xa; wg.ldb = d;
+    wg.c = dW1; wg.ldc = d; wg.c_gstride = static_cast<int64_t>(Hh) * d;
+    if ((e = moe::launch_bwd_gemm(wg, moe::kBwdWgrad, s)) != hipSuccess) return;
+    wg.a = dc; wg.c = dW3;
+    e = moe::launch_bwd_gemm(wg, moe::kBwdWgrad, s);
+  };
+  run(E, offsets, 0, H, x_perm, dy_perm, w1, w3, w2, static_cast<int64_t>(H) * d, w.dh, w.h, w.da,
+      w.dc, dx_perm, dw1, dw3, dw2);
+  if (e == hipSuccess && shared)
+    run(1, nullptr, static_cast<int>(T), Hs, x, dout, ws1, ws3, ws2, 0, w.dhs, w.hs, w.das, w.dcs,
+        dx_shared, dws1, dws3, dws2);
+  return hip_status(e);
+}
+
+moe_status moe_route_backward(const moe_shape* shape, const uint16_t* x, const float* w_router,
+                              const int32_t* topk_idx, const float* topk_gate, const float* dgate,
+                              float alpha, const uint16_t* dx_perm, const uint16_t* dx_shared,
+                              const int32_t* pos, const uint16_t* d_residual, uint16_t* dx,
+                              float* dw_router, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  moe_status st = check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (shape->tokens == 0) return MOE_OK;
+  if (!x || !w_router || !topk_idx || !topk_gate || !dgate || !dx_perm || !pos || !dx || !dw_router)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if ((shape->shared_hidden > 0) != (dx_shared != nullptr)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!(alpha >= 0.0f) || alpha > 3.0e38f) return MOE_ERR_INVALID_ARGUMENT;
+  const void* ptrs[] = {x, dx_perm, dx, dx_shared ? dx_shared : dx, d_residual ? d_residual : dx};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MOE_ERR_INVALID_ARGUMENT;
+  if ((st = check_bwd_ws(shape, workspace, workspace_bytes)) != MOE_OK) return st;
+  const BwdWorkspace w = carve_bwd(shape, workspace);
+  return hip_status(moe::launch_route_bwd(
+      x, w_router, topk_idx, topk_gate, dgate, alpha, dx_perm, dx_shared, pos, d_residual, dx,
+      dw_router, w.scores, w.freq, w.dlogit, w.dwr_part, w.splits, shape->tokens, shape->d_model,
+      shape->n_experts, shape->top_k, shape->seq_len, static_cast<hipStream_t>(stream)));
+}
+
 moe_status moe_update_bias(const moe_shape* shape, const int32_t* counts, float* bias,
                            float gamma, void* stream) {
   moe_status st = check_shape(shape);

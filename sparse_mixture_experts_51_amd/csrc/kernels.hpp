@@ -80,6 +80,46 @@ hipError_t launch_gemm_down(const GroupedGemmArgs& a, hipStream_t s);
 hipError_t launch_combine(const uint16_t* y_perm, const uint16_t* y_shared, const float* gate,
                           const int32_t* pos, const uint16_t* residual, uint16_t* out,
                           int64_t T, int d, int k, hipStream_t s);
+// Grouped GEMMs of the backward (bwd_gemm.hip): C_g = A_g B_g^T summed over K,
+// per expert group g of consecutive rows.
+struct BwdGemmArgs {
+  int groups;              // groups (experts), or 1 with offsets == NULL
+  const int32_t* offsets;  // [groups + 1] first row of each group, or NULL
+  int rows;                // rows of the single group when offsets == NULL
+  int ragged_k;            // 0: a group's rows are M (input gradients); 1: they are K (weight gradients)
+  int M, N, K;             // the sizes that are not a group's rows
+  int K2;                  // dgrad only: a second K segment from a2 / b2 (dx = da W1 + dc W3), else 0
+  const uint16_t* a;       // A: K-contiguous rows [rows, K] (dgrad) or rows [rows, M] (wgrad)
+  const uint16_t* a2;
+  int64_t lda;
+  const uint16_t* b;       // B: weights [N, K] or [K, N] (per group, b_gstride apart), or rows [rows, N] (wgrad)
+  const uint16_t* b2;
+  int64_t ldb, b_gstride;
+  void* c;                 // bf16 rows [rows, N] (dgrad) or fp32 [groups][M][N] (wgrad)
+  int64_t ldc, c_gstride;
+  const uint16_t* dh;      // recompute epilogue: dh in, h / da / dc out, rows [rows, N]
+  uint16_t* h;
+  uint16_t* da;
+  uint16_t* dc;
+  int64_t ld_h;
+};
+constexpr int kBwdDgradKM = 0;    // A K-contiguous, B stored [K, N], bf16 out
+constexpr int kBwdRecompute = 1;  // A K-contiguous, B = [W1; W3] rows [N, K], SwiGLU derivative out
+constexpr int kBwdWgrad = 2;      // both operands K-major rows, fp32 out
+hipError_t launch_bwd_gemm(const BwdGemmArgs& a, int kind, hipStream_t s);
+
+hipError_t launch_combine_bwd(const uint16_t* dout, const uint16_t* y_perm, const float* gate,
+                              const int32_t* pos, uint16_t* dy_perm, float* dgate, int64_t T,
+                              int d, int k, hipStream_t s);
+hipError_t launch_route_bwd(const uint16_t* x, const float* w_router, const int32_t* idx,
+                            const float* gate, const float* dgate, float alpha,
+                            const uint16_t* dx_perm, const uint16_t* dx_shared,
+                            const int32_t* pos, const uint16_t* d_residual, uint16_t* dx,
+                            float* dw_router, float* scores, float* freq, float* dlogit,
+                            float* dwr_part, int dwr_splits, int64_t T, int d, int E, int k,
+                            int S, hipStream_t s);
+int route_bwd_splits(int64_t T);
+
 hipError_t launch_rmsnorm(const uint16_t* x, const float* gain, float eps, uint16_t* out,
                           int64_t T, int d, hipStream_t s);
 hipError_t launch_update_bias(const int32_t* counts, float* bias, float gamma, int64_t T, int E,

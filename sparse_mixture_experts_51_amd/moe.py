@@ -27,7 +27,8 @@ MOE_ERR_SCRATCH_LIMIT = 5
 
 EXPORTED = ("moe_status_str", "moe_workspace_bytes", "moe_route", "moe_permute",
             "moe_permute_noalloc", "moe_grouped_ffn", "moe_combine", "moe_rmsnorm",
-            "moe_update_bias")
+            "moe_update_bias", "moe_backward_workspace_bytes", "moe_combine_backward",
+            "moe_grouped_ffn_backward", "moe_route_backward")
 
 
 class MoeError(RuntimeError):
@@ -90,6 +91,11 @@ def load() -> ctypes.CDLL:
     L.moe_combine.argtypes = [S, P, P, P, P, P, P, P]
     L.moe_rmsnorm.argtypes = [S, P, P, ctypes.c_float, P, P]
     L.moe_update_bias.argtypes = [S, P, P, ctypes.c_float, P]
+    L.moe_backward_workspace_bytes.argtypes = [S, ctypes.POINTER(ctypes.c_size_t)]
+    L.moe_combine_backward.argtypes = [S, P, P, P, P, P, P, P]
+    L.moe_grouped_ffn_backward.argtypes = [S] + [P] * 20 + [ctypes.c_size_t, P]
+    L.moe_route_backward.argtypes = [S, P, P, P, P, P, ctypes.c_float, P, P, P, P, P, P, P,
+                                     ctypes.c_size_t, P]
     for name in EXPORTED[1:]:
         getattr(L, name).restype = ctypes.c_int
     _lib = L
@@ -164,6 +170,79 @@ def moe_combine(shape: Shape, y_perm, y_shared, topk_gate, pos, residual, out, s
 def moe_rmsnorm(shape: Shape, x, gain, eps: float, out, stream=None):
     _ok(load().moe_rmsnorm(ctypes.byref(shape.c()), _p(x), _p(gain), ctypes.c_float(eps), _p(out),
                            _s(stream)), "moe_rmsnorm")
+
+
+def moe_backward_workspace_bytes(shape: Shape) -> int:
+    n = ctypes.c_size_t(0)
+    _ok(load().moe_backward_workspace_bytes(ctypes.byref(shape.c()), ctypes.byref(n)),
+        "moe_backward_workspace_bytes")
+    return int(n.value)
+
+
+def moe_combine_backward(shape: Shape, dout, y_perm, topk_gate, pos, dy_perm, dgate, stream=None):
+    _ok(load().moe_combine_backward(ctypes.byref(shape.c()), _p(dout), _p(y_perm), _p(topk_gate),
+                                    _p(pos), _p(dy_perm), _p(dgate), _s(stream)),
+        "moe_combine_backward")
+
+
+def moe_grouped_ffn_backward(shape: Shape, x, x_perm, offsets, w1, w3, w2, ws1, ws3, ws2, dy_perm,
+                             dout, dx_perm, dx_shared, dw1, dw3, dw2, dws1, dws3, dws2,
+                             workspace, stream=None):
+    wp, wn = _ws(workspace)
+    _ok(load().moe_grouped_ffn_backward(
+        ctypes.byref(shape.c()), _p(x), _p(x_perm), _p(offsets), _p(w1), _p(w3), _p(w2), _p(ws1),
+        _p(ws3), _p(ws2), _p(dy_perm), _p(dout), _p(dx_perm), _p(dx_shared), _p(dw1), _p(dw3),
+        _p(dw2), _p(dws1), _p(dws3), _p(dws2), wp, wn, _s(stream)), "moe_grouped_ffn_backward")
+
+
+def moe_route_backward(shape: Shape, x, w_router, topk_idx, topk_gate, dgate, alpha, dx_perm,
+                       dx_shared, pos, d_residual, dx, dw_router, workspace, stream=None):
+    wp, wn = _ws(workspace)
+    _ok(load().moe_route_backward(
+        ctypes.byref(shape.c()), _p(x), _p(w_router), _p(topk_idx), _p(topk_gate), _p(dgate),
+        ctypes.c_float(alpha), _p(dx_perm), _p(dx_shared), _p(pos), _p(d_residual), _p(dx),
+        _p(dw_router), wp, wn, _s(stream)), "moe_route_backward")
+
+
+def alloc_backward(shape: Shape, device="cuda") -> dict:
+    """Gradient buffers and workspace of one layer's backward, allocated with torch."""
+    T, d, E, k, H, Hs = (shape.tokens, shape.d_model, shape.n_experts, shape.top_k, shape.hidden,
+                         shape.shared_hidden)
+    f32, b16 = torch.float32, torch.bfloat16
+    ws = moe_backward_workspace_bytes(shape)
+    return {
+        "dy_perm": torch.empty((T * k, d), dtype=b16, device=device),
+        "dgate": torch.empty((T, k), dtype=f32, device=device),
+        "dx_perm": torch.empty((T * k, d), dtype=b16, device=device),
+        "dx_shared": torch.empty((T, d), dtype=b16, device=device) if Hs else None,
+        "dx": torch.empty((T, d), dtype=b16, device=device),
+        "dw_router": torch.empty((d, E), dtype=f32, device=device),
+        "dw1": torch.empty((E, H, d), dtype=f32, device=device),
+        "dw3": torch.empty((E, H, d), dtype=f32, device=device),
+        "dw2": torch.empty((E, d, H), dtype=f32, device=device),
+        "dws1": torch.empty((Hs, d), dtype=f32, device=device) if Hs else None,
+        "dws3": torch.empty((Hs, d), dtype=f32, device=device) if Hs else None,
+        "dws2": torch.empty((d, Hs), dtype=f32, device=device) if Hs else None,
+        "workspace": torch.empty((max(ws, 256),), dtype=torch.uint8, device=device),
+    }
+
+
+def layer_backward(shape: Shape, x, params: dict, fwd: dict, dout, grads: dict,
+                   alpha: float = 1e-4, d_residual=None, stream=None):
+    """The three backward calls after a forward whose buffers `fwd` (from
+    layer_forward with use_x_perm=True) hold the choices, rows and outputs."""
+    ws = grads["workspace"]
+    moe_combine_backward(shape, dout, fwd["y_perm"], fwd["topk_gate"], fwd["pos"],
+                         grads["dy_perm"], grads["dgate"], stream)
+    moe_grouped_ffn_backward(shape, x, fwd["x_perm"], fwd["offsets"], params["w1"], params["w3"],
+                             params["w2"], params.get("ws1"), params.get("ws3"), params.get("ws2"),
+                             grads["dy_perm"], dout if shape.shared_hidden else None,
+                             grads["dx_perm"], grads["dx_shared"], grads["dw1"], grads["dw3"],
+                             grads["dw2"], grads["dws1"], grads["dws3"], grads["dws2"], ws, stream)
+    moe_route_backward(shape, x, params["w_router"], fwd["topk_idx"], fwd["topk_gate"],
+                       grads["dgate"], alpha, grads["dx_perm"], grads["dx_shared"], fwd["pos"],
+                       d_residual, grads["dx"], grads["dw_router"], ws, stream)
+    return grads
 
 
 def moe_update_bias(shape: Shape, counts, bias, gamma: float = 1e-3, stream=None):

@@ -41,6 +41,36 @@ def test_exports_every_declared_symbol(L):
         assert hasattr(L, s), s
 
 
+def declared_prototypes():
+    """name -> list of parameter type strings, from include/moe.h."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    out = {}
+    for m in re.finditer(r"\b(moe_[a-z_]+)\s*\(([^)]*)\)\s*;", text):
+        params = [q.strip() for q in m.group(2).split(",") if q.strip()]
+        out[m.group(1)] = params
+    return out
+
+
+def test_binding_argtypes_match_the_header(L):
+    """Every ctypes prototype of the binding has the header's parameter count,
+    and size_t / float / int parameters sit where the header puts them."""
+    protos = declared_prototypes()
+    assert set(protos) == set(moe.EXPORTED)
+    for name, params in protos.items():
+        argtypes = getattr(L, name).argtypes
+        assert len(argtypes) == len(params), (name, len(argtypes), len(params))
+        for ctype, decl in zip(argtypes, params):
+            if "*" in decl:
+                assert ctype not in (ctypes.c_size_t, ctypes.c_float, ctypes.c_int), (name, decl)
+            elif decl.startswith("size_t"):
+                assert ctype is ctypes.c_size_t, (name, decl)
+            elif decl.startswith("float"):
+                assert ctype is ctypes.c_float, (name, decl)
+            else:
+                assert decl.startswith("int "), (name, decl)
+                assert ctype is ctypes.c_int, (name, decl)
+
+
 def test_exports_nothing_from_the_oracle(L):
     for s in ("oracle_route", "oracle_layer", "oracle_combine"):
         assert not hasattr(L, s)
