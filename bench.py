@@ -60,7 +60,92 @@ def parse():
                     help="time one layer's moe_grouped_ffn with HIP events in every N-th timed step")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain device copy of 1 GiB (counter calibration)")
+    ap.add_argument("--with-backward", action="store_true",
+                    help="also time training steps (forward, backward of every layer, bias "
+                         "updates) and report them as a 'train' object")
     return ap.parse_args()
+
+
+def time_training(args, wl, shape, params, xs, stream):
+    """Training steps: every layer's forward (x_perm gathered), then the
+    backward of every layer from the last to the first with a seeded upstream
+    gradient (stacked layers pass the residual's gradient on), then the bias
+    updates.  HIP events around one layer's moe_grouped_ffn_backward per
+    N-th step give the backward expert GEMMs' rate."""
+    import numpy as np
+    import torch
+
+    from sparse_mixture_experts_51_amd import moe, workloads
+
+    L = wl.layers
+    dev = "cuda:0"
+    stacked = L > 1
+    bufs = [moe.alloc_buffers(shape, dev, x_perm=True) for _ in range(L)]
+    grads = [moe.alloc_backward(shape, dev) for _ in range(L)]
+    dtop = workloads.normal((wl.tokens, wl.d_model), 1.0, 99991, dev, torch.bfloat16)
+    ev = []
+    n_x = len(xs)
+
+    def step(i, timed):
+        x = xs[i % n_x]
+        inputs = []
+        for l in range(L):
+            inputs.append(x)
+            moe.layer_forward(shape, x, params[l], bufs[l], residual=x if stacked else None,
+                              use_x_perm=True, stream=stream)
+            x = bufs[l]["out"]
+        dout = dtop
+        for l in reversed(range(L)):
+            b, g, p = bufs[l], grads[l], params[l]
+            ws = g["workspace"]
+            moe.moe_combine_backward(shape, dout, b["y_perm"], b["topk_gate"], b["pos"],
+                                     g["dy_perm"], g["dgate"], stream)
+            timed_l = timed is not None and timed % args.ffn_events_every == 0 and \
+                l == (timed // args.ffn_events_every) % L
+            if timed_l:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            moe.moe_grouped_ffn_backward(shape, inputs[l], b["x_perm"], b["offsets"], p["w1"],
+                                         p["w3"], p["w2"], p.get("ws1"), p.get("ws3"), p.get("ws2"),
+                                         g["dy_perm"], dout if shape.shared_hidden else None,
+                                         g["dx_perm"], g["dx_shared"], g["dw1"], g["dw3"],
+                                         g["dw2"], g["dws1"], g["dws3"], g["dws2"], ws, stream)
+            if timed_l:
+                e1.record(stream)
+                ev.append((e0, e1))
+            moe.moe_route_backward(shape, inputs[l], p["w_router"], b["topk_idx"], b["topk_gate"],
+                                   g["dgate"], 1e-4, g["dx_perm"], g["dx_shared"], b["pos"],
+                                   dout if stacked else None, g["dx"], g["dw_router"], ws, stream)
+            dout = g["dx"]
+        for l in range(L):
+            moe.moe_update_bias(shape, bufs[l]["counts"], params[l]["bias"], 1e-3, stream)
+
+    for i in range(args.warmup):
+        step(i, None)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i, i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    bwd_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    d, H, Hs, T, k = wl.d_model, wl.hidden, wl.shared_hidden, wl.tokens, wl.top_k
+    rows_h = T * k * H + T * Hs
+    algo = 12.0 * d * rows_h    # dgrad 6 d H + wgrad 6 d H per row
+    executed = 16.0 * d * rows_h  # plus the recompute of x W1^T, x W3^T
+    return {"ms_per_step": ms, "tokens_per_s": T * L / (ms * 1e-3),
+            "value_counts": "tokens x layers per second of forward + backward + bias update",
+            "backward_ffn_ms_per_launch": bwd_ms,
+            "backward_ffn_algorithmic_flop": algo, "backward_ffn_executed_flop": executed,
+            "backward_ffn_tflops": algo / (bwd_ms * 1e-3) / 1e12,
+            "backward_ffn_frac": algo / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "backward_ffn_executed_frac": executed / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "kernel": "moe_grouped_ffn_backward = the five grouped GEMMs of the routed experts "
+                      "and of the shared expert"}
 
 
 def hbm_read_probe():
@@ -242,6 +327,11 @@ def main():
         print(f"unknown workload {name!r}; one of {sorted(workloads.WORKLOADS)}", file=sys.stderr)
         sys.exit(2)
 
+    if args.with_backward and workloads.WORKLOADS[name].norm:
+        print("--with-backward: the backward of the pre-norm block's RMSNorm is not built",
+              file=sys.stderr)
+        sys.exit(2)
+
     if args.calibrate_copy:
         # a plain device-to-device copy of profiling.COPY_BYTES bytes, three times
         src = torch.empty(profiling.COPY_BYTES, dtype=torch.uint8, device="cuda:0").fill_(1)
@@ -401,6 +491,10 @@ def main():
         "update_bias_ms_per_step": bias_ms,
         "roofline": roof,
     }
+    if args.with_backward:
+        for l in range(L):
+            params[l]["bias"].copy_(bias0[l])
+        line["train"] = time_training(args, wl, shape, params, xs, stream)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds, params[0], xs[0])
     print(json.dumps(line), flush=True)

@@ -42,3 +42,12 @@ def test_first_timed_step_always_records_events():
     text = ast.get_source_segment(src, step)
     assert "timed % args.ffn_events_every == 0" in text
     assert "step(args.warmup + i, i)" in src
+
+
+def test_training_steps_of_the_normalised_block_are_refused():
+    """The RMSNorm of the pre-norm block has no backward here, so training
+    steps of that workload are refused before any GPU work."""
+    r = run_bench("--workload", "small_block_4096x4", "--with-backward")
+    assert r.returncode == 2
+    assert "RMSNorm" in r.stderr
+    assert r.stdout == ""
