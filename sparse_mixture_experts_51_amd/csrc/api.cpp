@@ -335,9 +335,31 @@ struct BwdWorkspace {
   float* freq;                     // [T/S, E]
   float* dlogit;                   // [T, E]
   float* dwr_part;                 // [splits, d, E]
+  float* wgrad_part;               // weight-gradient partial sums (split rows)
   int splits;
   size_t total;
 };
+// The weight-gradient launches of moe_grouped_ffn_backward: [0] dW2 = dy^T h,
+// [1] dW1 and dW3 = [da dc]^T x.  Segment 0 is the shared expert if there is
+// one, then the routed experts.
+struct WgradPlans {
+  int nseg;
+  moe::WgradPlan p[2];
+};
+WgradPlans wgrad_plans(const moe_shape* s) {
+  const int64_t T = s->tokens;
+  const int E = s->n_experts, H = s->hidden, Hs = s->shared_hidden, d = s->d_model;
+  const bool shared = Hs > 0;
+  WgradPlans w{};
+  w.nseg = shared ? 2 : 1;
+  const int64_t rows[2] = {shared ? T : T * s->top_k, T * s->top_k};
+  const int groups[2] = {shared ? 1 : E, E};
+  const int m2[2] = {d, d}, n2[2] = {shared ? Hs : H, H};
+  const int m13[2] = {2 * (shared ? Hs : H), 2 * H}, n13[2] = {d, d};
+  w.p[0] = moe::plan_wgrad(w.nseg, rows, groups, m2, n2);
+  w.p[1] = moe::plan_wgrad(w.nseg, rows, groups, m13, n13);
+  return w;
+}
 BwdWorkspace carve_bwd(const moe_shape* s, void* base) {
   BwdWorkspace w{};
   size_t off = 0;
@@ -361,6 +383,9 @@ BwdWorkspace carve_bwd(const moe_shape* s, void* base) {
   w.dlogit = reinterpret_cast<float*>(take(4 * T * E));
   w.splits = moe::route_bwd_splits(T);
   w.dwr_part = reinterpret_cast<float*>(take(4 * static_cast<int64_t>(w.splits) * d * E));
+  const WgradPlans wp = wgrad_plans(s);
+  w.wgrad_part = reinterpret_cast<float*>(
+      take(4 * static_cast<size_t>(std::max(wp.p[0].part_floats, wp.p[1].part_floats))));
   w.total = off;
   return w;
 }
@@ -419,48 +444,86 @@ moe_status moe_grouped_ffn_backward(const moe_shape* shape, const uint16_t* x,
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t T = shape->tokens;
   const int d = shape->d_model, E = shape->n_experts, H = shape->hidden, Hs = shape->shared_hidden;
-  hipError_t e = hipSuccess;
-  // one expert's (or the shared expert's) five GEMMs
-  auto run = [&](int groups, const int32_t* offs, int rows, int Hh, const uint16_t* xa,
-                 const uint16_t* dya, const uint16_t* W1, const uint16_t* W3, const uint16_t* W2,
-                 int64_t wstride, uint16_t* dh, uint16_t* h, uint16_t* da, uint16_t* dc,
-                 uint16_t* dxo, float* dW1, float* dW3, float* dW2) {
+  // segment 0: the shared expert (if any), then the routed experts
+  const int ns = shared ? 2 : 1;
+  moe::BwdSeg base[2]{};
+  for (int i = 0; i < ns; ++i) {
+    const bool sh = shared && i == 0;
+    base[i].groups = sh ? 1 : E;
+    base[i].offsets = sh ? nullptr : offsets;
+    base[i].rows = sh ? static_cast<int>(T) : 0;
+  }
+  auto seg_h = [&](int i) { return shared && i == 0 ? Hs : H; };
+  auto is_sh = [&](int i) { return shared && i == 0; };
+  auto launch = [&](auto&& fill, int kind) {
     moe::BwdGemmArgs g{};
-    g.groups = groups;
-    g.offsets = offs;
-    g.rows = rows;
-    // dh = dy W2  (W2 [d, H] read as [K, N])
-    g.ragged_k = 0; g.N = Hh; g.K = d; g.K2 = 0;
-    g.a = dya; g.lda = d; g.b = W2; g.ldb = Hh; g.b_gstride = wstride;
-    g.c = dh; g.ldc = Hh;
-    if ((e = moe::launch_bwd_gemm(g, moe::kBwdDgradKM, s)) != hipSuccess) return;
-    // a, c = x W1^T, x W3^T -> h, da, dc
-    moe::BwdGemmArgs r = g;
-    r.N = Hh; r.K = d; r.a = xa; r.lda = d; r.b = W1; r.b2 = W3; r.ldb = d;
-    r.c = nullptr; r.dh = dh; r.h = h; r.da = da; r.dc = dc; r.ld_h = Hh;
-    if ((e = moe::launch_bwd_gemm(r, moe::kBwdRecompute, s)) != hipSuccess) return;
-    // dx = da W1 + dc W3  (W1, W3 [H, d] read as [K, N])
-    moe::BwdGemmArgs x2 = g;
-    x2.N = d; x2.K = Hh; x2.K2 = Hh; x2.a = da; x2.a2 = dc; x2.lda = Hh;
-    x2.b = W1; x2.b2 = W3; x2.ldb = d; x2.c = dxo; x2.ldc = d;
-    if ((e = moe::launch_bwd_gemm(x2, moe::kBwdDgradKM, s)) != hipSuccess) return;
-    // dW2 = dy^T h,  dW1 = da^T x,  dW3 = dc^T x  (K = the group's rows)
-    moe::BwdGemmArgs wg{};
-    wg.groups = groups; wg.offsets = offs; wg.rows = rows; wg.ragged_k = 1;
-    wg.M = d; wg.N = Hh; wg.a = dya; wg.lda = d; wg.b = h; wg.ldb = Hh;
-    wg.c = dW2; wg.ldc = Hh; wg.c_gstride = static_cast<int64_t>(d) * Hh;
-    if ((e = moe::launch_bwd_gemm(wg, moe::kBwdWgrad, s)) != hipSuccess) return;
-    wg.M = Hh; wg.N = d; wg.a = da; wg.lda = Hh; wg.b = xa; wg.ldb = d;
-    wg.c = dW1; wg.ldc = d; wg.c_gstride = static_cast<int64_t>(Hh) * d;
-    if ((e = moe::launch_bwd_gemm(wg, moe::kBwdWgrad, s)) != hipSuccess) return;
-    wg.a = dc; wg.c = dW3;
-    e = moe::launch_bwd_gemm(wg, moe::kBwdWgrad, s);
+    g.nseg = ns;
+    for (int i = 0; i < ns; ++i) {
+      g.seg[i] = base[i];
+      fill(g.seg[i], i);
+    }
+    return moe::launch_bwd_gemm(g, kind, s);
   };
-  run(E, offsets, 0, H, x_perm, dy_perm, w1, w3, w2, static_cast<int64_t>(H) * d, w.dh, w.h, w.da,
-      w.dc, dx_perm, dw1, dw3, dw2);
-  if (e == hipSuccess && shared)
-    run(1, nullptr, static_cast<int>(T), Hs, x, dout, ws1, ws3, ws2, 0, w.dhs, w.hs, w.das, w.dcs,
-        dx_shared, dws1, dws3, dws2);
+  // dh = dy W2  (W2 [d, H] read as [K, N])
+  hipError_t e = launch(
+      [&](moe::BwdSeg& q, int i) {
+        const int Hh = seg_h(i);
+        q.N = Hh; q.K = d;
+        q.a = is_sh(i) ? dout : dy_perm; q.lda = d;
+        q.b = is_sh(i) ? ws2 : w2; q.ldb = Hh; q.b_gstride = is_sh(i) ? 0 : static_cast<int64_t>(d) * H;
+        q.c = is_sh(i) ? w.dhs : w.dh; q.ldc = Hh;
+      },
+      moe::kBwdDgradKM);
+  // a, c = x W1^T, x W3^T -> h, da, dc
+  if (e == hipSuccess)
+    e = launch(
+        [&](moe::BwdSeg& q, int i) {
+          const int Hh = seg_h(i);
+          q.N = Hh; q.K = d;
+          q.a = is_sh(i) ? x : x_perm; q.lda = d;
+          q.b = is_sh(i) ? ws1 : w1; q.b2 = is_sh(i) ? ws3 : w3; q.ldb = d;
+          q.b_gstride = is_sh(i) ? 0 : static_cast<int64_t>(H) * d;
+          q.dh = is_sh(i) ? w.dhs : w.dh; q.h = is_sh(i) ? w.hs : w.h;
+          q.da = is_sh(i) ? w.das : w.da; q.dc = is_sh(i) ? w.dcs : w.dc; q.ld_h = Hh;
+        },
+        moe::kBwdRecompute);
+  // dx = da W1 + dc W3  (W1, W3 [H, d] read as [K, N])
+  if (e == hipSuccess)
+    e = launch(
+        [&](moe::BwdSeg& q, int i) {
+          const int Hh = seg_h(i);
+          q.N = d; q.K = Hh; q.K2 = Hh;
+          q.a = is_sh(i) ? w.das : w.da; q.a2 = is_sh(i) ? w.dcs : w.dc; q.lda = Hh;
+          q.b = is_sh(i) ? ws1 : w1; q.b2 = is_sh(i) ? ws3 : w3; q.ldb = d;
+          q.b_gstride = is_sh(i) ? 0 : static_cast<int64_t>(H) * d;
+          q.c = is_sh(i) ? dx_shared : dx_perm; q.ldc = d;
+        },
+        moe::kBwdDgradKM);
+  // dW2 = dy^T h, then [dW1; dW3] = [da dc]^T x  (K = the group's rows)
+  const WgradPlans wp = wgrad_plans(shape);
+  if (e == hipSuccess)
+    e = launch(
+        [&](moe::BwdSeg& q, int i) {
+          const int Hh = seg_h(i);
+          q.M = d; q.N = Hh; q.M1 = d; q.split = wp.p[0].split;
+          q.a = is_sh(i) ? dout : dy_perm; q.lda = d;
+          q.b = is_sh(i) ? w.hs : w.h; q.ldb = Hh;
+          q.c = is_sh(i) ? dws2 : dw2; q.ldc = Hh; q.c_gstride = static_cast<int64_t>(d) * Hh;
+          q.part = w.wgrad_part + (i == 1 ? wp.p[0].slots[0] * d * seg_h(0) : 0);
+        },
+        moe::kBwdWgrad);
+  if (e == hipSuccess)
+    e = launch(
+        [&](moe::BwdSeg& q, int i) {
+          const int Hh = seg_h(i);
+          q.M = 2 * Hh; q.N = d; q.M1 = Hh; q.split = wp.p[1].split;
+          q.a = is_sh(i) ? w.das : w.da; q.a2 = is_sh(i) ? w.dcs : w.dc; q.lda = Hh;
+          q.b = is_sh(i) ? x : x_perm; q.ldb = d;
+          q.c = is_sh(i) ? dws1 : dw1; q.c2 = is_sh(i) ? dws3 : dw3; q.ldc = d;
+          q.c_gstride = static_cast<int64_t>(Hh) * d;
+          q.part = w.wgrad_part + (i == 1 ? wp.p[1].slots[0] * 2 * seg_h(0) * d : 0);
+        },
+        moe::kBwdWgrad);
   return hip_status(e);
 }
 

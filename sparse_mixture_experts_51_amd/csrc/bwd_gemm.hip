@@ -5,315 +5,677 @@
 // (moe_permute's order) and the upstream gradient already scaled by the gates
 // (moe_combine_backward), every product of an expert's backward is a GEMM over
 // contiguous rows, one per expert group:
-//   dh   = dy W2                      rows x H,  K = d        (dgrad)
+//   dh   = dy W2                      rows x H,  K = d        (input gradient)
 //   a, c = x W1^T, x W3^T  -> da, dc, h (SwiGLU derivative in the epilogue)
-//   dx   = da W1 + dc W3               rows x d,  K = 2H       (dgrad)
-//   dW2  = dy^T h                      d x H,     K = rows     (wgrad)
-//   dW1  = da^T x,  dW3 = dc^T x       H x d,     K = rows     (wgrad)
+//   dx   = da W1 + dc W3               rows x d,  K = 2H       (input gradient)
+//   dW2  = dy^T h                      d x H,     K = rows     (weight gradient)
+//   dW1  = da^T x,  dW3 = dc^T x       2H x d,    K = rows     (one launch)
 // so the weights are read as stored (W1, W3 [H, d]; W2 [d, H]) and the
 // operands come in two layouts: K contiguous (a row of K values) or K major
-// (a row per index of K).  The group's rows are the ragged M of a dgrad and
-// the ragged K of a wgrad; a group with no rows gets a zero weight gradient.
+// (a row per index of K).  The group's rows are the ragged M of an input
+// gradient and the ragged K of a weight gradient; a group with no rows gets
+// a zero weight gradient.  One launch covers the shared expert (one group of
+// all T rows, its own operands) and the routed experts.
 //
-// Tile 128 x 128 x 32, four waves of 64 x 64 (2 x 2 tiles of 32x32x16 MFMAs,
-// fp32 accumulators), two blocks per CU, persistent over units (group,
-// n-tile, m-tile) with the XCD-aware block order of the forward.  Tiles are
-// loaded to registers one K-step ahead (16-byte loads along the contiguous
-// direction) and stored to LDS in two stages.  A K-contiguous tile sits as
-// 64-byte rows (XOR-swizzled chunks) and gives a fragment per 16-byte read; a
-// K-major tile sits row per K index (rows padded by 16 bytes) and a fragment
-// is gathered from eight 2-byte reads.  The epilogue stores straight from the
-// accumulators: bf16 (input gradients, dh) or fp32 (weight gradients), or for
-// the recompute, h = silu(a) c, da = dh c silu'(a) and dc = dh silu(a).
+// Tile 128 x 128 x 64, four waves of 64 x 64 (2 x 2 MFMA tiles of 32x32x16,
+// fp32 accumulators), two blocks per CU, persistent over units (group, m-tile,
+// n-tile[, split]); each XCD runs an eighth of the units in order, so the
+// units of one group share its L2.  Each operand's K-step is loaded to
+// registers two steps ahead (kDepth): four 16-byte loads per thread, along
+// the contiguous direction.  Both layouts are staged in LDS
+// the same way, a row of the tile (an M or N index) holding its 64 K values as
+// eight 16-byte chunks, so every MFMA fragment is one 16-byte LDS read.  A
+// K-major operand gets there through a transpose in registers: a thread loads
+// 4 rows of K x 8 columns and writes 8 columns x 4 values of K (8 bytes each).
+// The chunk order within a row is XOR-swizzled with bits 1-3 of the row
+// (chunk ^ (row >> 1) ^ (row >> 3)): fragment reads and K-contiguous stores
+// hit 64 distinct banks per 16 lanes, the transposed stores two ways at most.
+//
+// Weight gradients with too few tiles to fill the chip (small d and H) split
+// a group's rows into pieces of `split` rows; each piece writes fp32 partial
+// sums and wgrad_reduce_kernel adds them in piece order, so the result does
+// not depend on timing.
 #include "common.hpp"
 #include "gemm_common.hpp"
 #include "kernels.hpp"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace moe {
 
 namespace {
-constexpr int kBTh = 256;                   // threads
-constexpr int kBBM = 128, kBBN = 128, kBBK = 32;
-constexpr int kBTM = 2, kBTN = 2;           // 32x32 tiles per wave
-constexpr int kKCh = kBBK / 8;              // 16-byte chunks per K-contiguous tile row (4)
-constexpr int kKMRow = kBBM + 8;            // K-major tile row in elements, padded (272 bytes)
-constexpr int kKMCh = kBBM / 8;             // 16-byte chunks per K-major tile row (16)
-constexpr int kBGroups = 1025;
-static_assert(kBBM == kBBN, "one staging layout serves both operands");
+constexpr int kTh = 256;                    // threads
+constexpr int kTM = 128, kTN = 128, kTK = 64;
+constexpr int kRowCh = kTK / 8;             // 16-byte chunks per staged row (8)
+constexpr int kStageU4 = kTM * kRowCh;      // one operand stage, in u32x4 (16 KB)
+constexpr int kMaxG = 1024 + 1;             // routed groups + the shared expert
+constexpr int kSplitTarget = 1024;          // weight-gradient units wanted per launch
+constexpr int kMinSplit = 512;              // rows per split at least (8 K-steps)
+#ifndef MOE_BWD_DEPTH
+#define MOE_BWD_DEPTH 2
+#endif
+constexpr int kDepth = MOE_BWD_DEPTH;       // K-steps loaded ahead, in registers
 
-__device__ __forceinline__ int bswz(int row, int chunk) {
-  return row * kKCh + (chunk ^ ((row >> 2) & (kKCh - 1)));
+static_assert(kTM == kTN, "one staging layout serves both operands");
+
+// u32x4 index of chunk c (8 values of K) of staged row r
+__device__ __forceinline__ int sidx(int r, int c) {
+  return r * kRowCh + ((c ^ (r >> 1) ^ (r >> 3)) & (kRowCh - 1));
+}
+
+__host__ __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// the segment's field f, for a wave-uniform segment index
+#define SEGF(sg, f) ((sg) ? a.seg[1].f : a.seg[0].f)
+
+// rows of group h of segment sg
+__device__ __forceinline__ int seg_group_rows(const BwdGemmArgs& a, int sg, int h) {
+  const int32_t* o = SEGF(sg, offsets);
+  return o ? o[h + 1] - o[h] : SEGF(sg, rows);
 }
 }  // namespace
 
-enum BwdEpi { kEpiBf16 = 0, kEpiF32 = 1, kEpiSwigluBwd = 2 };
-
-template <bool A_KC, bool B_KC, int EPI>
-__global__ __launch_bounds__(kBTh, 2) void bwd_gemm_kernel(BwdGemmArgs a) {
-  // staging: K-contiguous tiles as u32x4 [128 * 4], K-major tiles as
-  // uint16 [32][136]; one buffer per operand and stage, sized for the larger
-  constexpr int kStageU4 = (kBBK * kKMRow * 2 + 15) / 16 > kBBM * kKCh ? (kBBK * kKMRow * 2 + 15) / 16
-                                                                       : kBBM * kKCh;
-  __shared__ u32x4 lds_a[2][kStageU4];
-  __shared__ u32x4 lds_b[2][kStageU4];
-  __shared__ int unit_start[kBGroups + 1];
-  __shared__ int offs[kBGroups + 1];
-  __shared__ int wsum[kBTh / 64];
-  constexpr bool kPair = EPI == kEpiSwigluBwd;  // B rows [0,64) from b, [64,128) from b2
-  constexpr int kCols = kPair ? kBBN / 2 : kBBN;  // output columns per unit
+template <int KIND>
+__global__ __launch_bounds__(kTh, 2) void bwd_gemm_kernel(BwdGemmArgs a) {
+  // stages: A in lds[0], lds[1]; B in lds[2], lds[3].  The weight-gradient
+  // epilogue reuses lds[w] to stage wave w's 64 x 64 fp32 outputs.
+  __shared__ u32x4 lds[4][kStageU4];
+  u32x4 (*const lds_a)[kStageU4] = lds;
+  u32x4 (*const lds_b)[kStageU4] = lds + 2;
+  __shared__ int ustart[kMaxG + 1];  // first unit of each group
+  __shared__ int goff[kMaxG + 1];    // first row of each group in its segment's arrays
+  __shared__ int pslot[kMaxG + 1];   // wgrad: first partial-sum slot of each group
+  __shared__ int wsum[kTh / 64];
+  constexpr bool kDgrad = KIND == kBwdDgradKM;
+  constexpr bool kPair = KIND == kBwdRecompute;  // B rows [0,64) from b, [64,128) from b2
+  constexpr bool kWgrad = KIND == kBwdWgrad;
+  constexpr int kCols = kPair ? kTN / 2 : kTN;   // output columns per unit
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uni(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int G = a.groups;
-  auto group_rows = [&](int g) -> int {
-    return a.offsets ? a.offsets[g + 1] - a.offsets[g] : a.rows;
-  };
-  // ---- unit table
+  const int G0 = a.seg[0].groups;
+  const int G = G0 + (a.nseg > 1 ? a.seg[1].groups : 0);
+
+  // ---- unit table: per group, units = m-tiles x n-tiles x splits
   {
-    constexpr int kPer = (kBGroups + kBTh - 1) / kBTh;
-    const int per = (G + kBTh - 1) / kBTh;
-    int local[kPer];
-    int sum = 0;
-    for (int i = 0; i < per; ++i) {
-      const int g = tid * per + i;
-      int u = 0;
-      if (g < G) offs[g] = a.offsets ? a.offsets[g] : 0;
-      if (g < G) {
-        const int mt = a.ragged_k ? (a.M + kBBM - 1) / kBBM : (group_rows(g) + kBBM - 1) / kBBM;
-        u = mt * ((a.N + kCols - 1) / kCols);
+    constexpr int kPer = (kMaxG + kTh - 1) / kTh;
+    int lu[kPer], lp[kPer];
+    int su = 0, sp = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int gg = tid * kPer + i;
+      int u = 0, p = 0;
+      if (gg < G) {
+        const int sg = gg >= G0 ? 1 : 0;
+        const int h = gg - (sg ? G0 : 0);
+        const int32_t* o = SEGF(sg, offsets);
+        goff[gg] = o ? o[h] : 0;
+        const int R = seg_group_rows(a, sg, h);
+        if constexpr (kWgrad) {
+          const int split = SEGF(sg, split);
+          const int ns = split > 0 ? std::max(1, cdiv(R, split)) : 1;
+          u = cdiv(SEGF(sg, M), kTM) * cdiv(SEGF(sg, N), kTN) * ns;
+          p = ns > 1 ? ns : 0;
+        } else {
+          u = cdiv(R, kTM) * cdiv(SEGF(sg, N), kCols);
+        }
       }
-      local[i] = u;
-      sum += u;
+      lu[i] = u;
+      lp[i] = p;
+      su += u;
+      sp += p;
     }
-    int total;
-    int run = block_scan<kBTh>(sum, &total, wsum);
-    for (int i = 0; i < per; ++i) {
-      const int g = tid * per + i;
-      if (g < G) unit_start[g] = run;
-      run += local[i];
+    int tot_u, tot_p;
+    int run_u = block_scan<kTh>(su, &tot_u, wsum);
+    int run_p = block_scan<kTh>(sp, &tot_p, wsum);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int gg = tid * kPer + i;
+      if (gg < G) {
+        ustart[gg] = run_u;
+        pslot[gg] = run_p;
+      }
+      run_u += lu[i];
+      run_p += lp[i];
     }
     if (tid == 0) {
-      unit_start[G] = total;
-      offs[G] = a.offsets ? a.offsets[G] : a.rows;
+      ustart[G] = tot_u;
+      pslot[G] = tot_p;
     }
     __syncthreads();
   }
-  const int total_units = uni(unit_start[G]);
-  const int NB = gridDim.x;
-  const int lb = (blockIdx.x % kXcds) * (NB / kXcds) + blockIdx.x / kXcds;
+  const int total_units = uni(ustart[G]);
+  const int seg1_slot0 = uni(pslot[G0]);  // slots of segment 0 (segment 1 counts its own from 0)
+  // XCD x (blocks b with b % 8 == x) takes the x-th eighth of the units in
+  // order, so the units of a group (which share their rows and weights) run
+  // on one XCD and its L2
+  const int xcd = blockIdx.x % kXcds, per_xcd = gridDim.x / kXcds;
+  const int u_lo = static_cast<int>(static_cast<int64_t>(total_units) * xcd / kXcds);
+  const int u_hi = static_cast<int>(static_cast<int64_t>(total_units) * (xcd + 1) / kXcds);
 
-  // fragments of the MFMAs: weight-side (B) first, so a lane holds output row
-  // (lane & 31) and columns 8g + 4(lane >> 5) + 0..3 of each 32x32 tile
+  // fragments: weight-side (B) operand first, so a lane holds output row
+  // (lane & 31) and columns 8q + 4(lane >> 5) + 0..3 of each 32x32 tile
   const int fr = lane & 31, fhalf = lane >> 5;
-  auto read_frag = [&](const u32x4* buf, bool kc, int row, int ks) -> bf16x8 {
-    const int ch = 2 * ks + fhalf;
-    if (kc) return __builtin_bit_cast(bf16x8, buf[bswz(row, ch)]);
-    const uint16_t* e = reinterpret_cast<const uint16_t*>(buf) + (8 * ch) * kKMRow + row;
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      w[i] = static_cast<uint32_t>(e[(2 * i) * kKMRow]) | (static_cast<uint32_t>(e[(2 * i + 1) * kKMRow]) << 16);
-    return __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
-  };
+  // K-contiguous loads: chunk q = tid + 256 p is row q / 8, chunk q % 8;
+  // K-major loads: rows 4 kb .. 4 kb + 3 of K at columns 8 cb .. 8 cb + 7
+  const int cb = tid & 15, kb = tid >> 4;
 
-  for (int u = lb; u < total_units; u += NB) {
-    // ---- decode the unit (uniform)
+  // ---- a unit: its uniform description
+  struct Unit {
+    int gg, sg, g, off, R, M, N, K, m0, n0, kbeg, kend, nk, split_idx, nsplit;
+  };
+  auto decode = [&](int u) {
+    Unit t;
     int below = 0;
     for (int base = 0; base < G; base += 64) {
-      const int g = base + lane;
-      below += __popcll(__ballot(g < G && unit_start[g] <= u));
+      const int gi = base + lane;
+      below += __popcll(__ballot(gi < G && ustart[gi] <= u));
     }
-    const int g = uni(below - 1);
-    const int R = uni(offs[g + 1] - offs[g]);
-    const int off = uni(offs[g]);
-    const int mrows = a.ragged_k ? a.M : R;
-    const int mt = (mrows + kBBM - 1) / kBBM;
-    const int local = u - uni(unit_start[g]);
-    const int m0 = (local % mt) * kBBM;
-    const int n0 = (local / mt) * kCols;
-    const int Ktot = a.ragged_k ? R : a.K + a.K2;
-    const int nk = (Ktot + kBBK - 1) / kBBK;
-    const uint16_t* bg = a.b + static_cast<int64_t>(g) * a.b_gstride;
-    const uint16_t* bg2 = a.b2 ? a.b2 + static_cast<int64_t>(g) * a.b_gstride : nullptr;
+    t.gg = uni(below - 1);
+    t.sg = t.gg >= G0 ? 1 : 0;
+    t.g = t.gg - (t.sg ? G0 : 0);
+    t.off = uni(goff[t.gg]);
+    t.R = uni(seg_group_rows(a, t.sg, t.g));
+    const int local = u - uni(ustart[t.gg]);
+    t.M = SEGF(t.sg, M);
+    t.N = SEGF(t.sg, N);
+    t.K = SEGF(t.sg, K);
+    t.split_idx = 0;
+    t.nsplit = 1;
+    if constexpr (kWgrad) {
+      const int split = SEGF(t.sg, split);
+      t.nsplit = split > 0 ? std::max(1, cdiv(t.R, split)) : 1;
+      const int mt = cdiv(t.M, kTM);
+      const int tiles = mt * cdiv(t.N, kTN);
+      t.split_idx = local / tiles;
+      const int r = local - t.split_idx * tiles;
+      t.m0 = (r % mt) * kTM;
+      t.n0 = (r / mt) * kTN;
+      t.kbeg = t.nsplit > 1 ? t.split_idx * split : 0;
+      t.kend = t.nsplit > 1 ? std::min(t.R, t.kbeg + split) : t.R;
+    } else {
+      const int mt = cdiv(t.R, kTM);
+      t.m0 = (local % mt) * kTM;
+      t.n0 = (local / mt) * kCols;
+      t.kbeg = 0;
+      t.kend = t.K + SEGF(t.sg, K2);
+    }
+    t.nk = cdiv(t.kend - t.kbeg, kTK);
+    return t;
+  };
 
-    // ---- loads of K-step kt into registers: two 16-byte chunks per operand
-    // and thread; out-of-range elements are zero
-    auto load_tile = [&](bool is_a, bool kc, int kt, u32x4 (&v)[2]) {
-      const int k0 = kt * kBBK;
+  // ---- per-thread load addressing of the unit being loaded.  Loads are not
+  // predicated: an out-of-range chunk reads a valid address of the unit and
+  // is zeroed when it is stored to LDS, so the compiler can wait for one
+  // K-step's loads while later ones are in flight.
+  const uint16_t *A = nullptr, *A2 = nullptr, *B = nullptr, *B2 = nullptr;
+  int64_t lda = 0, ldb = 0, bgs = 0;
+  int a_row[4];                    // K-contiguous A: element offset of the row
+  bool a_ok[4];                    // ... inside the group
+  const uint16_t* kc_b[4];         // recompute B: weight row pointers
+  bool b_ok[4];                    // ... inside N
+  const uint16_t* km_a = nullptr;  // wgrad A: column base (in a or a2)
+  const uint16_t* km_a_row = nullptr;  // wgrad: this thread's first row of A and of B
+  const uint16_t* km_b_row = nullptr;
+  bool km_a_ok = false;
+  int km_b_col = 0;                // K-major B: first column
+  bool km_b_ok = false;
+  auto setup = [&](const Unit& t) {
+    A = SEGF(t.sg, a);
+    A2 = SEGF(t.sg, a2);
+    lda = SEGF(t.sg, lda);
+    B = SEGF(t.sg, b);
+    B2 = SEGF(t.sg, b2);
+    ldb = SEGF(t.sg, ldb);
+    bgs = static_cast<int64_t>(t.g) * SEGF(t.sg, b_gstride);
+    if constexpr (!kWgrad) {
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const int q = tid + kBTh * p;
-        v[p] = u32x4{0u, 0u, 0u, 0u};
-        if (kc) {
-          const int row = q / kKCh, ch = q % kKCh;  // row of the M (or N) tile, chunk of K
-          const int kk = k0 + ch * 8;
-          if (is_a) {
-            // A K-contiguous: dgrad rows (ragged M) of a [rows, K] (+ a2 for K2)
-            const int r = m0 + row;
-            if (r < mrows && kk < Ktot) {
-              const bool second = kk >= a.K;
-              const uint16_t* src = second ? a.a2 : a.a;
-              v[p] = *reinterpret_cast<const u32x4*>(src + static_cast<int64_t>(off + r) * a.lda +
-                                                       (second ? kk - a.K : kk));
-            }
-          } else {
-            // B K-contiguous: weight rows [N, K]; the pair layout takes rows
-            // [0, 64) from b and [64, 128) from b2 at the same columns
-            const int nrow = kPair ? n0 + (row % kCols) : n0 + row;
-            const uint16_t* src = kPair && row >= kCols ? bg2 : bg;
-            if (nrow < a.N && kk < Ktot) v[p] = *reinterpret_cast<const u32x4*>(src + static_cast<int64_t>(nrow) * a.ldb + kk);
-          }
-        } else {
-          const int krow = q / kKMCh, ch = q % kKMCh;  // index of K, chunk of M (or N)
-          const int kk = k0 + krow;
-          const int col = (is_a ? m0 : n0) + ch * 8;
-          const int ncols = is_a ? a.M : a.N;
-          if (kk < Ktot && col < ncols) {
-            if (a.ragged_k) {
-              // wgrad: both operands are expert-grouped rows (index of K = row)
-              const uint16_t* src = is_a ? a.a : a.b;
-              const int64_t ld = is_a ? a.lda : a.ldb;
-              v[p] = *reinterpret_cast<const u32x4*>(src + static_cast<int64_t>(off + kk) * ld + col);
-            } else {
-              // dgrad B K-major: a weight stored [K, N] (+ b2 for K2)
-              const bool second = kk >= a.K;
-              const uint16_t* src = second ? bg2 : bg;
-              v[p] = *reinterpret_cast<const u32x4*>(src + static_cast<int64_t>(second ? kk - a.K : kk) * a.ldb + col);
-            }
-          }
+      for (int p = 0; p < 4; ++p) {
+        const int row = (tid + kTh * p) >> 3;
+        a_ok[p] = t.m0 + row < t.R;
+        a_row[p] = (t.off + (a_ok[p] ? t.m0 + row : t.m0)) * static_cast<int>(lda);
+      }
+    }
+    if constexpr (kPair) {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int row = (tid + kTh * p) >> 3;
+        const int wrow = t.n0 + (row & (kCols - 1));
+        b_ok[p] = wrow < t.N;
+        kc_b[p] = (row < kCols ? B : B2) + bgs + static_cast<int64_t>(b_ok[p] ? wrow : t.n0) * ldb;
+      }
+    }
+    if constexpr (kDgrad || kWgrad) {
+      km_b_ok = t.n0 + 8 * cb < t.N;
+      km_b_col = km_b_ok ? t.n0 + 8 * cb : t.n0;
+    }
+    if constexpr (kWgrad) {
+      const int M1 = SEGF(t.sg, M1);
+      const int m = t.m0 + 8 * cb;
+      km_a_ok = m < t.M;
+      km_a = !km_a_ok ? A : (m < M1 ? A + m : A2 + (m - M1));
+      // rows 4 kb of the unit's first K-step (full K-steps advance from here)
+      km_a_row = km_a + static_cast<int64_t>(t.off + t.kbeg + 4 * kb) * lda;
+      km_b_row = B + static_cast<int64_t>(t.off + t.kbeg + 4 * kb) * ldb + km_b_col;
+    }
+  };
+
+  // ---- loads of K-step kt (16-byte chunks)
+  auto load_a = [&](const Unit& t, int kt, u32x4 (&v)[4]) {
+    const int k0 = t.kbeg + kt * kTK;
+    if constexpr (kWgrad) {
+      if (k0 + kTK <= t.kend) {
+        const uint16_t* p = km_a_row + static_cast<int64_t>(kt) * kTK * lda;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const u32x4*>(p + i * lda);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kk = std::min(k0 + 4 * kb + i, t.kend - 1);
+          v[i] = *reinterpret_cast<const u32x4*>(km_a + static_cast<int64_t>(t.off + kk) * lda);
         }
       }
-    };
-    auto store_tile = [&](u32x4* buf, bool kc, const u32x4 (&v)[2]) {
+    } else {
+      const bool second = k0 >= t.K;
+      const uint16_t* base = (second ? A2 : A) + (second ? k0 - t.K : k0);
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const int q = tid + kBTh * p;
-        if (kc) {
-          buf[bswz(q / kKCh, q % kKCh)] = v[p];
-        } else {
-          uint16_t* e = reinterpret_cast<uint16_t*>(buf) + (q / kKMCh) * kKMRow + (q % kKMCh) * 8;
-          *reinterpret_cast<u32x4*>(e) = v[p];
+      for (int p = 0; p < 4; ++p) {
+        const int ch = (tid + kTh * p) & 7;
+        v[p] = *reinterpret_cast<const u32x4*>(base + a_row[p] + 8 * ch);
+      }
+    }
+  };
+  auto load_b = [&](const Unit& t, int kt, u32x4 (&v)[4]) {
+    const int k0 = t.kbeg + kt * kTK;
+    if constexpr (kWgrad) {
+      if (k0 + kTK <= t.kend) {
+        const uint16_t* p = km_b_row + static_cast<int64_t>(kt) * kTK * ldb;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const u32x4*>(p + i * ldb);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kk = std::min(k0 + 4 * kb + i, t.kend - 1);
+          v[i] = *reinterpret_cast<const u32x4*>(B + static_cast<int64_t>(t.off + kk) * ldb + km_b_col);
         }
       }
-    };
-
-    f32x16 acc[kBTM][kBTN];
+    } else if constexpr (kDgrad) {
+      // a weight stored [K, N] (+ b2 for the K2 rows after K)
+      const bool second = k0 >= t.K;
+      const uint16_t* base = (second ? B2 : B) + bgs +
+                             static_cast<int64_t>((second ? k0 - t.K : k0) + 4 * kb) * ldb + km_b_col;
 #pragma unroll
-    for (int i = 0; i < kBTM; ++i)
+      for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const u32x4*>(base + i * ldb);
+    } else {
 #pragma unroll
-      for (int j = 0; j < kBTN; ++j) acc[i][j] = f32x16{};
-    // this wave's 32-row tiles (rows 32 (wm + 2 i)) and weight rows
-    auto tile_row = [&](int i) { return 32 * (wm + 2 * i); };
-    auto brow = [&](int j) { return kPair ? (j == 0 ? wn * 32 : kCols + wn * 32) : wn * 64 + 32 * j; };
-
-    u32x4 va[2], vb[2];
-    if (nk > 0) {
-      load_tile(true, A_KC, 0, va);
-      load_tile(false, B_KC, 0, vb);
-      store_tile(lds_a[0], A_KC, va);
-      store_tile(lds_b[0], B_KC, vb);
+      for (int p = 0; p < 4; ++p) {
+        const int ch = (tid + kTh * p) & 7;
+        v[p] = *reinterpret_cast<const u32x4*>(kc_b[p] + k0 + 8 * ch);
+      }
     }
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int st = kt & 1;
-      const bool more = kt + 1 < nk;
-      if (more) {
-        load_tile(true, A_KC, kt + 1, va);
-        load_tile(false, B_KC, kt + 1, vb);
-      }
+  };
+  // ---- stores of a loaded K-step into a stage (out-of-range chunks as zero)
+  const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
+  auto store_kc = [&](u32x4* buf, const u32x4 (&v)[4], const bool (&ok)[4]) {
 #pragma unroll
-      for (int ks = 0; ks < kBBK / 16; ++ks) {
-        bf16x8 af[kBTM], bfr[kBTN];
-#pragma unroll
-        for (int i = 0; i < kBTM; ++i) af[i] = read_frag(lds_a[st], A_KC, tile_row(i) + fr, ks);
-#pragma unroll
-        for (int j = 0; j < kBTN; ++j) bfr[j] = read_frag(lds_b[st], B_KC, brow(j) + fr, ks);
-#pragma unroll
-        for (int i = 0; i < kBTM; ++i)
-#pragma unroll
-          for (int j = 0; j < kBTN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
-      }
-      if (more) {
-        store_tile(lds_a[st ^ 1], A_KC, va);
-        store_tile(lds_b[st ^ 1], B_KC, vb);
-      }
-      __syncthreads();
+    for (int p = 0; p < 4; ++p) {
+      const int q = tid + kTh * p;
+      buf[sidx(q >> 3, q & 7)] = ok[p] ? v[p] : zero4;
     }
-
-    // ---- epilogue
-    const int lcol = fhalf * 4;
+  };
+  auto store_km = [&](u32x4* buf, const u32x4 (&v)[4], bool col_ok, const Unit& t, int kt) {
+    // column j of the 8 loaded: values of K 4 kb .. 4 kb + 3 -> 8 bytes of
+    // chunk kb / 2 of staged row 8 cb + j
+    const int krow = t.kbeg + kt * kTK + 4 * kb;
+    u32x4 z[4];
 #pragma unroll
-    for (int i = 0; i < kBTM; ++i) {
-      const int r = m0 + tile_row(i) + fr;  // row of the output (within the group for dgrad)
-      if (r >= mrows) continue;
-      if constexpr (EPI == kEpiSwigluBwd) {
-        const int64_t row = static_cast<int64_t>(off + r);
+    for (int i = 0; i < 4; ++i) z[i] = col_ok && krow + i < t.kend ? v[i] : zero4;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int w = j >> 1;
+      uint32_t lo, hi;
+      if (j & 1) {
+        lo = (z[0][w] >> 16) | (z[1][w] & 0xFFFF0000u);
+        hi = (z[2][w] >> 16) | (z[3][w] & 0xFFFF0000u);
+      } else {
+        lo = (z[0][w] & 0xFFFFu) | (z[1][w] << 16);
+        hi = (z[2][w] & 0xFFFFu) | (z[3][w] << 16);
+      }
+      uint2* dst = reinterpret_cast<uint2*>(buf + sidx(8 * cb + j, kb >> 1)) + (kb & 1);
+      *dst = make_uint2(lo, hi);
+    }
+  };
+  auto store_a = [&](u32x4* buf, const u32x4 (&v)[4], const Unit& t, int kt) {
+    if constexpr (kWgrad) store_km(buf, v, km_a_ok, t, kt);
+    else store_kc(buf, v, a_ok);
+  };
+  auto store_b = [&](u32x4* buf, const u32x4 (&v)[4], const Unit& t, int kt) {
+    if constexpr (kPair) store_kc(buf, v, b_ok);
+    else store_km(buf, v, km_b_ok, t, kt);
+  };
+
+  f32x16 acc[2][2];
+  auto arow = [&](int i) { return 64 * wm + 32 * i + fr; };
+  auto brow = [&](int j) { return (kPair ? (j == 0 ? 32 * wn : kCols + 32 * wn) : 64 * wn + 32 * j) + fr; };
+  auto compute = [&](const u32x4* sa, const u32x4* sb) {
+#pragma unroll
+    for (int ks = 0; ks < kTK / 16; ++ks) {
+      bf16x8 af[2], bfr[2];
+      const int ch = 2 * ks + fhalf;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) af[i] = __builtin_bit_cast(bf16x8, sa[sidx(arow(i), ch)]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) bfr[j] = __builtin_bit_cast(bf16x8, sb[sidx(brow(j), ch)]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // kDepth K-steps in registers: slot s holds the K-step that goes to stage s
+  // next; stage kt & 1 holds K-step kt while it is multiplied.  A unit's
+  // first kDepth K-steps are loaded before the previous unit's epilogue.
+  u32x4 ra[kDepth][4], rb[kDepth][4];
+  auto load_first = [&](const Unit& t) {
+    if (t.nk > 0) {
+      load_a(t, 0, ra[0]);
+      load_b(t, 0, rb[0]);
+    }
+    if constexpr (kDepth == 2) {
+      if (t.nk > 1) {
+        load_a(t, 1, ra[1]);
+        load_b(t, 1, rb[1]);
+      }
+    }
+  };
+  const int lcol = fhalf * 4;
+  // recompute epilogue: dh of this lane's outputs, read before the next
+  // unit's loads are issued
+  uint2 dhv[2][4];
+  auto epilogue_loads = [&](const Unit& t) {
+    if constexpr (kPair) {
+      const int64_t ldh = SEGF(t.sg, ld_h);
+      const uint16_t* dhp = SEGF(t.sg, dh);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = std::min(t.m0 + 64 * wm + 32 * i + fr, t.R - 1);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int col = n0 + wn * 32 + 8 * q + lcol;
-          if (col >= a.N) continue;
-          const uint2 dhv = *reinterpret_cast<const uint2*>(a.dh + row * a.ld_h + col);
-          const float dhf[4] = {bf16_to_f32(static_cast<uint16_t>(dhv.x)), bf16_to_f32(static_cast<uint16_t>(dhv.x >> 16)),
-                                bf16_to_f32(static_cast<uint16_t>(dhv.y)), bf16_to_f32(static_cast<uint16_t>(dhv.y >> 16))};
+          const int col = std::min(t.n0 + 32 * wn + 8 * q + lcol, t.N - 4);
+          dhv[i][q] = *reinterpret_cast<const uint2*>(dhp + static_cast<int64_t>(t.off + r) * ldh + col);
+        }
+      }
+    }
+  };
+  auto epilogue = [&](const Unit& t) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = t.m0 + 64 * wm + 32 * i + fr;  // output row (within the group for input gradients)
+      if constexpr (kPair) {
+        if (r >= t.R) continue;
+        const int64_t row = static_cast<int64_t>(t.off + r);
+        const int64_t ldh = SEGF(t.sg, ld_h);
+        uint16_t* hp = SEGF(t.sg, h);
+        uint16_t* dap = SEGF(t.sg, da);
+        uint16_t* dcp = SEGF(t.sg, dc);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = t.n0 + 32 * wn + 8 * q + lcol;
+          if (col >= t.N) continue;
+          const uint2 dv = dhv[i][q];
+          const float dhf[4] = {bf16_to_f32(static_cast<uint16_t>(dv.x)), bf16_to_f32(static_cast<uint16_t>(dv.x >> 16)),
+                                bf16_to_f32(static_cast<uint16_t>(dv.y)), bf16_to_f32(static_cast<uint16_t>(dv.y >> 16))};
           float hv[4], dav[4], dcv[4];
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const float ga = acc[i][0][4 * q + t], up = acc[i][1][4 * q + t];
-            const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-ga));
-            hv[t] = ga * sg * up;  // the forward's h, bit for bit
-            dav[t] = dhf[t] * up * sg * (1.0f + ga * (1.0f - sg));
-            dcv[t] = dhf[t] * ga * sg;
+          for (int e = 0; e < 4; ++e) {
+            const float ga = acc[i][0][4 * q + e], up = acc[i][1][4 * q + e];
+            const float sgm = __builtin_amdgcn_rcpf(1.0f + __expf(-ga));
+            hv[e] = ga * sgm * up;  // the forward's h, bit for bit
+            dav[e] = dhf[e] * up * sgm * (1.0f + ga * (1.0f - sgm));
+            dcv[e] = dhf[e] * ga * sgm;
           }
           auto pack4 = [](const float (&f)[4]) {
             return make_uint2(bf16x2_bits(f[0], f[1]), bf16x2_bits(f[2], f[3]));
           };
-          *reinterpret_cast<uint2*>(a.h + row * a.ld_h + col) = pack4(hv);
-          *reinterpret_cast<uint2*>(a.da + row * a.ld_h + col) = pack4(dav);
-          *reinterpret_cast<uint2*>(a.dc + row * a.ld_h + col) = pack4(dcv);
+          *reinterpret_cast<uint2*>(hp + row * ldh + col) = pack4(hv);
+          *reinterpret_cast<uint2*>(dap + row * ldh + col) = pack4(dav);
+          *reinterpret_cast<uint2*>(dcp + row * ldh + col) = pack4(dcv);
         }
-      } else {
+      } else if constexpr (kDgrad) {
+        if (r >= t.R) continue;
+        uint16_t* crow = static_cast<uint16_t*>(SEGF(t.sg, c)) + static_cast<int64_t>(t.off + r) * SEGF(t.sg, ldc);
 #pragma unroll
-        for (int j = 0; j < kBTN; ++j) {
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const int col = n0 + wn * 64 + 32 * j + 8 * q + lcol;
-            if (col >= a.N) continue;
-            const float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                                acc[i][j][4 * q + 3]};
-            if constexpr (EPI == kEpiF32) {
-              float* c = static_cast<float*>(a.c) + static_cast<int64_t>(g) * a.c_gstride +
-                         static_cast<int64_t>(r) * a.ldc + col;
-              *reinterpret_cast<float4*>(c) = make_float4(v[0], v[1], v[2], v[3]);
-            } else {
-              uint16_t* c = static_cast<uint16_t*>(a.c) + static_cast<int64_t>(off + r) * a.ldc + col;
-              *reinterpret_cast<uint2*>(c) = make_uint2(bf16x2_bits(v[0], v[1]), bf16x2_bits(v[2], v[3]));
-            }
+            const int col = t.n0 + 64 * wn + 32 * j + 8 * q + lcol;
+            if (col >= t.N) continue;
+            const f32x16& v = acc[i][j];
+            *reinterpret_cast<uint2*>(crow + col) =
+                make_uint2(bf16x2_bits(v[4 * q], v[4 * q + 1]), bf16x2_bits(v[4 * q + 2], v[4 * q + 3]));
+          }
+      }
+    }
+    if constexpr (kWgrad) {
+      // through LDS, so that a store instruction writes whole rows of 256
+      // bytes: this wave's 64 x 64 outputs as 64 rows of 16 chunks of four
+      // values, chunk c of row r at (c ^ (r & 15)); no other wave reads them
+      u32x4* stg = lds[wave];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int rr = 32 * i + fr, ch = 8 * j + 2 * q + fhalf;
+            const f32x16& v = acc[i][j];
+            stg[rr * 16 + (ch ^ (rr & 15))] =
+                u32x4{__float_as_uint(v[4 * q]), __float_as_uint(v[4 * q + 1]),
+                      __float_as_uint(v[4 * q + 2]), __float_as_uint(v[4 * q + 3])};
+          }
+      // M, N and M1 are multiples of 64: a wave's 64 x 64 block lies wholly
+      // inside or outside them, on one side of M1
+      const int rw = t.m0 + 64 * wm, cw = t.n0 + 64 * wn;
+      if (rw < t.M && cw < t.N) {
+        float* base;
+        int64_t ld;
+        if (t.nsplit > 1) {
+          const int slot = uni(pslot[t.gg]) - (t.sg ? seg1_slot0 : 0) + t.split_idx;
+          base = SEGF(t.sg, part) + (static_cast<int64_t>(slot) * t.M + rw) * t.N + cw;
+          ld = t.N;
+        } else {
+          const int M1 = SEGF(t.sg, M1);
+          const bool first = rw < M1;
+          base = static_cast<float*>(first ? SEGF(t.sg, c) : SEGF(t.sg, c2)) +
+                 static_cast<int64_t>(t.g) * SEGF(t.sg, c_gstride) +
+                 static_cast<int64_t>(first ? rw : rw - M1) * SEGF(t.sg, ldc) + cw;
+          ld = SEGF(t.sg, ldc);
+        }
+        u32x4* out = reinterpret_cast<u32x4*>(base + (lane >> 4) * ld + 4 * (lane & 15));
+        const int64_t step4 = ld;  // four rows of fp32, in u32x4
+        if (t.nsplit > 1) {
+          // partial sums: read back by wgrad_reduce_kernel, kept in L2
+#pragma unroll
+          for (int it = 0; it < 16; ++it) {
+            const int rr = 4 * it + (lane >> 4);
+            out[it * step4] = stg[rr * 16 + ((lane & 15) ^ (rr & 15))];
+          }
+        } else {
+          // final gradients: streamed past L2, which keeps the operands
+#pragma unroll
+          for (int it = 0; it < 16; ++it) {
+            const int rr = 4 * it + (lane >> 4);
+            __builtin_nontemporal_store(stg[rr * 16 + ((lane & 15) ^ (rr & 15))], out + it * step4);
           }
         }
       }
+      __syncthreads();  // the staging is the next unit's first stage
     }
+  };
+
+  int u = u_lo + static_cast<int>(blockIdx.x) / kXcds;
+  bool have = u < u_hi;
+  Unit cur{};
+  if (have) {
+    cur = decode(u);
+    setup(cur);
+    load_first(cur);
   }
+  while (have) {
+    if (cur.nk > 0) {
+      store_a(lds_a[0], ra[0], cur, 0);
+      store_b(lds_b[0], rb[0], cur, 0);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    auto step = [&](auto st_c, int kt) {
+      constexpr int st = decltype(st_c)::value;       // == kt & 1
+      constexpr int next = kDepth == 2 ? st ^ 1 : 0;  // slot of K-step kt + 1
+      if constexpr (kDepth == 2) {
+        if (kt + 2 < cur.nk) {
+          load_a(cur, kt + 2, ra[st]);
+          load_b(cur, kt + 2, rb[st]);
+        }
+      } else {
+        if (kt + 1 < cur.nk) {
+          load_a(cur, kt + 1, ra[0]);
+          load_b(cur, kt + 1, rb[0]);
+        }
+      }
+      compute(lds_a[st], lds_b[st]);
+      if (kt + 1 < cur.nk) {
+        store_a(lds_a[st ^ 1], ra[next], cur, kt + 1);
+        store_b(lds_b[st ^ 1], rb[next], cur, kt + 1);
+      }
+      __syncthreads();
+    };
+    for (int kt = 0; kt < cur.nk; kt += 2) {
+      step(std::integral_constant<int, 0>{}, kt);
+      if (kt + 1 < cur.nk) step(std::integral_constant<int, 1>{}, kt + 1);
+    }
+    // the next unit's first loads go out before this unit's stores
+    epilogue_loads(cur);
+    const int un = u + per_xcd;
+    const bool have_next = un < u_hi;
+    Unit nxt{};
+    if (have_next) {
+      nxt = decode(un);
+      setup(nxt);
+      load_first(nxt);
+    }
+    epilogue(cur);
+    cur = nxt;
+    u = un;
+    have = have_next;
+  }
+}
+
+// Sum of a split group's partial sums, in split order, into the weight
+// gradient.  blockIdx.y = group over both segments, x strides over M x N.
+__global__ __launch_bounds__(256) void wgrad_reduce_kernel(BwdGemmArgs a) {
+  __shared__ int before_s;
+  const int G0 = a.seg[0].groups;
+  const int gg = blockIdx.y;
+  const int sg = gg >= G0 ? 1 : 0;
+  const int g = gg - (sg ? G0 : 0);
+  const int split = SEGF(sg, split);
+  const int R = seg_group_rows(a, sg, g);
+  const int ns = split > 0 ? std::max(1, cdiv(R, split)) : 1;
+  if (ns <= 1) return;  // written by the GEMM itself
+  if (threadIdx.x < 64) {
+    int before = 0;  // slots of the segment's groups before g
+    for (int h = threadIdx.x; h < g; h += 64) {
+      const int n = std::max(1, cdiv(seg_group_rows(a, sg, h), split));
+      before += n > 1 ? n : 0;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) before += __shfl_xor(before, o, 64);
+    if (threadIdx.x == 0) before_s = before;
+  }
+  __syncthreads();
+  const int M = SEGF(sg, M), N = SEGF(sg, N), M1 = SEGF(sg, M1);
+  const int64_t MN = static_cast<int64_t>(M) * N;
+  const float* part = SEGF(sg, part) + static_cast<int64_t>(before_s) * MN;
+  float* c = static_cast<float*>(SEGF(sg, c));
+  float* c2 = static_cast<float*>(SEGF(sg, c2));
+  const int64_t ldc = SEGF(sg, ldc), cgs = SEGF(sg, c_gstride);
+  for (int64_t e = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 4; e < MN;
+       e += static_cast<int64_t>(gridDim.x) * blockDim.x * 4) {
+    float4 s = *reinterpret_cast<const float4*>(part + e);
+    for (int p = 1; p < ns; ++p) {
+      const float4 t = *reinterpret_cast<const float4*>(part + p * MN + e);
+      s.x += t.x;
+      s.y += t.y;
+      s.z += t.z;
+      s.w += t.w;
+    }
+    const int m = static_cast<int>(e / N), n = static_cast<int>(e % N);
+    float* dst = (m < M1 ? c + static_cast<int64_t>(m) * ldc : c2 + static_cast<int64_t>(m - M1) * ldc) +
+                 static_cast<int64_t>(g) * cgs + n;
+    *reinterpret_cast<float4*>(dst) = s;
+  }
+}
+
+WgradPlan plan_wgrad(int nseg, const int64_t* total_rows, const int* groups, const int* M,
+                     const int* N) {
+  WgradPlan p{};
+  int64_t units = 0, work = 0;
+  for (int i = 0; i < nseg; ++i) {
+    const int64_t tiles = static_cast<int64_t>(cdiv(M[i], kTM)) * cdiv(N[i], kTN);
+    units += groups[i] * tiles;
+    work += total_rows[i] * tiles;
+  }
+  if (units >= kSplitTarget) return p;
+  int64_t split = (work + kSplitTarget - 1) / kSplitTarget;
+  split = std::max<int64_t>(kMinSplit, (split + kTK - 1) / kTK * kTK);
+  p.split = static_cast<int>(std::min<int64_t>(split, int64_t{1} << 30));
+  for (int i = 0; i < nseg; ++i) {
+    // only groups of more than `split` rows take slots, ceil(R / split) <= 2 R / split of them
+    const int64_t rows = total_rows[i];
+    const int64_t s = std::min(rows / p.split + groups[i], 2 * rows / p.split);
+    p.slots[i] = rows > p.split ? s : 0;
+    p.part_floats += p.slots[i] * M[i] * N[i];
+  }
+  return p;
 }
 
 hipError_t launch_bwd_gemm(const BwdGemmArgs& a, int kind, hipStream_t s) {
   int grid = 2 * device_cus();
   grid = (grid / kXcds) * kXcds;
   if (grid <= 0) grid = kXcds;
-  const dim3 gd(grid), bd(kBTh);
+  const dim3 gd(grid), bd(kTh);
   switch (kind) {
-    case kBwdDgradKM:  // A rows x K, B stored [K, N]
-      hipLaunchKernelGGL((bwd_gemm_kernel<true, false, kEpiBf16>), gd, bd, 0, s, a);
+    case kBwdDgradKM:
+      hipLaunchKernelGGL(bwd_gemm_kernel<kBwdDgradKM>, gd, bd, 0, s, a);
       break;
-    case kBwdRecompute:  // A rows x K, B = [W1; W3] rows x K
-      hipLaunchKernelGGL((bwd_gemm_kernel<true, true, kEpiSwigluBwd>), gd, bd, 0, s, a);
+    case kBwdRecompute:
+      hipLaunchKernelGGL(bwd_gemm_kernel<kBwdRecompute>, gd, bd, 0, s, a);
       break;
-    case kBwdWgrad:  // both operands expert-grouped rows, K = rows
-      hipLaunchKernelGGL((bwd_gemm_kernel<false, false, kEpiF32>), gd, bd, 0, s, a);
+    case kBwdWgrad: {
+      hipLaunchKernelGGL(bwd_gemm_kernel<kBwdWgrad>, gd, bd, 0, s, a);
+      bool split = false;
+      int groups = 0;
+      int64_t mn = 0;
+      for (int i = 0; i < a.nseg; ++i) {
+        split = split || a.seg[i].split > 0;
+        groups += a.seg[i].groups;
+        mn = std::max<int64_t>(mn, static_cast<int64_t>(a.seg[i].M) * a.seg[i].N);
+      }
+      if (split) {
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int64_t bx = std::min<int64_t>((mn / 4 + 255) / 256, 64);
+        hipLaunchKernelGGL(wgrad_reduce_kernel, dim3(static_cast<unsigned>(bx), groups), dim3(256), 0, s, a);
+      }
       break;
+    }
     default:
       return hipErrorInvalidValue;
   }

@@ -81,32 +81,52 @@ hipError_t launch_combine(const uint16_t* y_perm, const uint16_t* y_shared, cons
                           const int32_t* pos, const uint16_t* residual, uint16_t* out,
                           int64_t T, int d, int k, hipStream_t s);
 // Grouped GEMMs of the backward (bwd_gemm.hip): C_g = A_g B_g^T summed over K,
-// per expert group g of consecutive rows.
-struct BwdGemmArgs {
-  int groups;              // groups (experts), or 1 with offsets == NULL
-  const int32_t* offsets;  // [groups + 1] first row of each group, or NULL
-  int rows;                // rows of the single group when offsets == NULL
-  int ragged_k;            // 0: a group's rows are M (input gradients); 1: they are K (weight gradients)
-  int M, N, K;             // the sizes that are not a group's rows
-  int K2;                  // dgrad only: a second K segment from a2 / b2 (dx = da W1 + dc W3), else 0
-  const uint16_t* a;       // A: K-contiguous rows [rows, K] (dgrad) or rows [rows, M] (wgrad)
+// per group g of consecutive rows.  A launch covers up to two segments of
+// groups with their own operands and sizes (the shared expert: one group of
+// `rows` rows; the routed experts: `groups` groups delimited by `offsets`).
+struct BwdSeg {
+  int groups;              // groups of the segment
+  const int32_t* offsets;  // [groups + 1] first row of each group, or NULL (one group of `rows`)
+  int rows;
+  int M, N;                // output size that is not a group's rows (wgrad: M x N per group;
+                           // input gradients: N columns)
+  int K, K2;               // input gradients: K from a / b, then K2 more from a2 / b2
+  int M1;                  // wgrad: output rows below M1 from a (into c), the rest from a2 (into c2)
+  int split;               // wgrad: rows per split of a group's rows (0: none)
+  const uint16_t* a;
   const uint16_t* a2;
   int64_t lda;
-  const uint16_t* b;       // B: weights [N, K] or [K, N] (per group, b_gstride apart), or rows [rows, N] (wgrad)
+  const uint16_t* b;
   const uint16_t* b2;
   int64_t ldb, b_gstride;
-  void* c;                 // bf16 rows [rows, N] (dgrad) or fp32 [groups][M][N] (wgrad)
+  void* c;                 // bf16 rows [rows, N] (input gradients) or fp32 [groups][M1][N] (wgrad)
+  void* c2;                // wgrad: fp32 [groups][M - M1][N]
   int64_t ldc, c_gstride;
+  float* part;             // wgrad with split: partial sums [slots][M][N]
   const uint16_t* dh;      // recompute epilogue: dh in, h / da / dc out, rows [rows, N]
   uint16_t* h;
   uint16_t* da;
   uint16_t* dc;
   int64_t ld_h;
 };
+struct BwdGemmArgs {
+  BwdSeg seg[2];
+  int nseg;                // 1 or 2; the groups of seg[0] come first in the unit order
+};
 constexpr int kBwdDgradKM = 0;    // A K-contiguous, B stored [K, N], bf16 out
 constexpr int kBwdRecompute = 1;  // A K-contiguous, B = [W1; W3] rows [N, K], SwiGLU derivative out
 constexpr int kBwdWgrad = 2;      // both operands K-major rows, fp32 out
 hipError_t launch_bwd_gemm(const BwdGemmArgs& a, int kind, hipStream_t s);
+// Weight-gradient splits: rows per split (0: none) and the partial-sum slots
+// a segment may need, for one launch over segments of total_rows[i] rows in
+// groups[i] groups with tiles of M[i] x N[i] outputs.
+struct WgradPlan {
+  int split;
+  int64_t slots[2];
+  int64_t part_floats;  // slots[0] * M[0] * N[0] + slots[1] * M[1] * N[1]
+};
+WgradPlan plan_wgrad(int nseg, const int64_t* total_rows, const int* groups, const int* M,
+                     const int* N);
 
 hipError_t launch_combine_bwd(const uint16_t* dout, const uint16_t* y_perm, const float* gate,
                               const int32_t* pos, uint16_t* dy_perm, float* dgate, int64_t T,

@@ -48,6 +48,10 @@ CASES = {
                                    cfg_id=154), 0.0),
     "many_idle_experts": (dict(tokens=64, seq_len=64, n_experts=64, top_k=2, cfg_id=155,
                                router_std=0.2), 1e-4),
+    # ~800 rows per expert and 1600 shared rows: weight gradients split into
+    # pieces of 512 rows (partial sums added in order); a wider shared expert
+    "split_rows_wide_shared": (dict(tokens=1600, seq_len=320, d_model=128, n_experts=4, top_k=2,
+                                    hidden=128, shared_hidden=192, cfg_id=157), 1e-4),
     "v3_dims_T16": (dict(tokens=16, seq_len=16, d_model=7168, n_experts=16, top_k=4, hidden=2048,
                          shared_hidden=2048, cfg_id=156, w_std=0.006, router_std=0.006,
                          bias_range=0.01), 1e-4),
@@ -92,3 +96,24 @@ def test_layer_backward_matches_oracle(name):
             check_close(host(grads[key]), ref[key], f"{name}.{key}")
     if name == "many_idle_experts":
         assert (counts == 0).any()
+
+
+def test_layer_backward_is_deterministic():
+    """Two runs of the backward give identical bits, the split weight
+    gradients included (their partial sums are added in a fixed order)."""
+    kw, alpha = CASES["split_rows_wide_shared"]
+    wl = workloads.custom(name="determinism", **kw)
+    shape = moe.Shape.of(wl)
+    x = workloads.tokens(wl, 0, DEV)
+    p = workloads.layer_params(wl, 0, DEV)
+    dout = workloads.normal((wl.tokens, wl.d_model), 1.0, 4242, DEV, torch.bfloat16)
+    fwd = moe.alloc_buffers(shape, DEV, x_perm=True)
+    moe.layer_forward(shape, x, p, fwd, use_x_perm=True)
+    runs = []
+    for _ in range(2):
+        grads = moe.alloc_backward(shape, DEV)
+        moe.layer_backward(shape, x, p, fwd, dout, grads, alpha=alpha)
+        torch.cuda.synchronize()
+        runs.append({k: v.clone() for k, v in grads.items() if torch.is_tensor(v)})
+    for key in ("dx", "dw_router", "dw1", "dw3", "dw2", "dws1", "dws3", "dws2"):
+        assert torch.equal(runs[0][key], runs[1][key]), key
