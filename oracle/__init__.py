@@ -95,6 +95,13 @@ def _declare(L):
     L.oracle_moe_forward_f64.argtypes = [I64, I32, I32, I32, I32, I32, I32, ctypes.c_double,
                                          P, P, P, P, P, P, P, P, P, P, P]
     L.oracle_moe_forward_f64.restype = None
+    D = ctypes.c_double
+    L.oracle_mla_prefill.argtypes = [I32] * 9 + [D] + [P] * 8 + [I32, P, P, P, I32]
+    L.oracle_mla_prefill.restype = None
+    L.oracle_mla_decode.argtypes = [I32] * 8 + [D] + [P] * 9 + [I32, P, P, P, I32]
+    L.oracle_mla_decode.restype = None
+    L.oracle_mla_rope.argtypes = [P, I32, D, D]
+    L.oracle_mla_rope.restype = None
 
 
 def default_threads() -> int:
@@ -391,3 +398,67 @@ def layer(x_bits, params: dict, k: int, seq_len: int = 0, alpha: float = 1e-4,
     if seq_len:
         res["seq_balance"] = seq_balance(r["scores"], r["idx"], seq_len, alpha)
     return res
+
+
+# ---------------------------------------------------------------- MLA attention
+
+MLA_KEYS = ("w_q", "w_dkv", "w_kr", "w_uk", "w_uv", "w_o")
+
+
+def _mla_dims(p: dict, n_heads: int):
+    wq, wdkv, wkr = _f64(p["w_q"]), _f64(p["w_dkv"]), _f64(p["w_kr"])
+    wuk, wuv, wo = _f64(p["w_uk"]), _f64(p["w_uv"]), _f64(p["w_o"])
+    d = wq.shape[1]
+    dc, dr = wdkv.shape[0], wkr.shape[0]
+    dn = wuk.shape[0] // n_heads
+    dv = wuv.shape[0] // n_heads
+    assert wq.shape[0] == n_heads * (dn + dr) and wo.shape == (d, n_heads * dv)
+    return (d, dc, dn, dr, dv), (wq, wdkv, wkr, wuk, wuv, wo)
+
+
+def mla_prefill(x, params: dict, n_heads: int, batch: int, seq: int, max_len: int,
+                residual=None, base: float = 10000.0, round_storage: bool = True,
+                nthreads: int | None = None) -> dict:
+    """MLA attention over `batch` sequences of `seq` tokens (positions 0..seq-1).
+    x: [batch*seq, d] bf16 bits or reals; params: the six weights (bf16 bits or
+    reals).  Returns fp64 arrays: out [batch*seq, d], cache_kv [batch, max_len,
+    dc] and cache_kr [batch, max_len, dr] (positions >= seq are zero)."""
+    (d, dc, dn, dr, dv), ws = _mla_dims(params, n_heads)
+    xd = _f64(x).reshape(batch * seq, d)
+    res = None if residual is None else _f64(residual).reshape(batch * seq, d)
+    out = np.zeros((batch * seq, d))
+    ckv = np.zeros((batch, max_len, dc))
+    ckr = np.zeros((batch, max_len, dr))
+    lib().oracle_mla_prefill(batch, seq, max_len, d, n_heads, dc, dn, dr, dv, float(base), _p(xd),
+                             *[_p(w) for w in ws], _p(res), int(bool(round_storage)), _p(ckv),
+                             _p(ckr), _p(out), nthreads or default_threads())
+    return {"out": out, "cache_kv": ckv, "cache_kr": ckr}
+
+
+def mla_decode(x, params: dict, n_heads: int, pos, cache_kv, cache_kr, residual=None,
+               base: float = 10000.0, round_storage: bool = True,
+               nthreads: int | None = None) -> dict:
+    """One decoding step: sequence b's new token x[b] at position pos[b]
+    attends to its cached positions 0..pos[b]-1 and itself.  The caches
+    (fp64 [batch, max_len, dc] / [.., dr], e.g. from mla_prefill) are copied,
+    the new entries written at pos[b].  Returns out [batch, d] and the caches."""
+    (d, dc, dn, dr, dv), ws = _mla_dims(params, n_heads)
+    ckv = np.array(cache_kv, dtype=np.float64, copy=True)
+    ckr = np.array(cache_kr, dtype=np.float64, copy=True)
+    batch, max_len = ckv.shape[0], ckv.shape[1]
+    xd = _f64(x).reshape(batch, d)
+    pv = _c(np.asarray(pos), np.int32)
+    assert ((pv >= 0) & (pv < max_len)).all()
+    res = None if residual is None else _f64(residual).reshape(batch, d)
+    out = np.zeros((batch, d))
+    lib().oracle_mla_decode(batch, max_len, d, n_heads, dc, dn, dr, dv, float(base), _p(pv),
+                            _p(xd), *[_p(w) for w in ws], _p(res), int(bool(round_storage)),
+                            _p(ckv), _p(ckr), _p(out), nthreads or default_threads())
+    return {"out": out, "cache_kv": ckv, "cache_kr": ckr}
+
+
+def mla_rope(u, pos: float, base: float = 10000.0) -> np.ndarray:
+    """The rotary map of a vector u (even length) at position pos."""
+    v = np.array(u, dtype=np.float64, copy=True)
+    lib().oracle_mla_rope(_p(v), v.shape[0], float(pos), float(base))
+    return v

@@ -838,3 +838,191 @@ void oracle_update_bias(int64_t T, int E, int k, const int32_t* counts, float* b
     bias[i] = bias[i] + gamma * sg;
   }
 }
+
+/* ------------------------------------------------------------------ */
+/* MLA attention (the other half of the block)                         */
+/* ------------------------------------------------------------------ */
+
+/* Multi-head latent attention as the pages describe it ([ZH] sections
+ * 190行代码到底装进了什么 and 先说结论; [VI] section Những gì có trong 190
+ * dòng code, and section Những gì đã được đơn giản hóa for the explicit
+ * decompression).  Per token, two things are cached: a latent of dc numbers
+ * (128 in the mini model) from which the heads' keys and values are
+ * decompressed, and one rotary key of dr numbers (16) shared by all heads --
+ * 144 numbers per token and layer instead of the 480 of plain multi-head
+ * attention with 6 heads.  The content part of keys and queries ("nope")
+ * carries no position; the rotary part is rotated with the position.
+ * READINGS (the pages give none of these formulas):
+ *   q_h      = W_q[h] x,  split into q_nope (dn) and q_rope (dr), q_rope rotated
+ *   c        = W_dkv x                      (the cached latent, dc)
+ *   k_r      = rope(W_kr x)                 (the cached rotary key, dr)
+ *   k_nope_h = W_uk[h] c,  v_h = W_uv[h] c  (decompressed explicitly)
+ *   score_h(i, s) = (q_nope_h(i).k_nope_h(s) + q_rope_h(i).k_r(s)) / sqrt(dn + dr),
+ *            causal (s <= i), softmax over s,
+ *   o_h(i)   = sum_s p_h(i, s) v_h(s),   out(i) = r(i) + W_o concat_h o_h(i).
+ * rope(u, p): pairs (u[2m], u[2m+1]) turn by the angle p * base^(-2m/dr),
+ * base 10000; p = the token's position in its sequence.  The weights are
+ * stored like the experts' ([N, K], K contiguous): W_q [nh (dn+dr), d],
+ * W_dkv [dc, d], W_kr [dr, d], W_uk [nh dn, dc], W_uv [nh dv, dc],
+ * W_o [d, nh dv].  round_storage = 1 rounds to bf16 where the GPU stores
+ * bf16 (q, c, k_r, k_nope, v, o and out); 0 keeps everything in fp64.
+ * Arguments are fp64 arrays (bf16 values widened). */
+
+static void mla_rope(double* u, int dr, double pos, double base) {
+  for (int m = 0; m < dr / 2; ++m) {
+    double ang = pos * pow(base, -2.0 * m / dr);
+    double c = cos(ang), s = sin(ang);
+    double a = u[2 * m], b = u[2 * m + 1];
+    u[2 * m] = a * c - b * s;
+    u[2 * m + 1] = a * s + b * c;
+  }
+}
+
+/* y[j] = sum_i W[j][i] x[i], i ascending, for j < n (W row-major [n, k]) */
+static void mla_matvec(int n, int k, const double* W, const double* x, double* y, int round) {
+  for (int j = 0; j < n; ++j) {
+    double acc = 0.0;
+    for (int i = 0; i < k; ++i) acc += W[(size_t)j * k + i] * x[i];
+    y[j] = keep_bf16(acc, round);
+  }
+}
+
+typedef struct {
+  int d, nh, dc, dn, dr, dv, Lmax, round;
+  double base;
+  const double *wq, *wdkv, *wkr, *wuk, *wuv, *wo;
+} mla_cfg;
+
+/* token x at position p: q [nh (dn+dr)], latent c [dc], rotary key kr [dr] */
+static void mla_project(const mla_cfg* m, const double* x, int p, double* q, double* c, double* kr) {
+  const int qw = m->dn + m->dr;
+  for (int h = 0; h < m->nh; ++h) {
+    double* qh = q + (size_t)h * qw;
+    mla_matvec(qw, m->d, m->wq + (size_t)h * qw * m->d, x, qh, 0);
+    mla_rope(qh + m->dn, m->dr, p, m->base);
+    for (int j = 0; j < qw; ++j) qh[j] = keep_bf16(qh[j], m->round);
+  }
+  mla_matvec(m->dc, m->d, m->wdkv, x, c, m->round);
+  mla_matvec(m->dr, m->d, m->wkr, x, kr, 0);
+  mla_rope(kr, m->dr, p, m->base);
+  for (int j = 0; j < m->dr; ++j) kr[j] = keep_bf16(kr[j], m->round);
+}
+
+/* One query (q at position i) against cached positions 0..i of one sequence
+ * (latents ckv [Lmax, dc], rotary keys ckr [Lmax, dr]); the keys and values
+ * of every head are decompressed from the latents first: kn [(i+1), nh, dn],
+ * vv [(i+1), nh, dv] (scratch).  Writes out [d] given the residual r [d]. */
+static void mla_attend(const mla_cfg* m, const double* q, int i, const double* ckv,
+                       const double* ckr, const double* r, double* kn, double* vv, double* sc,
+                       double* o, double* out) {
+  const int qw = m->dn + m->dr, n = i + 1;
+  for (int s = 0; s < n; ++s) {
+    mla_matvec(m->nh * m->dn, m->dc, m->wuk, ckv + (size_t)s * m->dc, kn + (size_t)s * m->nh * m->dn,
+               m->round);
+    mla_matvec(m->nh * m->dv, m->dc, m->wuv, ckv + (size_t)s * m->dc, vv + (size_t)s * m->nh * m->dv,
+               m->round);
+  }
+  const double scale = 1.0 / sqrt((double)qw);
+  for (int h = 0; h < m->nh; ++h) {
+    const double* qh = q + (size_t)h * qw;
+    double mx = -INFINITY;
+    for (int s = 0; s < n; ++s) {
+      double a = 0.0;
+      for (int j = 0; j < m->dn; ++j) a += qh[j] * kn[((size_t)s * m->nh + h) * m->dn + j];
+      for (int j = 0; j < m->dr; ++j) a += qh[m->dn + j] * ckr[(size_t)s * m->dr + j];
+      sc[s] = a * scale;
+      if (sc[s] > mx) mx = sc[s];
+    }
+    double z = 0.0;
+    for (int s = 0; s < n; ++s) {
+      sc[s] = exp(sc[s] - mx);
+      z += sc[s];
+    }
+    for (int j = 0; j < m->dv; ++j) {
+      double a = 0.0;
+      for (int s = 0; s < n; ++s) a += sc[s] / z * vv[((size_t)s * m->nh + h) * m->dv + j];
+      o[(size_t)h * m->dv + j] = keep_bf16(a, m->round);
+    }
+  }
+  for (int t = 0; t < m->d; ++t) {
+    double a = r ? r[t] : 0.0;
+    for (int j = 0; j < m->nh * m->dv; ++j) a += m->wo[(size_t)t * m->nh * m->dv + j] * o[j];
+    out[t] = keep_bf16(a, m->round);
+  }
+}
+
+typedef struct {
+  const mla_cfg* m;
+  int S;
+  const double *x, *res;
+  const int32_t* pos;  /* decode: position of each sequence's new token */
+  double *ckv, *ckr, *out;
+} mla_ctx;
+
+static void mla_prefill_seq(void* vctx, int64_t b) {
+  const mla_ctx* c = (const mla_ctx*)vctx;
+  const mla_cfg* m = c->m;
+  const int qw = m->dn + m->dr, S = c->S;
+  double* q = (double*)malloc(sizeof(double) * (size_t)S * m->nh * qw);
+  double* kn = (double*)malloc(sizeof(double) * (size_t)S * m->nh * m->dn);
+  double* vv = (double*)malloc(sizeof(double) * (size_t)S * m->nh * m->dv);
+  double* sc = (double*)malloc(sizeof(double) * S);
+  double* o = (double*)malloc(sizeof(double) * m->nh * m->dv);
+  double* ckv = c->ckv + (size_t)b * m->Lmax * m->dc;
+  double* ckr = c->ckr + (size_t)b * m->Lmax * m->dr;
+  for (int i = 0; i < S; ++i)
+    mla_project(m, c->x + ((size_t)b * S + i) * m->d, i, q + (size_t)i * m->nh * qw,
+                ckv + (size_t)i * m->dc, ckr + (size_t)i * m->dr);
+  for (int i = 0; i < S; ++i) {
+    const size_t row = (size_t)b * S + i;
+    mla_attend(m, q + (size_t)i * m->nh * qw, i, ckv, ckr, c->res ? c->res + row * m->d : NULL, kn,
+               vv, sc, o, c->out + row * m->d);
+  }
+  free(q); free(kn); free(vv); free(sc); free(o);
+}
+
+static void mla_decode_seq(void* vctx, int64_t b) {
+  const mla_ctx* c = (const mla_ctx*)vctx;
+  const mla_cfg* m = c->m;
+  const int qw = m->dn + m->dr, p = c->pos[b], n = p + 1;
+  double* q = (double*)malloc(sizeof(double) * m->nh * qw);
+  double* kn = (double*)malloc(sizeof(double) * (size_t)n * m->nh * m->dn);
+  double* vv = (double*)malloc(sizeof(double) * (size_t)n * m->nh * m->dv);
+  double* sc = (double*)malloc(sizeof(double) * n);
+  double* o = (double*)malloc(sizeof(double) * m->nh * m->dv);
+  double* ckv = c->ckv + (size_t)b * m->Lmax * m->dc;
+  double* ckr = c->ckr + (size_t)b * m->Lmax * m->dr;
+  mla_project(m, c->x + (size_t)b * m->d, p, q, ckv + (size_t)p * m->dc, ckr + (size_t)p * m->dr);
+  mla_attend(m, q, p, ckv, ckr, c->res ? c->res + (size_t)b * m->d : NULL, kn, vv, sc, o,
+             c->out + (size_t)b * m->d);
+  free(q); free(kn); free(vv); free(sc); free(o);
+}
+
+/* Prefill of B sequences of S tokens (positions 0..S-1): x [B S, d];
+ * writes the caches ckv [B, Lmax, dc], ckr [B, Lmax, dr] at positions
+ * 0..S-1 and out [B S, d] = res + attention (res may be NULL). */
+void oracle_mla_prefill(int B, int S, int Lmax, int d, int nh, int dc, int dn, int dr, int dv,
+                        double base, const double* x, const double* wq, const double* wdkv,
+                        const double* wkr, const double* wuk, const double* wuv, const double* wo,
+                        const double* res, int round_storage, double* ckv, double* ckr,
+                        double* out, int nthreads) {
+  mla_cfg m = {d, nh, dc, dn, dr, dv, Lmax, round_storage, base, wq, wdkv, wkr, wuk, wuv, wo};
+  mla_ctx c = {&m, S, x, res, NULL, ckv, ckr, out};
+  parallel_for(B, nthreads, mla_prefill_seq, &c);
+}
+
+/* One decoding step: sequence b's new token x [b] sits at position pos[b]
+ * (its cache holds positions 0..pos[b]-1); its latent and rotary key are
+ * written at pos[b] and it attends to positions 0..pos[b]. */
+void oracle_mla_decode(int B, int Lmax, int d, int nh, int dc, int dn, int dr, int dv, double base,
+                       const int32_t* pos, const double* x, const double* wq, const double* wdkv,
+                       const double* wkr, const double* wuk, const double* wuv, const double* wo,
+                       const double* res, int round_storage, double* ckv, double* ckr, double* out,
+                       int nthreads) {
+  mla_cfg m = {d, nh, dc, dn, dr, dv, Lmax, round_storage, base, wq, wdkv, wkr, wuk, wuv, wo};
+  mla_ctx c = {&m, 0, x, res, pos, ckv, ckr, out};
+  parallel_for(B, nthreads, mla_decode_seq, &c);
+}
+
+/* The rotation of the rotary part, exported for its pins. */
+void oracle_mla_rope(double* u, int dr, double pos, double base) { mla_rope(u, dr, pos, base); }
