@@ -307,6 +307,159 @@ def cpu_baseline(wl, target_s: float, params_dev=None, x_dev=None):
                       f"oracle, {dt:.1f} s on {threads} threads"}
 
 
+MLA_METRIC = "MLA attention tokens/sec (1 MI355X); % bf16 MFMA peak / % HBM peak"
+
+
+def mla_algorithmic(wl):
+    """FLOPs and HBM bytes of one MLA call by the definitions: the three
+    projections and the decompression (prefill) as matrix products, the
+    attention's scores and weighted sums; bytes = activations in and out,
+    weights, cache entries written and (decode) the cached rows read."""
+    d, H, dc, dn, dr, dv = wl.d_model, wl.n_heads, wl.d_latent, wl.d_nope, wl.d_rope, wl.d_v
+    qw = dn + dr
+    T = wl.tokens
+    proj = 2.0 * T * d * (H * qw + dc + dr)
+    outp = 2.0 * T * H * dv * d
+    wbytes = 2.0 * (H * qw * d + (dc + dr) * d + H * (dn + dv) * dc + d * H * dv)
+    if wl.decode:
+        n = wl.seq_len + 1  # keys per new token
+        attn = 2.0 * wl.batch * H * (dn * dc + n * (dc + dr) + n * dc + dv * dc)
+        flops = proj + attn + outp
+        byts = 2.0 * wl.batch * (2 * d + (dc + dr) * (n + 1)) + wbytes
+    else:
+        pairs = wl.batch * wl.seq_len * (wl.seq_len + 1) / 2.0  # causal (query, key) pairs
+        attn = 2.0 * H * pairs * (qw + dv)
+        flops = proj + 2.0 * T * dc * H * (dn + dv) + attn + outp
+        byts = 2.0 * T * (2 * d + dc + dr) + wbytes
+    return flops, byts
+
+
+def mla_cpu_baseline(wl, target_s, x, params):
+    """The MLA oracle on whole sequences of the workload (prefill) or on
+    sequences' decode steps (with their cache), until about target_s."""
+    import numpy as np
+
+    import oracle
+    threads = oracle.default_threads()
+    hp = {k: oracle.as_bf16_bits(v) for k, v in params.items()}
+    xb = oracle.as_bf16_bits(x)
+    done, dt = 0, 0.0
+    if wl.decode:
+        ckv = np.zeros((threads, wl.max_len, wl.d_latent))
+        ckr = np.zeros((threads, wl.max_len, wl.d_rope))
+        while dt < target_s and done < 64 * wl.batch:
+            t0 = time.perf_counter()
+            oracle.mla_decode(xb[:threads], hp, wl.n_heads, np.full(threads, wl.seq_len), ckv, ckr,
+                              nthreads=threads)
+            dt += time.perf_counter() - t0
+            done += threads
+        what = (f"{done} decode steps at position {wl.seq_len} ({threads} sequences per call, "
+                f"zero caches: the same arithmetic)")
+    else:
+        S = wl.seq_len
+        while dt < target_s and done < wl.batch:
+            n = min(threads, wl.batch - done)
+            t0 = time.perf_counter()
+            oracle.mla_prefill(xb[done * S:(done + n) * S], hp, wl.n_heads, n, S, wl.max_len,
+                               nthreads=threads)
+            dt += time.perf_counter() - t0
+            done += n
+        done *= S
+        what = f"{done // S} whole sequences of {S} tokens"
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        affinity = os.cpu_count() or 1
+    return {"value": done / dt, "unit": "tokens/s", "cores": threads, "cpu_model": cpu_model(),
+            "cpus_available": affinity, "kind": "oracle",
+            "sample": f"{what} of {wl.name}, fp64 oracle with explicit decompression, "
+                      f"{dt:.1f} s on {threads} threads"}
+
+
+def run_mla(args, name):
+    """MLA attention workloads: a step is one mla_prefill (all sequences of
+    the batch) or one mla_decode step of every sequence (the same position
+    each step, so every step does the same work); each call timed with HIP
+    events on its stream."""
+    import numpy as np
+    import torch
+
+    from sparse_mixture_experts_51_amd import moe, workloads
+
+    wl = workloads.MLA_WORKLOADS[name]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    moe.load()
+    params = workloads.mla_params(wl, 0, dev)
+    shape = moe.MlaShape(wl.batch, 0 if wl.decode else wl.seq_len, wl.max_len, wl.d_model,
+                         wl.n_heads, wl.d_latent, wl.d_nope, wl.d_rope, wl.d_v)
+    buf = moe.alloc_mla(shape, dev, decode=wl.decode)
+    stream = torch.cuda.current_stream()
+    if wl.decode:
+        # the caches hold seq_len tokens of every sequence
+        pshape = moe.MlaShape(wl.batch, wl.seq_len, wl.max_len, wl.d_model, wl.n_heads,
+                              wl.d_latent, wl.d_nope, wl.d_rope, wl.d_v)
+        pbuf = moe.alloc_mla(pshape, dev)
+        px = workloads.mla_tokens(wl, wl.batch * wl.seq_len, 0, dev)
+        moe.mla_prefill(pshape, px, params, buf["cache_kv"], buf["cache_kr"], pbuf["out"],
+                        workspace=pbuf["workspace"])
+        del pbuf
+        x = workloads.mla_tokens(wl, wl.batch, 1, dev)
+        pos = torch.full((wl.batch,), wl.seq_len, dtype=torch.int32, device=dev)
+
+        def call():
+            moe.mla_decode(shape, x, pos, params, buf["cache_kv"], buf["cache_kr"], buf["out"],
+                           residual=x, workspace=buf["workspace"], stream=stream)
+    else:
+        x = workloads.mla_tokens(wl, wl.tokens, 0, dev)
+
+        def call():
+            moe.mla_prefill(shape, x, params, buf["cache_kv"], buf["cache_kr"], buf["out"],
+                            residual=x, workspace=buf["workspace"], stream=stream)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = []
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        ev.append((e0, e1))
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    per = [a.elapsed_time(b) for a, b in ev]
+    med = float(np.median(per))
+    flops, byts = mla_algorithmic(wl)
+    tflops = flops / (med * 1e-3) / 1e12
+    gbs = byts / (med * 1e-3) / 1e9
+    line = {
+        "metric": MLA_METRIC, "value": wl.tokens / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": name, "batch": wl.batch, "seq_len": wl.seq_len,
+                   "max_len": wl.max_len, "d_model": wl.d_model, "n_heads": wl.n_heads,
+                   "d_latent": wl.d_latent, "d_nope": wl.d_nope, "d_rope": wl.d_rope,
+                   "d_v": wl.d_v, "decode": wl.decode},
+        "roofline": {"bound": "hbm" if wl.decode else "mfma",
+                     "achieved": gbs if wl.decode else tflops,
+                     "peak": PEAK_HBM_GBS if wl.decode else PEAK_BF16_TFLOPS,
+                     "unit": "GB/s" if wl.decode else "TFLOP/s",
+                     "frac": gbs / PEAK_HBM_GBS if wl.decode else tflops / PEAK_BF16_TFLOPS,
+                     "traffic": None, "kernel": "the whole mla_decode / mla_prefill call",
+                     "algorithmic_flop": flops, "algorithmic_bytes": byts,
+                     "ms_per_call_median": med, "tflops": tflops, "gbs": gbs},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = mla_cpu_baseline(wl, args.cpu_seconds, x, params)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.steps < 1 or args.warmup < 0 or args.ffn_events_every < 1:
@@ -323,8 +476,15 @@ def main():
     from sparse_mixture_experts_51_amd import moe, profiling, workloads
 
     name = args.workload or workloads.DEFAULT_BENCH_WORKLOAD
+    if name in workloads.MLA_WORKLOADS:
+        if args.with_backward or args.calibrate_copy:
+            print("--with-backward and --calibrate-copy apply to the MoE workloads", file=sys.stderr)
+            sys.exit(2)
+        run_mla(args, name)
+        return
     if name not in workloads.WORKLOADS:
-        print(f"unknown workload {name!r}; one of {sorted(workloads.WORKLOADS)}", file=sys.stderr)
+        print(f"unknown workload {name!r}; one of "
+              f"{sorted(workloads.WORKLOADS) + sorted(workloads.MLA_WORKLOADS)}", file=sys.stderr)
         sys.exit(2)
 
     if args.with_backward and workloads.WORKLOADS[name].norm:

@@ -23,7 +23,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["route.hip", "permute.hip", "grouped_gemm.hip", "combine.hip", "norm.hip", "bwd_gemm.hip",
-           "bwd.hip", "api.cpp"]
+           "bwd.hip", "mla.hip", "api.cpp", "mla_api.cpp"]
 PROBE_SOURCES = ["hbm_probe.hip"]
 HEADERS = ["common.hpp", "gemm_common.hpp", "kernels.hpp"]
 

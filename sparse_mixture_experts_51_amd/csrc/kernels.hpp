@@ -140,6 +140,46 @@ hipError_t launch_route_bwd(const uint16_t* x, const float* w_router, const int3
                             int S, hipStream_t s);
 int route_bwd_splits(int64_t T);
 
+// MLA attention (mla.hip)
+struct MlaGemmArgs {
+  int M, N, K;
+  const uint16_t* a;           // A rows [.., K]: output row t reads row (t / a_grp) a_grp_stride + t % a_grp
+  int64_t lda;
+  int a_grp, a_grp_stride;
+  const uint16_t* b0;          // B rows [N, K]: rows < n1 from b0, < n2 from b1, the rest from b2
+  const uint16_t* b1;
+  const uint16_t* b2;
+  int n1, n2;
+  uint16_t* c;                 // plain / residual epilogues: C [M, ldc]
+  int64_t ldc;
+  const uint16_t* res;         // residual [M, ldc] or NULL
+  // projection epilogue: columns < n1 -> q [M, n1] (head blocks of qw, the
+  // last dr of each turned), < n2 -> latent cache, the rest -> rotary cache
+  uint16_t* q;
+  uint16_t* ckv;
+  uint16_t* ckr;
+  int qw, dn, dr, dc, max_len;
+  int seq;                     // > 0: token t is position t % seq of sequence t / seq
+  const int32_t* pos;          // seq == 0: token t is sequence t at position pos[t]
+  float log2_base;
+};
+constexpr int kMlaEpiProj = 0, kMlaEpiPlain = 1, kMlaEpiRes = 2;
+hipError_t launch_mla_gemm(const MlaGemmArgs& a, int epi, hipStream_t s);
+struct MlaAttnArgs {
+  const uint16_t* q;    // [tokens, nh (dn + dr)]
+  const uint16_t* kvx;  // prefill: decompressed [tokens, nh dn | nh dv]
+  const uint16_t* ckv;  // caches [batch, max_len, dc] and [.., dr]
+  const uint16_t* ckr;
+  const uint16_t* w_uk;  // decode: [nh dn, dc], [nh dv, dc]
+  const uint16_t* w_uv;
+  const int32_t* pos;   // decode positions
+  uint16_t* o;          // [tokens, nh dv]
+  int seq, max_len, nh, dc, dn, dr, dv;
+  float scale;
+};
+hipError_t launch_mla_attn_prefill(const MlaAttnArgs& a, int batch, hipStream_t s);
+hipError_t launch_mla_attn_decode(const MlaAttnArgs& a, int batch, hipStream_t s);
+
 hipError_t launch_rmsnorm(const uint16_t* x, const float* gain, float eps, uint16_t* out,
                           int64_t T, int d, hipStream_t s);
 hipError_t launch_update_bias(const int32_t* counts, float* bias, float gamma, int64_t T, int E,

@@ -1,0 +1,451 @@
+// mla.hip -- MLA attention on gfx950: projections, cache writes, prefill and
+// decode attention.
+//
+// Multi-head latent attention as "190行JAX复刻DeepSeek V3" (openai-hub.com),
+// section 190行代码到底装进了什么, and "DeepSeek V3 viết lại bằng 190 dòng JAX
+// thuần" (lehuy.net), section Những gì có trong 190 dòng code, describe it: a
+// token caches a latent c (d_latent numbers) and one rotary key k_r (d_rope)
+// shared by the heads; a head's key is [W_uk[h] c, k_r] and its value
+// W_uv[h] c; the query's rotary part and k_r are turned by the position.
+//
+// Kernels:
+//   mla_gemm_kernel<EPI>   C = A B^T on bf16 MFMA, 64 x 64 x 64 tiles (four
+//       waves of 32 x 32), K-contiguous operands staged through LDS one step
+//       ahead.  Three epilogues: the input projection (q with its rotary
+//       part turned, the latent and the turned rotary key written into the
+//       caches at the token's position), plain bf16 (the prefill's
+//       decompressed keys and values) and bf16 with a residual (the output
+//       projection).
+//   mla_attn_prefill_kernel  one block per (query tile of 64, head,
+//       sequence); keys and values in chunks of 64 through LDS; one wave per
+//       16 query rows, a lane per key for the scores, online softmax in
+//       fp32, lanes split (value dim, key group) for P V.
+//   mla_attn_decode_kernel   one block per sequence; reads only the cache:
+//       each head's query is taken into latent space (q_nope^T W_uk[h]), the
+//       latent rows are scored and attended in chunks of 64 with online
+//       softmax, and W_uv[h] is applied to the attended latent.  This is the
+//       explicit decompression of the pages regrouped (associativity), so it
+//       equals it up to rounding order while reading 144 numbers per cached
+//       token instead of decompressing every key and value.
+#include "common.hpp"
+#include "gemm_common.hpp"
+#include "kernels.hpp"
+
+#include <math.h>
+
+namespace moe {
+
+namespace {
+constexpr int kTh = 256;
+constexpr int kGM = 64, kGN = 64, kGK = 64;  // GEMM tile
+constexpr int kGCh = kGK / 8;                 // 16-byte chunks per staged row
+
+__device__ __forceinline__ int gsidx(int r, int c) {
+  return r * kGCh + ((c ^ (r >> 1) ^ (r >> 3)) & (kGCh - 1));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// the pair (v0, v1) turned by position p, pair index m of d_rope numbers
+__device__ __forceinline__ void rope_pair(float& v0, float& v1, int m, int d_rope, float p,
+                                          float log2_base) {
+  const float inv = exp2f(-2.0f * static_cast<float>(m) / static_cast<float>(d_rope) * log2_base);
+  float s, c;
+  sincosf(p * inv, &s, &c);
+  const float a = v0, b = v1;
+  v0 = a * c - b * s;
+  v1 = a * s + b * c;
+}
+}  // namespace
+
+template <int EPI>
+__global__ __launch_bounds__(kTh) void mla_gemm_kernel(MlaGemmArgs a) {
+  __shared__ u32x4 sa[2][kGM * kGCh];
+  __shared__ u32x4 sb[2][kGN * kGCh];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uni(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m0 = blockIdx.x * kGM, n0 = blockIdx.y * kGN;
+  const int fr = lane & 31, fhalf = lane >> 5;
+
+  // two 16-byte chunks per thread and operand: chunk q = tid + 256 p is row
+  // q / 8, chunk q % 8 of the tile
+  const uint16_t* ap[2];
+  const uint16_t* bp[2];
+  bool aok[2], bok[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int row = (tid + kTh * p) >> 3;
+    const int t = m0 + row;
+    aok[p] = t < a.M;
+    const int arow = aok[p] ? (t / a.a_grp) * a.a_grp_stride + t % a.a_grp : 0;
+    ap[p] = a.a + static_cast<int64_t>(arow) * a.lda;
+    const int n = n0 + row;
+    bok[p] = n < a.N;
+    const int nn = bok[p] ? n : 0;
+    bp[p] = nn < a.n1 ? a.b0 + static_cast<int64_t>(nn) * a.K
+                      : (nn < a.n2 ? a.b1 + static_cast<int64_t>(nn - a.n1) * a.K
+                                   : a.b2 + static_cast<int64_t>(nn - a.n2) * a.K);
+  }
+  const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
+  u32x4 va[2], vb[2];
+  auto load = [&](int kt) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int ch = (tid + kTh * p) & 7;
+      const int k = kt * kGK + 8 * ch;
+      va[p] = aok[p] ? *reinterpret_cast<const u32x4*>(ap[p] + k) : zero4;
+      vb[p] = bok[p] ? *reinterpret_cast<const u32x4*>(bp[p] + k) : zero4;
+    }
+  };
+  auto store = [&](int st) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int q = tid + kTh * p;
+      sa[st][gsidx(q >> 3, q & 7)] = va[p];
+      sb[st][gsidx(q >> 3, q & 7)] = vb[p];
+    }
+  };
+  f32x16 acc = f32x16{};
+  const int nk = a.K / kGK;
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int st = kt & 1;
+    if (kt + 1 < nk) load(kt + 1);
+#pragma unroll
+    for (int ks = 0; ks < kGK / 16; ++ks) {
+      const bf16x8 af = __builtin_bit_cast(bf16x8, sa[st][gsidx(32 * wm + fr, 2 * ks + fhalf)]);
+      const bf16x8 bf = __builtin_bit_cast(bf16x8, sb[st][gsidx(32 * wn + fr, 2 * ks + fhalf)]);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf, af, acc, 0, 0, 0);
+    }
+    if (kt + 1 < nk) store(st ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: this lane holds row m, columns n .. n+3 per q
+  const int m = m0 + 32 * wm + fr;
+  if (m >= a.M) return;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int n = n0 + 32 * wn + 8 * q + 4 * fhalf;
+    if (n >= a.N) continue;
+    float v[4] = {acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+    if constexpr (EPI == kMlaEpiProj) {
+      // the token's sequence and position
+      int b, p;
+      if (a.seq > 0) {
+        b = m / a.seq;
+        p = m % a.seq;
+      } else {
+        b = m;
+        p = a.pos[m];
+      }
+      const bool in_cache = p >= 0 && p < a.max_len;
+      if (n < a.n1) {  // query of head n / qw
+        const int j = n % a.qw;
+        if (j >= a.dn) {
+          const int mr = (j - a.dn) >> 1;
+          rope_pair(v[0], v[1], mr, a.dr, static_cast<float>(p), a.log2_base);
+          rope_pair(v[2], v[3], mr + 1, a.dr, static_cast<float>(p), a.log2_base);
+        }
+        *reinterpret_cast<uint2*>(a.q + static_cast<int64_t>(m) * a.n1 + n) =
+            make_uint2(bf16x2_bits(v[0], v[1]), bf16x2_bits(v[2], v[3]));
+      } else if (!in_cache) {
+        continue;
+      } else if (n < a.n2) {  // latent
+        *reinterpret_cast<uint2*>(a.ckv + (static_cast<int64_t>(b) * a.max_len + p) * a.dc + (n - a.n1)) =
+            make_uint2(bf16x2_bits(v[0], v[1]), bf16x2_bits(v[2], v[3]));
+      } else {  // rotary key
+        const int j = n - a.n2;
+        rope_pair(v[0], v[1], j >> 1, a.dr, static_cast<float>(p), a.log2_base);
+        rope_pair(v[2], v[3], (j >> 1) + 1, a.dr, static_cast<float>(p), a.log2_base);
+        *reinterpret_cast<uint2*>(a.ckr + (static_cast<int64_t>(b) * a.max_len + p) * a.dr + j) =
+            make_uint2(bf16x2_bits(v[0], v[1]), bf16x2_bits(v[2], v[3]));
+      }
+    } else {
+      if constexpr (EPI == kMlaEpiRes) {
+        if (a.res) {
+          const uint2 r = *reinterpret_cast<const uint2*>(a.res + static_cast<int64_t>(m) * a.ldc + n);
+          v[0] += bf16_to_f32(static_cast<uint16_t>(r.x));
+          v[1] += bf16_to_f32(static_cast<uint16_t>(r.x >> 16));
+          v[2] += bf16_to_f32(static_cast<uint16_t>(r.y));
+          v[3] += bf16_to_f32(static_cast<uint16_t>(r.y >> 16));
+        }
+      }
+      *reinterpret_cast<uint2*>(a.c + static_cast<int64_t>(m) * a.ldc + n) =
+          make_uint2(bf16x2_bits(v[0], v[1]), bf16x2_bits(v[2], v[3]));
+    }
+  }
+}
+
+namespace {
+constexpr int kQT = 64;           // query rows per prefill block
+constexpr int kRowsPerWave = kQT / 4;
+constexpr int kMaxQwCh = 16;      // d_nope + d_rope <= 128
+constexpr int kKRow = 8 * kMaxQwCh + 8;  // staged key row (bf16), padded
+constexpr int kVRow = 64 + 8;            // staged value row (bf16), padded
+
+__device__ __forceinline__ float dot8(const u32x4& x, const u32x4& y) {
+  float s = 0.0f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    s = fmaf(__uint_as_float(x[w] << 16), __uint_as_float(y[w] << 16), s);
+    s = fmaf(__uint_as_float(x[w] & 0xFFFF0000u), __uint_as_float(y[w] & 0xFFFF0000u), s);
+  }
+  return s;
+}
+}  // namespace
+
+__global__ __launch_bounds__(kTh) void mla_attn_prefill_kernel(MlaAttnArgs a) {
+  __shared__ uint16_t qs[kQT * kKRow];
+  __shared__ uint16_t ks[64 * kKRow];
+  __shared__ uint16_t vs[64 * kVRow];
+  __shared__ float ps[4][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
+  const int i0 = blockIdx.x * kQT, h = blockIdx.y, b = blockIdx.z;
+  const int S = a.seq, qw = a.dn + a.dr, qwc = qw / 8, dv = a.dv;
+  const int G = 64 / dv, j = lane % dv, grp = lane / dv;
+  const int64_t qld = static_cast<int64_t>(a.nh) * qw;
+  const int64_t kvld = static_cast<int64_t>(a.nh) * (a.dn + dv);
+  const int64_t tok0 = static_cast<int64_t>(b) * S;
+
+  // queries of the tile
+  for (int idx = tid; idx < kQT * qwc; idx += kTh) {
+    const int r = idx / qwc, c = idx % qwc;
+    u32x4 v = u32x4{0u, 0u, 0u, 0u};
+    if (i0 + r < S) v = *reinterpret_cast<const u32x4*>(a.q + (tok0 + i0 + r) * qld + h * qw + 8 * c);
+    *reinterpret_cast<u32x4*>(qs + r * kKRow + 8 * c) = v;
+  }
+  float mrow[kRowsPerWave], lrow[kRowsPerWave], acc[kRowsPerWave];
+#pragma unroll
+  for (int r = 0; r < kRowsPerWave; ++r) {
+    mrow[r] = -INFINITY;
+    lrow[r] = 0.0f;
+    acc[r] = 0.0f;
+  }
+  const int last = min(i0 + kQT, S) - 1;  // last query of the tile
+  for (int c0 = 0; c0 <= last; c0 += 64) {
+    __syncthreads();  // the previous chunk is no longer read
+    // keys [k_nope_h, k_r] and values v_h of positions c0 .. c0+63
+    const int kch = a.dn / 8, rch = a.dr / 8, vch = dv / 8;
+    for (int idx = tid; idx < 64 * (qwc + vch); idx += kTh) {
+      const int r = idx / (qwc + vch), c = idx % (qwc + vch);
+      const int s = c0 + r;
+      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      if (s < S) {
+        if (c < kch)
+          v = *reinterpret_cast<const u32x4*>(a.kvx + (tok0 + s) * kvld + h * a.dn + 8 * c);
+        else if (c < kch + rch)
+          v = *reinterpret_cast<const u32x4*>(a.ckr + (static_cast<int64_t>(b) * a.max_len + s) * a.dr +
+                                              8 * (c - kch));
+        else
+          v = *reinterpret_cast<const u32x4*>(a.kvx + (tok0 + s) * kvld + a.nh * a.dn + h * dv +
+                                              8 * (c - qwc));
+      }
+      if (c < qwc) *reinterpret_cast<u32x4*>(ks + r * kKRow + 8 * c) = v;
+      else *reinterpret_cast<u32x4*>(vs + r * kVRow + 8 * (c - qwc)) = v;
+    }
+    __syncthreads();
+    // this lane's key row
+    u32x4 kr[kMaxQwCh];
+#pragma unroll
+    for (int c = 0; c < kMaxQwCh; ++c)
+      if (c < qwc) kr[c] = *reinterpret_cast<const u32x4*>(ks + lane * kKRow + 8 * c);
+    const int s = c0 + lane;
+#pragma unroll
+    for (int r = 0; r < kRowsPerWave; ++r) {
+      const int rr = wave * kRowsPerWave + r;
+      const int i = i0 + rr;
+      if (i > last || i < c0) continue;  // uniform per wave
+      float sc = 0.0f;
+#pragma unroll
+      for (int c = 0; c < kMaxQwCh; ++c)
+        if (c < qwc) sc += dot8(*reinterpret_cast<const u32x4*>(qs + rr * kKRow + 8 * c), kr[c]);
+      const bool ok = s <= i;
+      sc = ok ? sc * a.scale : -INFINITY;
+      const float mnew = fmaxf(mrow[r], wave_max(sc));
+      const float corr = __expf(mrow[r] - mnew);
+      const float p = ok ? __expf(sc - mnew) : 0.0f;
+      lrow[r] = lrow[r] * corr + wave_sum(p);
+      mrow[r] = mnew;
+      ps[wave][lane] = p;  // read back by the other lanes of this wave only
+      __builtin_amdgcn_wave_barrier();
+      float t = 0.0f;
+      for (int k2 = grp; k2 < 64; k2 += G) t = fmaf(ps[wave][k2], bf16_to_f32(vs[k2 * kVRow + j]), t);
+      __builtin_amdgcn_wave_barrier();
+      acc[r] = acc[r] * corr + t;
+    }
+  }
+  // combine the key groups and write o
+#pragma unroll
+  for (int r = 0; r < kRowsPerWave; ++r) {
+    const int rr = wave * kRowsPerWave + r;
+    const int i = i0 + rr;
+    float t = acc[r];
+    for (int o = dv; o < 64; o <<= 1) t += __shfl_xor(t, o, 64);
+    if (i <= last && grp == 0)
+      a.o[(tok0 + i) * static_cast<int64_t>(a.nh) * dv + h * dv + j] = f32_to_bf16(t / lrow[r]);
+  }
+}
+
+namespace {
+constexpr int kMaxLat = 256;   // d_latent
+constexpr int kMaxHeads = 16;
+constexpr int kHpw = kMaxHeads / 4;  // heads per wave at most
+constexpr int kCRow = kMaxLat + 64 + 8;  // staged cache row: latent, rotary key, pad
+}  // namespace
+
+__global__ __launch_bounds__(kTh) void mla_attn_decode_kernel(MlaAttnArgs a) {
+  __shared__ float qlat[kMaxHeads * kMaxLat];
+  __shared__ float qrope[kMaxHeads * 64];
+  __shared__ uint16_t crow[64 * kCRow];
+  __shared__ float ps[4][64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
+  const int b = blockIdx.x;
+  const int nh = a.nh, dc = a.dc, dn = a.dn, dr = a.dr, dv = a.dv, qw = dn + dr;
+  const int64_t orow = static_cast<int64_t>(b) * nh * dv;
+  const int p = a.pos[b];
+  if (p < 0 || p >= a.max_len) {
+    for (int idx = tid; idx < nh * dv; idx += kTh) a.o[orow + idx] = 0;
+    return;
+  }
+  // each head's query in latent space, and its rotary part
+  const uint16_t* qb = a.q + static_cast<int64_t>(b) * nh * qw;
+  for (int idx = tid; idx < nh * dc; idx += kTh) {
+    const int h = idx / dc, c = idx % dc;
+    float s = 0.0f;
+    for (int jj = 0; jj < dn; ++jj)
+      s = fmaf(bf16_to_f32(qb[h * qw + jj]), bf16_to_f32(a.w_uk[static_cast<int64_t>(h * dn + jj) * dc + c]), s);
+    qlat[h * kMaxLat + c] = s;
+  }
+  for (int idx = tid; idx < nh * dr; idx += kTh) qrope[(idx / dr) * 64 + idx % dr] = bf16_to_f32(qb[(idx / dr) * qw + dn + idx % dr]);
+
+  const int lc = dc / 64;  // latent numbers per lane in P V
+  float mh[kHpw], lh[kHpw], oacc[kHpw][kMaxLat / 64];
+#pragma unroll
+  for (int k = 0; k < kHpw; ++k) {
+    mh[k] = -INFINITY;
+    lh[k] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kMaxLat / 64; ++i) oacc[k][i] = 0.0f;
+  }
+  const int64_t cbase = static_cast<int64_t>(b) * a.max_len;
+  const int dcc = dc / 8, drc = dr / 8;
+  for (int c0 = 0; c0 <= p; c0 += 64) {
+    __syncthreads();
+    for (int idx = tid; idx < 64 * (dcc + drc); idx += kTh) {
+      const int r = idx / (dcc + drc), c = idx % (dcc + drc);
+      const int s = c0 + r;
+      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      if (s <= p) {
+        if (c < dcc) v = *reinterpret_cast<const u32x4*>(a.ckv + (cbase + s) * dc + 8 * c);
+        else v = *reinterpret_cast<const u32x4*>(a.ckr + (cbase + s) * dr + 8 * (c - dcc));
+      }
+      *reinterpret_cast<u32x4*>(crow + r * kCRow + (c < dcc ? 8 * c : kMaxLat + 8 * (c - dcc))) = v;
+    }
+    __syncthreads();
+    const int s = c0 + lane;
+    const bool ok = s <= p;
+#pragma unroll
+    for (int k = 0; k < kHpw; ++k) {
+      const int h = wave + 4 * k;
+      if (h >= nh) break;
+      float sc = 0.0f;
+      for (int c = 0; c < dcc; ++c) {
+        const u32x4 kv = *reinterpret_cast<const u32x4*>(crow + lane * kCRow + 8 * c);
+        const float* qv = qlat + h * kMaxLat + 8 * c;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          sc = fmaf(qv[2 * w], __uint_as_float(kv[w] << 16), sc);
+          sc = fmaf(qv[2 * w + 1], __uint_as_float(kv[w] & 0xFFFF0000u), sc);
+        }
+      }
+      for (int c = 0; c < drc; ++c) {
+        const u32x4 kv = *reinterpret_cast<const u32x4*>(crow + lane * kCRow + kMaxLat + 8 * c);
+        const float* qv = qrope + h * 64 + 8 * c;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          sc = fmaf(qv[2 * w], __uint_as_float(kv[w] << 16), sc);
+          sc = fmaf(qv[2 * w + 1], __uint_as_float(kv[w] & 0xFFFF0000u), sc);
+        }
+      }
+      sc = ok ? sc * a.scale : -INFINITY;
+      const float mnew = fmaxf(mh[k], wave_max(sc));
+      const float corr = __expf(mh[k] - mnew);
+      const float pr = ok ? __expf(sc - mnew) : 0.0f;
+      lh[k] = lh[k] * corr + wave_sum(pr);
+      mh[k] = mnew;
+      ps[wave][lane] = pr;
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int i = 0; i < kMaxLat / 64; ++i) {
+        if (i >= lc) break;
+        float t = 0.0f;
+        for (int k2 = 0; k2 < 64; ++k2) t = fmaf(ps[wave][k2], bf16_to_f32(crow[k2 * kCRow + lane + 64 * i]), t);
+        oacc[k][i] = oacc[k][i] * corr + t;
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+  // the attended latent of each head, then W_uv[h]
+  __syncthreads();
+  float* olat = qlat;  // reused
+#pragma unroll
+  for (int k = 0; k < kHpw; ++k) {
+    const int h = wave + 4 * k;
+    if (h >= nh) break;
+#pragma unroll
+    for (int i = 0; i < kMaxLat / 64; ++i)
+      if (i < lc) olat[h * kMaxLat + lane + 64 * i] = oacc[k][i] / lh[k];
+  }
+  __syncthreads();
+  for (int idx = tid; idx < nh * dv; idx += kTh) {
+    const int h = idx / dv;
+    const uint16_t* wr = a.w_uv + static_cast<int64_t>(idx) * dc;
+    float s = 0.0f;
+    for (int c = 0; c < dc; ++c) s = fmaf(bf16_to_f32(wr[c]), olat[h * kMaxLat + c], s);
+    a.o[orow + idx] = f32_to_bf16(s);
+  }
+}
+
+hipError_t launch_mla_gemm(const MlaGemmArgs& a, int epi, hipStream_t s) {
+  const dim3 grid((a.M + kGM - 1) / kGM, (a.N + kGN - 1) / kGN), block(kTh);
+  switch (epi) {
+    case kMlaEpiProj:
+      hipLaunchKernelGGL(mla_gemm_kernel<kMlaEpiProj>, grid, block, 0, s, a);
+      break;
+    case kMlaEpiPlain:
+      hipLaunchKernelGGL(mla_gemm_kernel<kMlaEpiPlain>, grid, block, 0, s, a);
+      break;
+    case kMlaEpiRes:
+      hipLaunchKernelGGL(mla_gemm_kernel<kMlaEpiRes>, grid, block, 0, s, a);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_mla_attn_prefill(const MlaAttnArgs& a, int batch, hipStream_t s) {
+  const dim3 grid((a.seq + kQT - 1) / kQT, a.nh, batch);
+  hipLaunchKernelGGL(mla_attn_prefill_kernel, grid, dim3(kTh), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_mla_attn_decode(const MlaAttnArgs& a, int batch, hipStream_t s) {
+  hipLaunchKernelGGL(mla_attn_decode_kernel, dim3(batch), dim3(kTh), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -28,7 +28,8 @@ MOE_ERR_SCRATCH_LIMIT = 5
 EXPORTED = ("moe_status_str", "moe_workspace_bytes", "moe_route", "moe_permute",
             "moe_permute_noalloc", "moe_grouped_ffn", "moe_combine", "moe_rmsnorm",
             "moe_update_bias", "moe_backward_workspace_bytes", "moe_combine_backward",
-            "moe_grouped_ffn_backward", "moe_route_backward")
+            "moe_grouped_ffn_backward", "moe_route_backward", "mla_workspace_bytes",
+            "mla_prefill", "mla_decode")
 
 
 class MoeError(RuntimeError):
@@ -64,6 +65,32 @@ class Shape:
                      wl.shared_hidden, wl.seq_len)
 
 
+class MlaShapeC(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("seq_len", ctypes.c_int32),
+                ("max_len", ctypes.c_int32), ("d_model", ctypes.c_int32),
+                ("n_heads", ctypes.c_int32), ("d_latent", ctypes.c_int32),
+                ("d_nope", ctypes.c_int32), ("d_rope", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("rope_base", ctypes.c_float)]
+
+
+@dataclass(frozen=True)
+class MlaShape:
+    batch: int
+    seq_len: int
+    max_len: int
+    d_model: int = 384
+    n_heads: int = 6
+    d_latent: int = 128
+    d_nope: int = 32
+    d_rope: int = 16
+    d_v: int = 32
+    rope_base: float = 10000.0
+
+    def c(self) -> MlaShapeC:
+        return MlaShapeC(self.batch, self.seq_len, self.max_len, self.d_model, self.n_heads,
+                         self.d_latent, self.d_nope, self.d_rope, self.d_v, self.rope_base)
+
+
 _lib = None
 
 
@@ -96,6 +123,10 @@ def load() -> ctypes.CDLL:
     L.moe_grouped_ffn_backward.argtypes = [S] + [P] * 20 + [ctypes.c_size_t, P]
     L.moe_route_backward.argtypes = [S, P, P, P, P, P, ctypes.c_float, P, P, P, P, P, P, P,
                                      ctypes.c_size_t, P]
+    M = ctypes.POINTER(MlaShapeC)
+    L.mla_workspace_bytes.argtypes = [M, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
+    L.mla_prefill.argtypes = [M] + [P] * 12 + [ctypes.c_size_t, P]
+    L.mla_decode.argtypes = [M] + [P] * 13 + [ctypes.c_size_t, P]
     for name in EXPORTED[1:]:
         getattr(L, name).restype = ctypes.c_int
     _lib = L
@@ -299,3 +330,44 @@ def block_forward(shape: Shape, x, params: dict, bufs: dict, eps: float = 1e-6,
     """Pre-norm residual block: out = x + MoE(RMSNorm(x)), all on one stream."""
     moe_rmsnorm(shape, x, params["norm"], eps, bufs["xn"], stream)
     return layer_forward(shape, bufs["xn"], params, bufs, residual=x, alpha=alpha, stream=stream)
+
+
+# ---------------------------------------------------------------- MLA attention (include/mla.h)
+
+MLA_WEIGHTS = ("w_q", "w_dkv", "w_kr", "w_uk", "w_uv", "w_o")
+
+
+def mla_workspace_bytes(shape: MlaShape, decode: bool = False) -> int:
+    n = ctypes.c_size_t(0)
+    _ok(load().mla_workspace_bytes(ctypes.byref(shape.c()), int(bool(decode)), ctypes.byref(n)),
+        "mla_workspace_bytes")
+    return int(n.value)
+
+
+def mla_prefill(shape: MlaShape, x, params: dict, cache_kv, cache_kr, out, residual=None,
+                workspace=None, stream=None):
+    wp, wn = _ws(workspace)
+    _ok(load().mla_prefill(ctypes.byref(shape.c()), _p(x), *[_p(params[k]) for k in MLA_WEIGHTS],
+                           _p(residual), _p(cache_kv), _p(cache_kr), _p(out), wp, wn, _s(stream)),
+        "mla_prefill")
+
+
+def mla_decode(shape: MlaShape, x, pos, params: dict, cache_kv, cache_kr, out, residual=None,
+               workspace=None, stream=None):
+    wp, wn = _ws(workspace)
+    _ok(load().mla_decode(ctypes.byref(shape.c()), _p(x), _p(pos),
+                          *[_p(params[k]) for k in MLA_WEIGHTS], _p(residual), _p(cache_kv),
+                          _p(cache_kr), _p(out), wp, wn, _s(stream)), "mla_decode")
+
+
+def alloc_mla(shape: MlaShape, device="cuda", decode: bool = False) -> dict:
+    """Caches, output and workspace of an MLA call, allocated with torch."""
+    b16 = torch.bfloat16
+    rows = shape.batch if decode else shape.batch * shape.seq_len
+    return {
+        "cache_kv": torch.zeros((shape.batch, shape.max_len, shape.d_latent), dtype=b16, device=device),
+        "cache_kr": torch.zeros((shape.batch, shape.max_len, shape.d_rope), dtype=b16, device=device),
+        "out": torch.empty((rows, shape.d_model), dtype=b16, device=device),
+        "workspace": torch.empty((max(mla_workspace_bytes(shape, decode), 256),), dtype=torch.uint8,
+                                 device=device),
+    }

@@ -243,3 +243,77 @@ def bf16_bits(t: torch.Tensor) -> torch.Tensor:
     """Reinterpret a bf16 tensor as its uint16 bit patterns (int16 storage)."""
     assert t.dtype == torch.bfloat16
     return t.view(torch.int16)
+
+
+# ---------------------------------------------------------------- MLA attention
+
+ROLE_MLA_X = 20
+ROLE_MLA_W = 21   # + index into MLA_WEIGHT_ROLES
+ROLE_MLA_RES = 28
+ROLE_MLA_POS = 29
+MLA_WEIGHT_ROLES = ("w_q", "w_dkv", "w_kr", "w_uk", "w_uv", "w_o")
+
+
+@dataclasses.dataclass(frozen=True)
+class MlaWorkload:
+    """The attention half of the mini block: 6 heads, a 128-number latent
+    and a 16-number shared rotary key per token, 32-number content keys and
+    values per head, 256-token context (190行JAX复刻DeepSeek V3, sections
+    190行代码到底装进了什么 and 先说结论); d_model 384 as for the MoE."""
+    name: str
+    cfg_id: int
+    batch: int           # sequences
+    seq_len: int         # prefill: tokens per sequence; decode: cached tokens before the new one
+    max_len: int
+    decode: bool
+    d_model: int = 384
+    n_heads: int = 6
+    d_latent: int = 128
+    d_nope: int = 32
+    d_rope: int = 16
+    d_v: int = 32
+    x_std: float = 1.0
+    w_std: float = 0.05
+    description: str = ""
+
+    @property
+    def tokens(self) -> int:
+        """Token rows of one call."""
+        return self.batch if self.decode else self.batch * self.seq_len
+
+
+MLA_WORKLOADS = {
+    "mla_prefill_32x256": MlaWorkload(
+        "mla_prefill_32x256", 30, 32, 256, 256, False,
+        description="MLA prefill of a mini training batch: 32 sequences x 256 tokens"),
+    "mla_decode_256x256": MlaWorkload(
+        "mla_decode_256x256", 31, 256, 255, 256, True,
+        description="MLA decode step of 256 sequences at position 255 (255 cached tokens each)"),
+}
+
+
+def mla_custom(name="mla_custom", cfg_id=40, batch=2, seq_len=70, max_len=80, decode=False, **kw):
+    return MlaWorkload(name, cfg_id, batch, seq_len, max_len, decode, **kw)
+
+
+def mla_params(wl: MlaWorkload, layer: int = 0, device="cpu") -> dict:
+    """The six MLA weights, bf16, N(0, w_std^2), stored [N, K]."""
+    H, d = wl.n_heads, wl.d_model
+    shapes = {"w_q": (H * (wl.d_nope + wl.d_rope), d), "w_dkv": (wl.d_latent, d),
+              "w_kr": (wl.d_rope, d), "w_uk": (H * wl.d_nope, wl.d_latent),
+              "w_uv": (H * wl.d_v, wl.d_latent), "w_o": (d, H * wl.d_v)}
+    return {k: normal(shapes[k], wl.w_std, seed_of(wl.cfg_id, layer, ROLE_MLA_W + i), device,
+                      torch.bfloat16)
+            for i, k in enumerate(MLA_WEIGHT_ROLES)}
+
+
+def mla_tokens(wl: MlaWorkload, rows: int, step: int = 0, device="cpu") -> torch.Tensor:
+    """Token rows (bf16, N(0, x_std^2)) for a prefill of rows tokens or a
+    decode step of rows sequences."""
+    return normal((rows, wl.d_model), wl.x_std, seed_of(wl.cfg_id, 0, ROLE_MLA_X, step=step),
+                  device, torch.bfloat16)
+
+
+def mla_residual(wl: MlaWorkload, rows: int, device="cpu") -> torch.Tensor:
+    return normal((rows, wl.d_model), 1.0, seed_of(wl.cfg_id, 0, ROLE_MLA_RES), device,
+                  torch.bfloat16)

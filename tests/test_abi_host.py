@@ -1,5 +1,6 @@
 """Host-side checks of the C ABI: the library loads, exports every symbol that
-include/moe.h declares, and rejects bad arguments before launching anything.
+include/moe.h and include/mla.h declare, and rejects bad arguments before
+launching anything.
 No kernel is launched here (no GPU needed): each call below fails validation."""
 import ctypes
 import os
@@ -10,7 +11,8 @@ import pytest
 from sparse_mixture_experts_51_amd import moe
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "moe.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("moe.h", "mla.h")]
+DECL = r"\b((?:moe|mla)_[a-z_]+)\s*\("
 
 # fake, 256-byte aligned device addresses: never dereferenced, validation fails first
 A = 0x7F0000000000
@@ -20,10 +22,13 @@ def fake(i=0):
     return ctypes.c_void_p(A + 0x100000 * (i + 1))
 
 
+def header_text():
+    text = "".join(open(h).read() for h in HEADERS)
+    return re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+
+
 def declared_symbols():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(m for m in re.findall(DECL, header_text()) if m not in ("moe_status",)))
 
 
 @pytest.fixture(scope="module")
@@ -42,10 +47,9 @@ def test_exports_every_declared_symbol(L):
 
 
 def declared_prototypes():
-    """name -> list of parameter type strings, from include/moe.h."""
-    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    """name -> list of parameter type strings, from the headers."""
     out = {}
-    for m in re.finditer(r"\b(moe_[a-z_]+)\s*\(([^)]*)\)\s*;", text):
+    for m in re.finditer(r"\b((?:moe|mla)_[a-z_]+)\s*\(([^)]*)\)\s*;", header_text()):
         params = [q.strip() for q in m.group(2).split(",") if q.strip()]
         out[m.group(1)] = params
     return out
@@ -297,3 +301,47 @@ def test_probe_rejects_unusable_sizes_before_launching():
         for buf, n, sink in ((fake(0), mib + 1, fake(1)), (fake(0), 0, fake(1)), (fake(0), -mib, fake(1)),
                              (None, mib, fake(1)), (fake(0), mib, None)):
             assert fn(buf, n, sink, None) == 1, name
+
+
+def mla_shape(**kw):
+    base = dict(batch=2, seq_len=64, max_len=128, d_model=384, n_heads=6, d_latent=128,
+                d_nope=32, d_rope=16, d_v=32, rope_base=10000.0)
+    base.update(kw)
+    return moe.MlaShapeC(*[base[f] for f, _ in moe.MlaShapeC._fields_])
+
+
+def test_mla_workspace_and_shape_checks(L):
+    n = ctypes.c_size_t(0)
+    assert L.mla_workspace_bytes(ctypes.byref(mla_shape()), 0, ctypes.byref(n)) == moe.MOE_OK
+    T, H = 2 * 64, 6
+    assert n.value >= 2 * T * H * (48 + 64 + 32)
+    assert L.mla_workspace_bytes(ctypes.byref(mla_shape()), 1, ctypes.byref(n)) == moe.MOE_OK
+    assert L.mla_workspace_bytes(ctypes.byref(mla_shape()), 0, None) == moe.MOE_ERR_INVALID_ARGUMENT
+    bad = [dict(seq_len=200), dict(max_len=0), dict(rope_base=1.0), dict(n_heads=0)]
+    for kw in bad:
+        assert L.mla_workspace_bytes(ctypes.byref(mla_shape(**kw)), 0, ctypes.byref(n)) == \
+            moe.MOE_ERR_INVALID_ARGUMENT, kw
+    unsupported = [dict(d_model=100), dict(d_latent=96), dict(d_latent=320), dict(d_v=24),
+                   dict(d_nope=100, d_rope=40), dict(n_heads=17, d_v=64), dict(d_rope=12)]
+    for kw in unsupported:
+        assert L.mla_workspace_bytes(ctypes.byref(mla_shape(**kw)), 0, ctypes.byref(n)) == \
+            moe.MOE_ERR_UNSUPPORTED, kw
+
+
+def test_mla_calls_refuse_bad_arguments(L):
+    s = ctypes.byref(mla_shape())
+    ws = fake(20)
+    w = [fake(i) for i in range(6)]
+    # a missing weight, a misaligned output, a small workspace, no positions
+    assert L.mla_prefill(s, fake(7), None, *w[1:], None, fake(8), fake(9), fake(10), ws, 1 << 30,
+                         None) == moe.MOE_ERR_INVALID_ARGUMENT
+    odd = ctypes.c_void_p(A + 2)
+    assert L.mla_prefill(s, fake(7), *w, None, fake(8), fake(9), odd, ws, 1 << 30, None) == \
+        moe.MOE_ERR_INVALID_ARGUMENT
+    assert L.mla_prefill(s, fake(7), *w, None, fake(8), fake(9), fake(10), ws, 16, None) == \
+        moe.MOE_ERR_WORKSPACE
+    assert L.mla_decode(s, fake(7), None, *w, None, fake(8), fake(9), fake(10), ws, 1 << 30,
+                        None) == moe.MOE_ERR_INVALID_ARGUMENT
+    # nothing to do: no launch, OK
+    empty = ctypes.byref(mla_shape(batch=0))
+    assert L.mla_prefill(empty, None, *w, None, None, None, None, None, 0, None) == moe.MOE_OK

@@ -1,0 +1,183 @@
+"""GPU parity of the MLA attention (mla_prefill, mla_decode) through the C ABI
+against the oracle (explicit decompression, bf16 at the same storage points).
+
+Tolerances.  Caches: the latent and the rotary key are one bf16 rounding of
+an fp32 sum over d (the oracle: fp64), the rotary key turned in fp32 -- at
+most one bf16 step apart, |err| <= 2^-7 |ref| + 1e-6 (one step of the
+larger neighbour).  Outputs: the MoE layer's bar, max|err| <= 2e-2 max|ref|
+and relative L2 <= 1e-2 (bf16 storage of q, the latent, keys, values and
+the heads' outputs; fp32 softmax and sums).  Decode is compared with the
+oracle run on the GPU's own cache (teacher forcing), since the GPU reads only
+the cache: W_uk is applied to the query instead of to every key."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import bits, f32, say
+from sparse_mixture_experts_51_amd import moe, workloads
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    moe.load()
+
+
+def shape_of(wl, batch=None, seq=None):
+    return moe.MlaShape(batch if batch is not None else wl.batch,
+                        seq if seq is not None else wl.seq_len, wl.max_len, wl.d_model,
+                        wl.n_heads, wl.d_latent, wl.d_nope, wl.d_rope, wl.d_v)
+
+
+def host_params(p):
+    return {k: bits(v) for k, v in p.items()}
+
+
+def check_close(g, r, what, max_rel=2e-2, rel_l2=1e-2):
+    g = np.asarray(g, np.float64)
+    r = np.asarray(r, np.float64)
+    err = np.abs(g - r)
+    rmax = np.abs(r).max(initial=0.0)
+    l2 = np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-30)
+    say(f"  {what}: max|err|={err.max(initial=0):.3e} (max|ref| {rmax:.3e}) rel_l2={l2:.3e}")
+    assert np.isfinite(g).all(), what
+    assert err.max(initial=0.0) <= max_rel * rmax + 1e-30, what
+    assert l2 <= rel_l2, what
+
+
+def check_cache(g, r, what):
+    g = np.asarray(g, np.float64)
+    r = np.asarray(r, np.float64)
+    err = np.abs(g - r)
+    bound = 2.0 ** -7 * np.abs(r) + 1e-6
+    n_diff = int((err > 0).sum())
+    say(f"  {what}: {n_diff} of {err.size} differ, max|err|={err.max(initial=0):.3e}")
+    assert (err <= bound).all(), what
+    assert n_diff <= 0.01 * err.size + 1, what
+
+
+def gpu_prefill(wl, x, p, res=None, batch=None, seq=None):
+    shape = shape_of(wl, batch, seq)
+    buf = moe.alloc_mla(shape, DEV)
+    moe.mla_prefill(shape, x, p, buf["cache_kv"], buf["cache_kr"], buf["out"], residual=res,
+                    workspace=buf["workspace"])
+    torch.cuda.synchronize()
+    return shape, buf
+
+
+PREFILL_CASES = {
+    # mini dims, two query tiles with a ragged tail, room left in the caches
+    "mini_B2_S70": dict(batch=2, seq_len=70, max_len=80, cfg_id=41),
+    # one token: attends only to itself
+    "mini_B3_S1": dict(batch=3, seq_len=1, max_len=4, cfg_id=42),
+    # other head sizes: 2 heads, d_v 64, latent 64, 16 + 8 key numbers
+    "small_heads_dv64": dict(batch=2, seq_len=130, max_len=130, cfg_id=43, d_model=128,
+                             n_heads=2, d_latent=64, d_nope=16, d_rope=8, d_v=64),
+    # many heads, d_v 16, latent 256, 64 + 64 key numbers
+    "wide_16heads": dict(batch=1, seq_len=65, max_len=96, cfg_id=44, d_model=256, n_heads=16,
+                         d_latent=256, d_nope=64, d_rope=64, d_v=16),
+}
+
+
+@pytest.mark.parametrize("name", list(PREFILL_CASES))
+def test_prefill_matches_oracle(name):
+    wl = workloads.mla_custom(name=name, **PREFILL_CASES[name])
+    say(f"[mla prefill] {name} B={wl.batch} S={wl.seq_len} L={wl.max_len} d={wl.d_model} "
+        f"H={wl.n_heads} dc={wl.d_latent} dn={wl.d_nope} dr={wl.d_rope} dv={wl.d_v}")
+    p = workloads.mla_params(wl, 0, DEV)
+    x = workloads.mla_tokens(wl, wl.tokens, 0, DEV)
+    res = workloads.mla_residual(wl, wl.tokens, DEV)
+    _, buf = gpu_prefill(wl, x, p, res)
+    ref = oracle.mla_prefill(bits(x), host_params(p), wl.n_heads, wl.batch, wl.seq_len,
+                             wl.max_len, residual=bits(res))
+    S = wl.seq_len
+    check_cache(f32(bits(buf["cache_kv"]))[:, :S], ref["cache_kv"][:, :S], f"{name}.cache_kv")
+    check_cache(f32(bits(buf["cache_kr"]))[:, :S], ref["cache_kr"][:, :S], f"{name}.cache_kr")
+    assert not bits(buf["cache_kv"])[:, S:].any()  # positions past the prefill untouched
+    check_close(f32(bits(buf["out"])), ref["out"], f"{name}.out")
+
+
+def test_decode_matches_oracle_on_the_gpu_cache():
+    """Prefill 70 tokens of 5 sequences on the GPU, then one decode step at
+    ragged positions (0, 63, 64, 70, and -1 which is skipped)."""
+    wl = workloads.mla_custom(name="decode", batch=5, seq_len=70, max_len=80, cfg_id=45)
+    p = workloads.mla_params(wl, 0, DEV)
+    x = workloads.mla_tokens(wl, wl.tokens, 0, DEV)
+    shape, buf = gpu_prefill(wl, x, p)
+    pos = torch.tensor([0, 63, 64, 70, -1], dtype=torch.int32, device=DEV)
+    xd = workloads.mla_tokens(wl, wl.batch, 1, DEV)
+    res = workloads.mla_residual(wl, wl.batch, DEV)
+    kv0 = f32(bits(buf["cache_kv"])).astype(np.float64)
+    kr0 = f32(bits(buf["cache_kr"])).astype(np.float64)
+    dshape = moe.MlaShape(wl.batch, 0, wl.max_len, wl.d_model, wl.n_heads, wl.d_latent,
+                          wl.d_nope, wl.d_rope, wl.d_v)
+    dbuf = moe.alloc_mla(dshape, DEV, decode=True)
+    moe.mla_decode(dshape, xd, pos, p, buf["cache_kv"], buf["cache_kr"], dbuf["out"],
+                   residual=res, workspace=dbuf["workspace"])
+    torch.cuda.synchronize()
+    hp = host_params(p)
+    valid = np.array([0, 1, 2, 3])
+    ref = oracle.mla_decode(bits(xd)[valid], hp, wl.n_heads, pos.cpu().numpy()[valid],
+                            kv0[valid], kr0[valid], residual=bits(res)[valid])
+    out = f32(bits(dbuf["out"])).astype(np.float64)
+    check_close(out[valid], ref["out"], "decode.out")
+    kv1 = f32(bits(buf["cache_kv"])).astype(np.float64)
+    kr1 = f32(bits(buf["cache_kr"])).astype(np.float64)
+    for i, b in enumerate(valid):
+        q = int(pos[b])
+        check_cache(kv1[b, q], ref["cache_kv"][i, q], f"decode.cache_kv[{b}]")
+        check_cache(kr1[b, q], ref["cache_kr"][i, q], f"decode.cache_kr[{b}]")
+        # the rest of the cache is untouched
+        mask = np.ones(wl.max_len, bool)
+        mask[q] = False
+        assert np.array_equal(kv1[b, mask], kv0[b, mask])
+    # the skipped sequence: output = residual, cache untouched
+    assert np.array_equal(bits(dbuf["out"])[4], bits(res)[4])
+    assert np.array_equal(kv1[4], kv0[4]) and np.array_equal(kr1[4], kr0[4])
+
+
+def test_prefill_full_size_sampled():
+    """mla_prefill_32x256 as the benchmark runs it; the oracle on sequences 0
+    and 31 (each sequence is independent)."""
+    wl = workloads.MLA_WORKLOADS["mla_prefill_32x256"]
+    p = workloads.mla_params(wl, 0, DEV)
+    x = workloads.mla_tokens(wl, wl.tokens, 0, DEV)
+    _, buf = gpu_prefill(wl, x, p)
+    S, d = wl.seq_len, wl.d_model
+    hp = host_params(p)
+    xs = bits(x).reshape(wl.batch, S, d)
+    out = f32(bits(buf["out"])).reshape(wl.batch, S, d)
+    for b in (0, wl.batch - 1):
+        ref = oracle.mla_prefill(xs[b], hp, wl.n_heads, 1, S, wl.max_len)
+        check_close(out[b], ref["out"], f"full.out[seq {b}]")
+        check_cache(f32(bits(buf["cache_kv"]))[b], ref["cache_kv"][0], f"full.cache_kv[{b}]")
+
+
+def test_decode_full_size_sampled():
+    """mla_decode_256x256: 256 sequences with 255 cached tokens decode
+    position 255; the oracle on 3 sampled sequences with the GPU's cache."""
+    wl = workloads.MLA_WORKLOADS["mla_decode_256x256"]
+    p = workloads.mla_params(wl, 0, DEV)
+    x = workloads.mla_tokens(wl, wl.batch * wl.seq_len, 0, DEV)
+    pshape = moe.MlaShape(wl.batch, wl.seq_len, wl.max_len)
+    buf = moe.alloc_mla(pshape, DEV)
+    moe.mla_prefill(pshape, x, p, buf["cache_kv"], buf["cache_kr"], buf["out"],
+                    workspace=buf["workspace"])
+    kv0 = f32(bits(buf["cache_kv"])).astype(np.float64)
+    kr0 = f32(bits(buf["cache_kr"])).astype(np.float64)
+    dshape = moe.MlaShape(wl.batch, 0, wl.max_len)
+    dbuf = moe.alloc_mla(dshape, DEV, decode=True)
+    pos = torch.full((wl.batch,), wl.seq_len, dtype=torch.int32, device=DEV)
+    xd = workloads.mla_tokens(wl, wl.batch, 1, DEV)
+    moe.mla_decode(dshape, xd, pos, p, buf["cache_kv"], buf["cache_kr"], dbuf["out"],
+                   workspace=dbuf["workspace"])
+    torch.cuda.synchronize()
+    sample = np.array([0, 97, 255])
+    ref = oracle.mla_decode(bits(xd)[sample], host_params(p), wl.n_heads,
+                            np.full(3, wl.seq_len), kv0[sample], kr0[sample])
+    check_close(f32(bits(dbuf["out"]))[sample], ref["out"], "decode_full.out")
