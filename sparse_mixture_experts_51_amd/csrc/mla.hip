@@ -16,10 +16,13 @@
 //       caches at the token's position), plain bf16 (the prefill's
 //       decompressed keys and values) and bf16 with a residual (the output
 //       projection).
-//   mla_attn_prefill_kernel  one block per (query tile of 64, head,
-//       sequence); keys and values in chunks of 64 through LDS; one wave per
-//       16 query rows, a lane per key for the scores, online softmax in
-//       fp32, lanes split (value dim, key group) for P V.
+//   mla_attn_prefill_mfma_kernel  one block per (128 queries, head,
+//       sequence), keys and values in chunks of 64 through LDS, scores and
+//       P V on 32x32x16 bf16 MFMAs with online softmax in fp32 (head sizes
+//       with d_nope + d_rope a multiple of 16 and d_v 32 or 64);
+//   mla_attn_prefill_kernel  the other head sizes: one block per (query tile
+//       of 64, head, sequence); one wave per 16 query rows, a lane per key
+//       for the scores, lanes split (value dim, key group) for P V.
 //   mla_attn_decode_kernel   one block per sequence; reads only the cache:
 //       each head's query is taken into latent space (q_nope^T W_uk[h]), the
 //       latent rows are scored and attended in chunks of 64 with online
@@ -300,6 +303,143 @@ __global__ __launch_bounds__(kTh) void mla_attn_prefill_kernel(MlaAttnArgs a) {
 }
 
 namespace {
+constexpr int kFQ = 128;  // queries per block of the matrix-core prefill (32 per wave)
+constexpr int kFK = 64;   // keys per staged chunk
+constexpr int kFKRow = 128 + 8;  // staged key row (bf16), padded: 16 rows hit distinct banks
+constexpr int kFVRow = kFK + 8;  // staged V^T row (bf16)
+}  // namespace
+
+// Prefill attention on the matrix cores (d_nope + d_rope a multiple of 16,
+// d_v = 32 DVT): per wave 32 queries; per 32-key slice, S = K Q^T on
+// 32x32x16 MFMAs (a lane then holds 16 scores of one query), online softmax
+// in fp32 across the lane pair that shares the query, and O += V^T P^T where
+// the scores' registers are the P operand as they stand: V^T is read with
+// the keys in the order the score tile holds them (keys 4g..4g+3 and
+// 8+4g..8+4g+3 of each 16 for lane half g).
+template <int DVT>
+__global__ __launch_bounds__(kTh) void mla_attn_prefill_mfma_kernel(MlaAttnArgs a) {
+  __shared__ uint16_t ks[kFK * kFKRow];
+  __shared__ uint16_t vt[32 * DVT * kFVRow];
+  const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
+  const int qb0 = blockIdx.x * kFQ, h = blockIdx.y, b = blockIdx.z;
+  const int S = a.seq, dn = a.dn, qw = a.dn + a.dr, kst = qw / 16, dv = 32 * DVT;
+  const int fr = lane & 31, fhalf = lane >> 5;
+  const int q0 = qb0 + 32 * wave;  // this wave's first query
+  const int64_t qld = static_cast<int64_t>(a.nh) * qw;
+  const int64_t kvld = static_cast<int64_t>(a.nh) * (dn + dv);
+  const int64_t tok0 = static_cast<int64_t>(b) * S;
+  const int my_q = q0 + fr;
+
+  bf16x8 qf[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    u32x4 v = u32x4{0u, 0u, 0u, 0u};
+    if (t < kst && my_q < S)
+      v = *reinterpret_cast<const u32x4*>(a.q + (tok0 + my_q) * qld + h * qw + 16 * t + 8 * fhalf);
+    qf[t] = __builtin_bit_cast(bf16x8, v);
+  }
+  float m_run = -INFINITY, l_run = 0.0f;
+  f32x16 oacc[DVT];
+#pragma unroll
+  for (int t = 0; t < DVT; ++t) oacc[t] = f32x16{};
+
+  const int last = min(qb0 + kFQ, S) - 1;
+  const int kch = dn / 8, qwc = qw / 8, vch = dv / 8;
+  for (int c0 = 0; c0 <= last; c0 += kFK) {
+    __syncthreads();
+    for (int idx = tid; idx < kFK * qwc; idx += kTh) {
+      const int r = idx / qwc, c = idx % qwc, key = c0 + r;
+      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      if (key < S)
+        v = c < kch ? *reinterpret_cast<const u32x4*>(a.kvx + (tok0 + key) * kvld + h * dn + 8 * c)
+                    : *reinterpret_cast<const u32x4*>(a.ckr + (static_cast<int64_t>(b) * a.max_len + key) * a.dr +
+                                                      8 * (c - kch));
+      *reinterpret_cast<u32x4*>(ks + r * kFKRow + 8 * c) = v;
+    }
+    for (int idx = tid; idx < kFK * vch; idx += kTh) {
+      const int r = idx / vch, c = idx % vch, key = c0 + r;
+      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      if (key < S) v = *reinterpret_cast<const u32x4*>(a.kvx + (tok0 + key) * kvld + a.nh * dn + h * dv + 8 * c);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        vt[(8 * c + 2 * w) * kFVRow + r] = static_cast<uint16_t>(v[w]);
+        vt[(8 * c + 2 * w + 1) * kFVRow + r] = static_cast<uint16_t>(v[w] >> 16);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int sub = 0; sub < kFK / 32; ++sub) {
+      const int c = c0 + 32 * sub;
+      if (c > q0 || q0 >= S) continue;  // uniform: keys past the wave's queries, or no queries
+      f32x16 sc = f32x16{};
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        if (t >= kst) break;
+        const bf16x8 kf = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(ks + (32 * sub + fr) * kFKRow + 16 * t + 8 * fhalf));
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[t], sc, 0, 0, 0);
+      }
+      // this lane: query my_q, keys c + 8q + 4 fhalf + e
+      float mx = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = c + 8 * q + 4 * fhalf + e;
+          const float v = key <= my_q ? sc[4 * q + e] * a.scale : -INFINITY;
+          sc[4 * q + e] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run, mx);
+      const float corr = __expf(m_run - m_new);
+      float ps = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = __expf(sc[i] - m_new);
+        sc[i] = p;
+        ps += p;
+      }
+      ps += __shfl_xor(ps, 32, 64);
+      l_run = l_run * corr + ps;
+      m_run = m_new;
+#pragma unroll
+      for (int t = 0; t < DVT; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[t][i] *= corr;
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const u32x4 pw = u32x4{bf16x2_bits(sc[8 * k2], sc[8 * k2 + 1]), bf16x2_bits(sc[8 * k2 + 2], sc[8 * k2 + 3]),
+                               bf16x2_bits(sc[8 * k2 + 4], sc[8 * k2 + 5]), bf16x2_bits(sc[8 * k2 + 6], sc[8 * k2 + 7])};
+        const bf16x8 pf = __builtin_bit_cast(bf16x8, pw);
+        const int kb = 32 * sub + 16 * k2 + 4 * fhalf;
+#pragma unroll
+        for (int t = 0; t < DVT; ++t) {
+          const uint16_t* row = vt + (32 * t + fr) * kFVRow;
+          const uint2 lo = *reinterpret_cast<const uint2*>(row + kb);
+          const uint2 hi = *reinterpret_cast<const uint2*>(row + kb + 8);
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+          oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, oacc[t], 0, 0, 0);
+        }
+      }
+    }
+  }
+  if (my_q < S) {
+    const float inv = 1.0f / l_run;
+    uint16_t* orow = a.o + (tok0 + my_q) * static_cast<int64_t>(a.nh) * dv + h * dv;
+#pragma unroll
+    for (int t = 0; t < DVT; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x16& v = oacc[t];
+        *reinterpret_cast<uint2*>(orow + 32 * t + 8 * q + 4 * fhalf) =
+            make_uint2(bf16x2_bits(v[4 * q] * inv, v[4 * q + 1] * inv),
+                       bf16x2_bits(v[4 * q + 2] * inv, v[4 * q + 3] * inv));
+      }
+  }
+}
+
+namespace {
 constexpr int kMaxLat = 256;   // d_latent
 constexpr int kMaxHeads = 16;
 constexpr int kHpw = kMaxHeads / 4;  // heads per wave at most
@@ -438,8 +578,14 @@ hipError_t launch_mla_gemm(const MlaGemmArgs& a, int epi, hipStream_t s) {
 }
 
 hipError_t launch_mla_attn_prefill(const MlaAttnArgs& a, int batch, hipStream_t s) {
-  const dim3 grid((a.seq + kQT - 1) / kQT, a.nh, batch);
-  hipLaunchKernelGGL(mla_attn_prefill_kernel, grid, dim3(kTh), 0, s, a);
+  if ((a.dn + a.dr) % 16 == 0 && (a.dv == 32 || a.dv == 64)) {
+    const dim3 grid((a.seq + kFQ - 1) / kFQ, a.nh, batch);
+    if (a.dv == 32) hipLaunchKernelGGL(mla_attn_prefill_mfma_kernel<1>, grid, dim3(kTh), 0, s, a);
+    else hipLaunchKernelGGL(mla_attn_prefill_mfma_kernel<2>, grid, dim3(kTh), 0, s, a);
+  } else {
+    const dim3 grid((a.seq + kQT - 1) / kQT, a.nh, batch);
+    hipLaunchKernelGGL(mla_attn_prefill_kernel, grid, dim3(kTh), 0, s, a);
+  }
   return hipGetLastError();
 }
 

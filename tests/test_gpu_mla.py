@@ -6,7 +6,8 @@ an fp32 sum over d (the oracle: fp64), the rotary key turned in fp32 -- at
 most one bf16 step apart, |err| <= 2^-7 |ref| + 1e-6 (one step of the
 larger neighbour).  Outputs: the MoE layer's bar, max|err| <= 2e-2 max|ref|
 and relative L2 <= 1e-2 (bf16 storage of q, the latent, keys, values and
-the heads' outputs; fp32 softmax and sums).  Decode is compared with the
+the heads' outputs; fp32 softmax and sums; the matrix-core prefill also
+rounds the softmax weights to bf16 for P V, relative 2^-9 per weight).  Decode is compared with the
 oracle run on the GPU's own cache (teacher forcing), since the GPU reads only
 the cache: W_uk is applied to the query instead of to every key."""
 import numpy as np
@@ -75,9 +76,12 @@ PREFILL_CASES = {
     "mini_B2_S70": dict(batch=2, seq_len=70, max_len=80, cfg_id=41),
     # one token: attends only to itself
     "mini_B3_S1": dict(batch=3, seq_len=1, max_len=4, cfg_id=42),
-    # other head sizes: 2 heads, d_v 64, latent 64, 16 + 8 key numbers
+    # other head sizes (the vector-unit prefill): 2 heads, d_v 64, latent 64, 16 + 8 key numbers
     "small_heads_dv64": dict(batch=2, seq_len=130, max_len=130, cfg_id=43, d_model=128,
                              n_heads=2, d_latent=64, d_nope=16, d_rope=8, d_v=64),
+    # the matrix-core prefill with d_v 64: 2 heads, 16 + 16 key numbers, two query blocks
+    "mfma_dv64": dict(batch=2, seq_len=150, max_len=160, cfg_id=46, d_model=128, n_heads=2,
+                      d_latent=64, d_nope=16, d_rope=16, d_v=64),
     # many heads, d_v 16, latent 256, 64 + 64 key numbers
     "wide_16heads": dict(batch=1, seq_len=65, max_len=96, cfg_id=44, d_model=256, n_heads=16,
                          d_latent=256, d_nope=64, d_rope=64, d_v=16),
