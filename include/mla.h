@@ -32,10 +32,10 @@
  * arguments checked on the host before anything is enqueued, nothing
  * allocated, calls only enqueue work on `stream`.
  *
- * Supported: d_model, d_latent and n_heads*d_v multiples of 64; d_latent <=
- * 256; d_nope, d_rope multiples of 8 with d_nope + d_rope <= 128; d_v in
+ * Supported: d_model and n_heads*d_v multiples of 64; d_latent in {64, 128,
+ * 256}; d_nope, d_rope multiples of 8 with d_nope + d_rope <= 128; d_v in
  * {8, 16, 32, 64}; 1 <= n_heads <= 16; seq_len <= max_len <= 65536;
- * batch * max_len < 2^31.
+ * batch * max_len < 2^31, batch <= 65535.
  */
 #ifndef MLA_H
 #define MLA_H
@@ -86,7 +86,8 @@ moe_status mla_prefill(const mla_shape* shape, const uint16_t* x, const uint16_t
  * gets a zero out row (plus its residual) and leaves its cache untouched.
  * The attention reads only the cache: W_uk is applied to the query (q_nope^T
  * W_uk[h] against each latent) and W_uv to the attended latent, which equals
- * the explicit decompression up to rounding order. */
+ * the explicit decompression up to rounding order; the cached positions are
+ * scored in chunks of 64 whose partial sums the workspace holds. */
 moe_status mla_decode(const mla_shape* shape, const uint16_t* x, const int32_t* pos,
                       const uint16_t* w_q, const uint16_t* w_dkv, const uint16_t* w_kr,
                       const uint16_t* w_uk, const uint16_t* w_uv, const uint16_t* w_o,

@@ -12,8 +12,8 @@
 // Work decomposition.  A unit is (group, n-tile, m-tile): BM rows of the group
 // against a BW-row weight tile (stage 1: BW/2 rows of W1 and the same rows of
 // W3; stage 2: BW rows of W2).  Units of one group are ordered n-tile major,
-// m-tile minor.  The grid is persistent; block b is remapped so that each XCD
-// (blocks b = x mod 8) walks a contiguous range of units and the A rows of
+// m-tile minor.  The grid is persistent; XCD x (blocks b = x mod 8) works
+// through the x-th eighth of the units in order, so the A rows and weights of
 // one expert stay in that XCD's L2.  Every block rebuilds the unit table from
 // offsets[] (no host round trip).
 //
@@ -205,9 +205,13 @@ __global__ __launch_bounds__(C::kAllThreads, C::BPC) void grouped_gemm_kernel(Gr
     __syncthreads();
   }
   const int total_units = uni(unit_start[ngroups]);
-  const int G = gridDim.x;
-  const int lb = (blockIdx.x % kXcds) * (G / kXcds) + blockIdx.x / kXcds;
-  if (lb >= total_units) return;
+  // XCD x (blocks b with b % 8 == x) takes the x-th eighth of the units in
+  // order: a group's units share its rows and weights in that XCD's L2
+  const int G = gridDim.x / kXcds;
+  const int ux = blockIdx.x % kXcds;
+  const int uend = static_cast<int>(static_cast<int64_t>(total_units) * (ux + 1) / kXcds);
+  const int lb = static_cast<int>(static_cast<int64_t>(total_units) * ux / kXcds) + blockIdx.x / kXcds;
+  if (lb >= uend) return;
   auto decode = [&](int u) __attribute__((always_inline)) {
     return decode_unit<C, kSwiGLU>(a, unit_start, offs, ngroups, u);
   };
@@ -681,7 +685,7 @@ __global__ __launch_bounds__(C::kAllThreads, C::BPC) void grouped_gemm_kernel(Gr
   // loads of step k + 2 (any extra younger memory operation makes the wait
   // stricter, not weaker).
   auto next_of = [&](int u) __attribute__((always_inline)) {
-    return u + G < total_units ? u + G : u;
+    return u + G < uend ? u + G : u;
   };
   auto vm_wait = [&]() __attribute__((always_inline)) {
     if constexpr (C::DMAB) {
@@ -705,7 +709,7 @@ __global__ __launch_bounds__(C::kAllThreads, C::BPC) void grouped_gemm_kernel(Gr
       auto st = [](int x) __attribute__((always_inline)) { return x >= NS ? x - NS : x; };
       Unit cu = decode(lb);
       lds_barrier();  // step 0 has landed
-      for (int u = lb; u < total_units; u += G) {
+      for (int u = lb; u < uend; u += G) {
         const Unit nu = decode(next_of(u));
         const int mrows = valid_tiles(cu.valid_rows);
         zero_acc();
@@ -725,7 +729,7 @@ __global__ __launch_bounds__(C::kAllThreads, C::BPC) void grouped_gemm_kernel(Gr
       // epilogue pass), so these waves issue no global load in the K-loop.
       Unit cu = decode(lb);
       lds_barrier();  // step 0 has landed
-      for (int u = lb; u < total_units; u += G) {
+      for (int u = lb; u < uend; u += G) {
         const Unit nu = decode(next_of(u));
         const int steps = cu.nk + (cu.nk & 1);
         const int mrows = valid_tiles(cu.valid_rows);
@@ -779,7 +783,7 @@ __global__ __launch_bounds__(C::kAllThreads, C::BPC) void grouped_gemm_kernel(Gr
     __builtin_amdgcn_s_waitcnt(0x0F70 | ((kFirst & 15) | ((kFirst >> 4) << 14)));
     lds_barrier();
     settle();  // free here: those loads are older than the A passes
-    for (int u = lb; u < total_units; u += G) {
+    for (int u = lb; u < uend; u += G) {
       const Src nxt = source_of_pending();
       const Unit nu = pend;
       prepare(next_of(next_of(u)));
@@ -828,7 +832,7 @@ __global__ __launch_bounds__(C::kAllThreads, C::BPC) void grouped_gemm_kernel(Gr
   vm_wait();
   lds_barrier();
   settle();  // those loads are older than the first two steps' loads
-  for (int u = lb; u < total_units; u += G) {
+  for (int u = lb; u < uend; u += G) {
     const Src nxt = source_of_pending();
     const Unit nu = pend;
     prepare(next_of(next_of(u)));

@@ -174,6 +174,7 @@ struct MlaAttnArgs {
   const uint16_t* w_uv;
   const int32_t* pos;   // decode positions
   uint16_t* o;          // [tokens, nh dv]
+  float* part;          // decode: per (sequence, head, 64 positions) max, sum, weighted latent
   int seq, max_len, nh, dc, dn, dr, dv;
   float scale;
 };

@@ -23,10 +23,11 @@
 //   mla_attn_prefill_kernel  the other head sizes: one block per (query tile
 //       of 64, head, sequence); one wave per 16 query rows, a lane per key
 //       for the scores, lanes split (value dim, key group) for P V.
-//   mla_attn_decode_kernel   one block per sequence; reads only the cache:
-//       each head's query is taken into latent space (q_nope^T W_uk[h]), the
-//       latent rows are scored and attended in chunks of 64 with online
-//       softmax, and W_uv[h] is applied to the attended latent.  This is the
+//   mla_decode_partial_kernel / mla_decode_combine_kernel   reads only the
+//       cache: one wave per (sequence, head, 64 cached positions) scores
+//       them against the head's query taken into latent space (q_nope^T
+//       W_uk[h]) and sums the weighted latents; the combine merges a head's
+//       chunks (softmax rescaled to the largest maximum) and applies W_uv[h].  This is the
 //       explicit decompression of the pages regrouped (associativity), so it
 //       equals it up to rounding order while reading 144 numbers per cached
 //       token instead of decompressing every key and value.
@@ -440,122 +441,172 @@ __global__ __launch_bounds__(kTh) void mla_attn_prefill_mfma_kernel(MlaAttnArgs 
 }
 
 namespace {
-constexpr int kMaxLat = 256;   // d_latent
-constexpr int kMaxHeads = 16;
-constexpr int kHpw = kMaxHeads / 4;  // heads per wave at most
-constexpr int kCRow = kMaxLat + 64 + 8;  // staged cache row: latent, rotary key, pad
+constexpr int kMaxLat = 256;  // d_latent
 }  // namespace
 
-__global__ __launch_bounds__(kTh) void mla_attn_decode_kernel(MlaAttnArgs a) {
-  __shared__ float qlat[kMaxHeads * kMaxLat];
-  __shared__ float qrope[kMaxHeads * 64];
-  __shared__ uint16_t crow[64 * kCRow];
-  __shared__ float ps[4][64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = uni(tid >> 6);
-  const int b = blockIdx.x;
-  const int nh = a.nh, dc = a.dc, dn = a.dn, dr = a.dr, dv = a.dv, qw = dn + dr;
-  const int64_t orow = static_cast<int64_t>(b) * nh * dv;
-  const int p = a.pos[b];
-  if (p < 0 || p >= a.max_len) {
-    for (int idx = tid; idx < nh * dv; idx += kTh) a.o[orow + idx] = 0;
+// Decode, split over the cache: one wave per (sequence, head, chunk of 64
+// cached positions) scores its chunk against the head's query taken into
+// latent space (W_uk[h]^T q_nope; a lane per cached row, the rows staged in
+// dynamic LDS for the weighted sum), and writes the chunk's max score, sum of weights and weighted latent sum;
+// mla_decode_combine_kernel merges a head's chunks and applies W_uv[h].
+// Block b runs on XCD b % 8; the heads and chunks of a sequence share its XCD
+// (and the cached rows in that L2).
+__global__ __launch_bounds__(64) void mla_decode_partial_kernel(MlaAttnArgs a, int batch, int nchunk) {
+  extern __shared__ uint16_t rows[];  // [64][d_latent + d_rope + 8]
+  __shared__ float qlat[kMaxLat];
+  __shared__ float qr[128];  // the head's query (content, then rotary part)
+  __shared__ float ps[64];
+  const int lane = threadIdx.x;
+  const int nh = a.nh, dc = a.dc, dn = a.dn, dr = a.dr, qw = dn + dr;
+  const int xcd = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
+  const int per_seq = nh * nchunk;
+  const int b = xcd + kXcds * (j / per_seq), rem = j % per_seq;
+  const int ci = rem / nh, h = rem % nh;
+  if (b >= batch) return;
+  float* part = a.part + ((static_cast<int64_t>(b) * nh + h) * nchunk + ci) * (dc + 2);
+  const int p = a.pos[b], c0 = 64 * ci;
+  if (p < 0 || p >= a.max_len || c0 > p) {
+    if (lane == 0) {
+      part[0] = -INFINITY;
+      part[1] = 0.0f;
+    }
     return;
   }
-  // each head's query in latent space, and its rotary part
-  const uint16_t* qb = a.q + static_cast<int64_t>(b) * nh * qw;
-  for (int idx = tid; idx < nh * dc; idx += kTh) {
-    const int h = idx / dc, c = idx % dc;
-    float s = 0.0f;
-    for (int jj = 0; jj < dn; ++jj)
-      s = fmaf(bf16_to_f32(qb[h * qw + jj]), bf16_to_f32(a.w_uk[static_cast<int64_t>(h * dn + jj) * dc + c]), s);
-    qlat[h * kMaxLat + c] = s;
-  }
-  for (int idx = tid; idx < nh * dr; idx += kTh) qrope[(idx / dr) * 64 + idx % dr] = bf16_to_f32(qb[(idx / dr) * qw + dn + idx % dr]);
-
-  const int lc = dc / 64;  // latent numbers per lane in P V
-  float mh[kHpw], lh[kHpw], oacc[kHpw][kMaxLat / 64];
-#pragma unroll
-  for (int k = 0; k < kHpw; ++k) {
-    mh[k] = -INFINITY;
-    lh[k] = 0.0f;
-#pragma unroll
-    for (int i = 0; i < kMaxLat / 64; ++i) oacc[k][i] = 0.0f;
-  }
+  const int rs = dc + dr + 8, dcc = dc / 8, rc = dcc + dr / 8;
+  // the chunk's cached rows into LDS, coalesced: a load instruction covers
+  // 64 / dcc whole latent rows (dcc, a power of two, 16-byte chunks per row)
+  const int s = c0 + lane;
+  const bool ok = s <= p;
   const int64_t cbase = static_cast<int64_t>(b) * a.max_len;
-  const int dcc = dc / 8, drc = dr / 8;
-  for (int c0 = 0; c0 <= p; c0 += 64) {
-    __syncthreads();
-    for (int idx = tid; idx < 64 * (dcc + drc); idx += kTh) {
-      const int r = idx / (dcc + drc), c = idx % (dcc + drc);
-      const int s = c0 + r;
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (s <= p) {
-        if (c < dcc) v = *reinterpret_cast<const u32x4*>(a.ckv + (cbase + s) * dc + 8 * c);
-        else v = *reinterpret_cast<const u32x4*>(a.ckr + (cbase + s) * dr + 8 * (c - dcc));
-      }
-      *reinterpret_cast<u32x4*>(crow + r * kCRow + (c < dcc ? 8 * c : kMaxLat + 8 * (c - dcc))) = v;
-    }
-    __syncthreads();
-    const int s = c0 + lane;
-    const bool ok = s <= p;
-#pragma unroll
-    for (int k = 0; k < kHpw; ++k) {
-      const int h = wave + 4 * k;
-      if (h >= nh) break;
-      float sc = 0.0f;
-      for (int c = 0; c < dcc; ++c) {
-        const u32x4 kv = *reinterpret_cast<const u32x4*>(crow + lane * kCRow + 8 * c);
-        const float* qv = qlat + h * kMaxLat + 8 * c;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          sc = fmaf(qv[2 * w], __uint_as_float(kv[w] << 16), sc);
-          sc = fmaf(qv[2 * w + 1], __uint_as_float(kv[w] & 0xFFFF0000u), sc);
-        }
-      }
-      for (int c = 0; c < drc; ++c) {
-        const u32x4 kv = *reinterpret_cast<const u32x4*>(crow + lane * kCRow + kMaxLat + 8 * c);
-        const float* qv = qrope + h * 64 + 8 * c;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          sc = fmaf(qv[2 * w], __uint_as_float(kv[w] << 16), sc);
-          sc = fmaf(qv[2 * w + 1], __uint_as_float(kv[w] & 0xFFFF0000u), sc);
-        }
-      }
-      sc = ok ? sc * a.scale : -INFINITY;
-      const float mnew = fmaxf(mh[k], wave_max(sc));
-      const float corr = __expf(mh[k] - mnew);
-      const float pr = ok ? __expf(sc - mnew) : 0.0f;
-      lh[k] = lh[k] * corr + wave_sum(pr);
-      mh[k] = mnew;
-      ps[wave][lane] = pr;
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int i = 0; i < kMaxLat / 64; ++i) {
-        if (i >= lc) break;
-        float t = 0.0f;
-        for (int k2 = 0; k2 < 64; ++k2) t = fmaf(ps[wave][k2], bf16_to_f32(crow[k2 * kCRow + lane + 64 * i]), t);
-        oacc[k][i] = oacc[k][i] * corr + t;
-      }
-      __builtin_amdgcn_wave_barrier();
-    }
+  const int lg = __builtin_ctz(dcc);
+  for (int idx = lane; idx < 64 * dcc; idx += 64) {
+    const int r = idx >> lg, c = idx & (dcc - 1);
+    u32x4 v = u32x4{0u, 0u, 0u, 0u};
+    if (c0 + r <= p) v = *reinterpret_cast<const u32x4*>(a.ckv + (cbase + c0 + r) * dc + 8 * c);
+    *reinterpret_cast<u32x4*>(rows + r * rs + 8 * c) = v;
   }
-  // the attended latent of each head, then W_uv[h]
+  for (int idx = lane; idx < 64 * (rc - dcc); idx += 64) {
+    const int r = idx / (rc - dcc), c = idx % (rc - dcc);
+    u32x4 v = u32x4{0u, 0u, 0u, 0u};
+    if (c0 + r <= p) v = *reinterpret_cast<const u32x4*>(a.ckr + (cbase + c0 + r) * dr + 8 * c);
+    *reinterpret_cast<u32x4*>(rows + r * rs + dc + 8 * c) = v;
+  }
+  // the head's query, then W_uk[h]^T q_nope: lane (row group g, 8-column
+  // chunk c8) sums rows g, g + groups, ... with 16-byte loads; the groups are
+  // added across lanes
+  const uint16_t* qb = a.q + (static_cast<int64_t>(b) * nh + h) * qw;
+  for (int jj = lane; jj < qw; jj += 64) qr[jj] = bf16_to_f32(qb[jj]);
   __syncthreads();
-  float* olat = qlat;  // reused
+  {
+    const int nc8 = dc / 8, groups = 64 / nc8, g = lane / nc8, c8 = lane % nc8;
+    float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    const uint16_t* wk = a.w_uk + static_cast<int64_t>(h) * dn * dc + 8 * c8;
+#pragma unroll 4
+    for (int jj = g; jj < dn; jj += groups) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(wk + static_cast<int64_t>(jj) * dc);
+      const float qj = qr[jj];
 #pragma unroll
-  for (int k = 0; k < kHpw; ++k) {
-    const int h = wave + 4 * k;
-    if (h >= nh) break;
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] = fmaf(qj, __uint_as_float(w[e] << 16), acc[2 * e]);
+        acc[2 * e + 1] = fmaf(qj, __uint_as_float(w[e] & 0xFFFF0000u), acc[2 * e + 1]);
+      }
+    }
 #pragma unroll
-    for (int i = 0; i < kMaxLat / 64; ++i)
-      if (i < lc) olat[h * kMaxLat + lane + 64 * i] = oacc[k][i] / lh[k];
+    for (int e = 0; e < 8; ++e)
+      for (int o = nc8; o < 64; o <<= 1) acc[e] += __shfl_xor(acc[e], o, 64);
+    if (g == 0)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qlat[8 * c8 + e] = acc[e];
   }
   __syncthreads();
-  for (int idx = tid; idx < nh * dv; idx += kTh) {
-    const int h = idx / dv;
-    const uint16_t* wr = a.w_uv + static_cast<int64_t>(idx) * dc;
+  float sc = 0.0f;
+#pragma unroll 2
+  for (int c = 0; c < rc; ++c) {
+    const u32x4 kv = *reinterpret_cast<const u32x4*>(rows + lane * rs + 8 * c);
+    const float* q8 = c < dcc ? qlat + 8 * c : qr + dn + 8 * (c - dcc);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      sc = fmaf(q8[2 * w], __uint_as_float(kv[w] << 16), sc);
+      sc = fmaf(q8[2 * w + 1], __uint_as_float(kv[w] & 0xFFFF0000u), sc);
+    }
+  }
+  sc = ok ? sc * a.scale : -INFINITY;
+  const float m = wave_max(sc);
+  const float pr = ok ? __expf(sc - m) : 0.0f;
+  const float l = wave_sum(pr);
+  ps[lane] = pr;
+  __syncthreads();
+  // weighted latent sum: lane (8-column chunk c8, key group kg) reads 16 bytes
+  // of every kg-th row; the key groups are added across lanes
+  {
+    const int nc8 = dc / 8, kgroups = 64 / nc8, kg = lane / nc8, c8 = lane % nc8;
+    float t[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 4
+    for (int k2 = kg; k2 < 64; k2 += kgroups) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(rows + k2 * rs + 8 * c8);
+      const float pk = ps[k2];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        t[2 * e] = fmaf(pk, __uint_as_float(v[e] << 16), t[2 * e]);
+        t[2 * e + 1] = fmaf(pk, __uint_as_float(v[e] & 0xFFFF0000u), t[2 * e + 1]);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      for (int o = nc8; o < 64; o <<= 1) t[e] += __shfl_xor(t[e], o, 64);
+    if (kg == 0)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part[2 + 8 * c8 + e] = t[e];
+  }
+  if (lane == 0) {
+    part[0] = m;
+    part[1] = l;
+  }
+}
+
+// Merges a head's chunks (rescaled to the largest chunk maximum) and applies
+// W_uv[h] to the attended latent: one wave per (sequence, head).
+__global__ __launch_bounds__(64) void mla_decode_combine_kernel(MlaAttnArgs a, int batch, int nchunk) {
+  __shared__ float olat[kMaxLat];
+  const int lane = threadIdx.x;
+  const int nh = a.nh, dc = a.dc, dv = a.dv;
+  const int b = blockIdx.x / nh, h = blockIdx.x % nh;
+  if (b >= batch) return;
+  const int64_t orow = (static_cast<int64_t>(b) * nh + h) * dv;
+  const int p = a.pos[b];
+  if (p < 0 || p >= a.max_len) {
+    for (int jj = lane; jj < dv; jj += 64) a.o[orow + jj] = 0;
+    return;
+  }
+  const int nc = p / 64 + 1;  // chunks with cached positions
+  const float* part = a.part + (static_cast<int64_t>(b) * nh + h) * nchunk * (dc + 2);
+  float M = -INFINITY;
+  for (int ci = 0; ci < nc; ++ci) M = fmaxf(M, part[ci * (dc + 2)]);
+  float L = 0.0f;
+  for (int ci = 0; ci < nc; ++ci) L += __expf(part[ci * (dc + 2)] - M) * part[ci * (dc + 2) + 1];
+  for (int c = lane; c < dc; c += 64) {
+    float t = 0.0f;
+    for (int ci = 0; ci < nc; ++ci) t += __expf(part[ci * (dc + 2)] - M) * part[ci * (dc + 2) + 2 + c];
+    olat[c] = t / L;
+  }
+  __syncthreads();
+  // W_uv[h] olat: lane (8-column chunk c8, row group g) takes rows g,
+  // g + groups, ... with 16-byte loads; the chunks are added across lanes
+  const int nc8 = dc / 8, groups = 64 / nc8, g = lane / nc8, c8 = lane % nc8;
+  const uint16_t* wv = a.w_uv + static_cast<int64_t>(h) * dv * dc + 8 * c8;
+  for (int j0 = 0; j0 < dv; j0 += groups) {
+    const int jj = j0 + g;
     float s = 0.0f;
-    for (int c = 0; c < dc; ++c) s = fmaf(bf16_to_f32(wr[c]), olat[h * kMaxLat + c], s);
-    a.o[orow + idx] = f32_to_bf16(s);
+    if (jj < dv) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(wv + static_cast<int64_t>(jj) * dc);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s = fmaf(__uint_as_float(w[e] << 16), olat[8 * c8 + 2 * e], s);
+        s = fmaf(__uint_as_float(w[e] & 0xFFFF0000u), olat[8 * c8 + 2 * e + 1], s);
+      }
+    }
+    for (int o = 1; o < nc8; o <<= 1) s += __shfl_xor(s, o, 64);
+    if (c8 == 0 && jj < dv) a.o[orow + jj] = f32_to_bf16(s);
   }
 }
 
@@ -590,7 +641,14 @@ hipError_t launch_mla_attn_prefill(const MlaAttnArgs& a, int batch, hipStream_t 
 }
 
 hipError_t launch_mla_attn_decode(const MlaAttnArgs& a, int batch, hipStream_t s) {
-  hipLaunchKernelGGL(mla_attn_decode_kernel, dim3(batch), dim3(kTh), 0, s, a);
+  const int nchunk = (a.max_len + 63) / 64;
+  const int per_seq = a.nh * nchunk;
+  const int blocks = kXcds * ((batch + kXcds - 1) / kXcds) * per_seq;
+  const size_t lds = sizeof(uint16_t) * 64 * static_cast<size_t>(a.dc + a.dr + 8);
+  hipLaunchKernelGGL(mla_decode_partial_kernel, dim3(blocks), dim3(64), lds, s, a, batch, nchunk);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(mla_decode_combine_kernel, dim3(batch * a.nh), dim3(64), 0, s, a, batch, nchunk);
   return hipGetLastError();
 }
 

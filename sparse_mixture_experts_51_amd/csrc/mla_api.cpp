@@ -21,7 +21,8 @@ moe_status check_shape(const mla_shape* s) {
   if (!(s->rope_base > 1.0f) || !std::isfinite(s->rope_base)) return MOE_ERR_INVALID_ARGUMENT;
   if (s->seq_len > s->max_len) return MOE_ERR_INVALID_ARGUMENT;
   if (s->d_model % 64 || s->d_latent % 64 || (s->n_heads * s->d_v) % 64) return MOE_ERR_UNSUPPORTED;
-  if (s->d_latent > 256 || s->n_heads > 16 || s->max_len > 65536) return MOE_ERR_UNSUPPORTED;
+  if (s->d_latent != 64 && s->d_latent != 128 && s->d_latent != 256) return MOE_ERR_UNSUPPORTED;
+  if (s->n_heads > 16 || s->max_len > 65536) return MOE_ERR_UNSUPPORTED;
   if (s->d_nope % 8 || s->d_rope % 8 || s->d_nope + s->d_rope > 128 || s->d_rope > 64)
     return MOE_ERR_UNSUPPORTED;
   if (s->d_v != 8 && s->d_v != 16 && s->d_v != 32 && s->d_v != 64) return MOE_ERR_UNSUPPORTED;
@@ -34,6 +35,7 @@ struct MlaWorkspace {
   uint16_t* q;    // [tokens, H (d_nope + d_rope)]
   uint16_t* kvx;  // prefill: [tokens, H d_nope | H d_v]
   uint16_t* o;    // [tokens, H d_v]
+  float* part;    // decode: [batch, H, max_len / 64, d_latent + 2] chunk partials
   size_t total;
 };
 MlaWorkspace carve(const mla_shape* s, int decode, void* base) {
@@ -49,6 +51,8 @@ MlaWorkspace carve(const mla_shape* s, int decode, void* base) {
   w.q = take(2 * T * H * (s->d_nope + s->d_rope));
   w.kvx = take(decode ? 0 : 2 * T * H * (s->d_nope + s->d_v));
   w.o = take(2 * T * H * s->d_v);
+  w.part = reinterpret_cast<float*>(
+      take(decode ? 4 * T * H * ((s->max_len + 63) / 64) * static_cast<int64_t>(s->d_latent + 2) : 0));
   w.total = off;
   return w;
 }
@@ -207,6 +211,7 @@ moe_status mla_decode(const mla_shape* shape, const uint16_t* x, const int32_t* 
     a.w_uk = w_uk;
     a.w_uv = w_uv;
     a.pos = pos;
+    a.part = w.part;
     e = moe::launch_mla_attn_decode(a, shape->batch, s);
   }
   if (e == hipSuccess)

@@ -321,7 +321,8 @@ def test_mla_workspace_and_shape_checks(L):
     for kw in bad:
         assert L.mla_workspace_bytes(ctypes.byref(mla_shape(**kw)), 0, ctypes.byref(n)) == \
             moe.MOE_ERR_INVALID_ARGUMENT, kw
-    unsupported = [dict(d_model=100), dict(d_latent=96), dict(d_latent=320), dict(d_v=24),
+    unsupported = [dict(d_model=100), dict(d_latent=96), dict(d_latent=192), dict(d_latent=320),
+                   dict(d_v=24),
                    dict(d_nope=100, d_rope=40), dict(n_heads=17, d_v=64), dict(d_rope=12)]
     for kw in unsupported:
         assert L.mla_workspace_bytes(ctypes.byref(mla_shape(**kw)), 0, ctypes.byref(n)) == \
