@@ -419,6 +419,30 @@ def run_mla(args, name):
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
+    launch = "eager"
+    if wl.decode:
+        # a decode step is five small launches: replay them as one captured
+        # HIP graph, as a serving loop would (the graph's replays match the
+        # eager call bit for bit, tests/test_gpu_mla.py)
+        stream = torch.cuda.Stream()
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            call()
+        torch.cuda.current_stream().wait_stream(stream)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            call()
+        eager_call = call
+
+        def call():  # noqa: F811
+            graph.replay()  # on the current stream, where the events go
+        for _ in range(args.warmup):
+            call()
+        torch.cuda.synchronize()
+        launch = "hip graph replay of one mla_decode call"
+        del eager_call
+        stream = torch.cuda.current_stream()
     ev = []
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
@@ -445,7 +469,7 @@ def run_mla(args, name):
         "config": {"workload": name, "batch": wl.batch, "seq_len": wl.seq_len,
                    "max_len": wl.max_len, "d_model": wl.d_model, "n_heads": wl.n_heads,
                    "d_latent": wl.d_latent, "d_nope": wl.d_nope, "d_rope": wl.d_rope,
-                   "d_v": wl.d_v, "decode": wl.decode},
+                   "d_v": wl.d_v, "decode": wl.decode, "launch": launch},
         "roofline": {"bound": "hbm" if wl.decode else "mfma",
                      "achieved": gbs if wl.decode else tflops,
                      "peak": PEAK_HBM_GBS if wl.decode else PEAK_BF16_TFLOPS,

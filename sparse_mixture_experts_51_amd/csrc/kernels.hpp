@@ -175,6 +175,7 @@ struct MlaAttnArgs {
   const int32_t* pos;   // decode positions
   uint16_t* o;          // [tokens, nh dv]
   float* part;          // decode: per (sequence, head, 64 positions) max, sum, weighted latent
+  uint16_t* qlat;       // decode: [batch, nh, dc] the heads' queries in latent space (bf16)
   int seq, max_len, nh, dc, dn, dr, dv;
   float scale;
 };

@@ -564,10 +564,175 @@ __global__ __launch_bounds__(64) void mla_decode_partial_kernel(MlaAttnArgs a, i
   }
 }
 
+// The heads' queries in latent space, once per decode step: one wave per
+// (sequence, head) writes bf16(W_uk[h]^T q_nope) to qlat [batch, nh, dc]
+// (lane: row group g, 8-column chunk c8 with 16-byte loads; groups added
+// across lanes).
+__global__ __launch_bounds__(64) void mla_decode_qlat_kernel(MlaAttnArgs a, int batch) {
+  __shared__ float qn[128];
+  const int lane = threadIdx.x;
+  const int nh = a.nh, dc = a.dc, dn = a.dn, qw = dn + a.dr;
+  const int b = blockIdx.x / nh, h = blockIdx.x % nh;
+  if (b >= batch) return;
+  const uint16_t* qb = a.q + (static_cast<int64_t>(b) * nh + h) * qw;
+  for (int jj = lane; jj < dn; jj += 64) qn[jj] = bf16_to_f32(qb[jj]);
+  __syncthreads();
+  const int nc8 = dc / 8, groups = 64 / nc8, g = lane / nc8, c8 = lane % nc8;
+  float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+  const uint16_t* wk = a.w_uk + static_cast<int64_t>(h) * dn * dc + 8 * c8;
+#pragma unroll 4
+  for (int jj = g; jj < dn; jj += groups) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(wk + static_cast<int64_t>(jj) * dc);
+    const float qj = qn[jj];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] = fmaf(qj, __uint_as_float(w[e] << 16), acc[2 * e]);
+      acc[2 * e + 1] = fmaf(qj, __uint_as_float(w[e] & 0xFFFF0000u), acc[2 * e + 1]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    for (int o = nc8; o < 64; o <<= 1) acc[e] += __shfl_xor(acc[e], o, 64);
+  if (g == 0)
+    *reinterpret_cast<u32x4*>(a.qlat + (static_cast<int64_t>(b) * nh + h) * dc + 8 * c8) =
+        u32x4{bf16x2_bits(acc[0], acc[1]), bf16x2_bits(acc[2], acc[3]), bf16x2_bits(acc[4], acc[5]),
+              bf16x2_bits(acc[6], acc[7])};
+}
+
+// Decode on the matrix cores: one wave per (sequence, chunk of 64 cached
+// positions) takes all heads at once (the 32 rows of the MFMA tile, heads
+// past nh zero).  Scores S = K Q^T over the latent and rotary key (K rows
+// read straight from the cache; positions past the token zeroed, so stale
+// cache contents never reach P V), softmax statistics per head over the
+// chunk, and O^T = V^T P^T with V^T the chunk's latents staged transposed in
+// LDS and P taken from the score registers as they stand (keys 4g..4g+3 and
+// 8+4g..8+4g+3 of each 16 for lane half g).  Writes the chunk's per-head max,
+// sum of weights and weighted latent sum, as mla_decode_partial_kernel does.
+template <int DC, int DR>
+__global__ __launch_bounds__(64) void mla_decode_mfma_kernel(MlaAttnArgs a, int batch, int nchunk) {
+  constexpr int KST = (DC + DR + 15) / 16;  // k-steps of the scores
+  constexpr int LST = DC / 16;              // of them, on the latent
+  constexpr int NCT = DC / 32;              // latent tiles of P V
+  constexpr int VROW = 64 + 8;              // staged V^T row (bf16)
+  __shared__ uint16_t vt[DC * VROW];
+  const int lane = threadIdx.x, fr = lane & 31, fhalf = lane >> 5;
+  const int nh = a.nh, qw = a.dn + DR;
+  const int xcd = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
+  const int b = xcd + kXcds * (j / nchunk), ci = j % nchunk;
+  if (b >= batch) return;
+  const int p = a.pos[b], c0 = 64 * ci;
+  if (p < 0 || p >= a.max_len || c0 > p) return;  // the combine reads only chunks with positions
+  // the heads' fragments: head fr, k = 16 t + 8 fhalf .. +7 (latent, then rotary part)
+  bf16x8 qf[KST];
+  const bool hv = fr < nh;
+  const int64_t hrow = static_cast<int64_t>(b) * nh + (hv ? fr : 0);
+#pragma unroll
+  for (int t = 0; t < KST; ++t) {
+    const int k = 16 * t + 8 * fhalf;
+    u32x4 v = u32x4{0u, 0u, 0u, 0u};
+    if (hv) {
+      if (k < DC) v = *reinterpret_cast<const u32x4*>(a.qlat + hrow * DC + k);
+      else if (k < DC + DR) v = *reinterpret_cast<const u32x4*>(a.q + hrow * qw + a.dn + (k - DC));
+    }
+    qf[t] = __builtin_bit_cast(bf16x8, v);
+  }
+  const int64_t cbase = static_cast<int64_t>(b) * a.max_len;
+  f32x16 sc[2];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int s = c0 + 32 * half + fr;  // this lane's key row
+    const bool kv = s <= p;
+    sc[half] = f32x16{};
+#pragma unroll
+    for (int t = 0; t < KST; ++t) {
+      const int k = 16 * t + 8 * fhalf;
+      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      if (kv) {
+        if (k < DC) v = *reinterpret_cast<const u32x4*>(a.ckv + (cbase + s) * DC + k);
+        else if (k < DC + DR) v = *reinterpret_cast<const u32x4*>(a.ckr + (cbase + s) * DR + (k - DC));
+      }
+      if (t < LST) {
+        // V^T: latent column k + i, key 32 half + fr
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          vt[(k + 2 * w) * VROW + 32 * half + fr] = static_cast<uint16_t>(v[w]);
+          vt[(k + 2 * w + 1) * VROW + 32 * half + fr] = static_cast<uint16_t>(v[w] >> 16);
+        }
+      }
+      sc[half] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v), qf[t], sc[half], 0, 0, 0);
+    }
+  }
+  // softmax statistics of head fr over the chunk (lanes fr and fr + 32 share it)
+  float mx = -INFINITY;
+#pragma unroll
+  for (int half = 0; half < 2; ++half)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = c0 + 32 * half + 8 * (i >> 2) + 4 * fhalf + (i & 3);
+      const float v = key <= p ? sc[half][i] * a.scale : -INFINITY;
+      sc[half][i] = v;
+      mx = fmaxf(mx, v);
+    }
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  float ls = 0.0f;
+#pragma unroll
+  for (int half = 0; half < 2; ++half)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float e = __expf(sc[half][i] - mx);
+      sc[half][i] = e;
+      ls += e;
+    }
+  ls += __shfl_xor(ls, 32, 64);
+  __syncthreads();  // V^T staged
+  f32x16 oacc[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) oacc[ct] = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const f32x16& pv = sc[ks >> 1];
+    const int q0 = 2 * (ks & 1);
+    const bf16x8 pf = __builtin_bit_cast(
+        bf16x8, u32x4{bf16x2_bits(pv[4 * q0], pv[4 * q0 + 1]), bf16x2_bits(pv[4 * q0 + 2], pv[4 * q0 + 3]),
+                      bf16x2_bits(pv[4 * q0 + 4], pv[4 * q0 + 5]), bf16x2_bits(pv[4 * q0 + 6], pv[4 * q0 + 7])});
+    const int kb = 16 * ks + 4 * fhalf;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const uint16_t* row = vt + (32 * ct + fr) * VROW;
+      const uint2 lo = *reinterpret_cast<const uint2*>(row + kb);
+      const uint2 hi = *reinterpret_cast<const uint2*>(row + kb + 8);
+      oacc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y}), pf, oacc[ct], 0, 0, 0);
+    }
+  }
+  // this lane: head fr, latent columns 32 ct + 8 q + 4 fhalf + e
+  if (hv) {
+    float* part = a.part + ((static_cast<int64_t>(b) * nh + fr) * nchunk + ci) * (DC + 2);
+    if (fhalf == 0) {
+      part[0] = mx;
+      part[1] = ls;
+    }
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x16& o = oacc[ct];
+        float* dst = part + 2 + 32 * ct + 8 * q + 4 * fhalf;
+        dst[0] = o[4 * q];
+        dst[1] = o[4 * q + 1];
+        dst[2] = o[4 * q + 2];
+        dst[3] = o[4 * q + 3];
+      }
+  }
+}
+
 // Merges a head's chunks (rescaled to the largest chunk maximum) and applies
-// W_uv[h] to the attended latent: one wave per (sequence, head).
+// W_uv[h] to the attended latent: one wave per (sequence, head).  Loads are
+// issued in batches (chunk statistics, then the chunks' latent sums, then
+// eight W_uv row pieces at a time) so that each phase costs one memory trip.
 __global__ __launch_bounds__(64) void mla_decode_combine_kernel(MlaAttnArgs a, int batch, int nchunk) {
   __shared__ float olat[kMaxLat];
+  __shared__ float wts[64];
   const int lane = threadIdx.x;
   const int nh = a.nh, dc = a.dc, dv = a.dv;
   const int b = blockIdx.x / nh, h = blockIdx.x % nh;
@@ -580,33 +745,57 @@ __global__ __launch_bounds__(64) void mla_decode_combine_kernel(MlaAttnArgs a, i
   }
   const int nc = p / 64 + 1;  // chunks with cached positions
   const float* part = a.part + (static_cast<int64_t>(b) * nh + h) * nchunk * (dc + 2);
+  // chunk statistics: chunk i in lane i (and i + 64, ...)
   float M = -INFINITY;
-  for (int ci = 0; ci < nc; ++ci) M = fmaxf(M, part[ci * (dc + 2)]);
+  for (int i = lane; i < nc; i += 64) M = fmaxf(M, part[static_cast<int64_t>(i) * (dc + 2)]);
+  M = wave_max(M);
   float L = 0.0f;
-  for (int ci = 0; ci < nc; ++ci) L += __expf(part[ci * (dc + 2)] - M) * part[ci * (dc + 2) + 1];
-  for (int c = lane; c < dc; c += 64) {
-    float t = 0.0f;
-    for (int ci = 0; ci < nc; ++ci) t += __expf(part[ci * (dc + 2)] - M) * part[ci * (dc + 2) + 2 + c];
-    olat[c] = t / L;
+  for (int i0 = 0; i0 < nc; i0 += 64) {
+    const int i = i0 + lane;
+    float w = 0.0f;
+    if (i < nc) {
+      w = __expf(part[static_cast<int64_t>(i) * (dc + 2)] - M);
+      L += w * part[static_cast<int64_t>(i) * (dc + 2) + 1];
+    }
+    __syncthreads();
+    wts[lane] = w;
+    __syncthreads();
+    for (int c = lane; c < dc; c += 64) {
+      float t = i0 > 0 ? olat[c] : 0.0f;
+#pragma unroll 4
+      for (int k = 0; k < min(64, nc - i0); ++k)
+        t = fmaf(wts[k], part[static_cast<int64_t>(i0 + k) * (dc + 2) + 2 + c], t);
+      olat[c] = t;
+    }
   }
+  L = wave_sum(L);
   __syncthreads();
-  // W_uv[h] olat: lane (8-column chunk c8, row group g) takes rows g,
-  // g + groups, ... with 16-byte loads; the chunks are added across lanes
+  // W_uv[h] olat / L: lane (8-column chunk c8, row group g), rows g, g +
+  // groups, ...; eight rows' 16-byte pieces loaded before they are used
   const int nc8 = dc / 8, groups = 64 / nc8, g = lane / nc8, c8 = lane % nc8;
   const uint16_t* wv = a.w_uv + static_cast<int64_t>(h) * dv * dc + 8 * c8;
-  for (int j0 = 0; j0 < dv; j0 += groups) {
-    const int jj = j0 + g;
-    float s = 0.0f;
-    if (jj < dv) {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(wv + static_cast<int64_t>(jj) * dc);
+  float ol[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ol[e] = olat[8 * c8 + e] / L;
+  for (int j0 = 0; j0 < dv; j0 += 8 * groups) {
+    u32x4 w[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int jj = j0 + groups * r + g;
+      w[r] = jj < dv ? *reinterpret_cast<const u32x4*>(wv + static_cast<int64_t>(jj) * dc) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int jj = j0 + groups * r + g;
+      float s = 0.0f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        s = fmaf(__uint_as_float(w[e] << 16), olat[8 * c8 + 2 * e], s);
-        s = fmaf(__uint_as_float(w[e] & 0xFFFF0000u), olat[8 * c8 + 2 * e + 1], s);
+        s = fmaf(__uint_as_float(w[r][e] << 16), ol[2 * e], s);
+        s = fmaf(__uint_as_float(w[r][e] & 0xFFFF0000u), ol[2 * e + 1], s);
       }
+      for (int o = 1; o < nc8; o <<= 1) s += __shfl_xor(s, o, 64);
+      if (c8 == 0 && jj < dv) a.o[orow + jj] = f32_to_bf16(s);
     }
-    for (int o = 1; o < nc8; o <<= 1) s += __shfl_xor(s, o, 64);
-    if (c8 == 0 && jj < dv) a.o[orow + jj] = f32_to_bf16(s);
   }
 }
 
@@ -642,10 +831,22 @@ hipError_t launch_mla_attn_prefill(const MlaAttnArgs& a, int batch, hipStream_t 
 
 hipError_t launch_mla_attn_decode(const MlaAttnArgs& a, int batch, hipStream_t s) {
   const int nchunk = (a.max_len + 63) / 64;
-  const int per_seq = a.nh * nchunk;
-  const int blocks = kXcds * ((batch + kXcds - 1) / kXcds) * per_seq;
-  const size_t lds = sizeof(uint16_t) * 64 * static_cast<size_t>(a.dc + a.dr + 8);
-  hipLaunchKernelGGL(mla_decode_partial_kernel, dim3(blocks), dim3(64), lds, s, a, batch, nchunk);
+  const bool mfma = a.dr == 16 && (a.dc == 128 || a.dc == 64);
+  if (mfma) {
+    hipLaunchKernelGGL(mla_decode_qlat_kernel, dim3(batch * a.nh), dim3(64), 0, s, a, batch);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int blocks = kXcds * ((batch + kXcds - 1) / kXcds) * nchunk;
+    if (a.dc == 128)
+      hipLaunchKernelGGL((mla_decode_mfma_kernel<128, 16>), dim3(blocks), dim3(64), 0, s, a, batch, nchunk);
+    else
+      hipLaunchKernelGGL((mla_decode_mfma_kernel<64, 16>), dim3(blocks), dim3(64), 0, s, a, batch, nchunk);
+  } else {
+    const int per_seq = a.nh * nchunk;
+    const int blocks = kXcds * ((batch + kXcds - 1) / kXcds) * per_seq;
+    const size_t lds = sizeof(uint16_t) * 64 * static_cast<size_t>(a.dc + a.dr + 8);
+    hipLaunchKernelGGL(mla_decode_partial_kernel, dim3(blocks), dim3(64), lds, s, a, batch, nchunk);
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(mla_decode_combine_kernel, dim3(batch * a.nh), dim3(64), 0, s, a, batch, nchunk);

@@ -36,6 +36,7 @@ struct MlaWorkspace {
   uint16_t* kvx;  // prefill: [tokens, H d_nope | H d_v]
   uint16_t* o;    // [tokens, H d_v]
   float* part;    // decode: [batch, H, max_len / 64, d_latent + 2] chunk partials
+  uint16_t* qlat; // decode: [batch, H, d_latent] the queries in latent space
   size_t total;
 };
 MlaWorkspace carve(const mla_shape* s, int decode, void* base) {
@@ -53,6 +54,7 @@ MlaWorkspace carve(const mla_shape* s, int decode, void* base) {
   w.o = take(2 * T * H * s->d_v);
   w.part = reinterpret_cast<float*>(
       take(decode ? 4 * T * H * ((s->max_len + 63) / 64) * static_cast<int64_t>(s->d_latent + 2) : 0));
+  w.qlat = take(decode ? 2 * T * H * s->d_latent : 0);
   w.total = off;
   return w;
 }
@@ -212,6 +214,7 @@ moe_status mla_decode(const mla_shape* shape, const uint16_t* x, const int32_t* 
     a.w_uv = w_uv;
     a.pos = pos;
     a.part = w.part;
+    a.qlat = w.qlat;
     e = moe::launch_mla_attn_decode(a, shape->batch, s);
   }
   if (e == hipSuccess)

@@ -106,10 +106,27 @@ def test_prefill_matches_oracle(name):
     check_close(f32(bits(buf["out"])), ref["out"], f"{name}.out")
 
 
-def test_decode_matches_oracle_on_the_gpu_cache():
+DECODE_CASES = {
+    # mini dims: the matrix-core decode (latent 128, rotary 16)
+    "mini": dict(batch=5, seq_len=70, max_len=80, cfg_id=45),
+    # the matrix-core decode with latent 64, 2 heads of d_v 64
+    "dc64_dv64": dict(batch=5, seq_len=70, max_len=130, cfg_id=47, d_model=128, n_heads=2,
+                      d_latent=64, d_nope=16, d_rope=16, d_v=64),
+    # the vector-unit decode (rotary 8), and (latent 256, rotary 64, 16 heads)
+    "dc64_dr8": dict(batch=5, seq_len=70, max_len=80, cfg_id=48, d_model=128, n_heads=2,
+                     d_latent=64, d_nope=16, d_rope=8, d_v=64),
+    "wide_16heads": dict(batch=5, seq_len=70, max_len=72, cfg_id=49, d_model=256, n_heads=16,
+                         d_latent=256, d_nope=64, d_rope=64, d_v=16),
+}
+
+
+@pytest.mark.parametrize("name", list(DECODE_CASES))
+def test_decode_matches_oracle_on_the_gpu_cache(name):
     """Prefill 70 tokens of 5 sequences on the GPU, then one decode step at
     ragged positions (0, 63, 64, 70, and -1 which is skipped)."""
-    wl = workloads.mla_custom(name="decode", batch=5, seq_len=70, max_len=80, cfg_id=45)
+    wl = workloads.mla_custom(name="decode_" + name, **DECODE_CASES[name])
+    say(f"[mla decode] {name} d={wl.d_model} H={wl.n_heads} dc={wl.d_latent} dn={wl.d_nope} "
+        f"dr={wl.d_rope} dv={wl.d_v}")
     p = workloads.mla_params(wl, 0, DEV)
     x = workloads.mla_tokens(wl, wl.tokens, 0, DEV)
     shape, buf = gpu_prefill(wl, x, p)
@@ -129,13 +146,13 @@ def test_decode_matches_oracle_on_the_gpu_cache():
     ref = oracle.mla_decode(bits(xd)[valid], hp, wl.n_heads, pos.cpu().numpy()[valid],
                             kv0[valid], kr0[valid], residual=bits(res)[valid])
     out = f32(bits(dbuf["out"])).astype(np.float64)
-    check_close(out[valid], ref["out"], "decode.out")
+    check_close(out[valid], ref["out"], f"decode_{name}.out")
     kv1 = f32(bits(buf["cache_kv"])).astype(np.float64)
     kr1 = f32(bits(buf["cache_kr"])).astype(np.float64)
     for i, b in enumerate(valid):
         q = int(pos[b])
-        check_cache(kv1[b, q], ref["cache_kv"][i, q], f"decode.cache_kv[{b}]")
-        check_cache(kr1[b, q], ref["cache_kr"][i, q], f"decode.cache_kr[{b}]")
+        check_cache(kv1[b, q], ref["cache_kv"][i, q], f"decode_{name}.cache_kv[{b}]")
+        check_cache(kr1[b, q], ref["cache_kr"][i, q], f"decode_{name}.cache_kr[{b}]")
         # the rest of the cache is untouched
         mask = np.ones(wl.max_len, bool)
         mask[q] = False
@@ -143,6 +160,30 @@ def test_decode_matches_oracle_on_the_gpu_cache():
     # the skipped sequence: output = residual, cache untouched
     assert np.array_equal(bits(dbuf["out"])[4], bits(res)[4])
     assert np.array_equal(kv1[4], kv0[4]) and np.array_equal(kr1[4], kr0[4])
+
+
+def test_decode_ignores_stale_cache_entries():
+    """Positions past a sequence's token may hold anything (here NaN): the
+    decode reads positions 0..pos only."""
+    wl = workloads.mla_custom(name="stale", batch=3, seq_len=40, max_len=128, cfg_id=50)
+    p = workloads.mla_params(wl, 0, DEV)
+    x = workloads.mla_tokens(wl, wl.tokens, 0, DEV)
+    _, buf = gpu_prefill(wl, x, p)
+    clean_kv = buf["cache_kv"].clone()
+    clean_kr = buf["cache_kr"].clone()
+    buf["cache_kv"][:, 41:] = float("nan")
+    buf["cache_kr"][:, 41:] = float("nan")
+    dshape = moe.MlaShape(wl.batch, 0, wl.max_len, wl.d_model, wl.n_heads, wl.d_latent,
+                          wl.d_nope, wl.d_rope, wl.d_v)
+    pos = torch.tensor([40, 3, 0], dtype=torch.int32, device=DEV)
+    xd = workloads.mla_tokens(wl, wl.batch, 1, DEV)
+    outs = []
+    for kv, kr in ((buf["cache_kv"], buf["cache_kr"]), (clean_kv, clean_kr)):
+        dbuf = moe.alloc_mla(dshape, DEV, decode=True)
+        moe.mla_decode(dshape, xd, pos, p, kv, kr, dbuf["out"], workspace=dbuf["workspace"])
+        torch.cuda.synchronize()
+        outs.append(bits(dbuf["out"]))
+    assert np.array_equal(outs[0], outs[1])
 
 
 def test_prefill_full_size_sampled():
@@ -185,3 +226,44 @@ def test_decode_full_size_sampled():
     ref = oracle.mla_decode(bits(xd)[sample], host_params(p), wl.n_heads,
                             np.full(3, wl.seq_len), kv0[sample], kr0[sample])
     check_close(f32(bits(dbuf["out"]))[sample], ref["out"], "decode_full.out")
+
+
+def test_decode_graph_replays_match_the_eager_call():
+    """mla_decode captured in a HIP graph (as bench.py replays it): every
+    replay, with eager work and synchronisation between replays, gives the
+    eager call's output and cache entries bit for bit."""
+    wl = workloads.mla_custom(name="graph", batch=16, seq_len=100, max_len=128, cfg_id=51)
+    p = workloads.mla_params(wl, 0, DEV)
+    x = workloads.mla_tokens(wl, wl.tokens, 0, DEV)
+    _, buf = gpu_prefill(wl, x, p)
+    dshape = moe.MlaShape(wl.batch, 0, wl.max_len, wl.d_model, wl.n_heads, wl.d_latent,
+                          wl.d_nope, wl.d_rope, wl.d_v)
+    pos = torch.full((wl.batch,), 100, dtype=torch.int32, device=DEV)
+    xd = workloads.mla_tokens(wl, wl.batch, 1, DEV)
+    dbuf = moe.alloc_mla(dshape, DEV, decode=True)
+
+    def call():
+        moe.mla_decode(dshape, xd, pos, p, buf["cache_kv"], buf["cache_kr"], dbuf["out"],
+                       residual=xd, workspace=dbuf["workspace"])
+    call()
+    torch.cuda.synchronize()
+    ref_out = bits(dbuf["out"]).copy()
+    ref_kv = bits(buf["cache_kv"]).copy()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        call()
+    for r in range(3):
+        dbuf["out"].fill_(0)                    # eager work between replays
+        junk = torch.randn(1 << 20, device=DEV).sum()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(dbuf["out"]), ref_out), r
+        assert np.array_equal(bits(buf["cache_kv"]), ref_kv), r
+        del junk
