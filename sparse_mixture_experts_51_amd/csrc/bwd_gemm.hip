@@ -577,6 +577,391 @@ __global__ __launch_bounds__(kTh, 2) void bwd_gemm_kernel(BwdGemmArgs a) {
   }
 }
 
+// ---- weight gradients ------------------------------------------------------
+//
+// dW[g] = A_g^T B_g, K = the group's rows: both operands K-major.  A step's
+// tiles (64 rows of K x 128 columns per operand) go from memory into LDS by
+// DMA as they are stored, one K row per 256 bytes, the four 64-byte pieces of
+// row k rotated by k mod 4.  gfx950's ds_read_b64_tr_b16 reads such a tile
+// transposed: within each 16 lanes, lane s names 4 values of row s / 4 and
+// receives 4 consecutive rows of one column, so two reads give a lane the 8
+// consecutive K values of its MFMA fragment and nothing is shuffled between
+// threads.  Per 32 lanes a read covers 4 rows x 64 bytes, which the rotation
+// puts on all 64 banks.
+//
+// Every unit issues the same memory operations in the same order: the DMA
+// of its step 0 (during the previous unit's last step), the DMA of its step 1
+// and the previous unit's 16 output stores (in the epilogue), then one DMA
+// per further step; a missing step is a DMA with every lane out of range and
+// a missing output block an empty descriptor.  So the waits count exactly (step 0: 24 younger
+// operations, step 1: 16, later steps: none) and a DMA never waits for the
+// stores issued after it.  LDS is touched only through asm, which the
+// compiler does not tie to the DMA it cannot track.
+namespace {
+constexpr int kWgT = 128;                                 // output tile, M and N
+constexpr int kWgK = 64;                                  // rows of K per step
+constexpr int kWgOp = kWgK * kWgT * 2;                    // bytes of one operand's step tile
+constexpr int kWgDma = kWgOp / (kTh * 16);                // DMA per thread, operand and step
+constexpr int kWgStage = 2 * kWgOp;                       // A tile, then B tile
+constexpr int kWgHalf = 32 * 64 * 4;                      // a wave's 32 x 64 fp32 half block
+constexpr unsigned kWgOut = 0x80000000u;                  // past every descriptor's range
+constexpr int kWgRsrcFlags = 0x00020000;                  // raw (untyped) buffer
+constexpr int kWgNT = 2;                                  // cache policy: non-temporal
+static_assert(kWgDma == 4, "four 1 KB DMA per thread, operand and step");
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));  // lgkmcnt, expcnt free
+}
+
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_ptr_t)p));
+}
+
+__device__ __forceinline__ bf16x8 cat8(v4i16 lo, v4i16 hi) {
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// One MFMA sub-step's fragments: two of each operand, each the two 4-value
+// halves of its 8 K values (the second 4 rows of K further), complete on return.
+template <int kOff>
+__device__ __forceinline__ void tr_frags(unsigned a0, unsigned a1, unsigned b0, unsigned b1,
+                                         bf16x8 (&af)[2], bf16x8 (&bf)[2]) {
+  v4i16 r[8];
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %1, %8 offset:%13\n\t"
+      "ds_read_b64_tr_b16 %2, %9 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %3, %9 offset:%13\n\t"
+      "ds_read_b64_tr_b16 %4, %10 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %5, %10 offset:%13\n\t"
+      "ds_read_b64_tr_b16 %6, %11 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %7, %11 offset:%13\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
+        "=&v"(r[7])
+      : "v"(a0), "v"(a1), "v"(b0), "v"(b1), "i"(kOff), "i"(kOff + 4 * 256)
+      : "memory");
+  af[0] = cat8(r[0], r[1]);
+  af[1] = cat8(r[2], r[3]);
+  bf[0] = cat8(r[4], r[5]);
+  bf[1] = cat8(r[6], r[7]);
+}
+
+// Eight 16-byte LDS writes (no wait: the same wave's reads come after them).
+__device__ __forceinline__ void lds_write8_b128(const unsigned (&ad)[8], const u32x4 (&v)[8]) {
+  asm volatile(
+      "ds_write_b128 %0, %8\n\t"
+      "ds_write_b128 %1, %9\n\t"
+      "ds_write_b128 %2, %10\n\t"
+      "ds_write_b128 %3, %11\n\t"
+      "ds_write_b128 %4, %12\n\t"
+      "ds_write_b128 %5, %13\n\t"
+      "ds_write_b128 %6, %14\n\t"
+      "ds_write_b128 %7, %15"
+      :
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7]),
+        "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7])
+      : "memory");
+}
+}  // namespace
+
+__global__ __launch_bounds__(kTh, 2) void wgrad_kernel(BwdGemmArgs a) {
+  __shared__ u32x4 lds[2][kWgStage / 16];  // two steps in flight: [stage][A tile | B tile]
+  __shared__ int ustart[kMaxG + 1];        // first unit of each group
+  __shared__ int goff[kMaxG + 1];          // first row of each group in its segment's arrays
+  __shared__ int grows[kMaxG + 1];         // rows of each group (read here, not from memory
+                                           // the stores may share: that would be a vector load)
+  __shared__ int wsum[kTh / 64];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uni(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int G0 = a.seg[0].groups;
+  const int G = G0 + (a.nseg > 1 ? a.seg[1].groups : 0);
+  auto mtiles = [&](int sg) {
+    const int M = SEGF(sg, M), M1 = SEGF(sg, M1);
+    return cdiv(M1, kWgT) + cdiv(M - M1, kWgT);
+  };
+
+  // ---- unit table: per group, (m-tiles of both halves) x n-tiles x splits
+  {
+    constexpr int kPer = (kMaxG + kTh - 1) / kTh;
+    int lu[kPer];
+    int su = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int gg = tid * kPer + i;
+      int u = 0;
+      if (gg < G) {
+        const int sg = gg >= G0 ? 1 : 0;
+        const int h = gg - (sg ? G0 : 0);
+        const int32_t* o = SEGF(sg, offsets);
+        goff[gg] = o ? o[h] : 0;
+        const int R = seg_group_rows(a, sg, h);
+        grows[gg] = R;
+        const int split = SEGF(sg, split);
+        const int ns = split > 0 ? std::max(1, cdiv(R, split)) : 1;
+        u = mtiles(sg) * cdiv(SEGF(sg, N), kWgT) * ns;
+      }
+      lu[i] = u;
+      su += u;
+    }
+    int tot_u;
+    int run_u = block_scan<kTh>(su, &tot_u, wsum);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int gg = tid * kPer + i;
+      if (gg < G) ustart[gg] = run_u;
+      run_u += lu[i];
+    }
+    if (tid == 0) ustart[G] = tot_u;
+    __syncthreads();
+  }
+  const int total_units = uni(ustart[G]);
+  // partial-sum slots of the segment's groups before group h (split mode):
+  // groups of more than `split` rows take one slot per piece
+  auto slots_before = [&](int sg, int h) {
+    const int split = SEGF(sg, split), gbase = sg ? G0 : 0;
+    int n = 0;
+    for (int base = 0; base < h; base += 64) {
+      const int hi = base + lane;
+      int v = 0;
+      if (hi < h) {
+        const int ns = std::max(1, cdiv(grows[gbase + hi], split));
+        v = ns > 1 ? ns : 0;
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+      n += v;
+    }
+    return uni(n);
+  };
+  const int xcd = blockIdx.x % kXcds, per_xcd = gridDim.x / kXcds;
+  const int u_lo = static_cast<int>(static_cast<int64_t>(total_units) * xcd / kXcds);
+  const int u_hi = static_cast<int>(static_cast<int64_t>(total_units) * (xcd + 1) / kXcds);
+
+  struct WUnit {
+    int gg, sg, g, half, m0, n0, kbeg, kend, nk, split_idx, nsplit;
+    __amdgpu_buffer_rsrc_t ra, rb;  // the unit's rows kbeg..kend-1 of A and of B
+    int va, vb;                     // this thread's DMA offset in step 0 (kWgOut: column outside)
+    int lda2, ldb2;                 // row pitch in bytes
+  };
+  // DMA instruction p of a thread covers rows 16 p + 4 wave .. + 3 of the
+  // step; lane l writes LDS bytes 16 l of them: row 16 p + 4 wave + l / 16,
+  // stored piece ((l & 15) >> 2), which holds logical piece ((l & 15) >> 2) ^
+  // (l >> 4) -- the rotation by the row mod 4 -- and chunk l & 3 of it.
+  const int dma_row = 4 * wave + (lane >> 4);
+  const int dma_col = 8 * (((((lane & 15) >> 2) ^ (lane >> 4)) << 2) | (lane & 3));
+  auto decode = [&](int u) {
+    WUnit t;
+    int below = 0;
+    for (int base = 0; base < G; base += 64) {
+      const int gi = base + lane;
+      below += __popcll(__ballot(gi < G && ustart[gi] <= u));
+    }
+    t.gg = uni(below - 1);
+    t.sg = t.gg >= G0 ? 1 : 0;
+    t.g = t.gg - (t.sg ? G0 : 0);
+    const int off = uni(goff[t.gg]);
+    const int R = uni(grows[t.gg]);
+    const int local = u - uni(ustart[t.gg]);
+    const int M = SEGF(t.sg, M), N = SEGF(t.sg, N), M1 = SEGF(t.sg, M1);
+    const int split = SEGF(t.sg, split);
+    t.nsplit = split > 0 ? std::max(1, cdiv(R, split)) : 1;
+    const int mt1 = cdiv(M1, kWgT), mt = mtiles(t.sg);
+    const int tiles = mt * cdiv(N, kWgT);
+    t.split_idx = local / tiles;
+    const int r = local - t.split_idx * tiles;
+    const int mi = r % mt;
+    t.n0 = (r / mt) * kWgT;
+    t.half = mi >= mt1 ? 1 : 0;
+    t.m0 = (t.half ? mi - mt1 : mi) * kWgT;
+    t.kbeg = t.nsplit > 1 ? t.split_idx * split : 0;
+    t.kend = t.nsplit > 1 ? std::min(R, t.kbeg + split) : R;
+    t.nk = std::max(1, cdiv(t.kend - t.kbeg, kWgK));
+    const int64_t lda = SEGF(t.sg, lda), ldb = SEGF(t.sg, ldb);
+    const int rows = t.kend - t.kbeg;
+    const uint16_t* A = t.half ? SEGF(t.sg, a2) : SEGF(t.sg, a);
+    const uint16_t* B = SEGF(t.sg, b);
+    t.ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(A + (off + t.kbeg) * lda), static_cast<short>(0),
+                                             static_cast<int>(rows * lda * 2), kWgRsrcFlags);
+    t.rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(B + (off + t.kbeg) * ldb), static_cast<short>(0),
+                                             static_cast<int>(rows * ldb * 2), kWgRsrcFlags);
+    const int acols = t.half ? M - M1 : M1;
+    t.va = t.m0 + dma_col < acols ? static_cast<int>((dma_row * lda + t.m0 + dma_col) * 2) : static_cast<int>(kWgOut);
+    t.vb = t.n0 + dma_col < N ? static_cast<int>((dma_row * ldb + t.n0 + dma_col) * 2) : static_cast<int>(kWgOut);
+    t.lda2 = static_cast<int>(lda * 2);
+    t.ldb2 = static_cast<int>(ldb * 2);
+    return t;
+  };
+
+  // ---- DMA of step kt of unit t into stage st (rows past the unit's K range
+  // are past its descriptors and arrive as zeros)
+  // (none: a step that does not exist, every lane out of range -- the same
+  // eight operations into the same stage, so the counts stay exact)
+  auto issue = [&](const WUnit& t, int kt, int st, bool none) {
+#pragma unroll
+    for (int p = 0; p < kWgDma; ++p) {
+      const int ra = (kt * kWgK + 16 * p) * t.lda2, rb = (kt * kWgK + 16 * p) * t.ldb2;
+      const int oa = none || t.va == static_cast<int>(kWgOut) ? static_cast<int>(kWgOut) : t.va + ra;
+      const int ob = none || t.vb == static_cast<int>(kWgOut) ? static_cast<int>(kWgOut) : t.vb + rb;
+      dma_b128(t.ra, &lds[st][(4 * p + wave) * 64], oa, 0);
+      dma_b128(t.rb, &lds[st][kWgOp / 16 + (4 * p + wave) * 64], ob, 0);
+    }
+  };
+
+  // ---- fragments: lane l reads 4 values of row (l & 15) / 4 (+ 8 for lanes
+  // 32..63), columns 16 ((l >> 4) & 1) + 4 (l & 3) of the 32-column tile; the
+  // tile's logical piece is rotated by that row mod 4
+  const int tr_row = 8 * (lane >> 5) + ((lane & 15) >> 2);
+  const int tr_in = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int tr_rot = (lane & 15) >> 2;
+  const unsigned lds0 = lds_addr(&lds[0][0]);
+  unsigned fa[2], fb[2];  // stage 0; stage 1 is kWgStage further
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    fa[i] = lds0 + tr_row * 256 + (((2 * wm + i) ^ tr_rot) << 6) + tr_in * 2;
+    fb[i] = lds0 + kWgOp + tr_row * 256 + (((2 * wn + i) ^ tr_rot) << 6) + tr_in * 2;
+  }
+  f32x16 acc[2][2];
+  auto compute = [&](int st) {
+    const unsigned so = st * kWgStage;
+    MOE_FOR(ks, kWgK / 16, {
+      bf16x8 af[2], bfr[2];
+      tr_frags<ks * 16 * 256>(fa[0] + so, fa[1] + so, fb[0] + so, fb[1] + so, af, bfr);
+      MOE_FOR(i, 2, {
+        MOE_FOR(j, 2, { acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0); })
+      })
+    })
+  };
+
+  // ---- epilogue: the wave's 64 x 64 block through its 8 KB of the stage the
+  // last step read, 32 rows at a time (rows of 16 chunks of four values,
+  // chunk c of row r at c ^ (r & 15)), into registers for 16 row stores
+  const int fr = lane & 31, fhalf = lane >> 5;
+  u32x4 outv[2][8];
+  auto stage_out = [&](int st) {
+    const unsigned base = lds0 + st * kWgStage + wave * kWgHalf;
+    MOE_FOR(h, 2, {
+      unsigned wa[8];
+      u32x4 wv[8];
+      MOE_FOR(j, 2, {
+        MOE_FOR(q, 4, {
+          const int ch = 8 * j + 2 * q + fhalf;
+          wa[4 * j + q] = base + (fr * 16 + (ch ^ (fr & 15))) * 16;
+          const f32x16& v = acc[h][j];
+          wv[4 * j + q] = u32x4{__float_as_uint(v[4 * q]), __float_as_uint(v[4 * q + 1]),
+                                __float_as_uint(v[4 * q + 2]), __float_as_uint(v[4 * q + 3])};
+        })
+      })
+      lds_write8_b128(wa, wv);
+      const u32x4* src[8];
+      MOE_FOR(it, 8, {
+        const int rr = 4 * it + (lane >> 4), ch = lane & 15;
+        src[it] = reinterpret_cast<const u32x4*>(&lds[st][0]) + wave * (kWgHalf / 16) + rr * 16 + (ch ^ (rr & 15));
+      })
+      lds_read_n<8>(src, outv[h]);
+    })
+  };
+  // 16 stores per thread: an empty descriptor for a block outside the output
+  auto store_out = [&](const WUnit& t) {
+    const int M = SEGF(t.sg, M), N = SEGF(t.sg, N), M1 = SEGF(t.sg, M1);
+    const int rw = t.m0 + 64 * wm, cw = t.n0 + 64 * wn;  // rw: row within the half
+    const bool inside = rw < (t.half ? M - M1 : M1) && cw < N;
+    float* base;
+    int64_t ld;
+    if (t.nsplit > 1) {
+      const int slot = slots_before(t.sg, t.g) + t.split_idx;
+      base = SEGF(t.sg, part) + (static_cast<int64_t>(slot) * M + (t.half ? M1 : 0) + rw) * N + cw;
+      ld = N;
+    } else {
+      base = static_cast<float*>(t.half ? SEGF(t.sg, c2) : SEGF(t.sg, c)) +
+             static_cast<int64_t>(t.g) * SEGF(t.sg, c_gstride) + static_cast<int64_t>(rw) * SEGF(t.sg, ldc) + cw;
+      ld = SEGF(t.sg, ldc);
+    }
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        inside ? base : SEGF(t.sg, part), static_cast<short>(0), inside ? static_cast<int>(64 * ld * 4) : 0,
+        kWgRsrcFlags);
+    const int lrow = lane >> 4, lcol = 4 * (lane & 15);
+    if (t.nsplit > 1) {
+      // partial sums: read back by wgrad_reduce_kernel, kept in L2
+      MOE_FOR(h, 2, {
+        MOE_FOR(it, 8, {
+          const int off = static_cast<int>(((32 * h + 4 * it + lrow) * ld + lcol) * 4);
+          __builtin_amdgcn_raw_buffer_store_b128(outv[h][it], rs, off, 0, 0);
+        })
+      })
+    } else {
+      // final gradients: streamed past L2, which keeps the operands
+      MOE_FOR(h, 2, {
+        MOE_FOR(it, 8, {
+          const int off = static_cast<int>(((32 * h + 4 * it + lrow) * ld + lcol) * 4);
+          __builtin_amdgcn_raw_buffer_store_b128(outv[h][it], rs, off, 0, kWgNT);
+        })
+      })
+    }
+  };
+
+  int u = u_lo + static_cast<int>(blockIdx.x) / kXcds;
+  if (u >= u_hi) return;  // nothing issued yet
+  WUnit cur = decode(u);
+  issue(cur, 0, 0, false);
+  issue(cur, 1, 1, cur.nk < 2);
+  bool first = true;
+  int gs = 0;  // stage parity of the unit's step 0
+  for (;;) {
+    const int un = u + per_xcd;
+    const bool have_next = un < u_hi;
+    WUnit nxt = cur;
+    if (have_next) nxt = decode(un);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    for (int kt = 0; kt < cur.nk; ++kt) {
+      const int st = (gs + kt) & 1;
+      if (kt == 0) {
+        // a unit of one step overwrites the stage of the empty step 1 below:
+        // that DMA too must have landed
+        if (cur.nk == 1) {
+          if (first) vm_wait<0>();
+          else vm_wait<16>();
+        } else {
+          if (first) vm_wait<2 * kWgDma>();
+          else vm_wait<2 * kWgDma + 16>();
+        }
+      } else if (kt == 1) {
+        if (first) vm_wait<0>();
+        else vm_wait<16>();
+      } else {
+        vm_wait<0>();
+      }
+      lds_barrier();  // every wave's DMA of this step has landed; the other stage is free
+      if (kt > 0 || cur.nk == 1) {
+        if (kt + 1 < cur.nk) issue(cur, kt + 1, st ^ 1, false);
+        else issue(nxt, 0, st ^ 1, !have_next);
+      }
+      compute(st);
+    }
+    const int st_last = (gs + cur.nk - 1) & 1;
+    lds_barrier();  // every wave is done with the last step's stage
+    stage_out(st_last);
+    lds_barrier();  // ... and with its staged outputs
+    issue(nxt, 1, st_last, !have_next || nxt.nk < 2);
+    store_out(cur);
+    if (!have_next) break;
+    gs = (gs + cur.nk) & 1;
+    cur = nxt;
+    u = un;
+    first = false;
+  }
+  vm_wait<0>();  // no DMA left in flight into LDS
+}
+
 // Sum of a split group's partial sums, in split order, into the weight
 // gradient.  blockIdx.y = group over both segments, x strides over M x N.
 __global__ __launch_bounds__(256) void wgrad_reduce_kernel(BwdGemmArgs a) {
@@ -659,7 +1044,7 @@ hipError_t launch_bwd_gemm(const BwdGemmArgs& a, int kind, hipStream_t s) {
       hipLaunchKernelGGL(bwd_gemm_kernel<kBwdRecompute>, gd, bd, 0, s, a);
       break;
     case kBwdWgrad: {
-      hipLaunchKernelGGL(bwd_gemm_kernel<kBwdWgrad>, gd, bd, 0, s, a);
+      hipLaunchKernelGGL(wgrad_kernel, gd, bd, 0, s, a);
       bool split = false;
       int groups = 0;
       int64_t mn = 0;
