@@ -589,25 +589,35 @@ __global__ __launch_bounds__(kTh, 2) void bwd_gemm_kernel(BwdGemmArgs a) {
 // threads.  Per 32 lanes a read covers 4 rows x 64 bytes, which the rotation
 // puts on all 64 banks.
 //
-// Every unit issues the same memory operations in the same order: the DMA
-// of its step 0 (during the previous unit's last step), the DMA of its step 1
-// and the previous unit's 16 output stores (in the epilogue), then one DMA
-// per further step; a missing step is a DMA with every lane out of range and
-// a missing output block an empty descriptor.  So the waits count exactly (step 0: 24 younger
-// operations, step 1: 16, later steps: none) and a DMA never waits for the
-// stores issued after it.  LDS is touched only through asm, which the
-// compiler does not tie to the DMA it cannot track.
+// Four waves (2 x 2 of 64 x 64), two blocks per CU, two step stages.  vmcnt
+// counts a wave's loads and stores in one order, so the DMA waited for must
+// not come after output stores that the write stream keeps in flight: every
+// unit issues the same operations in the same order -- the DMA of its step 0
+// (during the previous unit's last step), the DMA of its step 1 and the
+// previous unit's 16 output stores per thread (in the epilogue), then one
+// DMA per further step, with a DMA of every lane out of range for a step
+// that does not exist and an empty descriptor for an output block outside
+// the gradient -- and the waits count exactly: step 0 waits with 24 younger
+// operations in flight, step 1 with the 16 stores, later steps with none
+// (their DMA went out after the stores, which have had a unit's time).
+// (One block per CU with loader waves that issue only DMA, four stages
+// ahead, measured 8% slower: two independent blocks hide more.)  LDS is
+// touched only through asm, which the compiler does not tie to the DMA it
+// cannot track.
 namespace {
 constexpr int kWgT = 128;                                 // output tile, M and N
 constexpr int kWgK = 64;                                  // rows of K per step
+constexpr int kWgThreads = 256;
 constexpr int kWgOp = kWgK * kWgT * 2;                    // bytes of one operand's step tile
-constexpr int kWgDma = kWgOp / (kTh * 16);                // DMA per thread, operand and step
+constexpr int kWgDma = kWgOp / (kWgThreads * 16);         // DMA per thread, operand and step
+constexpr int kWgStep = 2 * kWgDma;                       // a thread's DMA of a step
+constexpr int kWgStores = kWgT * kWgT * 4 / (kWgThreads * 16);  // output stores per thread and unit
 constexpr int kWgStage = 2 * kWgOp;                       // A tile, then B tile
 constexpr int kWgHalf = 32 * 64 * 4;                      // a wave's 32 x 64 fp32 half block
 constexpr unsigned kWgOut = 0x80000000u;                  // past every descriptor's range
 constexpr int kWgRsrcFlags = 0x00020000;                  // raw (untyped) buffer
 constexpr int kWgNT = 2;                                  // cache policy: non-temporal
-static_assert(kWgDma == 4, "four 1 KB DMA per thread, operand and step");
+static_assert(kWgStep + kWgStores < 64 && kWgStores == 16, "vmcnt range; two halves of 8 stores");
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
@@ -669,13 +679,13 @@ __device__ __forceinline__ void lds_write8_b128(const unsigned (&ad)[8], const u
 }
 }  // namespace
 
-__global__ __launch_bounds__(kTh, 2) void wgrad_kernel(BwdGemmArgs a) {
-  __shared__ u32x4 lds[2][kWgStage / 16];  // two steps in flight: [stage][A tile | B tile]
+__global__ __launch_bounds__(kWgThreads, 2) void wgrad_kernel(BwdGemmArgs a) {
+  __shared__ u32x4 lds[2][kWgStage / 16];  // [stage][A tile | B tile]
   __shared__ int ustart[kMaxG + 1];        // first unit of each group
   __shared__ int goff[kMaxG + 1];          // first row of each group in its segment's arrays
   __shared__ int grows[kMaxG + 1];         // rows of each group (read here, not from memory
                                            // the stores may share: that would be a vector load)
-  __shared__ int wsum[kTh / 64];
+  __shared__ int wsum[kWgThreads / 64];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uni(tid >> 6);
@@ -689,7 +699,7 @@ __global__ __launch_bounds__(kTh, 2) void wgrad_kernel(BwdGemmArgs a) {
 
   // ---- unit table: per group, (m-tiles of both halves) x n-tiles x splits
   {
-    constexpr int kPer = (kMaxG + kTh - 1) / kTh;
+    constexpr int kPer = (kMaxG + kWgThreads - 1) / kWgThreads;
     int lu[kPer];
     int su = 0;
 #pragma unroll
@@ -711,7 +721,7 @@ __global__ __launch_bounds__(kTh, 2) void wgrad_kernel(BwdGemmArgs a) {
       su += u;
     }
     int tot_u;
-    int run_u = block_scan<kTh>(su, &tot_u, wsum);
+    int run_u = block_scan<kWgThreads>(su, &tot_u, wsum);
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int gg = tid * kPer + i;
@@ -750,8 +760,8 @@ __global__ __launch_bounds__(kTh, 2) void wgrad_kernel(BwdGemmArgs a) {
     int va, vb;                     // this thread's DMA offset in step 0 (kWgOut: column outside)
     int lda2, ldb2;                 // row pitch in bytes
   };
-  // DMA instruction p of a thread covers rows 16 p + 4 wave .. + 3 of the
-  // step; lane l writes LDS bytes 16 l of them: row 16 p + 4 wave + l / 16,
+  // DMA p of a wave covers rows 16 p + 4 wave .. + 3 of an operand's step
+  // tile; lane l writes LDS bytes 16 l of them: row 16 p + 4 wave + l / 16,
   // stored piece ((l & 15) >> 2), which holds logical piece ((l & 15) >> 2) ^
   // (l >> 4) -- the rotation by the row mod 4 -- and chunk l & 3 of it.
   const int dma_row = 4 * wave + (lane >> 4);
@@ -776,8 +786,20 @@ __global__ __launch_bounds__(kTh, 2) void wgrad_kernel(BwdGemmArgs a) {
     const int tiles = mt * cdiv(N, kWgT);
     t.split_idx = local / tiles;
     const int r = local - t.split_idx * tiles;
-    const int mi = r % mt;
-    t.n0 = (r / mt) * kWgT;
+    // the 32 units that an XCD's CUs run at once cover 4 m-tiles x 8 n-tiles
+    // where the tiles divide so, rather than 32 m-tiles of one n-tile: the
+    // tile that all of them would read is the hot spot (12% slower)
+    const int nt = tiles / mt;
+    int mi, ni;
+    if (mt % 4 == 0 && nt % 8 == 0) {
+      const int bi = r / 32, w = r % 32;
+      mi = (bi % (mt / 4)) * 4 + w % 4;
+      ni = (bi / (mt / 4)) * 8 + w / 4;
+    } else {
+      mi = r % mt;
+      ni = r / mt;
+    }
+    t.n0 = ni * kWgT;
     t.half = mi >= mt1 ? 1 : 0;
     t.m0 = (t.half ? mi - mt1 : mi) * kWgT;
     t.kbeg = t.nsplit > 1 ? t.split_idx * split : 0;
@@ -804,13 +826,13 @@ __global__ __launch_bounds__(kTh, 2) void wgrad_kernel(BwdGemmArgs a) {
   // (none: a step that does not exist, every lane out of range -- the same
   // eight operations into the same stage, so the counts stay exact)
   auto issue = [&](const WUnit& t, int kt, int st, bool none) {
+    const bool oa_out = none || t.va == static_cast<int>(kWgOut);
+    const bool ob_out = none || t.vb == static_cast<int>(kWgOut);
 #pragma unroll
     for (int p = 0; p < kWgDma; ++p) {
       const int ra = (kt * kWgK + 16 * p) * t.lda2, rb = (kt * kWgK + 16 * p) * t.ldb2;
-      const int oa = none || t.va == static_cast<int>(kWgOut) ? static_cast<int>(kWgOut) : t.va + ra;
-      const int ob = none || t.vb == static_cast<int>(kWgOut) ? static_cast<int>(kWgOut) : t.vb + rb;
-      dma_b128(t.ra, &lds[st][(4 * p + wave) * 64], oa, 0);
-      dma_b128(t.rb, &lds[st][kWgOp / 16 + (4 * p + wave) * 64], ob, 0);
+      dma_b128(t.ra, &lds[st][(4 * p + wave) * 64], oa_out ? static_cast<int>(kWgOut) : t.va + ra, 0);
+      dma_b128(t.rb, &lds[st][kWgOp / 16 + (4 * p + wave) * 64], ob_out ? static_cast<int>(kWgOut) : t.vb + rb, 0);
     }
   };
 
@@ -841,18 +863,20 @@ __global__ __launch_bounds__(kTh, 2) void wgrad_kernel(BwdGemmArgs a) {
 
   // ---- epilogue: the wave's 64 x 64 block through its 8 KB of the stage the
   // last step read, 32 rows at a time (rows of 16 chunks of four values,
-  // chunk c of row r at c ^ (r & 15)), into registers for 16 row stores
+  // chunk c of row r at c ^ (r & 15)), into registers; then 16 row stores,
+  // to an empty descriptor for a block outside the output
   const int fr = lane & 31, fhalf = lane >> 5;
+  const int lrow = lane >> 4, lcol = 4 * (lane & 15);
   u32x4 outv[2][8];
   auto stage_out = [&](int st) {
-    const unsigned base = lds0 + st * kWgStage + wave * kWgHalf;
+    const unsigned sbase = lds0 + st * kWgStage + wave * kWgHalf;
     MOE_FOR(h, 2, {
       unsigned wa[8];
       u32x4 wv[8];
       MOE_FOR(j, 2, {
         MOE_FOR(q, 4, {
           const int ch = 8 * j + 2 * q + fhalf;
-          wa[4 * j + q] = base + (fr * 16 + (ch ^ (fr & 15))) * 16;
+          wa[4 * j + q] = sbase + (fr * 16 + (ch ^ (fr & 15))) * 16;
           const f32x16& v = acc[h][j];
           wv[4 * j + q] = u32x4{__float_as_uint(v[4 * q]), __float_as_uint(v[4 * q + 1]),
                                 __float_as_uint(v[4 * q + 2]), __float_as_uint(v[4 * q + 3])};
@@ -861,13 +885,12 @@ __global__ __launch_bounds__(kTh, 2) void wgrad_kernel(BwdGemmArgs a) {
       lds_write8_b128(wa, wv);
       const u32x4* src[8];
       MOE_FOR(it, 8, {
-        const int rr = 4 * it + (lane >> 4), ch = lane & 15;
+        const int rr = 4 * it + lrow, ch = lane & 15;
         src[it] = reinterpret_cast<const u32x4*>(&lds[st][0]) + wave * (kWgHalf / 16) + rr * 16 + (ch ^ (rr & 15));
       })
       lds_read_n<8>(src, outv[h]);
     })
   };
-  // 16 stores per thread: an empty descriptor for a block outside the output
   auto store_out = [&](const WUnit& t) {
     const int M = SEGF(t.sg, M), N = SEGF(t.sg, N), M1 = SEGF(t.sg, M1);
     const int rw = t.m0 + 64 * wm, cw = t.n0 + 64 * wn;  // rw: row within the half
@@ -886,7 +909,6 @@ __global__ __launch_bounds__(kTh, 2) void wgrad_kernel(BwdGemmArgs a) {
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         inside ? base : SEGF(t.sg, part), static_cast<short>(0), inside ? static_cast<int>(64 * ld * 4) : 0,
         kWgRsrcFlags);
-    const int lrow = lane >> 4, lcol = 4 * (lane & 15);
     if (t.nsplit > 1) {
       // partial sums: read back by wgrad_reduce_kernel, kept in L2
       MOE_FOR(h, 2, {
@@ -911,8 +933,8 @@ __global__ __launch_bounds__(kTh, 2) void wgrad_kernel(BwdGemmArgs a) {
   WUnit cur = decode(u);
   issue(cur, 0, 0, false);
   issue(cur, 1, 1, cur.nk < 2);
-  bool first = true;
-  int gs = 0;  // stage parity of the unit's step 0
+  bool first = true;  // no stores issued yet
+  int gs = 0;         // stage of the unit's step 0
   for (;;) {
     const int un = u + per_xcd;
     const bool have_next = un < u_hi;
@@ -929,14 +951,14 @@ __global__ __launch_bounds__(kTh, 2) void wgrad_kernel(BwdGemmArgs a) {
         // that DMA too must have landed
         if (cur.nk == 1) {
           if (first) vm_wait<0>();
-          else vm_wait<16>();
+          else vm_wait<kWgStores>();
         } else {
-          if (first) vm_wait<2 * kWgDma>();
-          else vm_wait<2 * kWgDma + 16>();
+          if (first) vm_wait<kWgStep>();
+          else vm_wait<kWgStep + kWgStores>();
         }
       } else if (kt == 1) {
         if (first) vm_wait<0>();
-        else vm_wait<16>();
+        else vm_wait<kWgStores>();
       } else {
         vm_wait<0>();
       }
@@ -1044,7 +1066,7 @@ hipError_t launch_bwd_gemm(const BwdGemmArgs& a, int kind, hipStream_t s) {
       hipLaunchKernelGGL(bwd_gemm_kernel<kBwdRecompute>, gd, bd, 0, s, a);
       break;
     case kBwdWgrad: {
-      hipLaunchKernelGGL(wgrad_kernel, gd, bd, 0, s, a);
+      hipLaunchKernelGGL(wgrad_kernel, gd, dim3(kWgThreads), 0, s, a);
       bool split = false;
       int groups = 0;
       int64_t mn = 0;
