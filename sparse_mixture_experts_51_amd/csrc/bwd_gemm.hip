@@ -17,22 +17,24 @@
 // a zero weight gradient.  One launch covers the shared expert (one group of
 // all T rows, its own operands) and the routed experts.
 //
-// Tile 128 x 128 x 64, four waves of 64 x 64 (2 x 2 MFMA tiles of 32x32x16,
-// fp32 accumulators), two blocks per CU, persistent over units (group, m-tile,
-// n-tile[, split]); each XCD runs an eighth of the units in order, so the
-// units of one group share its L2.  Each operand's K-step is loaded to
-// registers two steps ahead (kDepth): four 16-byte loads per thread, along
-// the contiguous direction.  Both layouts are staged in LDS
-// the same way, a row of the tile (an M or N index) holding its 64 K values as
-// eight 16-byte chunks, so every MFMA fragment is one 16-byte LDS read.  A
-// K-major operand gets there through a transpose in registers: a thread loads
-// 4 rows of K x 8 columns and writes 8 columns x 4 values of K (8 bytes each).
-// The chunk order within a row is XOR-swizzled with bits 1-3 of the row
-// (chunk ^ (row >> 1) ^ (row >> 3)): fragment reads and K-contiguous stores
-// hit 64 distinct banks per 16 lanes, the transposed stores two ways at most.
+// Input gradients and the recompute (bwd_gemm_kernel): tile 128 x 128 x 64,
+// four waves of 64 x 64 (2 x 2 MFMA tiles of 32x32x16, fp32 accumulators),
+// two blocks per CU, persistent over units (group, m-tile, n-tile); each XCD
+// runs an eighth of the units in order, so the units of one group share its
+// L2.  Each operand's K-step is loaded to registers two steps ahead (kDepth):
+// four 16-byte loads per thread, along the contiguous direction.  Both layouts
+// are staged in LDS the same way, a row of the tile (an M or N index) holding
+// its 64 K values as eight 16-byte chunks, so every MFMA fragment is one
+// 16-byte LDS read.  A K-major operand (the weight of dh and dx) gets there
+// through a transpose in registers: a thread loads 4 rows of K x 8 columns
+// and writes 8 columns x 4 values of K (8 bytes each).  The chunk order within
+// a row is XOR-swizzled with bits 1-3 of the row (chunk ^ (row >> 1) ^
+// (row >> 3)): fragment reads and K-contiguous stores hit 64 distinct banks
+// per 16 lanes, the transposed stores two ways at most.
 //
-// Weight gradients with too few tiles to fill the chip (small d and H) split
-// a group's rows into pieces of `split` rows; each piece writes fp32 partial
+// Weight gradients (wgrad_kernel, described above it) have both operands K
+// major.  With too few tiles to fill the chip (small d and H) they split a
+// group's rows into pieces of `split` rows; each piece writes fp32 partial
 // sums and wgrad_reduce_kernel adds them in piece order, so the result does
 // not depend on timing.
 #include "common.hpp"
@@ -78,18 +80,16 @@ __device__ __forceinline__ int seg_group_rows(const BwdGemmArgs& a, int sg, int 
 
 template <int KIND>
 __global__ __launch_bounds__(kTh, 2) void bwd_gemm_kernel(BwdGemmArgs a) {
-  // stages: A in lds[0], lds[1]; B in lds[2], lds[3].  The weight-gradient
-  // epilogue reuses lds[w] to stage wave w's 64 x 64 fp32 outputs.
+  // stages: A in lds[0], lds[1]; B in lds[2], lds[3]
   __shared__ u32x4 lds[4][kStageU4];
   u32x4 (*const lds_a)[kStageU4] = lds;
   u32x4 (*const lds_b)[kStageU4] = lds + 2;
   __shared__ int ustart[kMaxG + 1];  // first unit of each group
   __shared__ int goff[kMaxG + 1];    // first row of each group in its segment's arrays
-  __shared__ int pslot[kMaxG + 1];   // wgrad: first partial-sum slot of each group
   __shared__ int wsum[kTh / 64];
   constexpr bool kDgrad = KIND == kBwdDgradKM;
   constexpr bool kPair = KIND == kBwdRecompute;  // B rows [0,64) from b, [64,128) from b2
-  constexpr bool kWgrad = KIND == kBwdWgrad;
+  static_assert(KIND == kBwdDgradKM || KIND == kBwdRecompute, "input gradients and the recompute");
   constexpr int kCols = kPair ? kTN / 2 : kTN;   // output columns per unit
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -98,56 +98,37 @@ __global__ __launch_bounds__(kTh, 2) void bwd_gemm_kernel(BwdGemmArgs a) {
   const int G0 = a.seg[0].groups;
   const int G = G0 + (a.nseg > 1 ? a.seg[1].groups : 0);
 
-  // ---- unit table: per group, units = m-tiles x n-tiles x splits
+  // ---- unit table: per group, units = m-tiles x n-tiles
   {
     constexpr int kPer = (kMaxG + kTh - 1) / kTh;
-    int lu[kPer], lp[kPer];
-    int su = 0, sp = 0;
+    int lu[kPer];
+    int su = 0;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int gg = tid * kPer + i;
-      int u = 0, p = 0;
+      int u = 0;
       if (gg < G) {
         const int sg = gg >= G0 ? 1 : 0;
         const int h = gg - (sg ? G0 : 0);
         const int32_t* o = SEGF(sg, offsets);
         goff[gg] = o ? o[h] : 0;
-        const int R = seg_group_rows(a, sg, h);
-        if constexpr (kWgrad) {
-          const int split = SEGF(sg, split);
-          const int ns = split > 0 ? std::max(1, cdiv(R, split)) : 1;
-          u = cdiv(SEGF(sg, M), kTM) * cdiv(SEGF(sg, N), kTN) * ns;
-          p = ns > 1 ? ns : 0;
-        } else {
-          u = cdiv(R, kTM) * cdiv(SEGF(sg, N), kCols);
-        }
+        u = cdiv(seg_group_rows(a, sg, h), kTM) * cdiv(SEGF(sg, N), kCols);
       }
       lu[i] = u;
-      lp[i] = p;
       su += u;
-      sp += p;
     }
-    int tot_u, tot_p;
+    int tot_u;
     int run_u = block_scan<kTh>(su, &tot_u, wsum);
-    int run_p = block_scan<kTh>(sp, &tot_p, wsum);
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int gg = tid * kPer + i;
-      if (gg < G) {
-        ustart[gg] = run_u;
-        pslot[gg] = run_p;
-      }
+      if (gg < G) ustart[gg] = run_u;
       run_u += lu[i];
-      run_p += lp[i];
     }
-    if (tid == 0) {
-      ustart[G] = tot_u;
-      pslot[G] = tot_p;
-    }
+    if (tid == 0) ustart[G] = tot_u;
     __syncthreads();
   }
   const int total_units = uni(ustart[G]);
-  const int seg1_slot0 = uni(pslot[G0]);  // slots of segment 0 (segment 1 counts its own from 0)
   // XCD x (blocks b with b % 8 == x) takes the x-th eighth of the units in
   // order, so the units of a group (which share their rows and weights) run
   // on one XCD and its L2
@@ -164,7 +145,7 @@ __global__ __launch_bounds__(kTh, 2) void bwd_gemm_kernel(BwdGemmArgs a) {
 
   // ---- a unit: its uniform description
   struct Unit {
-    int gg, sg, g, off, R, M, N, K, m0, n0, kbeg, kend, nk, split_idx, nsplit;
+    int gg, sg, g, off, R, N, K, m0, n0, kend, nk;
   };
   auto decode = [&](int u) {
     Unit t;
@@ -179,30 +160,13 @@ __global__ __launch_bounds__(kTh, 2) void bwd_gemm_kernel(BwdGemmArgs a) {
     t.off = uni(goff[t.gg]);
     t.R = uni(seg_group_rows(a, t.sg, t.g));
     const int local = u - uni(ustart[t.gg]);
-    t.M = SEGF(t.sg, M);
     t.N = SEGF(t.sg, N);
     t.K = SEGF(t.sg, K);
-    t.split_idx = 0;
-    t.nsplit = 1;
-    if constexpr (kWgrad) {
-      const int split = SEGF(t.sg, split);
-      t.nsplit = split > 0 ? std::max(1, cdiv(t.R, split)) : 1;
-      const int mt = cdiv(t.M, kTM);
-      const int tiles = mt * cdiv(t.N, kTN);
-      t.split_idx = local / tiles;
-      const int r = local - t.split_idx * tiles;
-      t.m0 = (r % mt) * kTM;
-      t.n0 = (r / mt) * kTN;
-      t.kbeg = t.nsplit > 1 ? t.split_idx * split : 0;
-      t.kend = t.nsplit > 1 ? std::min(t.R, t.kbeg + split) : t.R;
-    } else {
-      const int mt = cdiv(t.R, kTM);
-      t.m0 = (local % mt) * kTM;
-      t.n0 = (local / mt) * kCols;
-      t.kbeg = 0;
-      t.kend = t.K + SEGF(t.sg, K2);
-    }
-    t.nk = cdiv(t.kend - t.kbeg, kTK);
+    const int mt = cdiv(t.R, kTM);
+    t.m0 = (local % mt) * kTM;
+    t.n0 = (local / mt) * kCols;
+    t.kend = t.K + SEGF(t.sg, K2);
+    t.nk = cdiv(t.kend, kTK);
     return t;
   };
 
@@ -216,10 +180,6 @@ __global__ __launch_bounds__(kTh, 2) void bwd_gemm_kernel(BwdGemmArgs a) {
   bool a_ok[4];                    // ... inside the group
   const uint16_t* kc_b[4];         // recompute B: weight row pointers
   bool b_ok[4];                    // ... inside N
-  const uint16_t* km_a = nullptr;  // wgrad A: column base (in a or a2)
-  const uint16_t* km_a_row = nullptr;  // wgrad: this thread's first row of A and of B
-  const uint16_t* km_b_row = nullptr;
-  bool km_a_ok = false;
   int km_b_col = 0;                // K-major B: first column
   bool km_b_ok = false;
   auto setup = [&](const Unit& t) {
@@ -230,13 +190,11 @@ __global__ __launch_bounds__(kTh, 2) void bwd_gemm_kernel(BwdGemmArgs a) {
     B2 = SEGF(t.sg, b2);
     ldb = SEGF(t.sg, ldb);
     bgs = static_cast<int64_t>(t.g) * SEGF(t.sg, b_gstride);
-    if constexpr (!kWgrad) {
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int row = (tid + kTh * p) >> 3;
-        a_ok[p] = t.m0 + row < t.R;
-        a_row[p] = (t.off + (a_ok[p] ? t.m0 + row : t.m0)) * static_cast<int>(lda);
-      }
+    for (int p = 0; p < 4; ++p) {
+      const int row = (tid + kTh * p) >> 3;
+      a_ok[p] = t.m0 + row < t.R;
+      a_row[p] = (t.off + (a_ok[p] ? t.m0 + row : t.m0)) * static_cast<int>(lda);
     }
     if constexpr (kPair) {
 #pragma unroll
@@ -247,61 +205,26 @@ __global__ __launch_bounds__(kTh, 2) void bwd_gemm_kernel(BwdGemmArgs a) {
         kc_b[p] = (row < kCols ? B : B2) + bgs + static_cast<int64_t>(b_ok[p] ? wrow : t.n0) * ldb;
       }
     }
-    if constexpr (kDgrad || kWgrad) {
+    if constexpr (kDgrad) {
       km_b_ok = t.n0 + 8 * cb < t.N;
       km_b_col = km_b_ok ? t.n0 + 8 * cb : t.n0;
-    }
-    if constexpr (kWgrad) {
-      const int M1 = SEGF(t.sg, M1);
-      const int m = t.m0 + 8 * cb;
-      km_a_ok = m < t.M;
-      km_a = !km_a_ok ? A : (m < M1 ? A + m : A2 + (m - M1));
-      // rows 4 kb of the unit's first K-step (full K-steps advance from here)
-      km_a_row = km_a + static_cast<int64_t>(t.off + t.kbeg + 4 * kb) * lda;
-      km_b_row = B + static_cast<int64_t>(t.off + t.kbeg + 4 * kb) * ldb + km_b_col;
     }
   };
 
   // ---- loads of K-step kt (16-byte chunks)
   auto load_a = [&](const Unit& t, int kt, u32x4 (&v)[4]) {
-    const int k0 = t.kbeg + kt * kTK;
-    if constexpr (kWgrad) {
-      if (k0 + kTK <= t.kend) {
-        const uint16_t* p = km_a_row + static_cast<int64_t>(kt) * kTK * lda;
+    const int k0 = kt * kTK;
+    const bool second = k0 >= t.K;
+    const uint16_t* base = (second ? A2 : A) + (second ? k0 - t.K : k0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const u32x4*>(p + i * lda);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int kk = std::min(k0 + 4 * kb + i, t.kend - 1);
-          v[i] = *reinterpret_cast<const u32x4*>(km_a + static_cast<int64_t>(t.off + kk) * lda);
-        }
-      }
-    } else {
-      const bool second = k0 >= t.K;
-      const uint16_t* base = (second ? A2 : A) + (second ? k0 - t.K : k0);
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int ch = (tid + kTh * p) & 7;
-        v[p] = *reinterpret_cast<const u32x4*>(base + a_row[p] + 8 * ch);
-      }
+    for (int p = 0; p < 4; ++p) {
+      const int ch = (tid + kTh * p) & 7;
+      v[p] = *reinterpret_cast<const u32x4*>(base + a_row[p] + 8 * ch);
     }
   };
   auto load_b = [&](const Unit& t, int kt, u32x4 (&v)[4]) {
-    const int k0 = t.kbeg + kt * kTK;
-    if constexpr (kWgrad) {
-      if (k0 + kTK <= t.kend) {
-        const uint16_t* p = km_b_row + static_cast<int64_t>(kt) * kTK * ldb;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const u32x4*>(p + i * ldb);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int kk = std::min(k0 + 4 * kb + i, t.kend - 1);
-          v[i] = *reinterpret_cast<const u32x4*>(B + static_cast<int64_t>(t.off + kk) * ldb + km_b_col);
-        }
-      }
-    } else if constexpr (kDgrad) {
+    const int k0 = kt * kTK;
+    if constexpr (kDgrad) {
       // a weight stored [K, N] (+ b2 for the K2 rows after K)
       const bool second = k0 >= t.K;
       const uint16_t* base = (second ? B2 : B) + bgs +
@@ -328,7 +251,7 @@ __global__ __launch_bounds__(kTh, 2) void bwd_gemm_kernel(BwdGemmArgs a) {
   auto store_km = [&](u32x4* buf, const u32x4 (&v)[4], bool col_ok, const Unit& t, int kt) {
     // column j of the 8 loaded: values of K 4 kb .. 4 kb + 3 -> 8 bytes of
     // chunk kb / 2 of staged row 8 cb + j
-    const int krow = t.kbeg + kt * kTK + 4 * kb;
+    const int krow = kt * kTK + 4 * kb;
     u32x4 z[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) z[i] = col_ok && krow + i < t.kend ? v[i] : zero4;
@@ -347,10 +270,7 @@ __global__ __launch_bounds__(kTh, 2) void bwd_gemm_kernel(BwdGemmArgs a) {
       *dst = make_uint2(lo, hi);
     }
   };
-  auto store_a = [&](u32x4* buf, const u32x4 (&v)[4], const Unit& t, int kt) {
-    if constexpr (kWgrad) store_km(buf, v, km_a_ok, t, kt);
-    else store_kc(buf, v, a_ok);
-  };
+  auto store_a = [&](u32x4* buf, const u32x4 (&v)[4], const Unit&, int) { store_kc(buf, v, a_ok); };
   auto store_b = [&](u32x4* buf, const u32x4 (&v)[4], const Unit& t, int kt) {
     if constexpr (kPair) store_kc(buf, v, b_ok);
     else store_km(buf, v, km_b_ok, t, kt);
@@ -459,61 +379,6 @@ __global__ __launch_bounds__(kTh, 2) void bwd_gemm_kernel(BwdGemmArgs a) {
                 make_uint2(bf16x2_bits(v[4 * q], v[4 * q + 1]), bf16x2_bits(v[4 * q + 2], v[4 * q + 3]));
           }
       }
-    }
-    if constexpr (kWgrad) {
-      // through LDS, so that a store instruction writes whole rows of 256
-      // bytes: this wave's 64 x 64 outputs as 64 rows of 16 chunks of four
-      // values, chunk c of row r at (c ^ (r & 15)); no other wave reads them
-      u32x4* stg = lds[wave];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int rr = 32 * i + fr, ch = 8 * j + 2 * q + fhalf;
-            const f32x16& v = acc[i][j];
-            stg[rr * 16 + (ch ^ (rr & 15))] =
-                u32x4{__float_as_uint(v[4 * q]), __float_as_uint(v[4 * q + 1]),
-                      __float_as_uint(v[4 * q + 2]), __float_as_uint(v[4 * q + 3])};
-          }
-      // M, N and M1 are multiples of 64: a wave's 64 x 64 block lies wholly
-      // inside or outside them, on one side of M1
-      const int rw = t.m0 + 64 * wm, cw = t.n0 + 64 * wn;
-      if (rw < t.M && cw < t.N) {
-        float* base;
-        int64_t ld;
-        if (t.nsplit > 1) {
-          const int slot = uni(pslot[t.gg]) - (t.sg ? seg1_slot0 : 0) + t.split_idx;
-          base = SEGF(t.sg, part) + (static_cast<int64_t>(slot) * t.M + rw) * t.N + cw;
-          ld = t.N;
-        } else {
-          const int M1 = SEGF(t.sg, M1);
-          const bool first = rw < M1;
-          base = static_cast<float*>(first ? SEGF(t.sg, c) : SEGF(t.sg, c2)) +
-                 static_cast<int64_t>(t.g) * SEGF(t.sg, c_gstride) +
-                 static_cast<int64_t>(first ? rw : rw - M1) * SEGF(t.sg, ldc) + cw;
-          ld = SEGF(t.sg, ldc);
-        }
-        u32x4* out = reinterpret_cast<u32x4*>(base + (lane >> 4) * ld + 4 * (lane & 15));
-        const int64_t step4 = ld;  // four rows of fp32, in u32x4
-        if (t.nsplit > 1) {
-          // partial sums: read back by wgrad_reduce_kernel, kept in L2
-#pragma unroll
-          for (int it = 0; it < 16; ++it) {
-            const int rr = 4 * it + (lane >> 4);
-            out[it * step4] = stg[rr * 16 + ((lane & 15) ^ (rr & 15))];
-          }
-        } else {
-          // final gradients: streamed past L2, which keeps the operands
-#pragma unroll
-          for (int it = 0; it < 16; ++it) {
-            const int rr = 4 * it + (lane >> 4);
-            __builtin_nontemporal_store(stg[rr * 16 + ((lane & 15) ^ (rr & 15))], out + it * step4);
-          }
-        }
-      }
-      __syncthreads();  // the staging is the next unit's first stage
     }
   };
 
