@@ -240,12 +240,20 @@ __global__ __launch_bounds__(C::kAllThreads, C::BPC) void grouped_gemm_kernel(Gr
     int a_off[LA];                        // per thread, bytes (kOutOfRange: no row)
     int b_row[LB];                        // uniform, bytes: weight row base of each pass
     int b_thr;                            // per thread, bytes
+    int rot;                              // K-step the unit starts at (down stage of the streaming tile)
     int nk;                               // K-steps with data
     int rows;                             // valid A rows of the unit
   };
   // Above any descriptor range (ranges are clamped to 2^31 - 1 bytes); offsets
   // are advanced in unsigned arithmetic, so they stay out of range.
   constexpr unsigned kOutOfRange = 0x80000000u;
+  // Down stage of the streaming tile: each unit starts its K loop at its own
+  // step (and wraps round), so that units running together read different
+  // column offsets of their 4 KB weight rows (prefill down stage 1553 ->
+  // 1520 us; rotating the SwiGLU stage's 14 KB rows gained nothing).  The
+  // sums run in another order, so y differs from the unrotated kernel's in
+  // rounding.
+  constexpr bool kRotK = !kSwiGLU && C::PW > 0 && !C::DMAA;
   int pend_row[LA];  // prepared unit: group row / token per thread row
   int pend_map[LA];   // prepared unit: perm_src[pend_row] when gathering (in flight)
   int map_ready[LA];  // the same values once landed (see settle)
@@ -322,6 +330,7 @@ __global__ __launch_bounds__(C::kAllThreads, C::BPC) void grouped_gemm_kernel(Gr
     const int b_chunk = C::DMAB ? (ld_chunk ^ ((ld_row >> 1) & (kChunksPerRow - 1))) : ld_chunk;
     sr.b_thr = (ld_row * K + b_chunk * 8) * 2;
     sr.nk = pu.nk;
+    sr.rot = kRotK ? (pu.n0 / C::BW + 3 * pu.g) % pu.nk : 0;
     return sr;
   };
   auto source_of_pending = [&]() __attribute__((always_inline)) {
@@ -347,7 +356,9 @@ __global__ __launch_bounds__(C::kAllThreads, C::BPC) void grouped_gemm_kernel(Gr
     const bool nxt = f >= steps0;
     const int j = nxt ? f - steps0 : f;
     const int nk = nxt ? c1.nk : c0.nk;
-    const int kb = (j < nk ? j : nk - 1) * (kBK * 2);
+    int kj = (j < nk ? j : nk - 1) + (nxt ? c1.rot : c0.rot);
+    if (kj >= nk) kj -= nk;
+    const int kb = kj * (kBK * 2);
     const __amdgpu_buffer_rsrc_t ra = nxt ? c1.ra : c0.ra;
     const __amdgpu_buffer_rsrc_t rb0 = nxt ? c1.rb0 : c0.rb0;
     const __amdgpu_buffer_rsrc_t rb1 = nxt ? c1.rb1 : c0.rb1;

@@ -395,12 +395,27 @@ __global__ __launch_bounds__(256) void router_scores_mfma_kernel(
     const float* wr = &wt[c & 1][lane * kMfRow];                      // B: expert lane
     const bool more = c + 1 < nch;
     const int nb = (c + 1) & 1;  // the buffers step c - 1 read
+    // operands of 16 indices of d per group, read one group ahead so that
+    // the LDS latency hides behind the previous group's MFMA chain
+    float4 xa[2][4], wa[2][4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      xa[0][q] = *reinterpret_cast<const float4*>(xr + 4 * q);
+      wa[0][q] = *reinterpret_cast<const float4*>(wr + 4 * q);
+    }
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
+      const int cb = g & 1;
+      if (g + 1 < 8) {
 #pragma unroll
-      for (int k = 16 * g; k < 16 * g + 16; k += 4) {
-        const float4 a4 = *reinterpret_cast<const float4*>(xr + k);
-        const float4 b4 = *reinterpret_cast<const float4*>(wr + k);
+        for (int q = 0; q < 4; ++q) {
+          xa[cb ^ 1][q] = *reinterpret_cast<const float4*>(xr + 16 * (g + 1) + 4 * q);
+          wa[cb ^ 1][q] = *reinterpret_cast<const float4*>(wr + 16 * (g + 1) + 4 * q);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 a4 = xa[cb][q], b4 = wa[cb][q];
         acc = __builtin_amdgcn_mfma_f32_16x16x1f32(a4.x, b4.x, acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x1f32(a4.y, b4.y, acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_16x16x1f32(a4.z, b4.z, acc, 0, 0, 0);
