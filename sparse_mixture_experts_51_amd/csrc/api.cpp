@@ -474,19 +474,35 @@ moe_status moe_grouped_ffn_backward(const moe_shape* shape, const uint16_t* x,
         q.c = is_sh(i) ? w.dhs : w.dh; q.ldc = Hh;
       },
       moe::kBwdDgradKM);
-  // a, c = x W1^T, x W3^T -> h, da, dc
-  if (e == hipSuccess)
-    e = launch(
-        [&](moe::BwdSeg& q, int i) {
-          const int Hh = seg_h(i);
-          q.N = Hh; q.K = d;
-          q.a = is_sh(i) ? x : x_perm; q.lda = d;
-          q.b = is_sh(i) ? ws1 : w1; q.b2 = is_sh(i) ? ws3 : w3; q.ldb = d;
-          q.b_gstride = is_sh(i) ? 0 : static_cast<int64_t>(H) * d;
-          q.dh = is_sh(i) ? w.dhs : w.dh; q.h = is_sh(i) ? w.hs : w.h;
-          q.da = is_sh(i) ? w.das : w.da; q.dc = is_sh(i) ? w.dcs : w.dc; q.ld_h = Hh;
-        },
-        moe::kBwdRecompute);
+  // a, c = x W1^T, x W3^T again -> h, da, dc: the forward's SwiGLU GEMM (same
+  // tiles and sums, so h is the forward's) with the backward epilogue
+  if (e == hipSuccess) {
+    moe::GroupedGemmArgs g{};
+    g.a_routed = x_perm;
+    g.a_shared = shared ? x : nullptr;
+    g.a_routed_bytes = 2 * static_cast<int64_t>(d) * T * shape->top_k;
+    g.a_shared_bytes = 2 * static_cast<int64_t>(d) * T;
+    g.w_routed = w1;
+    g.w3_routed = w3;
+    g.w_shared = shared ? ws1 : nullptr;
+    g.w3_shared = shared ? ws3 : nullptr;
+    g.c_routed = w.h;
+    g.c_shared = shared ? w.hs : nullptr;
+    g.offsets = offsets;
+    g.T = T;
+    g.E = E;
+    g.top_k = shape->top_k;
+    g.K_r = g.K_s = d;
+    g.N_r = H;
+    g.N_s = Hs;
+    g.dh_routed = w.dh;
+    g.dh_shared = shared ? w.dhs : nullptr;
+    g.da_routed = w.da;
+    g.da_shared = shared ? w.das : nullptr;
+    g.dc_routed = w.dc;
+    g.dc_shared = shared ? w.dcs : nullptr;
+    e = moe::launch_gemm_swiglu_bwd(g, s);
+  }
   // dx = da W1 + dc W3  (W1, W3 [H, d] read as [K, N])
   if (e == hipSuccess)
     e = launch(

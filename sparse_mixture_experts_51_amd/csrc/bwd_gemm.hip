@@ -6,7 +6,9 @@
 // (moe_combine_backward), every product of an expert's backward is a GEMM over
 // contiguous rows, one per expert group:
 //   dh   = dy W2                      rows x H,  K = d        (input gradient)
-//   a, c = x W1^T, x W3^T  -> da, dc, h (SwiGLU derivative in the epilogue)
+//   a, c = x W1^T, x W3^T  -> da, dc, h (the forward's SwiGLU GEMM again,
+//                                         grouped_gemm.hip, with the SwiGLU
+//                                         derivative in its epilogue)
 //   dx   = da W1 + dc W3               rows x d,  K = 2H       (input gradient)
 //   dW2  = dy^T h                      d x H,     K = rows     (weight gradient)
 //   dW1  = da^T x,  dW3 = dc^T x       2H x d,    K = rows     (one launch)
@@ -17,7 +19,7 @@
 // a zero weight gradient.  One launch covers the shared expert (one group of
 // all T rows, its own operands) and the routed experts.
 //
-// Input gradients and the recompute (bwd_gemm_kernel): tile 128 x 128 x 64,
+// Input gradients (bwd_gemm_kernel): tile 128 x 128 x 64,
 // four waves of 64 x 64 (2 x 2 MFMA tiles of 32x32x16, fp32 accumulators),
 // two blocks per CU, persistent over units (group, m-tile, n-tile); each XCD
 // runs an eighth of the units in order, so the units of one group share its
@@ -25,7 +27,7 @@
 // four 16-byte loads per thread, along the contiguous direction.  Both layouts
 // are staged in LDS the same way, a row of the tile (an M or N index) holding
 // its 64 K values as eight 16-byte chunks, so every MFMA fragment is one
-// 16-byte LDS read.  A K-major operand (the weight of dh and dx) gets there
+// 16-byte LDS read.  The K-major operand (the weight of dh and dx) gets there
 // through a transpose in registers: a thread loads 4 rows of K x 8 columns
 // and writes 8 columns x 4 values of K (8 bytes each).  The chunk order within
 // a row is XOR-swizzled with bits 1-3 of the row (chunk ^ (row >> 1) ^
@@ -87,10 +89,8 @@ __global__ __launch_bounds__(kTh, 2) void bwd_gemm_kernel(BwdGemmArgs a) {
   __shared__ int ustart[kMaxG + 1];  // first unit of each group
   __shared__ int goff[kMaxG + 1];    // first row of each group in its segment's arrays
   __shared__ int wsum[kTh / 64];
-  constexpr bool kDgrad = KIND == kBwdDgradKM;
-  constexpr bool kPair = KIND == kBwdRecompute;  // B rows [0,64) from b, [64,128) from b2
-  static_assert(KIND == kBwdDgradKM || KIND == kBwdRecompute, "input gradients and the recompute");
-  constexpr int kCols = kPair ? kTN / 2 : kTN;   // output columns per unit
+  static_assert(KIND == kBwdDgradKM, "input gradients");
+  constexpr int kCols = kTN;                     // output columns per unit
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uni(tid >> 6);
@@ -178,8 +178,6 @@ __global__ __launch_bounds__(kTh, 2) void bwd_gemm_kernel(BwdGemmArgs a) {
   int64_t lda = 0, ldb = 0, bgs = 0;
   int a_row[4];                    // K-contiguous A: element offset of the row
   bool a_ok[4];                    // ... inside the group
-  const uint16_t* kc_b[4];         // recompute B: weight row pointers
-  bool b_ok[4];                    // ... inside N
   int km_b_col = 0;                // K-major B: first column
   bool km_b_ok = false;
   auto setup = [&](const Unit& t) {
@@ -196,19 +194,8 @@ __global__ __launch_bounds__(kTh, 2) void bwd_gemm_kernel(BwdGemmArgs a) {
       a_ok[p] = t.m0 + row < t.R;
       a_row[p] = (t.off + (a_ok[p] ? t.m0 + row : t.m0)) * static_cast<int>(lda);
     }
-    if constexpr (kPair) {
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int row = (tid + kTh * p) >> 3;
-        const int wrow = t.n0 + (row & (kCols - 1));
-        b_ok[p] = wrow < t.N;
-        kc_b[p] = (row < kCols ? B : B2) + bgs + static_cast<int64_t>(b_ok[p] ? wrow : t.n0) * ldb;
-      }
-    }
-    if constexpr (kDgrad) {
-      km_b_ok = t.n0 + 8 * cb < t.N;
-      km_b_col = km_b_ok ? t.n0 + 8 * cb : t.n0;
-    }
+    km_b_ok = t.n0 + 8 * cb < t.N;
+    km_b_col = km_b_ok ? t.n0 + 8 * cb : t.n0;
   };
 
   // ---- loads of K-step kt (16-byte chunks)
@@ -223,21 +210,13 @@ __global__ __launch_bounds__(kTh, 2) void bwd_gemm_kernel(BwdGemmArgs a) {
     }
   };
   auto load_b = [&](const Unit& t, int kt, u32x4 (&v)[4]) {
+    // a weight stored [K, N] (+ b2 for the K2 rows after K)
     const int k0 = kt * kTK;
-    if constexpr (kDgrad) {
-      // a weight stored [K, N] (+ b2 for the K2 rows after K)
-      const bool second = k0 >= t.K;
-      const uint16_t* base = (second ? B2 : B) + bgs +
-                             static_cast<int64_t>((second ? k0 - t.K : k0) + 4 * kb) * ldb + km_b_col;
+    const bool second = k0 >= t.K;
+    const uint16_t* base = (second ? B2 : B) + bgs +
+                           static_cast<int64_t>((second ? k0 - t.K : k0) + 4 * kb) * ldb + km_b_col;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const u32x4*>(base + i * ldb);
-    } else {
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int ch = (tid + kTh * p) & 7;
-        v[p] = *reinterpret_cast<const u32x4*>(kc_b[p] + k0 + 8 * ch);
-      }
-    }
+    for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const u32x4*>(base + i * ldb);
   };
   // ---- stores of a loaded K-step into a stage (out-of-range chunks as zero)
   const u32x4 zero4 = u32x4{0u, 0u, 0u, 0u};
@@ -272,13 +251,12 @@ __global__ __launch_bounds__(kTh, 2) void bwd_gemm_kernel(BwdGemmArgs a) {
   };
   auto store_a = [&](u32x4* buf, const u32x4 (&v)[4], const Unit&, int) { store_kc(buf, v, a_ok); };
   auto store_b = [&](u32x4* buf, const u32x4 (&v)[4], const Unit& t, int kt) {
-    if constexpr (kPair) store_kc(buf, v, b_ok);
-    else store_km(buf, v, km_b_ok, t, kt);
+    store_km(buf, v, km_b_ok, t, kt);
   };
 
   f32x16 acc[2][2];
   auto arow = [&](int i) { return 64 * wm + 32 * i + fr; };
-  auto brow = [&](int j) { return (kPair ? (j == 0 ? 32 * wn : kCols + 32 * wn) : 64 * wn + 32 * j) + fr; };
+  auto brow = [&](int j) { return 64 * wn + 32 * j + fr; };
   auto compute = [&](const u32x4* sa, const u32x4* sb) {
 #pragma unroll
     for (int ks = 0; ks < kTK / 16; ++ks) {
@@ -313,72 +291,22 @@ __global__ __launch_bounds__(kTh, 2) void bwd_gemm_kernel(BwdGemmArgs a) {
     }
   };
   const int lcol = fhalf * 4;
-  // recompute epilogue: dh of this lane's outputs, read before the next
-  // unit's loads are issued
-  uint2 dhv[2][4];
-  auto epilogue_loads = [&](const Unit& t) {
-    if constexpr (kPair) {
-      const int64_t ldh = SEGF(t.sg, ld_h);
-      const uint16_t* dhp = SEGF(t.sg, dh);
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int r = std::min(t.m0 + 64 * wm + 32 * i + fr, t.R - 1);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = std::min(t.n0 + 32 * wn + 8 * q + lcol, t.N - 4);
-          dhv[i][q] = *reinterpret_cast<const uint2*>(dhp + static_cast<int64_t>(t.off + r) * ldh + col);
-        }
-      }
-    }
-  };
   auto epilogue = [&](const Unit& t) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int r = t.m0 + 64 * wm + 32 * i + fr;  // output row (within the group for input gradients)
-      if constexpr (kPair) {
-        if (r >= t.R) continue;
-        const int64_t row = static_cast<int64_t>(t.off + r);
-        const int64_t ldh = SEGF(t.sg, ld_h);
-        uint16_t* hp = SEGF(t.sg, h);
-        uint16_t* dap = SEGF(t.sg, da);
-        uint16_t* dcp = SEGF(t.sg, dc);
+      const int r = t.m0 + 64 * wm + 32 * i + fr;  // output row within the group
+      if (r >= t.R) continue;
+      uint16_t* crow = static_cast<uint16_t*>(SEGF(t.sg, c)) + static_cast<int64_t>(t.off + r) * SEGF(t.sg, ldc);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int col = t.n0 + 32 * wn + 8 * q + lcol;
+          const int col = t.n0 + 64 * wn + 32 * j + 8 * q + lcol;
           if (col >= t.N) continue;
-          const uint2 dv = dhv[i][q];
-          const float dhf[4] = {bf16_to_f32(static_cast<uint16_t>(dv.x)), bf16_to_f32(static_cast<uint16_t>(dv.x >> 16)),
-                                bf16_to_f32(static_cast<uint16_t>(dv.y)), bf16_to_f32(static_cast<uint16_t>(dv.y >> 16))};
-          float hv[4], dav[4], dcv[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float ga = acc[i][0][4 * q + e], up = acc[i][1][4 * q + e];
-            const float sgm = __builtin_amdgcn_rcpf(1.0f + __expf(-ga));
-            hv[e] = ga * sgm * up;  // the forward's h, bit for bit
-            dav[e] = dhf[e] * up * sgm * (1.0f + ga * (1.0f - sgm));
-            dcv[e] = dhf[e] * ga * sgm;
-          }
-          auto pack4 = [](const float (&f)[4]) {
-            return make_uint2(bf16x2_bits(f[0], f[1]), bf16x2_bits(f[2], f[3]));
-          };
-          *reinterpret_cast<uint2*>(hp + row * ldh + col) = pack4(hv);
-          *reinterpret_cast<uint2*>(dap + row * ldh + col) = pack4(dav);
-          *reinterpret_cast<uint2*>(dcp + row * ldh + col) = pack4(dcv);
+          const f32x16& v = acc[i][j];
+          *reinterpret_cast<uint2*>(crow + col) =
+              make_uint2(bf16x2_bits(v[4 * q], v[4 * q + 1]), bf16x2_bits(v[4 * q + 2], v[4 * q + 3]));
         }
-      } else if constexpr (kDgrad) {
-        if (r >= t.R) continue;
-        uint16_t* crow = static_cast<uint16_t*>(SEGF(t.sg, c)) + static_cast<int64_t>(t.off + r) * SEGF(t.sg, ldc);
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int col = t.n0 + 64 * wn + 32 * j + 8 * q + lcol;
-            if (col >= t.N) continue;
-            const f32x16& v = acc[i][j];
-            *reinterpret_cast<uint2*>(crow + col) =
-                make_uint2(bf16x2_bits(v[4 * q], v[4 * q + 1]), bf16x2_bits(v[4 * q + 2], v[4 * q + 3]));
-          }
-      }
     }
   };
 
@@ -426,7 +354,6 @@ __global__ __launch_bounds__(kTh, 2) void bwd_gemm_kernel(BwdGemmArgs a) {
       if (kt + 1 < cur.nk) step(std::integral_constant<int, 1>{}, kt + 1);
     }
     // the next unit's first loads go out before this unit's stores
-    epilogue_loads(cur);
     const int un = u + per_xcd;
     const bool have_next = un < u_hi;
     Unit nxt{};
@@ -926,9 +853,6 @@ hipError_t launch_bwd_gemm(const BwdGemmArgs& a, int kind, hipStream_t s) {
   switch (kind) {
     case kBwdDgradKM:
       hipLaunchKernelGGL(bwd_gemm_kernel<kBwdDgradKM>, gd, bd, 0, s, a);
-      break;
-    case kBwdRecompute:
-      hipLaunchKernelGGL(bwd_gemm_kernel<kBwdRecompute>, gd, bd, 0, s, a);
       break;
     case kBwdWgrad: {
       hipLaunchKernelGGL(wgrad_kernel, gd, dim3(kWgThreads), 0, s, a);

@@ -153,8 +153,9 @@ __device__ __forceinline__ Unit decode_unit(const GroupedGemmArgs& a, const int*
   return r;
 }
 
-template <class C, bool kSwiGLU>
+template <class C, bool kSwiGLU, bool kBwd = false>
 __global__ __launch_bounds__(C::kAllThreads, C::BPC) void grouped_gemm_kernel(GroupedGemmArgs a) {
+  static_assert(!kBwd || kSwiGLU, "the backward epilogue is the SwiGLU stage's");
   constexpr int kThreads = C::kThreads, RPP = C::kRowsPerPass;
   constexpr int LA = C::kLoadsA, LB = C::kLoadsB, TM = C::TM, TN = C::TN;
   __shared__ u32x4 lds_a[C::NSA][C::BM * kChunksPerRow];  // buffers or DMA stages
@@ -610,6 +611,58 @@ __global__ __launch_bounds__(C::kAllThreads, C::BPC) void grouped_gemm_kernel(Gr
   static_assert(kPassRows > 0 && C16 >= 8 && (C16 & (C16 - 1)) == 0, "output staging layout");
   auto epilogue = [&](const Unit& cu, int mrows, int fa, int fb) __attribute__((always_inline)) {
     uint16_t* cbase = cu.routed ? a.c_routed : a.c_shared;
+    if constexpr (kBwd) {
+      // Backward: each lane's quads straight from the accumulators -- dh
+      // read, h (the forward's, bit for bit), da = dh up s (1 + a (1 - s))
+      // and dc = dh a s (s = sigmoid(a)) written as 8-byte words -- with the
+      // staging form's two barriers per pass, which the loader waves count.
+      const uint16_t* dhp = cu.routed ? a.dh_routed : a.dh_shared;
+      uint16_t* dap = cu.routed ? a.da_routed : a.da_shared;
+      uint16_t* dcp = cu.routed ? a.dc_routed : a.dc_shared;
+      MOE_FOR(p, kPasses, {
+        const int r_lo = p * kPassRows;
+        MOE_FOR(i, TM, {
+          const int r_tile = tile_row(i) - r_lo;
+          if (i < mrows && r_tile >= 0 && r_tile < kPassRows) {
+            const int rr = tile_row(i) + lrow;  // row of the unit
+            const bool row_ok = rr < cu.valid_rows;
+            const int64_t base = (static_cast<int64_t>(cu.orow0) + (row_ok ? rr : 0)) * cu.N;
+            MOE_FOR(j, TN / 2, {
+              const int col0 = cu.n0 + wn * HC + 32 * j + lcol;
+              uint2 dv[4];
+              MOE_FOR(g, 4, {
+                const int col = col0 + 8 * g;
+                dv[g] = *reinterpret_cast<const uint2*>(dhp + base + (col < cu.N ? col : cu.N - 4));
+              })
+              MOE_FOR(g, 4, {
+                const int col = col0 + 8 * g;
+                if (row_ok && col < cu.N) {
+                  const uint32_t dw[2] = {dv[g].x, dv[g].y};
+                  float hv[4], dav[4], dcv[4];
+                  MOE_FOR(t, 4, {
+                    const float ga = acc[i][j][4 * g + t], up = acc[i][j + TN / 2][4 * g + t];
+                    const float dhf = __uint_as_float((t & 1 ? dw[t >> 1] >> 16 : dw[t >> 1] & 0xFFFFu) << 16);
+                    const float sgm = __builtin_amdgcn_rcpf(1.0f + __expf(-ga));
+                    hv[t] = ga * sgm * up;
+                    dav[t] = dhf * up * sgm * (1.0f + ga * (1.0f - sgm));
+                    dcv[t] = dhf * ga * sgm;
+                  })
+                  auto pack = [](const float (&f)[4]) __attribute__((always_inline)) {
+                    return make_uint2(bf16x2_bits(f[0], f[1]), bf16x2_bits(f[2], f[3]));
+                  };
+                  *reinterpret_cast<uint2*>(cbase + base + col) = pack(hv);
+                  *reinterpret_cast<uint2*>(dap + base + col) = pack(dav);
+                  *reinterpret_cast<uint2*>(dcp + base + col) = pack(dcv);
+                }
+              })
+            })
+          }
+        })
+        lds_barrier();
+        lds_barrier();
+      })
+      return;
+    }
     auto sw = [](int r) __attribute__((always_inline)) { return C16 >= 16 ? (r & 15) : ((r >> 1) & 7); };
     auto row_ptr = [&](int r) __attribute__((always_inline)) {
       return r < kRowsA ? reinterpret_cast<unsigned char*>(&lds_a[fa][0]) + r * RB
@@ -924,17 +977,17 @@ static bool big_groups(const GroupedGemmArgs& a) {
   return a.T * a.top_k / (a.E > 0 ? a.E : 1) >= 512;
 }
 
-template <class C, bool kSwiGLU>
+template <class C, bool kSwiGLU, bool kBwd>
 static void launch_cfg(const GroupedGemmArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((grouped_gemm_kernel<C, kSwiGLU>), dim3(persistent_grid<C>()), dim3(C::kAllThreads),
-                     0, s, a);
+  hipLaunchKernelGGL((grouped_gemm_kernel<C, kSwiGLU, kBwd>), dim3(persistent_grid<C>()),
+                     dim3(C::kAllThreads), 0, s, a);
 }
 
-template <bool kSwiGLU>
+template <bool kSwiGLU, bool kBwd = false>
 static hipError_t launch_gemm(const GroupedGemmArgs& a, hipStream_t s) {
   if (streaming_shape(a)) {
     if (!a.w_shared) {
-      launch_cfg<kStream, kSwiGLU>(a, s);
+      launch_cfg<kStream, kSwiGLU, kBwd>(a, s);
       return hipGetLastError();
     }
     // The streaming tile would cover the shared expert's T rows in T / BM
@@ -946,7 +999,7 @@ static hipError_t launch_gemm(const GroupedGemmArgs& a, hipStream_t s) {
     routed.w_shared = routed.w3_shared = nullptr;
     routed.a_shared = nullptr;
     routed.c_shared = nullptr;
-    launch_cfg<kStream, kSwiGLU>(routed, s);
+    launch_cfg<kStream, kSwiGLU, kBwd>(routed, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     GroupedGemmArgs shared = a;  // one group: the shared expert's T rows
@@ -956,23 +1009,26 @@ static hipError_t launch_gemm(const GroupedGemmArgs& a, hipStream_t s) {
     shared.a_row_map = nullptr;
     shared.c_routed = nullptr;
     constexpr int kMinK = kBK * (kBigL::NSA - 1);
-    if (a.T >= 512 && a.K_s >= kMinK) launch_cfg<kBigL, kSwiGLU>(shared, s);
-    else launch_cfg<kCompute, kSwiGLU>(shared, s);
+    if (a.T >= 512 && a.K_s >= kMinK) launch_cfg<kBigL, kSwiGLU, kBwd>(shared, s);
+    else launch_cfg<kCompute, kSwiGLU, kBwd>(shared, s);
     return hipGetLastError();
   }
   // With long K the loader-wave form pays off (about 1024 rows per expert at
   // d = 7168, H = 2048: FFN 3.54 -> 3.39 ms, bit-identical); the mini model's
   // four to six K-steps per unit gain nothing from it.
   if (big_groups(a)) {
-    if (a.K_r >= kLongK && (!a.w_shared || a.K_s >= kLongK)) launch_cfg<kBigL, kSwiGLU>(a, s);
-    else launch_cfg<kBig, kSwiGLU>(a, s);
+    if (a.K_r >= kLongK && (!a.w_shared || a.K_s >= kLongK)) launch_cfg<kBigL, kSwiGLU, kBwd>(a, s);
+    else launch_cfg<kBig, kSwiGLU, kBwd>(a, s);
   } else {
-    launch_cfg<kCompute, kSwiGLU>(a, s);
+    launch_cfg<kCompute, kSwiGLU, kBwd>(a, s);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_swiglu(const GroupedGemmArgs& a, hipStream_t s) { return launch_gemm<true>(a, s); }
 hipError_t launch_gemm_down(const GroupedGemmArgs& a, hipStream_t s) { return launch_gemm<false>(a, s); }
+hipError_t launch_gemm_swiglu_bwd(const GroupedGemmArgs& a, hipStream_t s) {
+  return launch_gemm<true, true>(a, s);
+}
 
 }  // namespace moe

@@ -73,8 +73,19 @@ struct GroupedGemmArgs {
   int top_k;     // choices per token (tile configuration heuristic)
   int K_r, K_s;  // reduction lengths
   int N_r, N_s;  // output columns
+  // SwiGLU stage of the backward (launch_gemm_swiglu_bwd): dh in, c = h, and
+  // the derivatives da, dc out, all [rows, N] like c
+  const uint16_t* dh_routed;
+  const uint16_t* dh_shared;
+  uint16_t* da_routed;
+  uint16_t* da_shared;
+  uint16_t* dc_routed;
+  uint16_t* dc_shared;
 };
 hipError_t launch_gemm_swiglu(const GroupedGemmArgs& a, hipStream_t s);
+// The SwiGLU stage again in the backward: the same tiles, MFMA order and h
+// as the forward launch on the same shape, with h, da and dc written.
+hipError_t launch_gemm_swiglu_bwd(const GroupedGemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_down(const GroupedGemmArgs& a, hipStream_t s);
 
 hipError_t launch_combine(const uint16_t* y_perm, const uint16_t* y_shared, const float* gate,
@@ -103,18 +114,12 @@ struct BwdSeg {
   void* c2;                // wgrad: fp32 [groups][M - M1][N]
   int64_t ldc, c_gstride;
   float* part;             // wgrad with split: partial sums [slots][M][N]
-  const uint16_t* dh;      // recompute epilogue: dh in, h / da / dc out, rows [rows, N]
-  uint16_t* h;
-  uint16_t* da;
-  uint16_t* dc;
-  int64_t ld_h;
 };
 struct BwdGemmArgs {
   BwdSeg seg[2];
   int nseg;                // 1 or 2; the groups of seg[0] come first in the unit order
 };
 constexpr int kBwdDgradKM = 0;    // A K-contiguous, B stored [K, N], bf16 out
-constexpr int kBwdRecompute = 1;  // A K-contiguous, B = [W1; W3] rows [N, K], SwiGLU derivative out
 constexpr int kBwdWgrad = 2;      // both operands K-major rows, fp32 out
 hipError_t launch_bwd_gemm(const BwdGemmArgs& a, int kind, hipStream_t s);
 // Weight-gradient splits: rows per split (0: none) and the partial-sum slots
