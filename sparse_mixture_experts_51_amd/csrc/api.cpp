@@ -455,25 +455,52 @@ moe_status moe_grouped_ffn_backward(const moe_shape* shape, const uint16_t* x,
   }
   auto seg_h = [&](int i) { return shared && i == 0 ? Hs : H; };
   auto is_sh = [&](int i) { return shared && i == 0; };
-  auto launch = [&](auto&& fill, int kind) {
+  // all segments, or the shared expert's alone (nseg = 0: nothing to do)
+  auto launch = [&](auto&& fill, int kind, bool shared_only = false) {
     moe::BwdGemmArgs g{};
-    g.nseg = ns;
-    for (int i = 0; i < ns; ++i) {
+    g.nseg = shared_only ? (shared ? 1 : 0) : ns;
+    for (int i = 0; i < g.nseg; ++i) {
       g.seg[i] = base[i];
       fill(g.seg[i], i);
     }
-    return moe::launch_bwd_gemm(g, kind, s);
+    return g.nseg > 0 ? moe::launch_bwd_gemm(g, kind, s) : hipSuccess;
+  };
+  // Input gradients of the routed experts on the forward's streaming tile
+  // with K-major weights where the shape takes it (weight-streaming shapes);
+  // then the backward's own kernel for the rest.
+  auto routed_dgrad = [&](const uint16_t* ar, const uint16_t* ar2, const uint16_t* wr,
+                          const uint16_t* wr2, int K, int K2, int N, uint16_t* c, bool* done) {
+    moe::GroupedGemmArgs g{};
+    g.a_routed = ar;
+    g.a2_routed = ar2;
+    g.a_routed_bytes = 2 * static_cast<int64_t>(K) * T * shape->top_k;
+    g.w_routed = wr;
+    g.w3_routed = wr2;
+    g.c_routed = c;
+    g.offsets = offsets;
+    g.T = T;
+    g.E = E;
+    g.top_k = shape->top_k;
+    g.K_r = K;
+    g.K2_r = K2;
+    g.N_r = N;
+    const hipError_t r = moe::launch_gemm_dgrad(g, s);
+    *done = r == hipSuccess;
+    return r == hipErrorNotSupported ? hipSuccess : r;
   };
   // dh = dy W2  (W2 [d, H] read as [K, N])
-  hipError_t e = launch(
-      [&](moe::BwdSeg& q, int i) {
-        const int Hh = seg_h(i);
-        q.N = Hh; q.K = d;
-        q.a = is_sh(i) ? dout : dy_perm; q.lda = d;
-        q.b = is_sh(i) ? ws2 : w2; q.ldb = Hh; q.b_gstride = is_sh(i) ? 0 : static_cast<int64_t>(d) * H;
-        q.c = is_sh(i) ? w.dhs : w.dh; q.ldc = Hh;
-      },
-      moe::kBwdDgradKM);
+  bool dh_done = false;
+  hipError_t e = routed_dgrad(dy_perm, nullptr, w2, nullptr, d, 0, H, w.dh, &dh_done);
+  if (e == hipSuccess)
+    e = launch(
+        [&](moe::BwdSeg& q, int i) {
+          const int Hh = seg_h(i);
+          q.N = Hh; q.K = d;
+          q.a = is_sh(i) ? dout : dy_perm; q.lda = d;
+          q.b = is_sh(i) ? ws2 : w2; q.ldb = Hh; q.b_gstride = is_sh(i) ? 0 : static_cast<int64_t>(d) * H;
+          q.c = is_sh(i) ? w.dhs : w.dh; q.ldc = Hh;
+        },
+        moe::kBwdDgradKM, dh_done);
   // a, c = x W1^T, x W3^T again -> h, da, dc: the forward's SwiGLU GEMM (same
   // tiles and sums, so h is the forward's) with the backward epilogue
   if (e == hipSuccess) {
@@ -504,6 +531,8 @@ moe_status moe_grouped_ffn_backward(const moe_shape* shape, const uint16_t* x,
     e = moe::launch_gemm_swiglu_bwd(g, s);
   }
   // dx = da W1 + dc W3  (W1, W3 [H, d] read as [K, N])
+  bool dx_done = false;
+  if (e == hipSuccess) e = routed_dgrad(w.da, w.dc, w1, w3, H, H, d, dx_perm, &dx_done);
   if (e == hipSuccess)
     e = launch(
         [&](moe::BwdSeg& q, int i) {
@@ -514,7 +543,7 @@ moe_status moe_grouped_ffn_backward(const moe_shape* shape, const uint16_t* x,
           q.b_gstride = is_sh(i) ? 0 : static_cast<int64_t>(H) * d;
           q.c = is_sh(i) ? dx_shared : dx_perm; q.ldc = d;
         },
-        moe::kBwdDgradKM);
+        moe::kBwdDgradKM, dx_done);
   // dW2 = dy^T h, then [dW1; dW3] = [da dc]^T x  (K = the group's rows)
   const WgradPlans wp = wgrad_plans(shape);
   if (e == hipSuccess)

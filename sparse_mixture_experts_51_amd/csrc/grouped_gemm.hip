@@ -112,17 +112,40 @@ __device__ __forceinline__ int swz(int row, int chunk) {
   return row * kChunksPerRow + (chunk ^ ((row >> 1) & (kChunksPerRow - 1)));
 }
 
+// Two MFMA fragments of a K-major tile (rows of K, 512 bytes apart), read
+// transposed by ds_read_b64_tr_b16: within each 16 lanes, lane s names 4
+// values of row s / 4 and receives 4 consecutive rows of one column, so a
+// fragment's 8 values of K are two reads, the second 4 rows further.
+// Complete on return (the wait is in the asm).
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+template <int kOff>
+__device__ __forceinline__ void tr_read2(unsigned a0, unsigned a1, bf16x8& f0, bf16x8& f1) {
+  v4i16 r[4];
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4 offset:%6\n\t"
+      "ds_read_b64_tr_b16 %1, %4 offset:%7\n\t"
+      "ds_read_b64_tr_b16 %2, %5 offset:%6\n\t"
+      "ds_read_b64_tr_b16 %3, %5 offset:%7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+      : "v"(a0), "v"(a1), "i"(kOff), "i"(kOff + 4 * 512)
+      : "memory");
+  f0 = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r[0], r[1], 0, 1, 2, 3, 4, 5, 6, 7));
+  f1 = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r[2], r[3], 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // Wave-uniform description of one unit (held in scalar registers).
 struct Unit {
   int g;           // group (E = shared)
   int valid_rows;  // rows of this m-tile that exist
   int n0;          // first output column
   int K, N, nk;
+  int nk1;         // K-major weights: K-steps of the first part (A, W; then A2, W3)
   int orow0;       // output row of the tile's first row
   int routed;      // 1: routed expert group, 0: shared expert
 };
 
-template <class C, bool kSwiGLU>
+template <class C, bool kSwiGLU, bool kWKM = false>
 __device__ __forceinline__ Unit decode_unit(const GroupedGemmArgs& a, const int* unit_start,
                                             const int* offs, int ngroups, int u) {
   // The group is the last one whose first unit is <= u (unit_start does not
@@ -148,14 +171,20 @@ __device__ __forceinline__ Unit decode_unit(const GroupedGemmArgs& a, const int*
   r.K = r.routed ? a.K_r : a.K_s;
   r.N = r.routed ? a.N_r : a.N_s;
   r.nk = r.K / kBK;
+  if constexpr (kWKM) {
+    r.nk1 = r.nk;
+    r.nk += a.K2_r / kBK;  // routed groups only
+  }
   r.n0 = n_tile * (kSwiGLU ? C::BW / 2 : C::BW);
   r.orow0 = uni(grow0 + m0);
   return r;
 }
 
-template <class C, bool kSwiGLU, bool kBwd = false>
+template <class C, bool kSwiGLU, bool kBwd = false, bool kWKM = false>
 __global__ __launch_bounds__(C::kAllThreads, C::BPC) void grouped_gemm_kernel(GroupedGemmArgs a) {
   static_assert(!kBwd || kSwiGLU, "the backward epilogue is the SwiGLU stage's");
+  // K-major weights: the streaming tile's plain-output form only
+  static_assert(!kWKM || (!kSwiGLU && C::PW > 0 && C::DMAB && !C::DMAA), "K-major weights");
   constexpr int kThreads = C::kThreads, RPP = C::kRowsPerPass;
   constexpr int LA = C::kLoadsA, LB = C::kLoadsB, TM = C::TM, TN = C::TN;
   __shared__ u32x4 lds_a[C::NSA][C::BM * kChunksPerRow];  // buffers or DMA stages
@@ -214,7 +243,7 @@ __global__ __launch_bounds__(C::kAllThreads, C::BPC) void grouped_gemm_kernel(Gr
   const int lb = static_cast<int>(static_cast<int64_t>(total_units) * ux / kXcds) + blockIdx.x / kXcds;
   if (lb >= uend) return;
   auto decode = [&](int u) __attribute__((always_inline)) {
-    return decode_unit<C, kSwiGLU>(a, unit_start, offs, ngroups, u);
+    return decode_unit<C, kSwiGLU, kWKM>(a, unit_start, offs, ngroups, u);
   };
 
   // loader thread geometry (the loader waves follow the MFMA waves)
@@ -238,6 +267,9 @@ __global__ __launch_bounds__(C::kAllThreads, C::BPC) void grouped_gemm_kernel(Gr
   // tiles of the next unit.
   struct Src {
     __amdgpu_buffer_rsrc_t ra, rb0, rb1;  // A rows; W1 (or W2) rows; W3 rows
+    __amdgpu_buffer_rsrc_t ra2;           // K-major weights: A rows of the second part
+    int nk1;                              // ... and the K-steps of the first part
+    int wkm_step;                         // ... and the bytes of one step's 64 rows of K
     int a_off[LA];                        // per thread, bytes (kOutOfRange: no row)
     int b_row[LB];                        // uniform, bytes: weight row base of each pass
     int b_thr;                            // per thread, bytes
@@ -304,6 +336,15 @@ __global__ __launch_bounds__(C::kAllThreads, C::BPC) void grouped_gemm_kernel(Gr
         kSwiGLU ? (routed ? a.w3_routed + static_cast<int64_t>(g) * N * K : a.w3_shared) : w0;
     sr.rb0 = rsrc(w0, wbytes);
     sr.rb1 = rsrc(w1, wbytes);
+    if constexpr (kWKM) {
+      // [K, N] per group; the second part [K2, N] from w3_routed and a2_routed
+      const int K2 = a.K2_r;
+      sr.rb1 = rsrc(K2 > 0 ? a.w3_routed + static_cast<int64_t>(g) * N * K2 : w0,
+                    static_cast<int64_t>(N) * (K2 > 0 ? K2 : K) * 2);
+      sr.ra2 = rsrc(K2 > 0 ? a.a2_routed : a.a_routed, a.a_routed_bytes);
+      sr.nk1 = pu.nk1;
+      sr.wkm_step = kBK * N * 2;
+    }
     // A by DMA: lane l writes physical chunk l % 8 of its row, so it loads the
     // logical chunk the swizzle puts there (as for the weights below).
     const int a_chunk = C::DMAA ? (ld_chunk ^ ((ld_row >> 1) & (kChunksPerRow - 1))) : ld_chunk;
@@ -317,19 +358,33 @@ __global__ __launch_bounds__(C::kAllThreads, C::BPC) void grouped_gemm_kernel(Gr
     // weight tile: SwiGLU stage rows [0, BW/2) = W1[n0..], [BW/2, BW) = W3[n0..]
     // (each load pass lies in one half, so one descriptor per pass); down
     // stage rows [0, BW) = W2[n0..]
-    MOE_FOR(i, LB, {
-      constexpr int t0 = RPP * i;
-      int wrow = kSwiGLU ? n0 + t0 % (C::BW / 2) : n0 + t0;
-      if (wrow >= N) wrow = 0;
-      sr.b_row[i] = uni(wrow * K * 2);
-    })
-    // Register path: thread (ld_row, ld_chunk) loads that logical chunk and
-    // stores it swizzled.  DMA path: lane l of a wave writes physical slot
-    // l % 8 of row ld_row (8 rows per wave and pass), so it loads the logical
-    // chunk that the swizzle puts there (pass offsets are multiples of 64 rows
-    // and leave the swizzle unchanged).
-    const int b_chunk = C::DMAB ? (ld_chunk ^ ((ld_row >> 1) & (kChunksPerRow - 1))) : ld_chunk;
-    sr.b_thr = (ld_row * K + b_chunk * 8) * 2;
+    if constexpr (kWKM) {
+      // The stage holds the step's 64 rows of K x BW columns, 512 bytes per
+      // row of K, the row's 64-byte pieces p stored at p ^ (row & 3) (within
+      // each half row), which the transposing fragment reads need to meet
+      // every bank once.  Pass i of loader wave w is LDS block 4 i + w (1 KB):
+      // rows of K 2 (4 i + w) and + 1, lane l at row + (l >> 5), stored
+      // 16-byte chunk l & 31.  Pass offsets (uniform) go in the scalar offset.
+      const int kq = (2 * lwave + (lane >> 5)) & 3;  // that row & 3
+      const int sp = (lane & 31) >> 2;
+      const int col = 8 * (((sp ^ kq) << 2) | (lane & 3));
+      MOE_FOR(i, LB, { sr.b_row[i] = uni(2 * (4 * i + lwave) * N * 2); })
+      sr.b_thr = ((lane >> 5) * N + n0 + col) * 2;
+    } else {
+      MOE_FOR(i, LB, {
+        constexpr int t0 = RPP * i;
+        int wrow = kSwiGLU ? n0 + t0 % (C::BW / 2) : n0 + t0;
+        if (wrow >= N) wrow = 0;
+        sr.b_row[i] = uni(wrow * K * 2);
+      })
+      // Register path: thread (ld_row, ld_chunk) loads that logical chunk and
+      // stores it swizzled.  DMA path: lane l of a wave writes physical slot
+      // l % 8 of row ld_row (8 rows per wave and pass), so it loads the logical
+      // chunk that the swizzle puts there (pass offsets are multiples of 64 rows
+      // and leave the swizzle unchanged).
+      const int b_chunk = C::DMAB ? (ld_chunk ^ ((ld_row >> 1) & (kChunksPerRow - 1))) : ld_chunk;
+      sr.b_thr = (ld_row * K + b_chunk * 8) * 2;
+    }
     sr.nk = pu.nk;
     sr.rot = kRotK ? (pu.n0 / C::BW + 3 * pu.g) % pu.nk : 0;
     return sr;
@@ -359,11 +414,22 @@ __global__ __launch_bounds__(C::kAllThreads, C::BPC) void grouped_gemm_kernel(Gr
     const int nk = nxt ? c1.nk : c0.nk;
     int kj = (j < nk ? j : nk - 1) + (nxt ? c1.rot : c0.rot);
     if (kj >= nk) kj -= nk;
-    const int kb = kj * (kBK * 2);
-    const __amdgpu_buffer_rsrc_t ra = nxt ? c1.ra : c0.ra;
-    const __amdgpu_buffer_rsrc_t rb0 = nxt ? c1.rb0 : c0.rb0;
+    int kb = kj * (kBK * 2);
+    __amdgpu_buffer_rsrc_t ra = nxt ? c1.ra : c0.ra;
+    __amdgpu_buffer_rsrc_t rb0 = nxt ? c1.rb0 : c0.rb0;
     const __amdgpu_buffer_rsrc_t rb1 = nxt ? c1.rb1 : c0.rb1;
-    const int bt = (nxt ? c1.b_thr : c0.b_thr) + kb;
+    int bt = (nxt ? c1.b_thr : c0.b_thr) + kb;
+    int bk = 0;  // K-major weights: the step's rows of K, in the scalar offset
+    if constexpr (kWKM) {
+      const int nk1 = nxt ? c1.nk1 : c0.nk1;
+      const bool second = kj >= nk1;
+      const int kp = second ? kj - nk1 : kj;  // step within its part
+      kb = kp * (kBK * 2);
+      ra = second ? (nxt ? c1.ra2 : c0.ra2) : ra;
+      rb0 = second ? rb1 : rb0;
+      bt = nxt ? c1.b_thr : c0.b_thr;
+      bk = kp * (nxt ? c1.wkm_step : c0.wkm_step);
+    }
     sl.rows = nxt ? c1.rows : c0.rows;
     if constexpr (!C::DMAA) {
       MOE_FOR(i, LA, {
@@ -385,7 +451,7 @@ __global__ __launch_bounds__(C::kAllThreads, C::BPC) void grouped_gemm_kernel(Gr
         // FFN 4.71 -> 4.57 ms, bit-identical); the all-DMA tiles, whose
         // weights later m-tiles read again from L2, keep the default.
         dma_b128<kCachePolicyNT>(up ? rb1 : rb0, &lds_b[bstage][(RPP * i + 8 * lwave) * kChunksPerRow], bt,
-                                 br);
+                                 br + bk);
       } else {
         // non-temporal: each weight byte is read once per unit and never
         // again in the launch (decode FFN 3.19 -> 2.88 ms, bit-identical)
@@ -446,7 +512,16 @@ __global__ __launch_bounds__(C::kAllThreads, C::BPC) void grouped_gemm_kernel(Gr
         if (i < mrows)
           af[i] = __builtin_bit_cast(bf16x8, lds_a[buf][swz(tile_row(i) + fr, ch)]);
       })
-      if constexpr (C::DMAB) {
+      if constexpr (kWKM) {
+        // K-major weight stage (see source_of): fragment j of sub-step ks is
+        // rows 16 ks .. + 15 of its 32 columns, logical piece brow(j) / 32
+        const unsigned sb = static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_ptr_t)&lds_b[bstage][0]));
+        const unsigned base = sb + (8 * (lane >> 5) + ((lane & 15) >> 2)) * 512 +
+                              (16 * ((lane >> 4) & 1) + 4 * (lane & 3)) * 2;
+        const int rot = (lane & 15) >> 2;
+        tr_read2<ks * 16 * 512>(base + ((((brow(0) >> 5) ^ rot)) << 6), base + ((((brow(1) >> 5) ^ rot)) << 6),
+                                bfr[0], bfr[1]);
+      } else if constexpr (C::DMAB) {
         // The compiler would put a full vmcnt(0) before any LDS read of a
         // buffer that DMA writes, which drains the prefetched loads; vm_wait
         // already orders these reads after the DMA, so they are issued in asm.
@@ -977,9 +1052,9 @@ static bool big_groups(const GroupedGemmArgs& a) {
   return a.T * a.top_k / (a.E > 0 ? a.E : 1) >= 512;
 }
 
-template <class C, bool kSwiGLU, bool kBwd>
+template <class C, bool kSwiGLU, bool kBwd, bool kWKM = false>
 static void launch_cfg(const GroupedGemmArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((grouped_gemm_kernel<C, kSwiGLU, kBwd>), dim3(persistent_grid<C>()),
+  hipLaunchKernelGGL((grouped_gemm_kernel<C, kSwiGLU, kBwd, kWKM>), dim3(persistent_grid<C>()),
                      dim3(C::kAllThreads), 0, s, a);
 }
 
@@ -1029,6 +1104,15 @@ hipError_t launch_gemm_swiglu(const GroupedGemmArgs& a, hipStream_t s) { return 
 hipError_t launch_gemm_down(const GroupedGemmArgs& a, hipStream_t s) { return launch_gemm<false>(a, s); }
 hipError_t launch_gemm_swiglu_bwd(const GroupedGemmArgs& a, hipStream_t s) {
   return launch_gemm<true, true>(a, s);
+}
+// The streaming tile with K-major weights: routed groups only, whole weight
+// tiles (N a multiple of the tile's columns) and whole K-steps in each part.
+hipError_t launch_gemm_dgrad(const GroupedGemmArgs& a, hipStream_t s) {
+  if (!streaming_shape(a) || a.w_shared || a.N_r % kStream::BW || a.K_r % kBK || a.K2_r % kBK ||
+      (a.K2_r > 0 && (!a.w3_routed || !a.a2_routed)))
+    return hipErrorNotSupported;
+  launch_cfg<kStream, false, false, true>(a, s);
+  return hipGetLastError();
 }
 
 }  // namespace moe

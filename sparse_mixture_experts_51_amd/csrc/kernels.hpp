@@ -81,11 +81,20 @@ struct GroupedGemmArgs {
   uint16_t* da_shared;
   uint16_t* dc_routed;
   uint16_t* dc_shared;
+  // Input gradients (launch_gemm_dgrad): the weights are stored [K, N] (K
+  // major) -- w_routed [E][K_r][N_r], then K2_r more rows of K from w3_routed
+  // [E][K2_r][N_r] against the A rows of a2_routed (row stride K_r too)
+  const uint16_t* a2_routed;
+  int K2_r;
 };
 hipError_t launch_gemm_swiglu(const GroupedGemmArgs& a, hipStream_t s);
 // The SwiGLU stage again in the backward: the same tiles, MFMA order and h
 // as the forward launch on the same shape, with h, da and dc written.
 hipError_t launch_gemm_swiglu_bwd(const GroupedGemmArgs& a, hipStream_t s);
+// C = A W (+ A2 W3) with K-major weights, routed groups only, on the
+// streaming tile; hipErrorNotSupported for shapes it does not take (the
+// caller then uses the backward's own kernel).
+hipError_t launch_gemm_dgrad(const GroupedGemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_down(const GroupedGemmArgs& a, hipStream_t s);
 
 hipError_t launch_combine(const uint16_t* y_perm, const uint16_t* y_shared, const float* gate,
