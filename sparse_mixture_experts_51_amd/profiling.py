@@ -97,8 +97,8 @@ def traffic(fetch_dir: str, write_dir: str) -> dict:
         # one FFN call runs each grouped_gemm instance once (the SwiGLU and down
         # stages, each possibly split into a routed and a shared-expert launch):
         # per call, the mean dispatch of every instance, summed
-        gemm = {k: [v for _, v in lst] for k, lst in d.items() if "grouped_gemm" in k}
-        if not any("true>(" in k for k in gemm) or not any("false>(" in k for k in gemm):
+        gemm = {k: [v for _, v in lst] for k, lst in d.items() if _forward_gemm(k)}
+        if not any(gemm_flags(k)[0] for k in gemm) or not any(not gemm_flags(k)[0] for k in gemm):
             raise RuntimeError(f"no grouped_gemm dispatches in the {counter} run")
         kib = sum(sum(v) / len(v) for v in gemm.values())
         res[counter] = {"kib_per_launch": kib, "factor": factor, "bytes_per_launch": kib * 1024 * factor,
@@ -158,18 +158,35 @@ def _stats_by_kernel(stats_csv: str) -> dict:
     return {r["Name"]: (int(r["Calls"]), float(r["AverageNs"]) * 1e-9) for r in rows}
 
 
+def gemm_flags(name: str) -> tuple:
+    """(SwiGLU stage?, backward epilogue?, K-major weights?) of a
+    `grouped_gemm_kernel<TileCfg<...>, bool, bool, bool>` instance name."""
+    base = name.split("(")[0]
+    rest = base[base.index("TileCfg<"):]
+    rest = rest[rest.index(">") + 1:]
+    flags = [f.strip() == "true" for f in rest.replace(">", "").split(",") if f.strip()]
+    flags += [False] * (3 - len(flags))
+    return flags[0], flags[1], flags[2]
+
+
+def _forward_gemm(name: str) -> bool:
+    return "grouped_gemm" in name and not any(gemm_flags(name)[1:])
+
+
 def _mean_per_kernel(rows, counter) -> dict:
     d = _per_dispatch(rows, counter)
     return {k: sum(v for _, v in lst) / len(lst) for k, lst in d.items()}
 
 
 def short_name(name: str) -> str:
-    """`void moe::grouped_gemm_kernel<moe::TileCfg<192, 256, ...>, true>(...)`
-    -> `grouped_gemm_kernel<192x256, SwiGLU>`; other kernels keep their bare name."""
+    """`void moe::grouped_gemm_kernel<moe::TileCfg<192, 256, ...>, true, false, false>(...)`
+    -> `grouped_gemm_kernel<192x256, SwiGLU>` (the backward's instances: SwiGLU-bwd,
+    dgrad); other kernels keep their bare name."""
     base = name.split("(")[0].replace("void ", "").replace("moe::", "")
     if base.startswith("grouped_gemm_kernel"):
         cfg = base[base.index("TileCfg<") + 8:].split(">")[0].split(",")
-        stage = "SwiGLU" if base.rstrip(">").endswith("true") else "down"
+        swiglu, bwd, wkm = gemm_flags(base)
+        stage = ("SwiGLU-bwd" if bwd else "SwiGLU") if swiglu else ("dgrad" if wkm else "down")
         loaders = int(cfg[8]) if len(cfg) > 8 else 0
         tile = f"{cfg[0].strip()}x{cfg[1].strip()}" + (f"+{loaders}ldr" if loaders else "")
         return f"grouped_gemm_kernel<{tile}, {stage}>"
