@@ -66,6 +66,8 @@ def stats_markdown(stats_csv: str, command: str, title: str) -> str:
            "|---|---:|---:|---:|---:|---:|"]
     for r in rows:
         name = r["Name"].replace("|", "/")
+        if "grouped_gemm_kernel<" in name:
+            name = short_name(name)  # the template flags would be cut off below
         if len(name) > 90:
             name = name[:87] + "..."
         out.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
