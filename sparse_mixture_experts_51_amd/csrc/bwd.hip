@@ -156,53 +156,79 @@ __global__ __launch_bounds__(kBwdThreads) void dlogit_kernel(
 }
 
 // ---- dx = bf16( d_residual + dx_shared + sum_j dx_perm[pos] + dlogit W_r^T ).
-// A block computes a 64-token x 64-column tile: the router term as a small
-// fp32 GEMM over the experts (tiles of 16 experts staged in LDS), then adds
-// the expert rows.  Each thread holds 4 tokens x 4 columns.
-constexpr int kDxT = 64, kDxC = 64, kDxE = 16;
+// A block computes a 64-token x 64-column tile.  The router term is an fp32
+// GEMM over the experts on the matrix cores (v_mfma_f32_32x32x2_f32, each wave
+// a 32 x 32 quarter): tiles of 32 experts of dlogit and of W_r are staged in
+// LDS (a row per token or column, padded to 33 floats, so the 32 rows that a
+// fragment read touches fall on distinct banks); the next tile's loads are in
+// flight while the current one is multiplied.  The accumulators go through
+// LDS once more (over the staging space), and each thread then adds 4 tokens
+// x 4 columns of the expert rows to its sums.
+constexpr int kDxT = 64, kDxC = 64, kDxE = 32, kDxPad = kDxE + 1, kDxOut = kDxC + 4;
+constexpr int kDxLoads = kDxE * kDxT / kBwdThreads;  // per thread and operand
+static_assert(kDxT == kDxC && kDxLoads * kBwdThreads == kDxE * kDxT, "staging map");
 __global__ __launch_bounds__(kBwdThreads) void dx_assemble_kernel(
     const float* __restrict__ dlogit, const float* __restrict__ w_router,
     const uint16_t* __restrict__ dx_perm, const uint16_t* __restrict__ dx_shared,
     const int32_t* __restrict__ pos, const uint16_t* __restrict__ d_residual,
     uint16_t* __restrict__ dx, int64_t T, int d, int E, int k) {
-  __shared__ float sl[kDxE][kDxT + 1];  // dlogit tile [expert][token]
-  __shared__ float sw[kDxE][kDxC + 1];  // W_r tile [expert][column]
-  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;  // 16 x 16 threads
+  // staging: dlogit [token][expert], then W_r [column][expert]; afterwards the
+  // router term [token][column]
+  __shared__ __attribute__((aligned(16))) float smem[kDxT * kDxOut];
+  static_assert(2 * kDxT * kDxPad <= kDxT * kDxOut, "staging fits the output tile");
+  float (*const sl)[kDxPad] = reinterpret_cast<float (*)[kDxPad]>(smem);
+  float (*const sw)[kDxPad] = reinterpret_cast<float (*)[kDxPad]>(smem + kDxT * kDxPad);
+  float (*const so)[kDxOut] = reinterpret_cast<float (*)[kDxOut]>(smem);
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int wt = 32 * (wave >> 1), wc = 32 * (wave & 1);  // the wave's quarter
   const int64_t t0 = static_cast<int64_t>(blockIdx.y) * kDxT;
   const int c0 = blockIdx.x * kDxC;
-  float acc[4][4] = {};
-  for (int e0 = 0; e0 < E; e0 += kDxE) {
-    for (int i = threadIdx.x; i < kDxE * kDxT; i += kBwdThreads) {
-      const int ee = i % kDxE, tt = i / kDxE;
-      const int64_t t = t0 + tt;
-      sl[ee][tt] = (t < T && e0 + ee < E) ? dlogit[t * E + e0 + ee] : 0.0f;
+  // thread i stages expert i % 32 of rows i / 32 + 8 q
+  const int se = threadIdx.x % kDxE, sr = threadIdx.x / kDxE;
+  float rl[kDxLoads], rw[kDxLoads];
+  auto load = [&](int e0) {
+    const bool ein = e0 + se < E;
+#pragma unroll
+    for (int q = 0; q < kDxLoads; ++q) {
+      const int r = sr + (kBwdThreads / kDxE) * q;
+      const int64_t t = t0 + r;
+      rl[q] = (ein && t < T) ? dlogit[t * E + e0 + se] : 0.0f;
+      rw[q] = (ein && c0 + r < d) ? w_router[static_cast<int64_t>(c0 + r) * E + e0 + se] : 0.0f;
     }
-    for (int i = threadIdx.x; i < kDxE * kDxC; i += kBwdThreads) {
-      const int ee = i % kDxE, cc = i / kDxE;
-      sw[ee][cc] = (c0 + cc < d && e0 + ee < E) ? w_router[static_cast<int64_t>(c0 + cc) * E + e0 + ee] : 0.0f;
+  };
+  f32x16 acc = {};
+  load(0);
+  for (int e0 = 0; e0 < E; e0 += kDxE) {
+#pragma unroll
+    for (int q = 0; q < kDxLoads; ++q) {
+      const int r = sr + (kBwdThreads / kDxE) * q;
+      sl[r][se] = rl[q];
+      sw[r][se] = rw[q];
     }
     __syncthreads();
+    if (e0 + kDxE < E) load(e0 + kDxE);
+    // lane: row (token / column) lane % 32, expert 2 s + lane / 32
 #pragma unroll
-    for (int ee = 0; ee < kDxE; ++ee) {
-      float lv[4], wv[4];
-#pragma unroll
-      for (int a = 0; a < 4; ++a) lv[a] = sl[ee][ty + 16 * a];
-#pragma unroll
-      for (int b = 0; b < 4; ++b) wv[b] = sw[ee][tx * 4 + b];
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = fmaf(lv[a], wv[b], acc[a][b]);
+    for (int s = 0; s < kDxE / 2; ++s) {
+      const int ee = 2 * s + lane / 32;
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(sl[wt + lane % 32][ee], sw[wc + lane % 32][ee], acc, 0, 0, 0);
     }
     __syncthreads();
   }
+  // lane holds tokens 8 (v / 4) + 4 (lane / 32) + v % 4 of column lane % 32
+#pragma unroll
+  for (int v = 0; v < 16; ++v) so[wt + 8 * (v / 4) + 4 * (lane / 32) + v % 4][wc + lane % 32] = acc[v];
+  __syncthreads();
+  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;  // 16 x 16 threads
   const int64_t nrows = T * k;
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
-    const int64_t t = t0 + ty + 16 * a;
+    const int tt = ty + 16 * a;
+    const int64_t t = t0 + tt;
     const int c = c0 + tx * 4;
     if (t >= T || c >= d) continue;
-    float v[4] = {acc[a][0], acc[a][1], acc[a][2], acc[a][3]};
+    const f32x4 r = *reinterpret_cast<const f32x4*>(&so[tt][tx * 4]);
+    float v[4] = {r[0], r[1], r[2], r[3]};
     auto add4 = [&](const uint16_t* src) {
       const uint2 w = *reinterpret_cast<const uint2*>(src);
       v[0] += bf16_to_f32(static_cast<uint16_t>(w.x));
@@ -221,45 +247,79 @@ __global__ __launch_bounds__(kBwdThreads) void dx_assemble_kernel(
 }
 
 // ---- dW_r = x^T dlogit: partial sums over token splits, then a reduction of
-// the splits in order (deterministic).  A block: 64 columns of x x 16 experts
-// over one split of the tokens, tokens staged 32 at a time.
-constexpr int kWrC = 64, kWrE = 16, kWrT = 32, kWrSplitTokens = 256;
+// the splits in order (deterministic).  A block: 64 columns of x x 64 experts
+// over one split of the tokens, on the matrix cores (v_mfma_f32_32x32x2_f32,
+// each wave a 32 x 32 quarter; x is bf16, exact in fp32).  Tokens are staged
+// 32 at a time in LDS as fp32, a row per token, the next 32 tokens' loads in
+// flight while the current ones are multiplied; a fragment read takes 32
+// consecutive entries of one row (lanes 0-31) and of the next (lanes 32-63),
+// and rows of 96 floats put the two halves on different banks.
+constexpr int kWrC = 64, kWrE = 64, kWrT = 32, kWrRow = 96, kWrSplitTokens = 512;
+constexpr int kWrX = kWrT * kWrC / (8 * kBwdThreads);   // 8-column pieces of x per thread
+constexpr int kWrL = kWrT * kWrE / kBwdThreads;         // dlogit values per thread
+static_assert(kWrX == 1 && kWrL * kBwdThreads == kWrT * kWrE, "staging map");
 __global__ __launch_bounds__(kBwdThreads) void dwr_partial_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ dlogit, float* __restrict__ part,
     int64_t T, int d, int E) {
-  __shared__ float sx[kWrT][kWrC + 1];
-  __shared__ float sl[kWrT][kWrE + 1];
+  __shared__ float sx[kWrT][kWrRow];  // x tile [token][column]
+  __shared__ float sl[kWrT][kWrRow];  // dlogit tile [token][expert]
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int wcol = 32 * (wave >> 1), wexp = 32 * (wave & 1);  // the wave's quarter
   const int c0 = blockIdx.x * kWrC, e0 = blockIdx.y * kWrE;
   const int64_t tb = static_cast<int64_t>(blockIdx.z) * kWrSplitTokens;
   const int64_t te = tb + kWrSplitTokens < T ? tb + kWrSplitTokens : T;
-  const int tc = threadIdx.x % kWrC;      // column of x
-  const int tg = threadIdx.x / kWrC;      // 4 groups of 4 experts
-  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int64_t t0 = tb; t0 < te; t0 += kWrT) {
-    for (int i = threadIdx.x; i < kWrT * kWrC; i += kBwdThreads) {
-      const int tt = i / kWrC, cc = i % kWrC;
-      const int64_t t = t0 + tt;
-      sx[tt][cc] = (t < te && c0 + cc < d) ? bf16_to_f32(x[t * d + c0 + cc]) : 0.0f;
-    }
-    for (int i = threadIdx.x; i < kWrT * kWrE; i += kBwdThreads) {
-      const int tt = i / kWrE, ee = i % kWrE;
-      const int64_t t = t0 + tt;
-      sl[tt][ee] = (t < te && e0 + ee < E) ? dlogit[t * E + e0 + ee] : 0.0f;
-    }
-    __syncthreads();
-    for (int tt = 0; tt < kWrT; ++tt) {
-      const float xv = sx[tt][tc];
+  // thread i stages columns 8 (i % 8) .. + 7 of token i / 8, and expert i % 64
+  // of tokens i / 64 + 4 q
+  const int xt = threadIdx.x / 8, xc = 8 * (threadIdx.x % 8);
+  const int le = threadIdx.x % kWrE, lt = threadIdx.x / kWrE;
+  const bool xvec = d % 8 == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0;
+  uint16_t rx[8];
+  float rl[kWrL];
+  auto load = [&](int64_t t0) {
+    const int64_t t = t0 + xt;
+    const int c = c0 + xc;
+    if (xvec && t < te && c + 8 <= d) {
+      const uint4 w = *reinterpret_cast<const uint4*>(x + t * d + c);
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc[q] = fmaf(xv, sl[tt][tg * 4 + q], acc[q]);
+      for (int j = 0; j < 4; ++j) {
+        rx[2 * j] = static_cast<uint16_t>(ww[j]);
+        rx[2 * j + 1] = static_cast<uint16_t>(ww[j] >> 16);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) rx[j] = (t < te && c + j < d) ? x[t * d + c + j] : uint16_t{0};
+    }
+#pragma unroll
+    for (int q = 0; q < kWrL; ++q) {
+      const int64_t tq = t0 + lt + (kBwdThreads / kWrE) * q;
+      rl[q] = (tq < te && e0 + le < E) ? dlogit[tq * E + e0 + le] : 0.0f;
+    }
+  };
+  f32x16 acc = {};
+  if (tb < te) load(tb);
+  for (int64_t t0 = tb; t0 < te; t0 += kWrT) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sx[xt][xc + j] = bf16_to_f32(rx[j]);
+#pragma unroll
+    for (int q = 0; q < kWrL; ++q) sl[lt + (kBwdThreads / kWrE) * q][le] = rl[q];
+    __syncthreads();
+    if (t0 + kWrT < te) load(t0 + kWrT);
+    // lane: column / expert lane % 32 of token 2 s + lane / 32
+#pragma unroll
+    for (int s = 0; s < kWrT / 2; ++s) {
+      const int tt = 2 * s + lane / 32;
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(sx[tt][wcol + lane % 32], sl[tt][wexp + lane % 32], acc, 0, 0, 0);
     }
     __syncthreads();
   }
-  const int c = c0 + tc;
-  if (c >= d) return;
+  // lane holds columns 8 (v / 4) + 4 (lane / 32) + v % 4 of expert lane % 32
+  const int e = e0 + wexp + lane % 32;
+  if (e >= E) return;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = e0 + tg * 4 + q;
-    if (e < E) part[(static_cast<int64_t>(blockIdx.z) * d + c) * E + e] = acc[q];
+  for (int v = 0; v < 16; ++v) {
+    const int c = c0 + wcol + 8 * (v / 4) + 4 * (lane / 32) + v % 4;
+    if (c < d) part[(static_cast<int64_t>(blockIdx.z) * d + c) * E + e] = acc[v];
   }
 }
 
