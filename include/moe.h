@@ -37,6 +37,10 @@
  *
  * Supported shapes: 1 <= E <= 1024, 1 <= k <= min(E, 32), d, H and Hs
  * multiples of 64, T*(k+1) < 2^31.  When seq_len > 0 it must divide T.
+ * The grouped GEMMs address x, and one expert's weights, with 32-bit byte
+ * offsets: 2*T*d, 2*H*d and 2*Hs*d must stay below 2^31 (else
+ * MOE_ERR_UNSUPPORTED).  x_perm, h and the outputs have no such limit.  The
+ * backward calls also need 2*T*k*max(d, H, Hs) < 2^31.
  */
 #ifndef MOE_H
 #define MOE_H

@@ -75,12 +75,23 @@ moe_status check_shape(const moe_shape* s) {
   if (s->d_model % 64 || s->hidden % 64 || s->shared_hidden % 64) return MOE_ERR_UNSUPPORTED;
   if (s->tokens * (static_cast<int64_t>(s->top_k) + 1) >= (int64_t{1} << 31))
     return MOE_ERR_UNSUPPORTED;
-  // grouped-GEMM operands are addressed with 32-bit byte offsets
-  const int64_t widest = std::max<int64_t>({s->d_model, s->hidden, s->shared_hidden});
-  if (2 * s->tokens * s->top_k * widest >= (int64_t{1} << 31) ||
+  // The grouped GEMMs address one expert's weights, and the token rows of x
+  // they gather, with 32-bit byte offsets; the rows of x_perm and h are
+  // addressed from each tile's first row, so their size is not limited.
+  if (2 * s->tokens * s->d_model >= (int64_t{1} << 31) ||
       2 * static_cast<int64_t>(s->hidden) * s->d_model >= (int64_t{1} << 31) ||
       2 * static_cast<int64_t>(s->shared_hidden) * s->d_model >= (int64_t{1} << 31))
     return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// The backward calls: their GEMMs also address whole [T*k, d or H] operands
+// with 32-bit byte offsets.
+moe_status check_bwd_shape(const moe_shape* s) {
+  const moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  const int64_t widest = std::max<int64_t>({s->d_model, s->hidden, s->shared_hidden});
+  if (2 * s->tokens * s->top_k * widest >= (int64_t{1} << 31)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -398,7 +409,7 @@ moe_status check_bwd_ws(const moe_shape* s, void* ws, size_t bytes) {
 
 moe_status moe_backward_workspace_bytes(const moe_shape* shape, size_t* bytes) {
   if (!bytes) return MOE_ERR_INVALID_ARGUMENT;
-  const moe_status st = check_shape(shape);
+  const moe_status st = check_bwd_shape(shape);
   if (st != MOE_OK) return st;
   *bytes = carve_bwd(shape, nullptr).total;
   return MOE_OK;
@@ -407,7 +418,7 @@ moe_status moe_backward_workspace_bytes(const moe_shape* shape, size_t* bytes) {
 moe_status moe_combine_backward(const moe_shape* shape, const uint16_t* dout, const uint16_t* y_perm,
                                 const float* topk_gate, const int32_t* pos, uint16_t* dy_perm,
                                 float* dgate, void* stream) {
-  moe_status st = check_shape(shape);
+  moe_status st = check_bwd_shape(shape);
   if (st != MOE_OK) return st;
   if (shape->tokens == 0) return MOE_OK;
   if (!dout || !y_perm || !topk_gate || !pos || !dy_perm || !dgate) return MOE_ERR_INVALID_ARGUMENT;
@@ -425,7 +436,7 @@ moe_status moe_grouped_ffn_backward(const moe_shape* shape, const uint16_t* x,
                                     uint16_t* dx_perm, uint16_t* dx_shared, float* dw1, float* dw3,
                                     float* dw2, float* dws1, float* dws3, float* dws2,
                                     void* workspace, size_t workspace_bytes, void* stream) {
-  moe_status st = check_shape(shape);
+  moe_status st = check_bwd_shape(shape);
   if (st != MOE_OK) return st;
   if (shape->tokens == 0) return MOE_OK;
   const bool shared = shape->shared_hidden > 0;
@@ -578,7 +589,7 @@ moe_status moe_route_backward(const moe_shape* shape, const uint16_t* x, const f
                               const int32_t* pos, const uint16_t* d_residual, uint16_t* dx,
                               float* dw_router, void* workspace, size_t workspace_bytes,
                               void* stream) {
-  moe_status st = check_shape(shape);
+  moe_status st = check_bwd_shape(shape);
   if (st != MOE_OK) return st;
   if (shape->tokens == 0) return MOE_OK;
   if (!x || !w_router || !topk_idx || !topk_gate || !dgate || !dx_perm || !pos || !dx || !dw_router)

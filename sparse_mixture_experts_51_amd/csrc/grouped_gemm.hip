@@ -329,7 +329,14 @@ __global__ __launch_bounds__(C::kAllThreads, C::BPC) void grouped_gemm_kernel(Gr
     const bool routed = pu.routed;
     const int K = pu.K, N = pu.N, g = pu.g, n0 = pu.n0;
     const bool gather = routed && a.a_row_map;
-    sr.ra = routed ? rsrc(a.a_routed, a.a_routed_bytes) : rsrc(a.a_shared, a.a_shared_bytes);
+    // Rows that are not gathered are the unit's own consecutive rows of A:
+    // their descriptor starts at the unit's first row, so the 32-bit offsets
+    // stay within one tile however large the buffer is.  Gathered rows are
+    // token rows of x, addressed from x itself.
+    const int64_t a_row0 = gather ? 0 : pu.orow0;
+    const uint16_t* a_base = (routed ? a.a_routed : a.a_shared) + a_row0 * K;
+    const int64_t a_bytes = gather ? a.a_routed_bytes : static_cast<int64_t>(pu.valid_rows) * K * 2;
+    sr.ra = rsrc(a_base, a_bytes);
     const int64_t wbytes = static_cast<int64_t>(N) * K * 2;
     const uint16_t* w0 = routed ? a.w_routed + static_cast<int64_t>(g) * N * K : a.w_shared;
     const uint16_t* w1 =
@@ -341,7 +348,8 @@ __global__ __launch_bounds__(C::kAllThreads, C::BPC) void grouped_gemm_kernel(Gr
       const int K2 = a.K2_r;
       sr.rb1 = rsrc(K2 > 0 ? a.w3_routed + static_cast<int64_t>(g) * N * K2 : w0,
                     static_cast<int64_t>(N) * (K2 > 0 ? K2 : K) * 2);
-      sr.ra2 = rsrc(K2 > 0 ? a.a2_routed : a.a_routed, a.a_routed_bytes);
+      // the second part's rows: the same rows of a2_routed (row stride K too)
+      sr.ra2 = K2 > 0 ? rsrc(a.a2_routed + a_row0 * K, a_bytes) : sr.ra;
       sr.nk1 = pu.nk1;
       sr.wkm_step = kBK * N * 2;
     }
@@ -349,7 +357,7 @@ __global__ __launch_bounds__(C::kAllThreads, C::BPC) void grouped_gemm_kernel(Gr
     // logical chunk the swizzle puts there (as for the weights below).
     const int a_chunk = C::DMAA ? (ld_chunk ^ ((ld_row >> 1) & (kChunksPerRow - 1))) : ld_chunk;
     MOE_FOR(i, LA, {
-      int row = gather ? ready[i] : prow[i];
+      int row = gather ? ready[i] : prow[i] - pu.orow0;
       if (gather && (row < 0 || row >= a.T)) row = 0;  // malformed permutation: stay in bounds
       sr.a_off[i] = ld_row + RPP * i < pu.valid_rows ? (row * K + a_chunk * 8) * 2
                                                      : static_cast<int>(kOutOfRange);

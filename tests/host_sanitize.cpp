@@ -175,11 +175,17 @@ void abi_part() {
   const moe_shape bad[] = {shape_of(-1, 64, 4, 2, 64, 64, 0), shape_of(8, 0, 4, 2, 64, 64, 0),
                            shape_of(8, 64, 4, 5, 64, 64, 0), shape_of(9, 64, 4, 2, 64, 64, 4),
                            shape_of(8, 60, 4, 2, 64, 64, 0), shape_of(8, 64, 2000, 2, 64, 64, 0),
-                           shape_of(20000, 7168, 256, 8, 2048, 2048, 0)};
+                           shape_of(149797, 7168, 256, 8, 2048, 2048, 0)};
   for (const moe_shape& s : bad) {
     size_t b = 0;
     CHECK(moe_workspace_bytes(&s, &b) != MOE_OK);
     CHECK(moe_backward_workspace_bytes(&s, &b) != MOE_OK);
+  }
+  {  // x_perm and h beyond 2 GiB: the forward takes it, the backward does not
+    const moe_shape wide = shape_of(20000, 7168, 256, 8, 2048, 2048, 0);
+    size_t b = 0;
+    CHECK(moe_workspace_bytes(&wide, &b) == MOE_OK && b % 256 == 0);
+    CHECK(moe_backward_workspace_bytes(&wide, &b) == MOE_ERR_UNSUPPORTED);
   }
   size_t b = 0;
   CHECK(moe_workspace_bytes(nullptr, &b) == MOE_ERR_INVALID_ARGUMENT);

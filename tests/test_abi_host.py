@@ -110,6 +110,30 @@ def test_bad_shapes(L, kw, code):
                              None) == code
 
 
+def test_operand_offset_limits(L):
+    """The forward GEMMs address x_perm and h per tile, so a V3-wide layer above
+    2 GiB of x_perm is accepted; x itself and one expert's weights must stay
+    below 2 GiB, and the backward keeps the whole-operand limit."""
+    n = ctypes.c_size_t(0)
+    v3 = dict(d_model=7168, n_experts=256, top_k=8, hidden=2048, shared_hidden=2048, seq_len=0)
+    big = shape(tokens=32768, **v3)  # x_perm 3.8 GB, h 1.2 GB
+    assert L.moe_workspace_bytes(ctypes.byref(big.c()), ctypes.byref(n)) == moe.MOE_OK
+    assert n.value >= 2 * (32768 * 8 * 2048 + 32768 * 2048)
+    assert L.moe_backward_workspace_bytes(ctypes.byref(big.c()), ctypes.byref(n)) == \
+        moe.MOE_ERR_UNSUPPORTED
+    ok_bwd = shape(tokens=18723, **v3)  # 2*T*k*d just below 2^31
+    assert L.moe_backward_workspace_bytes(ctypes.byref(ok_bwd.c()), ctypes.byref(n)) == moe.MOE_OK
+    x_at_2g = shape(tokens=(1 << 30) // 7168 + 1, **v3)  # x reaches 2 GiB
+    assert L.moe_workspace_bytes(ctypes.byref(x_at_2g.c()), ctypes.byref(n)) == \
+        moe.MOE_ERR_UNSUPPORTED
+    x_below = shape(tokens=(1 << 30) // 7168, **v3)
+    assert L.moe_workspace_bytes(ctypes.byref(x_below.c()), ctypes.byref(n)) == moe.MOE_OK
+    w_2g = shape(tokens=64, d_model=1 << 15, n_experts=8, top_k=2, hidden=1 << 15,
+                 shared_hidden=0, seq_len=0)  # one expert's weights: 2 GiB
+    assert L.moe_workspace_bytes(ctypes.byref(w_2g.c()), ctypes.byref(n)) == \
+        moe.MOE_ERR_UNSUPPORTED
+
+
 def test_null_shape_and_bytes(L):
     assert L.moe_workspace_bytes(None, None) == moe.MOE_ERR_INVALID_ARGUMENT
     assert L.moe_route(None, fake(0), fake(1), fake(2), fake(3), fake(4), None, None,

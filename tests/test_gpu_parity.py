@@ -532,6 +532,67 @@ def full_size_check(name, p):
         check_bf16_close(g["y_shared"][rows], ysh, f"{name}.y_shared[{len(rows)} rows]")
 
 
+# Layers whose x_perm and y_perm (and in the first case h) exceed 2 GiB: the
+# grouped GEMM addresses a tile's own rows of x_perm and h from the tile's
+# first row, so 32-bit offsets suffice however large those buffers are.
+#   wide_k_eq_E: every token to all 8 experts, 80 000 tokens at d = 7168,
+#     H = 2048: x_perm and y_perm 9.2 GB, h 2.6 GB, the 256x128 loader-wave tile;
+#   wide_stream: 1024 experts of H = 256 (weights 11.3 GB), 200 rows each:
+#     the weight-streaming tile, x_perm 2.9 GB.
+WIDE_CASES = {
+    "wide_k_eq_E": custom(tokens=80000, d_model=7168, n_experts=8, top_k=8, hidden=2048,
+                          shared_hidden=2048, cfg_id=131, w_std=0.006, router_std=0.006,
+                          bias_range=0.01),
+    "wide_stream": custom(tokens=25600, d_model=7168, n_experts=1024, top_k=8, hidden=256,
+                          shared_hidden=256, cfg_id=132, w_std=0.006, router_std=0.006,
+                          bias_range=0.01),
+}
+
+
+@pytest.mark.parametrize("name", list(WIDE_CASES))
+def test_forward_beyond_32bit_operand_offsets(name):
+    wl = WIDE_CASES[name]
+    shape = moe.Shape.of(wl)
+    T, d, k = wl.tokens, wl.d_model, wl.top_k
+    assert 2 * T * k * d >= 1 << 31  # refused before the per-tile descriptors
+    say(f"[wide] {name}: T={T} E={wl.n_experts} k={k} H={wl.hidden}, x_perm "
+        f"{2 * T * k * d / 1e9:.1f} GB")
+    x, p = inputs(wl, DEV)
+    bufs = run_layer(shape, x, p, use_x_perm=True)
+    y_perm_xp = bufs["y_perm"].clone()
+    out_xp = bufs["out"].clone()
+    run_layer(shape, x, p, use_x_perm=False, bufs=bufs)  # rows gathered through perm_src
+    assert torch.equal(bufs["y_perm"], y_perm_xp) and torch.equal(bufs["out"], out_xp)
+    del y_perm_xp, out_xp
+    idx = host(bufs["topk_idx"])
+    perm_src = host(bufs["perm_src"])
+    offsets = host(bufs["offsets"])
+    # routing of sampled tokens, and their whole layer output
+    xb = bits(x)
+    sample = np.unique(np.linspace(0, T - 1, 9).astype(int))
+    ref = oracle.route(xb[sample], host(p["w_router"]), host(p["bias"]), k)
+    near = ref["margin"] < 1e-6
+    same = np.all(idx[sample] == ref["idx"], axis=1)
+    assert (same | near).all()
+    sample, ref_idx = sample[same], ref["idx"][same]
+    ref_gate = np.zeros((T, k), np.float32)
+    full_idx = np.zeros((T, k), np.int32)
+    ref_gate[sample], full_idx[sample] = ref["gate"][same], ref_idx
+    out = sampled_outputs(x, p, sample, full_idx, ref_gate)
+    got = bits(bufs["out"][torch.as_tensor(sample, device=DEV)])
+    check_bf16_close(got, out, f"{name}.out[sampled {len(sample)} tokens]")
+    # y_perm rows at both sides of the 2 GiB byte offset of x_perm and at the end
+    edge = (1 << 31) // (2 * d)
+    rows = sorted({0, edge - 1, edge, edge + 1, T * k - 1})
+    ys = []
+    for r in rows:
+        e = int(np.searchsorted(offsets, r, side="right") - 1)
+        ys.append(oracle.expert_ffn(xb[perm_src[r]], bits(p["w1"][e]), bits(p["w3"][e]),
+                                    bits(p["w2"][e])))
+    got = bits(bufs["y_perm"][torch.as_tensor(rows, device=DEV)])
+    check_bf16_close(got, np.stack(ys), f"{name}.y_perm[rows {rows}]")
+
+
 def test_mini_train_stacked_layers_teacher_forced():
     """Six stacked layers with the residual stream, two steps with the bias
     update in between; the oracle is fed the GPU's layer inputs and biases."""
