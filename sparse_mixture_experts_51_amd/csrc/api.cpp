@@ -54,6 +54,7 @@ Workspace carve_workspace(void* base, int64_t T, int d, int E, int k, int H, int
   w.blk_base = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * nblk * E));
   w.h_routed = reinterpret_cast<uint16_t*>(take(sizeof(uint16_t) * T * k * H));
   w.h_shared = reinterpret_cast<uint16_t*>(take(sizeof(uint16_t) * T * Hs));
+  w.unit_counters = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * kUnitCounters));
   w.total = off;
   return w;
 }
@@ -286,7 +287,10 @@ moe_status moe_grouped_ffn(const moe_shape* shape, const uint16_t* x, const uint
   g1.K_s = d;
   g1.N_r = H;
   g1.N_s = Hs;
-  hipError_t e = moe::launch_gemm_swiglu(g1, s);
+  g1.unit_counter = w.unit_counters;
+  hipError_t e = moe::launch_zero_counters(w.unit_counters, moe::kUnitCounters, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = moe::launch_gemm_swiglu(g1, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
 
   moe::GroupedGemmArgs g2{};
@@ -307,6 +311,7 @@ moe_status moe_grouped_ffn(const moe_shape* shape, const uint16_t* x, const uint
   g2.K_s = Hs;
   g2.N_r = d;
   g2.N_s = d;
+  g2.unit_counter = w.unit_counters + moe::kUnitCounters / 2;
   return hip_status(moe::launch_gemm_down(g2, s));
 }
 

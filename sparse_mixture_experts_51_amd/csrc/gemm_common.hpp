@@ -95,6 +95,23 @@ __device__ __forceinline__ void lds_write_b64(void* p, uint64_t v) {
   const unsigned a = static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_ptr_t)p));
   asm volatile("ds_write_b64 %0, %1" : : "v"(a), "v"(v) : "memory");
 }
+// A 4-byte write and a 4-byte read (complete on return), for small LDS
+// tables shared through the same barriers.
+__device__ __forceinline__ void lds_write_b32(void* p, int v) {
+  const unsigned a = static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_ptr_t)p));
+  asm volatile("ds_write_b32 %0, %1" : : "v"(a), "v"(v) : "memory");
+}
+__device__ __forceinline__ int lds_read_b32(const void* p) {
+  const unsigned a = static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_ptr_t)p));
+  int v;
+  asm volatile(
+      "ds_read_b32 %0, %1\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v)
+      : "v"(a)
+      : "memory");
+  return v;
+}
 // ... and a 16-byte read, complete on return.
 __device__ __forceinline__ u32x4 lds_read_b128(const void* p) {
   const unsigned a = static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_ptr_t)p));

@@ -165,7 +165,29 @@ __device__ __forceinline__ Unit decode_unit(const GroupedGemmArgs& a, const int*
   const int rows = r.routed ? uni(offs[r.g + 1]) - grow0 : static_cast<int>(a.T);
   const int mt = (rows + C::BM - 1) / C::BM;
   const int local = u - uni(unit_start[r.g]);
-  const int n_tile = local / mt, m_tile = local % mt;
+  // Units run n-tile major, m-tile minor, so the units an XCD runs together
+  // share a weight tile across m-tiles and an A tile across n-tiles.  A group
+  // of very many m-tiles (the shared expert over tens of thousands of tokens,
+  // whose x no longer fits the MALL) is walked in panels of kPanel m-tiles:
+  // otherwise the XCD's concurrent units would be m-tiles of one n-tile, and
+  // every A tile would come from HBM again for each of the group's n-tiles
+  // (V3 layer at 32768 tokens: FFN 29.6 -> 28.9 ms; with panels from 8
+  // m-tiles on, no gain at 4096 tokens and the mini model a little slower).
+  constexpr int kPanel = 4;
+  int n_tile, m_tile;
+  if (mt >= 64) {
+    constexpr int cols = kSwiGLU ? C::BW / 2 : C::BW;
+    const int nt = ((r.routed ? a.N_r : a.N_s) + cols - 1) / cols;
+    const int full = mt / kPanel;  // whole panels; the last one holds mt % kPanel m-tiles
+    const int panel = local / (kPanel * nt);
+    const int h = panel < full ? kPanel : mt - full * kPanel;
+    const int within = local - panel * kPanel * nt;
+    n_tile = within / h;
+    m_tile = panel * kPanel + within % h;
+  } else {
+    n_tile = local / mt;
+    m_tile = local % mt;
+  }
   const int m0 = m_tile * C::BM;
   r.valid_rows = uni((rows - m0) < C::BM ? (rows - m0) : C::BM);
   r.K = r.routed ? a.K_r : a.K_s;
@@ -240,8 +262,43 @@ __global__ __launch_bounds__(C::kAllThreads, C::BPC) void grouped_gemm_kernel(Gr
   const int G = gridDim.x / kXcds;
   const int ux = blockIdx.x % kXcds;
   const int uend = static_cast<int>(static_cast<int64_t>(total_units) * (ux + 1) / kXcds);
-  const int lb = static_cast<int>(static_cast<int64_t>(total_units) * ux / kXcds) + blockIdx.x / kXcds;
+  const int ustart = static_cast<int>(static_cast<int64_t>(total_units) * ux / kXcds);
+  const int lb = ustart + blockIdx.x / kXcds;
   if (lb >= uend) return;
+  // Unit order.  Static: a block runs lb, lb + G, lb + 2G, ...  Dynamic (the
+  // loader-wave all-DMA tile given counters, in launches of at least 64
+  // units per block): the first two units are the static ones, every later
+  // one is claimed from the XCD's counter, so the units an XCD runs at any
+  // time stay a window of consecutive units.  In the static order, blocks
+  // that share a weight or A tile drift apart over a long launch: in the V3
+  // layer at 32768 tokens (160 SwiGLU units per block) the blocks that share
+  // a weight tile started a median 540 us apart, four units, and 40 us apart
+  // with the claims (FFN 29.2 -> 27.7 ms).  With about 20 units per block
+  // (1024 rows per expert over 4096 tokens) the static order keeps them
+  // 25 us apart and its fixed m-tile per block does better than the claims
+  // (FFN 3.25 vs 3.43 ms).  Thread 0 claims the unit of iteration i + 3 at
+  // the start of iteration i and publishes it in useq after that iteration's
+  // K-loop; the epilogue's barriers make it visible before any wave reads it.
+  constexpr int kEnd = 0x7FFFFFFF;
+  constexpr bool kDynTile = C::PW > 0 && C::DMAA;
+  const bool dyn = kDynTile && a.unit_counter != nullptr &&
+                   total_units >= 64 * static_cast<int64_t>(gridDim.x);
+  __shared__ int useq[4];
+  // (useq is accessed in asm: the compiler would otherwise wait for every LDS
+  // DMA in flight before a plain access)
+  auto publish = [&](int i, int claim) __attribute__((always_inline)) {
+    const int64_t u = static_cast<int64_t>(ustart) + 2 * static_cast<int64_t>(G) + claim;
+    lds_write_b32(&useq[i & 3], u < uend ? static_cast<int>(u) : kEnd);
+  };
+  auto unit_at = [&](int i) __attribute__((always_inline)) {  // the block's i-th unit or kEnd
+    if (i == 0) return lb;
+    if (!dyn || i == 1) {
+      const int64_t u = lb + static_cast<int64_t>(i) * G;
+      return u < uend ? static_cast<int>(u) : kEnd;
+    }
+    return uni(lds_read_b32(&useq[i & 3]));
+  };
+  if (dyn && tid == 0) publish(2, atomicAdd(a.unit_counter + ux, 1));
   auto decode = [&](int u) __attribute__((always_inline)) {
     return decode_unit<C, kSwiGLU, kWKM>(a, unit_start, offs, ngroups, u);
   };
@@ -855,9 +912,12 @@ __global__ __launch_bounds__(C::kAllThreads, C::BPC) void grouped_gemm_kernel(Gr
       constexpr int NS = C::NSA, D = NS - 1;
       auto st = [](int x) __attribute__((always_inline)) { return x >= NS ? x - NS : x; };
       Unit cu = decode(lb);
-      lds_barrier();  // step 0 has landed
-      for (int u = lb; u < uend; u += G) {
-        const Unit nu = decode(next_of(u));
+      lds_barrier();  // step 0 has landed (and useq holds iteration 2's unit)
+      for (int i = 0, u = lb; u < uend; ++i) {
+        const int un = unit_at(i + 1);
+        const Unit nu = decode(un < uend ? un : u);
+        int claim = 0;
+        if (dyn && tid == 0) claim = atomicAdd(a.unit_counter + ux, 1);
         const int mrows = valid_tiles(cu.valid_rows);
         zero_acc();
         for (int kt = 0; kt < cu.nk; ++kt) {
@@ -865,8 +925,10 @@ __global__ __launch_bounds__(C::kAllThreads, C::BPC) void grouped_gemm_kernel(Gr
           lds_barrier();
           cs = st(cs + 1);
         }
+        if (dyn && tid == 0) publish(i + 3, claim);
         epilogue(cu, mrows, st(cs + D), st(cs + D));  // the stage the last step read
         cu = nu;
+        u = un;
       }
       return;
     }
@@ -900,7 +962,7 @@ __global__ __launch_bounds__(C::kAllThreads, C::BPC) void grouped_gemm_kernel(Gr
   Unit cu;
   int row0[LA], map0[LA], ready0[LA];
   prepare_into(lb, cu, row0, map0);
-  prepare(next_of(lb));
+  prepare(unit_at(1) < uend ? unit_at(1) : lb);
   if constexpr (C::DMAA) {
     // All-DMA tiles in NS stages, D = NS - 1 steps ahead: the DMA of step
     // k + D (running into the next unit's first steps) is issued at step k
@@ -930,10 +992,11 @@ __global__ __launch_bounds__(C::kAllThreads, C::BPC) void grouped_gemm_kernel(Gr
     __builtin_amdgcn_s_waitcnt(0x0F70 | ((kFirst & 15) | ((kFirst >> 4) << 14)));
     lds_barrier();
     settle();  // free here: those loads are older than the A passes
-    for (int u = lb; u < uend; u += G) {
+    for (int i = 0, u = lb; u < uend; ++i) {
       const Src nxt = source_of_pending();
       const Unit nu = pend;
-      prepare(next_of(next_of(u)));
+      const int u1 = unit_at(i + 1), u2 = unit_at(i + 2);
+      prepare(u2 < uend ? u2 : (u1 < uend ? u1 : u));
       const int mrows = valid_tiles(cu.valid_rows);
       zero_acc();
       for (int kt = 0; kt < cur.nk; ++kt) {
@@ -966,6 +1029,7 @@ __global__ __launch_bounds__(C::kAllThreads, C::BPC) void grouped_gemm_kernel(Gr
       }
       cur = nxt;
       cu = nu;
+      u = u1;
     }
     return;
   }
@@ -1086,6 +1150,7 @@ static hipError_t launch_gemm(const GroupedGemmArgs& a, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     GroupedGemmArgs shared = a;  // one group: the shared expert's T rows
+    shared.unit_counter = a.unit_counter ? a.unit_counter + 8 : nullptr;
     shared.E = 0;
     shared.w_routed = shared.w3_routed = nullptr;
     shared.a_routed = nullptr;
@@ -1105,6 +1170,14 @@ static hipError_t launch_gemm(const GroupedGemmArgs& a, hipStream_t s) {
   } else {
     launch_cfg<kCompute, kSwiGLU, kBwd>(a, s);
   }
+  return hipGetLastError();
+}
+
+__global__ void zero_counters_kernel(int32_t* p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
+}
+hipError_t launch_zero_counters(int32_t* p, int n, hipStream_t s) {
+  hipLaunchKernelGGL(zero_counters_kernel, dim3(1), dim3(64), 0, s, p, n);
   return hipGetLastError();
 }
 

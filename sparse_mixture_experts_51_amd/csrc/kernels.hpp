@@ -19,6 +19,7 @@ struct Workspace {
   int32_t* blk_base;      // [nblk, E] first row of each (block, expert)
   uint16_t* h_routed;     // [T*k, H] bf16 hidden activations, expert-grouped rows
   uint16_t* h_shared;     // [T, Hs] bf16 hidden activations of the shared expert
+  int32_t* unit_counters; // [kUnitCounters] work counters of the grouped-GEMM launches
   size_t total;
 };
 
@@ -86,7 +87,14 @@ struct GroupedGemmArgs {
   // [E][K2_r][N_r] against the A rows of a2_routed (row stride K_r too)
   const uint16_t* a2_routed;
   int K2_r;
+  // Per-XCD unit counters (16 ints, zero at launch: the first 8 for this
+  // launch, the next 8 for the shared expert's own launch beside streaming
+  // tiles).  With them the loader-wave all-DMA tile hands out units in order
+  // as blocks become free; NULL keeps the static round-robin order.
+  int32_t* unit_counter;
 };
+constexpr int kUnitCounters = 32;  // two launches of 16
+hipError_t launch_zero_counters(int32_t* p, int n, hipStream_t s);
 hipError_t launch_gemm_swiglu(const GroupedGemmArgs& a, hipStream_t s);
 // The SwiGLU stage again in the backward: the same tiles, MFMA order and h
 // as the forward launch on the same shape, with h, da and dc written.

@@ -98,6 +98,14 @@ WORKLOADS = {
         "v3_decode_64", 5, 4, 64, 0, 7168, 256, 8, 2048, 2048, 1, 1,
         1.0, 0.006, 0.006, "uniform", 0.01, 0.0,
         "DeepSeek-V3-shaped decode step, 64 independent tokens"),
+    # The same V3-shaped layer (the prefill's weights) over eight 4096-token
+    # sequences: about 1024 rows per expert, past the ridge of the bf16
+    # matrix cores (about 1100 FLOP per byte of weights), so the whole layer,
+    # not only one GPU's expert-parallel share, is matrix-core-bound.
+    "v3_prefill_32768": Workload(
+        "v3_prefill_32768", 8, 4, 32768, 4096, 7168, 256, 8, 2048, 2048, 1, 1,
+        1.0, 0.006, 0.006, "uniform", 0.01, 0.0,
+        "DeepSeek-V3-shaped prefill layer, 8 sequences x 4096 tokens (~1024 rows per expert)"),
     # The grouped-FFN shape one GPU holds under 8-way expert parallelism of the
     # V3 layer (32 of the 256 experts, about 1024 rows each, the shared expert
     # on the GPU's own 4096 tokens), built as a layer of 32 experts with top-8

@@ -552,12 +552,30 @@ WIDE_CASES = {
 @pytest.mark.parametrize("name", list(WIDE_CASES))
 def test_forward_beyond_32bit_operand_offsets(name):
     wl = WIDE_CASES[name]
+    x, p = inputs(wl, DEV)
+    wide_layer_check(wl, x, p)
+
+
+def test_v3_prefill_32768_sampled(v3_weights):
+    """The V3 layer over 32768 tokens (about 1024 rows per expert), on the
+    prefill's weights: routing and permutation of every token against the
+    oracle's integer work, sampled tokens and rows against the oracle."""
+    wl = workloads.WORKLOADS["v3_prefill_32768"]
+    assert wl.weight_cfg_id == workloads.WORKLOADS["v3_prefill_4096"].weight_cfg_id
+    x = workloads.tokens(wl, 0, DEV)
+    wide_layer_check(wl, x, v3_weights)
+
+
+def wide_layer_check(wl, x, p):
+    """Run the layer with x_perm and with the gather through perm_src (the two
+    must agree bit for bit), then compare sampled tokens' routing and outputs
+    and y_perm rows on both sides of x_perm's 2 GiB byte offset with the oracle."""
     shape = moe.Shape.of(wl)
+    name = wl.name
     T, d, k = wl.tokens, wl.d_model, wl.top_k
     assert 2 * T * k * d >= 1 << 31  # refused before the per-tile descriptors
     say(f"[wide] {name}: T={T} E={wl.n_experts} k={k} H={wl.hidden}, x_perm "
         f"{2 * T * k * d / 1e9:.1f} GB")
-    x, p = inputs(wl, DEV)
     bufs = run_layer(shape, x, p, use_x_perm=True)
     y_perm_xp = bufs["y_perm"].clone()
     out_xp = bufs["out"].clone()
@@ -567,8 +585,19 @@ def test_forward_beyond_32bit_operand_offsets(name):
     idx = host(bufs["topk_idx"])
     perm_src = host(bufs["perm_src"])
     offsets = host(bufs["offsets"])
-    # routing of sampled tokens, and their whole layer output
+    pm = oracle.permute(idx, wl.n_experts)  # the oracle's grouping of the GPU's choices
+    for key in ("counts", "offsets", "perm_src", "pos"):
+        assert np.array_equal(host(bufs[key]), pm[key]), key
     xb = bits(x)
+    if wl.seq_len:  # the last sequence: every token's routing and its balance statistic
+        S = wl.seq_len
+        last = oracle.route(xb[T - S:], host(p["w_router"]), host(p["bias"]), k)
+        g_last = {key: host(bufs[key])[T - S:] for key in ("topk_idx", "topk_gate", "margin")}
+        check_routing(g_last, last, f"{name}.route[last sequence]")
+        L = oracle.seq_balance(last["scores"], idx[T - S:], S, 1e-4)
+        got = host(bufs["seq_balance"])[-1:]
+        assert np.abs(got - L).max() / np.abs(L).max() <= 1e-5, (got, L)
+    # routing of sampled tokens, and their whole layer output
     sample = np.unique(np.linspace(0, T - 1, 9).astype(int))
     ref = oracle.route(xb[sample], host(p["w_router"]), host(p["bias"]), k)
     near = ref["margin"] < 1e-6
