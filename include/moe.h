@@ -173,7 +173,8 @@ moe_status moe_permute_noalloc(const moe_shape* shape, const int32_t* topk_idx, 
  *   w1, w3   [E, H, d] bf16; w2 [E, d, H] bf16 (in)
  *   ws1, ws3 [Hs, d] bf16; ws2 [d, Hs] bf16 (in; NULL iff Hs == 0)
  *   y_perm   [T*k, d] bf16 (out); y_shared [T, d] bf16 (out; NULL iff Hs == 0)
- *   workspace >= moe_workspace_bytes(shape) bytes (holds h)             */
+ *   workspace >= moe_workspace_bytes(shape) bytes (holds h, and the work
+ *            counters of the GEMM launches, which the call zeroes itself)  */
 moe_status moe_grouped_ffn(const moe_shape* shape, const uint16_t* x, const uint16_t* x_perm,
                            const int32_t* perm_src, const int32_t* offsets, const uint16_t* w1,
                            const uint16_t* w3, const uint16_t* w2, const uint16_t* ws1,
