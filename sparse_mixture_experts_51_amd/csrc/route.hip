@@ -255,7 +255,9 @@ static RouterCfg router_cfg(int64_t T, int d, int E, int want_blocks, bool whole
   // over d, so parallelism is bounded by T*E lanes).  A chunk of d is the
   // whole of d when x and W_r tiles fit the LDS budget; else the longest
   // power-of-two double-buffered chunk that fits.
-  const int Emax = next_pow2(E) < 64 ? next_pow2(E) : 64;
+  // W_r is staged in 16-byte pieces of 4 experts, so a tile spans at least 4
+  // (with E < 4 the missing experts are zero-filled and never stored)
+  const int Emax = next_pow2(E) < 4 ? 4 : (next_pow2(E) < 64 ? next_pow2(E) : 64);
   auto ept_of = [](int BE) { return BE >= 64 ? 4 : (BE >= 32 ? 2 : 1); };
   RouterCfg best{0, 0, 0, 0, -1, 0};
   const int be_list[4] = {64, 32, 16, 8};

@@ -46,6 +46,10 @@ ROUTE_CASES = {
                             cfg_id=96, router_std=0.1),
     "k_equals_E": custom(tokens=100, d_model=64, n_experts=8, top_k=8, cfg_id=97),
     "k1": custom(tokens=300, n_experts=16, top_k=1, cfg_id=98),
+    # fewer experts than the router's 4-expert W_r pieces (a tile of 4, two
+    # of them absent)
+    "E2_k1": custom(tokens=300, seq_len=150, d_model=64, n_experts=2, top_k=1, cfg_id=175,
+                    router_std=0.2),
     "T1": custom(tokens=1, n_experts=16, top_k=4, cfg_id=99),
     # two 16-lane rows per token in the selection: separate select kernel
     # (250-token sequences do not split into whole blocks) and fused routing
@@ -419,6 +423,43 @@ def test_layer_end_to_end_mini_2048_and_dense_formulation():
     check_bf16_close(g["out"][sample], dense, "mini_2048.out vs dense-masked")
 
 
+# Degenerate shapes of the whole layer: one expert (k = E = 1, every gate
+# exactly 1), one token, the narrowest dims the kernels take (d = H = 64), no
+# shared expert, a shared expert narrower than the routed ones, every token
+# in one sequence of odd length, and a ragged number of tokens around the
+# 256-token permutation block.
+DEGENERATE = {
+    "E1_k1": custom(tokens=300, seq_len=100, d_model=64, n_experts=1, top_k=1, hidden=64,
+                    shared_hidden=64, cfg_id=171, router_std=0.1),
+    "T1_no_shared": custom(tokens=1, seq_len=1, d_model=128, n_experts=4, top_k=2, hidden=64,
+                           shared_hidden=0, cfg_id=172, router_std=0.1),
+    "E2_k2_d64": custom(tokens=257, seq_len=257, d_model=64, n_experts=2, top_k=2, hidden=128,
+                        shared_hidden=64, cfg_id=173, router_std=0.1),
+    "narrow_shared_T513": custom(tokens=513, seq_len=171, d_model=192, n_experts=12, top_k=3,
+                                 hidden=192, shared_hidden=64, cfg_id=174, router_std=0.1),
+}
+
+
+@pytest.mark.parametrize("name", list(DEGENERATE))
+def test_layer_degenerate_shapes(name):
+    wl = DEGENERATE[name]
+    say(f"[degenerate] {name}: T={wl.tokens} S={wl.seq_len} d={wl.d_model} E={wl.n_experts} "
+        f"k={wl.top_k} H={wl.hidden} Hs={wl.shared_hidden}")
+    shape = moe.Shape.of(wl)
+    x, p = inputs(wl, DEV)
+    g = gpu_host(run_layer(shape, x, p))
+    ref = oracle.layer(bits(x), host_params(p), wl.top_k, wl.seq_len)
+    check_routing(g, ref, name)
+    for key in ("counts", "offsets", "perm_src", "pos"):
+        assert np.array_equal(g[key], ref[key]), key
+    if wl.top_k == 1:
+        assert np.all(g["topk_gate"] == 1.0)
+    check_bf16_close(g["out"], ref["out"], f"{name}.out")
+    if wl.seq_len:
+        rel = np.abs(g["seq_balance"] - ref["seq_balance"]) / np.abs(ref["seq_balance"])
+        assert rel.max() <= 1e-5, rel.max()
+
+
 def test_layer_is_deterministic_and_residual_path():
     wl = custom(tokens=1536, seq_len=256, cfg_id=131)
     shape = moe.Shape.of(wl)
@@ -541,10 +582,10 @@ def full_size_check(name, p):
 #     the weight-streaming tile, x_perm 2.9 GB.
 WIDE_CASES = {
     "wide_k_eq_E": custom(tokens=80000, d_model=7168, n_experts=8, top_k=8, hidden=2048,
-                          shared_hidden=2048, cfg_id=131, w_std=0.006, router_std=0.006,
+                          shared_hidden=2048, cfg_id=161, w_std=0.006, router_std=0.006,
                           bias_range=0.01),
     "wide_stream": custom(tokens=25600, d_model=7168, n_experts=1024, top_k=8, hidden=256,
-                          shared_hidden=256, cfg_id=132, w_std=0.006, router_std=0.006,
+                          shared_hidden=256, cfg_id=162, w_std=0.006, router_std=0.006,
                           bias_range=0.01),
 }
 
