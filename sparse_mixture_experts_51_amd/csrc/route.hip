@@ -347,27 +347,42 @@ __global__ __launch_bounds__(256) void router_scores_mfma_kernel(
   // (4 experts of one index of d) = index q / 16, experts 4 (q % 16)
   constexpr int kXP = kMfTok * kMfKC / 8 / 256;  // x pieces per thread (4)
   constexpr int kWP = kMfKC * kMfExp / 4 / 256;  // W pieces per thread (8)
-  uint4 px[kXP];
-  float4 pw[kWP];
+  // Buffer loads: each thread's byte offsets are fixed and a chunk moves only
+  // the scalar offset, so a fetch is twelve load instructions with no address
+  // arithmetic or branches between them (64-bit address sums and a branch per
+  // row check made the compiler wait for the first loads of a chunk before
+  // issuing the rest).  The x descriptor covers this block's rows that exist:
+  // a row past T reads as zeros and its scores are never stored.
+  const int64_t xrows = T - t0 < kMfTok ? T - t0 : kMfTok;
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(x + t0 * d), static_cast<short>(0), static_cast<int>(xrows * d * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(w_router + e0), static_cast<short>(0),
+      static_cast<int>((static_cast<int64_t>(d) * E - e0) * 4), 0x00020000);
+  int xoff[kXP], woff[kWP];
+#pragma unroll
+  for (int i = 0; i < kXP; ++i) {
+    const int p = tid + 256 * i;
+    xoff[i] = (p / 16) * d * 2 + (p % 16) * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < kWP; ++i) {
+    const int q = tid + 256 * i;
+    woff[i] = ((q / 16) * E + (q % 16) * 4) * 4;
+  }
+  u32x4 px[kXP], pw[kWP];
   auto fetch = [&](int c) {
+    const int xs_off = c * kMfKC * 2, ws_off = c * kMfKC * E * 4;
 #pragma unroll
-    for (int i = 0; i < kXP; ++i) {
-      const int p = tid + 256 * i;
-      const int64_t t = t0 + p / 16;
-      px[i] = t < T ? *reinterpret_cast<const uint4*>(x + t * d + c * kMfKC + (p % 16) * 8)
-                    : make_uint4(0, 0, 0, 0);
-    }
+    for (int i = 0; i < kXP; ++i)  // read once: non-temporal
+      px[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, xoff[i], xs_off, 2);
 #pragma unroll
-    for (int i = 0; i < kWP; ++i) {
-      const int q = tid + 256 * i;
-      pw[i] = *reinterpret_cast<const float4*>(w_router + static_cast<int64_t>(c * kMfKC + q / 16) * E + e0 +
-                                               (q % 16) * 4);
-    }
+    for (int i = 0; i < kWP; ++i) pw[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, woff[i], ws_off, 0);
   };
   auto stash_x = [&](int b, int i) __attribute__((always_inline)) {
     const int p = tid + 256 * i;
     float f[8];
-    bf16x8_to_f32(px[i], f);
+    bf16x8_to_f32(make_uint4(px[i][0], px[i][1], px[i][2], px[i][3]), f);
     float* dst = &xs[b][(p / 16) * kMfRow + (p % 16) * 8];
     *reinterpret_cast<float4*>(dst) = make_float4(f[0], f[1], f[2], f[3]);
     *reinterpret_cast<float4*>(dst + 4) = make_float4(f[4], f[5], f[6], f[7]);
@@ -375,10 +390,10 @@ __global__ __launch_bounds__(256) void router_scores_mfma_kernel(
   auto stash_w = [&](int b, int i) __attribute__((always_inline)) {
     const int q = tid + 256 * i;
     const int kk = q / 16, e = (q % 16) * 4;
-    wt[b][(e + 0) * kMfRow + kk] = pw[i].x;
-    wt[b][(e + 1) * kMfRow + kk] = pw[i].y;
-    wt[b][(e + 2) * kMfRow + kk] = pw[i].z;
-    wt[b][(e + 3) * kMfRow + kk] = pw[i].w;
+    wt[b][(e + 0) * kMfRow + kk] = __uint_as_float(pw[i][0]);
+    wt[b][(e + 1) * kMfRow + kk] = __uint_as_float(pw[i][1]);
+    wt[b][(e + 2) * kMfRow + kk] = __uint_as_float(pw[i][2]);
+    wt[b][(e + 3) * kMfRow + kk] = __uint_as_float(pw[i][3]);
   };
   auto stash = [&](int b) {
 #pragma unroll
@@ -415,6 +430,10 @@ __global__ __launch_bounds__(256) void router_scores_mfma_kernel(
           wa[cb ^ 1][q] = *reinterpret_cast<const float4*>(wr + 16 * (g + 1) + 4 * q);
         }
       }
+      // keeps those reads ahead of this group's MFMAs: left to itself the
+      // scheduler sinks them to a few MFMAs before their use, and the chain
+      // then waits on LDS reads queued behind the other waves'
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const float4 a4 = xa[cb][q], b4 = wa[cb][q];
@@ -445,8 +464,11 @@ __global__ __launch_bounds__(256) void router_scores_mfma_kernel(
 
 hipError_t launch_router_scores(const uint16_t* x, const float* w_router, float* scores,
                                 int64_t T, int d, int E, hipStream_t s) {
+  // (the kernel's buffer offsets are 32-bit: a block's rows of x and all of
+  // W_r stay below 2 GiB)
   if (T >= 1024 && E % kMfExp == 0 && d % kMfKC == 0 && (reinterpret_cast<uintptr_t>(x) & 15) == 0 &&
-      (reinterpret_cast<uintptr_t>(w_router) & 15) == 0) {
+      (reinterpret_cast<uintptr_t>(w_router) & 15) == 0 && static_cast<int64_t>(d) * E * 4 < 0x7FFFFFFF &&
+      static_cast<int64_t>(kMfTok) * d * 2 < 0x7FFFFFFF) {
     const dim3 grid(static_cast<unsigned>((T + kMfTok - 1) / kMfTok), static_cast<unsigned>(E / kMfExp));
     hipLaunchKernelGGL(router_scores_mfma_kernel, grid, dim3(256), 0, s, x, w_router, scores, T, d, E);
     return hipGetLastError();
