@@ -186,6 +186,48 @@ def hbm_read_probe():
     return out
 
 
+def hbm_stream_probe(stages):
+    """Achievable HBM read rate (GB/s) of a weight stream whose units write
+    output as they go: moe_probe_hbm_read_write over about 8 GiB, best of four
+    passes, once per entry of `stages`, name -> (bytes written per byte read,
+    weight row bytes).  Returns name -> (written per read as run, GB/s)."""
+    import ctypes
+
+    import torch
+
+    from sparse_mixture_experts_51_amd import build as _build
+
+    P = ctypes.CDLL(_build.PROBE_LIB)
+    fn = P.moe_probe_hbm_read_write
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                   ctypes.c_void_p, ctypes.c_void_p]
+    cap = 8 << 30
+    buf = torch.ones(cap // 2, dtype=torch.bfloat16, device="cuda:0")
+    sink = torch.zeros(4096, dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    rates = {}
+    for key, (ratio, row) in stages.items():
+        piece = 256 * row
+        nbytes = cap // piece * piece
+        per = min(piece, max(16, int(round(ratio * piece / 16)) * 16))
+        out = torch.empty(nbytes // piece * per // 4, dtype=torch.int32, device="cuda:0")
+        best = 0.0
+        for _ in range(4):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            if fn(buf.data_ptr(), nbytes, row, out.data_ptr(), per, sink.data_ptr(), stream.cuda_stream) != 0:
+                raise RuntimeError("moe_probe_hbm_read_write failed")
+            e1.record(stream)
+            torch.cuda.synchronize()
+            best = max(best, nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+        rates[key] = (per / piece, best)
+        del out
+    del buf, sink
+    return rates
+
+
 def ffn_algorithmic(wl, counts_per_layer):
     """Algorithmic FLOPs and HBM bytes of one moe_grouped_ffn call per layer:
     FLOPs = 6*d*H per routed row + 6*d*Hs per shared row; bytes = weights of
@@ -659,6 +701,27 @@ def main():
                               "moe_probe_hbm_read (LDS DMA, 32 KiB steps, one block per CU) and "
                               "moe_probe_hbm_read_nt (non-temporal 16-byte register loads)")
     roof["hbm_frac_of_probe"] = byts / t_s / 1e9 / probe
+    if roof["bound"] == "hbm":
+        # The two routed stages stream the touched experts' weights and write
+        # h (SwiGLU) and y_perm (down) as their units finish: the same stream
+        # with writes in the same ratio, on the probe, gives their time at the
+        # achievable rate.
+        d, H, T, k = wl.d_model, wl.hidden, wl.tokens, wl.top_k
+        r_sw, w_sw = 4.0 * H * d * touched, 2.0 * T * k * H
+        r_dn, w_dn = 2.0 * H * d * touched, 2.0 * T * k * d
+        # (W1 and W3 rows hold d values, W2 rows H)
+        rates = hbm_stream_probe({"swiglu": (w_sw / r_sw, 2 * d), "down": (w_dn / r_dn, 2 * H)})
+        routed_ms = (r_sw / (rates["swiglu"][1] * 1e9) + r_dn / (rates["down"][1] * 1e9)) * 1e3
+        roof["stream_probe"] = {
+            "kind": "moe_probe_hbm_read_write over about 8 GiB, best of four passes: the read rate of "
+                    "an LDS-DMA stream of 256-row weight tiles with the stage's row length, 128 bytes of "
+                    "each row per step, that writes after each tile what the routed stage writes per "
+                    "tile of weights",
+            "swiglu_written_per_read": rates["swiglu"][0], "swiglu_read_gbs": rates["swiglu"][1],
+            "down_written_per_read": rates["down"][0], "down_read_gbs": rates["down"][1],
+            "routed_weight_bytes": r_sw + r_dn,
+            "routed_streams_ms_at_probe": routed_ms,
+        }
 
     line = {
         "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1,

@@ -9,6 +9,12 @@
 // - Non-temporal register loads: eight blocks of 256 threads per CU, each
 //   thread with eight 16-byte loads in flight, grid-strided -- the pattern of
 //   the register-path weight loads.
+// - LDS DMA in the grouped GEMM's weight pattern (128 bytes of each of 256
+//   weight rows per step, rows a given stride apart), fetched across unit
+//   boundaries, and after every unit a burst of 16-byte non-temporal stores
+//   to an output buffer -- a weight stream whose units each write their
+//   output tile, as the GEMM's do (the SwiGLU stage writes h, the down stage
+//   y), at a chosen ratio of written to read bytes.
 //
 // Each thread folds what it read into a per-thread value so that the loads
 // have a consumer.
@@ -63,6 +69,69 @@ __global__ __launch_bounds__(kThreads) void hbm_read_kernel(const unsigned char*
   if (acc == 0x9E3779B9u) sink[blockIdx.x] = acc;  // keeps the reads; practically never stored
 }
 
+// The read-and-write stream, in the grouped GEMM's weight pattern: a piece is
+// 256 rows of row_bytes, and a 32 KiB step reads 128 bytes of every row (one
+// 64-wide K-step of a 256-row weight tile), starting at column p mod (steps
+// per piece) and wrapping round, as units that run together start their K
+// loops at different steps.  A block's pieces (blockIdx.x, + gridDim.x, ...)
+// form one sequence of steps, fetched two steps ahead across piece
+// boundaries as the GEMM fetches across units; after the last step of piece p
+// the block writes out_chunks 16-byte chunks at out + p * out_chunks while the
+// next piece's first steps are in flight.
+__global__ __launch_bounds__(kThreads) void hbm_read_write_kernel(const unsigned char* __restrict__ buf,
+                                                                  int pieces, int row_bytes,
+                                                                  u32x4* __restrict__ out, int out_chunks,
+                                                                  uint32_t* __restrict__ sink) {
+  __shared__ u32x4 ring[kStages][kStep / 16];
+  const int tid = threadIdx.x, wave = tid >> 6;
+  constexpr int kRows = 256, kRowsPerPass = kThreads / 8;  // 8 lanes of 16 bytes per 128-byte row piece
+  const int steps = row_bytes / 128;
+  const int mine = static_cast<int>(blockIdx.x) < pieces
+                       ? (pieces - static_cast<int>(blockIdx.x) + static_cast<int>(gridDim.x) - 1) /
+                             static_cast<int>(gridDim.x)
+                       : 0;
+  const int total = mine * steps;
+  uint32_t acc = 0;
+  auto issue = [&](int g, int st) {
+    if (g >= total) g = total - 1;  // past the end: the last step again
+    const int i = g / steps;
+    const int64_t p = static_cast<int64_t>(blockIdx.x) + static_cast<int64_t>(i) * gridDim.x;
+    int col = g - i * steps + static_cast<int>(p % steps);
+    if (col >= steps) col -= steps;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<unsigned char*>(buf) + p * kRows * row_bytes, static_cast<short>(0), kRows * row_bytes,
+        0x00020000);
+#pragma unroll
+    for (int j = 0; j < kPasses; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)&ring[st][j * kThreads + wave * 64], 16,
+                                               (j * kRowsPerPass + tid / 8) * row_bytes + (tid % 8) * 16,
+                                               col * 128, 0, kPolicyNT);
+  };
+  if (total > 0) {
+    issue(0, 0);
+    issue(1, 1);
+    for (int g = 0; g < total; ++g) {
+      issue(g + 2, (g + 2) % kStages);
+      // all but the newest kPasses memory operations are done (stores count
+      // too), so step g + 1 has landed
+      __builtin_amdgcn_s_waitcnt(0x0F70 | kPasses);
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      acc ^= ring[g % kStages][tid][0];
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) before the stage is reused
+      __builtin_amdgcn_s_barrier();
+      if (g % steps == steps - 1) {
+        const int64_t p = static_cast<int64_t>(blockIdx.x) + static_cast<int64_t>(g / steps) * gridDim.x;
+        u32x4* dst = out + p * out_chunks;
+        for (int c = tid; c < out_chunks; c += kThreads)
+          __builtin_nontemporal_store(u32x4{acc, static_cast<uint32_t>(p), static_cast<uint32_t>(c), 0u}, dst + c);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): nothing in flight into the ring
+  }
+  if (acc == 0x9E3779B9u) sink[blockIdx.x] = acc;  // keeps the reads; practically never stored
+}
+
 constexpr int kNtThreads = 256;
 constexpr int kNtBlocksPerCu = 8;
 constexpr int kNtInFlight = 8;  // 16-byte loads per thread per trip
@@ -106,6 +175,25 @@ extern "C" int moe_probe_hbm_read(const void* buf, int64_t bytes, uint32_t* sink
   if (pieces > 0x7FFFFFFF) return 1;
   hipLaunchKernelGGL(hbm_read_kernel, dim3(cus), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
                      static_cast<const unsigned char*>(buf), static_cast<int>(pieces), sink);
+  return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+// The weight-pattern stream with writes: pieces of 256 rows of row_bytes,
+// out_per_piece bytes written after each (piece p's at out + p * out_per_piece).
+extern "C" int moe_probe_hbm_read_write(const void* buf, int64_t bytes, int64_t row_bytes, void* out,
+                                        int64_t out_per_piece, uint32_t* sink, void* stream) {
+  if (!buf || !out || !sink || row_bytes <= 0 || row_bytes % 128 != 0 || row_bytes > kPiece) return 1;
+  const int64_t piece = 256 * row_bytes;
+  if (bytes <= 0 || bytes % piece != 0 || out_per_piece <= 0 || out_per_piece > piece || out_per_piece % 16 != 0 ||
+      (reinterpret_cast<uintptr_t>(out) & 15) != 0)
+    return 1;
+  int cus = 0;
+  if (compute_units(&cus) != 0) return 1;
+  const int64_t pieces = bytes / piece;
+  if (pieces > 0x7FFFFFFF) return 1;
+  hipLaunchKernelGGL(hbm_read_write_kernel, dim3(cus), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const unsigned char*>(buf), static_cast<int>(pieces), static_cast<int>(row_bytes),
+                     static_cast<u32x4*>(out), static_cast<int>(out_per_piece / 16), sink);
   return hipGetLastError() == hipSuccess ? 0 : 1;
 }
 

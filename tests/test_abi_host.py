@@ -303,7 +303,7 @@ def test_probe_library_exports_its_declared_symbols():
         build.build()
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "moe_probe.h")).read(), flags=re.S)
     syms = sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
-    assert syms == ["moe_probe_hbm_read", "moe_probe_hbm_read_nt"]
+    assert syms == ["moe_probe_hbm_read", "moe_probe_hbm_read_nt", "moe_probe_hbm_read_write"]
     P = ctypes.CDLL(build.PROBE_LIB)
     L = moe.load()
     for name in syms:
@@ -325,6 +325,22 @@ def test_probe_rejects_unusable_sizes_before_launching():
         for buf, n, sink in ((fake(0), mib + 1, fake(1)), (fake(0), 0, fake(1)), (fake(0), -mib, fake(1)),
                              (None, mib, fake(1)), (fake(0), mib, None)):
             assert fn(buf, n, sink, None) == 1, name
+    fn = P.moe_probe_hbm_read_write
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                   ctypes.c_void_p, ctypes.c_void_p]
+    misaligned = ctypes.c_void_p(fake(2).value + 8)
+    for buf, n, row, out, per, sink in (
+            (fake(0), mib + 1, 4096, fake(2), 4096, fake(1)),        # not whole pieces
+            (fake(0), 0, 4096, fake(2), 4096, fake(1)),
+            (fake(0), mib, 14336, fake(2), 4096, fake(1)),           # 1 MiB is no whole 3.5 MiB piece
+            (fake(0), mib, 100, fake(2), 4096, fake(1)),             # row not a multiple of 128
+            (fake(0), 2 * mib * 256, 2 * mib, fake(2), 4096, fake(1)),  # row above 1 MiB
+            (None, mib, 4096, fake(2), 4096, fake(1)), (fake(0), mib, 4096, None, 4096, fake(1)),
+            (fake(0), mib, 4096, fake(2), 4096, None), (fake(0), mib, 4096, fake(2), 0, fake(1)),
+            (fake(0), mib, 4096, fake(2), 24, fake(1)), (fake(0), mib, 4096, fake(2), mib + 16, fake(1)),
+            (fake(0), mib, 4096, misaligned, 4096, fake(1))):
+        assert fn(buf, n, row, out, per, sink, None) == 1, (n, row, per)
 
 
 def mla_shape(**kw):

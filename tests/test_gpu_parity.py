@@ -207,6 +207,23 @@ def test_hbm_probe_reads_and_leaves_the_sink():
         assert fn(buf.data_ptr(), 16 << 20, sink.data_ptr(), None) == 0
         torch.cuda.synchronize()
         assert torch.all(sink == 7), name
+    fn = P.moe_probe_hbm_read_write
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                   ctypes.c_void_p, ctypes.c_void_p]
+    per = 4096
+    for row, n in ((4096, 16 << 20), (14336, 14 << 20)):
+        say(f"[probe] moe_probe_hbm_read_write over {n >> 20} MiB, rows of {row} bytes, {per} bytes per piece")
+        pieces = n // (256 * row)
+        out = torch.zeros(pieces * per // 4, dtype=torch.int32, device=DEV)
+        assert fn(buf.data_ptr(), n, row, out.data_ptr(), per, sink.data_ptr(), None) == 0
+        torch.cuda.synchronize()
+        assert torch.all(sink == 7)
+        # piece p wrote its 16-byte chunks c at p * per, each holding (.., p, c, 0)
+        words = out.view(pieces, per // 16, 4).cpu()
+        assert torch.equal(words[:, :, 1], torch.arange(pieces).view(-1, 1).expand(pieces, per // 16).int())
+        assert torch.equal(words[:, :, 2], torch.arange(per // 16).view(1, -1).expand(pieces, per // 16).int())
+        assert torch.all(words[:, :, 3] == 0)
 
 
 def test_permute_zero_tokens_writes_zero_loads():
