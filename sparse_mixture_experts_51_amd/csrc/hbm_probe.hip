@@ -1,6 +1,6 @@
 // hbm_probe.hip -- the achievable HBM read rate, for the measurements (a
 // library of its own, libmoe_probe.so, next to libmoe.so; not part of the
-// MoE interface).  Two ways of reading:
+// MoE interface).  Three ways of reading:
 //
 // - LDS DMA: one block per CU streams whole 1 MiB pieces of a buffer, 32 KiB
 //   per step, straight into a three-stage LDS ring, two steps ahead, with the
