@@ -228,6 +228,16 @@ def hbm_stream_probe(stages):
     return rates
 
 
+def routed_stream_stages(wl, touched):
+    """Per routed stage of moe_grouped_ffn: (weight bytes read, output bytes
+    written, weight row bytes).  SwiGLU reads W1 and W3 of the touched
+    experts (rows of d) and writes h (T*k rows of H); down reads W2 (rows of
+    H) and writes y_perm (T*k rows of d); bf16 throughout."""
+    d, H, T, k = wl.d_model, wl.hidden, wl.tokens, wl.top_k
+    return {"swiglu": (4.0 * H * d * touched, 2.0 * T * k * H, 2 * d),
+            "down": (2.0 * H * d * touched, 2.0 * T * k * d, 2 * H)}
+
+
 def ffn_algorithmic(wl, counts_per_layer):
     """Algorithmic FLOPs and HBM bytes of one moe_grouped_ffn call per layer:
     FLOPs = 6*d*H per routed row + 6*d*Hs per shared row; bytes = weights of
@@ -706,11 +716,9 @@ def main():
         # h (SwiGLU) and y_perm (down) as their units finish: the same stream
         # with writes in the same ratio, on the probe, gives their time at the
         # achievable rate.
-        d, H, T, k = wl.d_model, wl.hidden, wl.tokens, wl.top_k
-        r_sw, w_sw = 4.0 * H * d * touched, 2.0 * T * k * H
-        r_dn, w_dn = 2.0 * H * d * touched, 2.0 * T * k * d
-        # (W1 and W3 rows hold d values, W2 rows H)
-        rates = hbm_stream_probe({"swiglu": (w_sw / r_sw, 2 * d), "down": (w_dn / r_dn, 2 * H)})
+        stages = routed_stream_stages(wl, touched)
+        rates = hbm_stream_probe({key: (w / r, row) for key, (r, w, row) in stages.items()})
+        r_sw, r_dn = stages["swiglu"][0], stages["down"][0]
         routed_ms = (r_sw / (rates["swiglu"][1] * 1e9) + r_dn / (rates["down"][1] * 1e9)) * 1e3
         roof["stream_probe"] = {
             "kind": "moe_probe_hbm_read_write over about 8 GiB, best of four passes: the read rate of "

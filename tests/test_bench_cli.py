@@ -51,3 +51,24 @@ def test_training_steps_of_the_normalised_block_are_refused():
     assert r.returncode == 2
     assert "RMSNorm" in r.stderr
     assert r.stdout == ""
+
+
+def test_routed_stream_stages_match_the_layer_shapes():
+    """The read+write probe is run at each routed stage's own mix: written over
+    read bytes is T*k*H / (2*E*H*d) = T*k/(2*E*d) for SwiGLU (h against W1 and
+    W3) and T*k/(E*H) for down (y_perm against W2) when every expert has rows;
+    at the V3 prefill shape (4096 tokens, top-8, 256 experts, d 7168, H 2048)
+    that is 1/112 and 1/16."""
+    sys.path.insert(0, ROOT)
+    import bench
+    from sparse_mixture_experts_51_amd import workloads
+    wl = workloads.WORKLOADS["v3_prefill_4096"]
+    st = bench.routed_stream_stages(wl, wl.n_experts)
+    (r_sw, w_sw, row_sw), (r_dn, w_dn, row_dn) = st["swiglu"], st["down"]
+    assert w_sw / r_sw == 1 / 112 and w_dn / r_dn == 1 / 16
+    assert (row_sw, row_dn) == (2 * 7168, 2 * 2048)
+    # together the two stages read every routed weight once
+    assert r_sw + r_dn == 2.0 * 3 * 2048 * 7168 * 256
+    # fewer touched experts: reads shrink, writes (one row per routed token) do not
+    half = bench.routed_stream_stages(wl, 128)
+    assert half["swiglu"][0] == r_sw / 2 and half["swiglu"][1] == w_sw
