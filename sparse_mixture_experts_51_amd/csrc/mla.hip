@@ -612,6 +612,7 @@ template <int DC, int DR>
 __global__ __launch_bounds__(64) void mla_decode_mfma_kernel(MlaAttnArgs a, int batch, int nchunk) {
   constexpr int KST = (DC + DR + 15) / 16;  // k-steps of the scores
   constexpr int LST = DC / 16;              // of them, on the latent
+  static_assert(DR == 16 && DC % 16 == 0, "one rotary step of 16 after the latent steps");
   constexpr int NCT = DC / 32;              // latent tiles of P V
   constexpr int VROW = 64 + 8;              // staged V^T row (bf16)
   __shared__ uint16_t vt[DC * VROW];
@@ -637,20 +638,36 @@ __global__ __launch_bounds__(64) void mla_decode_mfma_kernel(MlaAttnArgs a, int 
     qf[t] = __builtin_bit_cast(bf16x8, v);
   }
   const int64_t cbase = static_cast<int64_t>(b) * a.max_len;
-  f32x16 sc[2];
+  // The chunk's cache rows by buffer loads, all issued before the first is
+  // used: the descriptors cover the rows 0..p of this sequence, so a key row
+  // past p reads zeros (its score is masked below), and whether a piece is
+  // latent or rotary is fixed per step.  (With a bounds branch per load the
+  // compiler waited for each load before the next.)
+  const __amdgpu_buffer_rsrc_t rkv = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.ckv + cbase * DC), static_cast<short>(0), (p + 1) * DC * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rkr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.ckr + cbase * DR), static_cast<short>(0), (p + 1) * DR * 2, 0x00020000);
+  u32x4 rows[2][KST];
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     const int s = c0 + 32 * half + fr;  // this lane's key row
-    const bool kv = s <= p;
+#pragma unroll
+    for (int t = 0; t < KST; ++t) {
+      const int k = 16 * t + 8 * fhalf;
+      if (t < LST)
+        rows[half][t] = __builtin_amdgcn_raw_buffer_load_b128(rkv, (s * DC + k) * 2, 0, 0);
+      else
+        rows[half][t] = __builtin_amdgcn_raw_buffer_load_b128(rkr, (s * DR + (k - DC)) * 2, 0, 0);
+    }
+  }
+  f32x16 sc[2];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
     sc[half] = f32x16{};
 #pragma unroll
     for (int t = 0; t < KST; ++t) {
       const int k = 16 * t + 8 * fhalf;
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (kv) {
-        if (k < DC) v = *reinterpret_cast<const u32x4*>(a.ckv + (cbase + s) * DC + k);
-        else if (k < DC + DR) v = *reinterpret_cast<const u32x4*>(a.ckr + (cbase + s) * DR + (k - DC));
-      }
+      const u32x4 v = rows[half][t];
       if (t < LST) {
         // V^T: latent column k + i, key 32 half + fr
 #pragma unroll

@@ -297,6 +297,11 @@ MLA_WORKLOADS = {
     "mla_decode_256x256": MlaWorkload(
         "mla_decode_256x256", 31, 256, 255, 256, True,
         description="MLA decode step of 256 sequences at position 255 (255 cached tokens each)"),
+    # A long context, where reading the 144-number-per-token cache dominates
+    # the step (256 x 4096 x 144 bf16 = 302 MB).
+    "mla_decode_256x4096": MlaWorkload(
+        "mla_decode_256x4096", 32, 256, 4095, 4096, True,
+        description="MLA decode step of 256 sequences at position 4095 (4095 cached tokens each)"),
 }
 
 

@@ -203,18 +203,25 @@ def test_prefill_full_size_sampled():
         check_cache(f32(bits(buf["cache_kv"]))[b], ref["cache_kv"][0], f"full.cache_kv[{b}]")
 
 
-def test_decode_full_size_sampled():
-    """mla_decode_256x256: 256 sequences with 255 cached tokens decode
-    position 255; the oracle on 3 sampled sequences with the GPU's cache."""
-    wl = workloads.MLA_WORKLOADS["mla_decode_256x256"]
+@pytest.mark.parametrize("name", ["mla_decode_256x256", "mla_decode_256x4096"])
+def test_decode_full_size_sampled(name):
+    """The decode workloads as the benchmark runs them (256 sequences decode
+    the position after their seq_len cached tokens: 255, or 4095 for the long
+    context); the oracle on 3 sampled sequences with the GPU's cache."""
+    wl = workloads.MLA_WORKLOADS[name]
+    say(f"[mla decode] {name}: prefill {wl.batch} x {wl.seq_len}, then one decode step")
     p = workloads.mla_params(wl, 0, DEV)
     x = workloads.mla_tokens(wl, wl.batch * wl.seq_len, 0, DEV)
     pshape = moe.MlaShape(wl.batch, wl.seq_len, wl.max_len)
     buf = moe.alloc_mla(pshape, DEV)
     moe.mla_prefill(pshape, x, p, buf["cache_kv"], buf["cache_kr"], buf["out"],
                     workspace=buf["workspace"])
-    kv0 = f32(bits(buf["cache_kv"])).astype(np.float64)
-    kr0 = f32(bits(buf["cache_kr"])).astype(np.float64)
+    del x
+    sample = np.array([0, 97, wl.batch - 1])
+    idx = torch.as_tensor(sample, device=DEV)
+    # the sampled sequences' caches before the step (only these go to the host)
+    kv0 = f32(bits(buf["cache_kv"][idx])).astype(np.float64)
+    kr0 = f32(bits(buf["cache_kr"][idx])).astype(np.float64)
     dshape = moe.MlaShape(wl.batch, 0, wl.max_len)
     dbuf = moe.alloc_mla(dshape, DEV, decode=True)
     pos = torch.full((wl.batch,), wl.seq_len, dtype=torch.int32, device=DEV)
@@ -222,10 +229,9 @@ def test_decode_full_size_sampled():
     moe.mla_decode(dshape, xd, pos, p, buf["cache_kv"], buf["cache_kr"], dbuf["out"],
                    workspace=dbuf["workspace"])
     torch.cuda.synchronize()
-    sample = np.array([0, 97, 255])
     ref = oracle.mla_decode(bits(xd)[sample], host_params(p), wl.n_heads,
-                            np.full(3, wl.seq_len), kv0[sample], kr0[sample])
-    check_close(f32(bits(dbuf["out"]))[sample], ref["out"], "decode_full.out")
+                            np.full(3, wl.seq_len), kv0, kr0)
+    check_close(f32(bits(dbuf["out"]))[sample], ref["out"], f"{name}.out")
 
 
 def test_decode_graph_replays_match_the_eager_call():
