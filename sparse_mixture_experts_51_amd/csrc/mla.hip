@@ -599,17 +599,19 @@ __global__ __launch_bounds__(64) void mla_decode_qlat_kernel(MlaAttnArgs a, int 
               bf16x2_bits(acc[6], acc[7])};
 }
 
-// Decode on the matrix cores: one wave per (sequence, chunk of 64 cached
-// positions) takes all heads at once (the 32 rows of the MFMA tile, heads
-// past nh zero).  Scores S = K Q^T over the latent and rotary key (K rows
-// read straight from the cache; positions past the token zeroed, so stale
-// cache contents never reach P V), softmax statistics per head over the
-// chunk, and O^T = V^T P^T with V^T the chunk's latents staged transposed in
-// LDS and P taken from the score registers as they stand (keys 4g..4g+3 and
-// 8+4g..8+4g+3 of each 16 for lane half g).  Writes the chunk's per-head max,
-// sum of weights and weighted latent sum, as mla_decode_partial_kernel does.
+// Decode on the matrix cores: one wave per (sequence, run of cps chunks of
+// 64 cached positions) takes all heads at once (the 32 rows of the MFMA
+// tile, heads past nh zero).  Per chunk: scores S = K Q^T over the latent and
+// rotary key (K rows read straight from the cache; positions past the token
+// zeroed, so stale cache contents never reach P V), and O^T += V^T P^T with
+// V^T the chunk's latents staged transposed in LDS and P taken from the
+// score registers as they stand (keys 4g..4g+3 and 8+4g..8+4g+3 of each 16
+// for lane half g); the softmax statistics run across the block's chunks,
+// the accumulated sums rescaled when the maximum grows.  Writes the run's
+// per-head max, sum of weights and weighted latent sum into partial slot
+// `split` (a slot per chunk in mla_decode_partial_kernel).
 template <int DC, int DR>
-__global__ __launch_bounds__(64) void mla_decode_mfma_kernel(MlaAttnArgs a, int batch, int nchunk) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void mla_decode_mfma_kernel(MlaAttnArgs a, int batch, int nchunk, int cps) {
   constexpr int KST = (DC + DR + 15) / 16;  // k-steps of the scores
   constexpr int LST = DC / 16;              // of them, on the latent
   static_assert(DR == 16 && DC % 16 == 0, "one rotary step of 16 after the latent steps");
@@ -618,11 +620,12 @@ __global__ __launch_bounds__(64) void mla_decode_mfma_kernel(MlaAttnArgs a, int 
   __shared__ uint16_t vt[DC * VROW];
   const int lane = threadIdx.x, fr = lane & 31, fhalf = lane >> 5;
   const int nh = a.nh, qw = a.dn + DR;
+  const int nsplit = (nchunk + cps - 1) / cps;
   const int xcd = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
-  const int b = xcd + kXcds * (j / nchunk), ci = j % nchunk;
+  const int b = xcd + kXcds * (j / nsplit), split = j % nsplit;
   if (b >= batch) return;
-  const int p = a.pos[b], c0 = 64 * ci;
-  if (p < 0 || p >= a.max_len || c0 > p) return;  // the combine reads only chunks with positions
+  const int p = a.pos[b], cfirst = split * cps;
+  if (p < 0 || p >= a.max_len || 64 * cfirst > p) return;  // the combine reads only runs with positions
   // the heads' fragments: head fr, k = 16 t + 8 fhalf .. +7 (latent, then rotary part)
   bf16x8 qf[KST];
   const bool hv = fr < nh;
@@ -638,7 +641,7 @@ __global__ __launch_bounds__(64) void mla_decode_mfma_kernel(MlaAttnArgs a, int 
     qf[t] = __builtin_bit_cast(bf16x8, v);
   }
   const int64_t cbase = static_cast<int64_t>(b) * a.max_len;
-  // The chunk's cache rows by buffer loads, all issued before the first is
+  // Cache rows by buffer loads, a chunk's all issued before the first is
   // used: the descriptors cover the rows 0..p of this sequence, so a key row
   // past p reads zeros (its score is masked below), and whether a piece is
   // latent or rotary is fixed per step.  (With a bounds branch per load the
@@ -647,87 +650,103 @@ __global__ __launch_bounds__(64) void mla_decode_mfma_kernel(MlaAttnArgs a, int 
       const_cast<uint16_t*>(a.ckv + cbase * DC), static_cast<short>(0), (p + 1) * DC * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t rkr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(a.ckr + cbase * DR), static_cast<short>(0), (p + 1) * DR * 2, 0x00020000);
-  u32x4 rows[2][KST];
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    const int s = c0 + 32 * half + fr;  // this lane's key row
-#pragma unroll
-    for (int t = 0; t < KST; ++t) {
-      const int k = 16 * t + 8 * fhalf;
-      if (t < LST)
-        rows[half][t] = __builtin_amdgcn_raw_buffer_load_b128(rkv, (s * DC + k) * 2, 0, 0);
-      else
-        rows[half][t] = __builtin_amdgcn_raw_buffer_load_b128(rkr, (s * DR + (k - DC)) * 2, 0, 0);
-    }
-  }
-  f32x16 sc[2];
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    sc[half] = f32x16{};
-#pragma unroll
-    for (int t = 0; t < KST; ++t) {
-      const int k = 16 * t + 8 * fhalf;
-      const u32x4 v = rows[half][t];
-      if (t < LST) {
-        // V^T: latent column k + i, key 32 half + fr
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          vt[(k + 2 * w) * VROW + 32 * half + fr] = static_cast<uint16_t>(v[w]);
-          vt[(k + 2 * w + 1) * VROW + 32 * half + fr] = static_cast<uint16_t>(v[w] >> 16);
-        }
-      }
-      sc[half] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v), qf[t], sc[half], 0, 0, 0);
-    }
-  }
-  // softmax statistics of head fr over the chunk (lanes fr and fr + 32 share it)
-  float mx = -INFINITY;
-#pragma unroll
-  for (int half = 0; half < 2; ++half)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = c0 + 32 * half + 8 * (i >> 2) + 4 * fhalf + (i & 3);
-      const float v = key <= p ? sc[half][i] * a.scale : -INFINITY;
-      sc[half][i] = v;
-      mx = fmaxf(mx, v);
-    }
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-  float ls = 0.0f;
-#pragma unroll
-  for (int half = 0; half < 2; ++half)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float e = __expf(sc[half][i] - mx);
-      sc[half][i] = e;
-      ls += e;
-    }
-  ls += __shfl_xor(ls, 32, 64);
-  __syncthreads();  // V^T staged
+  float mrun = -INFINITY, lrun = 0.0f;  // head fr's running max and sum of weights
   f32x16 oacc[NCT];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) oacc[ct] = f32x16{};
+  const int cend = cfirst + cps < nchunk ? cfirst + cps : nchunk;
+  for (int ci = cfirst; ci < cend && 64 * ci <= p; ++ci) {
+    const int c0 = 64 * ci;
+    if (ci > cfirst) __syncthreads();  // the previous chunk's P V has read V^T
+    u32x4 rows[2][KST];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    const f32x16& pv = sc[ks >> 1];
-    const int q0 = 2 * (ks & 1);
-    const bf16x8 pf = __builtin_bit_cast(
-        bf16x8, u32x4{bf16x2_bits(pv[4 * q0], pv[4 * q0 + 1]), bf16x2_bits(pv[4 * q0 + 2], pv[4 * q0 + 3]),
-                      bf16x2_bits(pv[4 * q0 + 4], pv[4 * q0 + 5]), bf16x2_bits(pv[4 * q0 + 6], pv[4 * q0 + 7])});
-    const int kb = 16 * ks + 4 * fhalf;
+    for (int half = 0; half < 2; ++half) {
+      const int s = c0 + 32 * half + fr;  // this lane's key row
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      const uint16_t* row = vt + (32 * ct + fr) * VROW;
-      const uint2 lo = *reinterpret_cast<const uint2*>(row + kb);
-      const uint2 hi = *reinterpret_cast<const uint2*>(row + kb + 8);
-      oacc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y}), pf, oacc[ct], 0, 0, 0);
+      for (int t = 0; t < KST; ++t) {
+        const int k = 16 * t + 8 * fhalf;
+        if (t < LST)
+          rows[half][t] = __builtin_amdgcn_raw_buffer_load_b128(rkv, (s * DC + k) * 2, 0, 0);
+        else
+          rows[half][t] = __builtin_amdgcn_raw_buffer_load_b128(rkr, (s * DR + (k - DC)) * 2, 0, 0);
+      }
+    }
+    f32x16 sc[2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      sc[half] = f32x16{};
+#pragma unroll
+      for (int t = 0; t < KST; ++t) {
+        const int k = 16 * t + 8 * fhalf;
+        const u32x4 v = rows[half][t];
+        if (t < LST) {
+          // V^T: latent column k + i, key 32 half + fr
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            vt[(k + 2 * w) * VROW + 32 * half + fr] = static_cast<uint16_t>(v[w]);
+            vt[(k + 2 * w + 1) * VROW + 32 * half + fr] = static_cast<uint16_t>(v[w] >> 16);
+          }
+        }
+        sc[half] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v), qf[t], sc[half], 0, 0, 0);
+      }
+    }
+    // softmax statistics of head fr (lanes fr and fr + 32 share it): the
+    // chunk's maximum joins the running one, and what was summed under the
+    // old maximum is rescaled to the new
+    float mx = -INFINITY;
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = c0 + 32 * half + 8 * (i >> 2) + 4 * fhalf + (i & 3);
+        const float v = key <= p ? sc[half][i] * a.scale : -INFINITY;
+        sc[half][i] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mnew = fmaxf(mrun, mx);  // finite: the chunk holds key c0 <= p
+    const float alpha = __expf(mrun - mnew);  // 0 for the first chunk
+    float ls = 0.0f;
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float e = __expf(sc[half][i] - mnew);
+        sc[half][i] = e;
+        ls += e;
+      }
+    ls += __shfl_xor(ls, 32, 64);
+    lrun = lrun * alpha + ls;
+    mrun = mnew;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[ct][i] *= alpha;
+    __syncthreads();  // V^T staged
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const f32x16& pv = sc[ks >> 1];
+      const int q0 = 2 * (ks & 1);
+      const bf16x8 pf = __builtin_bit_cast(
+          bf16x8, u32x4{bf16x2_bits(pv[4 * q0], pv[4 * q0 + 1]), bf16x2_bits(pv[4 * q0 + 2], pv[4 * q0 + 3]),
+                        bf16x2_bits(pv[4 * q0 + 4], pv[4 * q0 + 5]), bf16x2_bits(pv[4 * q0 + 6], pv[4 * q0 + 7])});
+      const int kb = 16 * ks + 4 * fhalf;
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        const uint16_t* row = vt + (32 * ct + fr) * VROW;
+        const uint2 lo = *reinterpret_cast<const uint2*>(row + kb);
+        const uint2 hi = *reinterpret_cast<const uint2*>(row + kb + 8);
+        oacc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y}), pf, oacc[ct], 0, 0, 0);
+      }
     }
   }
   // this lane: head fr, latent columns 32 ct + 8 q + 4 fhalf + e
   if (hv) {
-    float* part = a.part + ((static_cast<int64_t>(b) * nh + fr) * nchunk + ci) * (DC + 2);
+    float* part = a.part + ((static_cast<int64_t>(b) * nh + fr) * nchunk + split) * (DC + 2);
     if (fhalf == 0) {
-      part[0] = mx;
-      part[1] = ls;
+      part[0] = mrun;
+      part[1] = lrun;
     }
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
@@ -743,11 +762,12 @@ __global__ __launch_bounds__(64) void mla_decode_mfma_kernel(MlaAttnArgs a, int 
   }
 }
 
-// Merges a head's chunks (rescaled to the largest chunk maximum) and applies
-// W_uv[h] to the attended latent: one wave per (sequence, head).  Loads are
-// issued in batches (chunk statistics, then the chunks' latent sums, then
-// eight W_uv row pieces at a time) so that each phase costs one memory trip.
-__global__ __launch_bounds__(64) void mla_decode_combine_kernel(MlaAttnArgs a, int batch, int nchunk) {
+// Merges a head's partial slots (each covers cps chunks of 64 positions;
+// rescaled to the largest maximum) and applies W_uv[h] to the attended
+// latent: one wave per (sequence, head).  Loads are issued in batches (slot
+// statistics, then the slots' latent sums, then eight W_uv row pieces at a
+// time) so that each phase costs one memory trip.
+__global__ __launch_bounds__(64) void mla_decode_combine_kernel(MlaAttnArgs a, int batch, int nchunk, int cps) {
   __shared__ float olat[kMaxLat];
   __shared__ float wts[64];
   const int lane = threadIdx.x;
@@ -760,7 +780,7 @@ __global__ __launch_bounds__(64) void mla_decode_combine_kernel(MlaAttnArgs a, i
     for (int jj = lane; jj < dv; jj += 64) a.o[orow + jj] = 0;
     return;
   }
-  const int nc = p / 64 + 1;  // chunks with cached positions
+  const int nc = p / 64 / cps + 1;  // slots with cached positions
   const float* part = a.part + (static_cast<int64_t>(b) * nh + h) * nchunk * (dc + 2);
   // chunk statistics: chunk i in lane i (and i + 64, ...)
   float M = -INFINITY;
@@ -849,15 +869,23 @@ hipError_t launch_mla_attn_prefill(const MlaAttnArgs& a, int batch, hipStream_t 
 hipError_t launch_mla_attn_decode(const MlaAttnArgs& a, int batch, hipStream_t s) {
   const int nchunk = (a.max_len + 63) / 64;
   const bool mfma = a.dr == 16 && (a.dc == 128 || a.dc == 64);
+  int cps = 1;  // chunks per partial slot
   if (mfma) {
     hipLaunchKernelGGL(mla_decode_qlat_kernel, dim3(batch * a.nh), dim3(64), 0, s, a, batch);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int blocks = kXcds * ((batch + kXcds - 1) / kXcds) * nchunk;
+    // chunks per block: runs of up to 8 chunks while the grid keeps about 8
+    // blocks per CU (long contexts then write and merge 8x fewer partials)
+    const int64_t seqs = kXcds * ((static_cast<int64_t>(batch) + kXcds - 1) / kXcds);
+    const int64_t want = 8 * static_cast<int64_t>(device_cus());
+    while (cps < 8 && seqs * ((nchunk + 2 * cps - 1) / (2 * cps)) >= want) cps *= 2;
+    const int64_t blocks = seqs * ((nchunk + cps - 1) / cps);
     if (a.dc == 128)
-      hipLaunchKernelGGL((mla_decode_mfma_kernel<128, 16>), dim3(blocks), dim3(64), 0, s, a, batch, nchunk);
+      hipLaunchKernelGGL((mla_decode_mfma_kernel<128, 16>), dim3(static_cast<unsigned>(blocks)), dim3(64), 0, s, a,
+                         batch, nchunk, cps);
     else
-      hipLaunchKernelGGL((mla_decode_mfma_kernel<64, 16>), dim3(blocks), dim3(64), 0, s, a, batch, nchunk);
+      hipLaunchKernelGGL((mla_decode_mfma_kernel<64, 16>), dim3(static_cast<unsigned>(blocks)), dim3(64), 0, s, a,
+                         batch, nchunk, cps);
   } else {
     const int per_seq = a.nh * nchunk;
     const int blocks = kXcds * ((batch + kXcds - 1) / kXcds) * per_seq;
@@ -866,7 +894,7 @@ hipError_t launch_mla_attn_decode(const MlaAttnArgs& a, int batch, hipStream_t s
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(mla_decode_combine_kernel, dim3(batch * a.nh), dim3(64), 0, s, a, batch, nchunk);
+  hipLaunchKernelGGL(mla_decode_combine_kernel, dim3(batch * a.nh), dim3(64), 0, s, a, batch, nchunk, cps);
   return hipGetLastError();
 }
 

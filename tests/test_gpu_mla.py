@@ -234,6 +234,47 @@ def test_decode_full_size_sampled(name):
     check_close(f32(bits(dbuf["out"]))[sample], ref["out"], f"{name}.out")
 
 
+def test_decode_runs_of_chunks_at_ragged_positions():
+    """Enough sequences that a decode block takes a run of chunks (256
+    sequences x 16 chunks of 64 positions: two chunks per block), every
+    sequence's cache filled to 1023 rows, decode positions that start, end or
+    fall inside a run (0, 63, 64, 127, 128, 129, 700, 1023) and skipped
+    sequences (-1); the oracle on the sampled sequences with the GPU's cache
+    (rows past a position are stale and must be ignored)."""
+    wl = workloads.mla_custom(name="runs", batch=256, seq_len=1023, max_len=1024, cfg_id=52)
+    say(f"[mla decode] runs of chunks: {wl.batch} x {wl.max_len}")
+    p = workloads.mla_params(wl, 0, DEV)
+    x = workloads.mla_tokens(wl, wl.batch * wl.seq_len, 0, DEV)
+    pshape = moe.MlaShape(wl.batch, wl.seq_len, wl.max_len)
+    buf = moe.alloc_mla(pshape, DEV)
+    moe.mla_prefill(pshape, x, p, buf["cache_kv"], buf["cache_kr"], buf["out"],
+                    workspace=buf["workspace"])
+    del x
+    gen = torch.Generator().manual_seed(52)
+    pos = torch.randint(0, wl.max_len, (wl.batch,), generator=gen).to(torch.int32)
+    pos[::37] = -1
+    sample = np.array([3, 10, 40, 41, 90, 128, 200, 255])
+    for b, q in zip(sample, (0, 63, 64, 127, 128, 129, 700, 1023)):
+        pos[b] = q
+    pos_d = pos.to(DEV)
+    idx = torch.as_tensor(sample, device=DEV)
+    kv0 = f32(bits(buf["cache_kv"][idx])).astype(np.float64)
+    kr0 = f32(bits(buf["cache_kr"][idx])).astype(np.float64)
+    dshape = moe.MlaShape(wl.batch, 0, wl.max_len)
+    dbuf = moe.alloc_mla(dshape, DEV, decode=True)
+    xd = workloads.mla_tokens(wl, wl.batch, 1, DEV)
+    res = workloads.mla_residual(wl, wl.batch, DEV)
+    moe.mla_decode(dshape, xd, pos_d, p, buf["cache_kv"], buf["cache_kr"], dbuf["out"],
+                   residual=res, workspace=dbuf["workspace"])
+    torch.cuda.synchronize()
+    ref = oracle.mla_decode(bits(xd)[sample], host_params(p), wl.n_heads, pos.numpy()[sample],
+                            kv0, kr0, residual=bits(res)[sample])
+    check_close(f32(bits(dbuf["out"]))[sample], ref["out"], "runs.out")
+    # skipped sequences: output = residual
+    skipped = np.nonzero(pos.numpy() < 0)[0]
+    assert np.array_equal(bits(dbuf["out"])[skipped], bits(res)[skipped])
+
+
 def test_decode_graph_replays_match_the_eager_call():
     """mla_decode captured in a HIP graph (as bench.py replays it): every
     replay, with eager work and synchronisation between replays, gives the
